@@ -1,0 +1,181 @@
+// extern "C" entry points of libua.so: argument checks, workspace carving and
+// kernel dispatch.  No device memory is read or allocated here.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/ua.h"
+#include "ua_kernels.hpp"
+
+namespace {
+
+using ua::LayerArgs;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+ua_status check_dims(const ua_dims* d) {
+  if (!d) return UA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H_q < 1 || d->H_kv < 1 || d->d_model < 1 || d->gate_rank < 1) return UA_ERR_INVALID_ARG;
+  if (d->H_q % d->H_kv != 0) return UA_ERR_INVALID_ARG;
+  if (d->terms < 0 || d->terms > 7) return UA_ERR_INVALID_ARG;
+  if (d->dtype != UA_F32 && d->dtype != UA_BF16) return UA_ERR_INVALID_ARG;
+  if (d->y_dtype != UA_F32 && d->y_dtype != UA_BF16) return UA_ERR_INVALID_ARG;
+  if (!(d->rope_base > 1.0) || !isfinite(d->rope_base)) return UA_ERR_INVALID_ARG;
+  if (!(d->sm_scale >= 0.0f) || !isfinite(d->sm_scale)) return UA_ERR_INVALID_ARG;
+  if (d->d_head != 64 && d->d_head != 128) return UA_ERR_UNSUPPORTED;
+  const int G = d->H_q / d->H_kv;
+  if (G != 1 && G != 2 && G != 3 && G != 4 && G != 8) return UA_ERR_UNSUPPORTED;
+  if (d->H_kv > ua::kMaxHkv || d->gate_rank > ua::kMaxRank) return UA_ERR_UNSUPPORTED;
+  if (d->d_model % 8 != 0 || d->d_model > ua::kMaxDModel) return UA_ERR_UNSUPPORTED;
+  if ((int64_t)d->B * d->H_kv > ua::kMaxSeg) return UA_ERR_UNSUPPORTED;
+  return UA_OK;
+}
+
+ua_status check_cache(const ua_cache* c) {
+  if (!c) return UA_ERR_INVALID_ARG;
+  if (!c->K || !c->V || !c->logbias || !c->kgate || !c->seg_off || !c->seg_len || !c->seg_cap || !c->next_pos ||
+      !c->status)
+    return UA_ERR_INVALID_ARG;
+  if (!aligned(c->K, 16) || !aligned(c->V, 16) || !aligned(c->logbias, 4) || !aligned(c->kgate, 4) ||
+      !aligned(c->seg_off, 8) || !aligned(c->seg_len, 4) || !aligned(c->seg_cap, 4) || !aligned(c->next_pos, 4) ||
+      !aligned(c->status, 4))
+    return UA_ERR_INVALID_ARG;
+  if (c->total_slots < 1 || c->total_slots > ((int64_t)1 << 40)) return UA_ERR_INVALID_ARG;
+  return UA_OK;
+}
+
+ua_status check_params(const ua_params* p) {
+  if (!p || !p->W_dec || !p->b_dec || !p->W_dn || !p->W_up) return UA_ERR_INVALID_ARG;
+  if (!aligned(p->W_dec, 4) || !aligned(p->b_dec, 4) || !aligned(p->W_dn, 4) || !aligned(p->W_up, 4) ||
+      (p->b_up && !aligned(p->b_up, 4)))
+    return UA_ERR_INVALID_ARG;
+  return UA_OK;
+}
+
+ua_status check_tokens(const ua_tokens* t) {
+  if (!t || !t->q || !t->k || !t->v || !t->x) return UA_ERR_INVALID_ARG;
+  if (!aligned(t->q, 16) || !aligned(t->k, 16) || !aligned(t->v, 16) || !aligned(t->x, 16)) return UA_ERR_INVALID_ARG;
+  return UA_OK;
+}
+
+bool bad_log_p(float log_p) { return isnan(log_p) || log_p > 0.0f; }
+
+LayerArgs make_args(const ua_dims* d, const ua_params* p, const ua_cache* c, const ua_tokens* t, void* y) {
+  LayerArgs a{};
+  a.B = d->B;
+  a.H_q = d->H_q;
+  a.H_kv = d->H_kv;
+  a.d = d->d_head;
+  a.D_model = d->d_model;
+  a.r = d->gate_rank;
+  a.terms = d->terms;
+  a.bf16 = d->dtype == UA_BF16;
+  a.y_bf16 = d->y_dtype == UA_BF16;
+  a.scale = d->sm_scale != 0.0f ? d->sm_scale : (float)(1.0 / sqrt((double)d->d_head));
+  a.rope_base = d->rope_base;
+  if (p) {
+    a.W_dec = p->W_dec;
+    a.b_dec = p->b_dec;
+    a.W_dn = p->W_dn;
+    a.W_up = p->W_up;
+    a.b_up = p->b_up;
+  }
+  if (t) {
+    a.q = t->q;
+    a.k = t->k;
+    a.v = t->v;
+    a.x = t->x;
+  }
+  a.K = c->K;
+  a.V = c->V;
+  a.lam = c->logbias;
+  a.lk = c->kgate;
+  a.seg_off = c->seg_off;
+  a.seg_len = c->seg_len;
+  a.seg_cap = c->seg_cap;
+  a.next_pos = c->next_pos;
+  a.status = c->status;
+  a.total_slots = c->total_slots;
+  a.y = y;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ua_workspace_bytes(const ua_dims* dims, int32_t max_tokens_per_call, int64_t total_slots, int32_t max_seg_cap) {
+  if (check_dims(dims) != UA_OK || total_slots < 1 || max_tokens_per_call < 1 || max_seg_cap < 1) return 0;
+  ua_cache c{};
+  c.total_slots = total_slots;
+  LayerArgs a = make_args(dims, nullptr, &c, nullptr, nullptr);
+  size_t n = ua::decode_ws_bytes(a, ua::decode_tile_entries(a.d));
+  const size_t nc = ua::compact_ws_bytes(a);
+  if (nc > n) n = nc;
+  const size_t np = ua::prefill_ws_bytes(a, max_tokens_per_call, max_seg_cap);
+  if (np > n) n = np;
+  return n;
+}
+
+ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
+                         float log_p, void* y, void* ws, size_t ws_bytes, void* stream) {
+  ua_status s;
+  if ((s = check_dims(dims)) != UA_OK) return s;
+  if ((s = check_params(params)) != UA_OK) return s;
+  if ((s = check_cache(cache)) != UA_OK) return s;
+  if ((s = check_tokens(in)) != UA_OK) return s;
+  if (!y || !aligned(y, 16) || bad_log_p(log_p)) return UA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
+  LayerArgs a = make_args(dims, params, cache, in, y);
+  const int twg = ua::decode_tile_entries(a.d);
+  if (ws_bytes < ua::decode_ws_bytes(a, twg)) return UA_ERR_WORKSPACE;
+  ua::DecodeWs w = ua::decode_ws_carve(a, ws, twg);
+  const hipError_t e = ua::launch_decode(a, w, log_p, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
+                     int32_t n_tokens, void* y, void* ws, size_t ws_bytes, void* stream) {
+  ua_status s;
+  if ((s = check_dims(dims)) != UA_OK) return s;
+  if ((s = check_params(params)) != UA_OK) return s;
+  if ((s = check_cache(cache)) != UA_OK) return s;
+  if ((s = check_tokens(in)) != UA_OK) return s;
+  if (!y || !aligned(y, 16) || n_tokens < 1) return UA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
+  LayerArgs a = make_args(dims, params, cache, in, y);
+  if (ws_bytes < ua::prefill_ws_bytes(a, n_tokens, 1)) return UA_ERR_WORKSPACE;
+  const hipError_t e = ua::launch_prefill(a, n_tokens, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return UA_ERR_UNSUPPORTED;
+  if (e == hipErrorOutOfMemory) return UA_ERR_WORKSPACE;
+  return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+ua_status ua_compact(const ua_dims* dims, const ua_cache* cache, float log_p, int32_t* kept_idx, void* ws,
+                     size_t ws_bytes, void* stream) {
+  ua_status s;
+  if ((s = check_dims(dims)) != UA_OK) return s;
+  if ((s = check_cache(cache)) != UA_OK) return s;
+  if (bad_log_p(log_p)) return UA_ERR_INVALID_ARG;
+  if (kept_idx && !aligned(kept_idx, 4)) return UA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
+  LayerArgs a = make_args(dims, nullptr, cache, nullptr, nullptr);
+  if (ws_bytes < ua::compact_ws_bytes(a)) return UA_ERR_WORKSPACE;
+  const hipError_t e = ua::launch_compact(a, log_p, kept_idx, ws, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+const char* ua_status_string(int32_t status) {
+  switch (status) {
+    case UA_OK: return "ok";
+    case UA_ERR_INVALID_ARG: return "invalid argument";
+    case UA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case UA_ERR_WORKSPACE: return "workspace too small";
+    case UA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int32_t ua_abi_version(void) { return UA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,186 @@
+// Device primitives shared by the UA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ua {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Element load of an input that is either bf16 or fp32.
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (BF16) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[i]);
+  } else {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+}
+
+// Eight consecutive elements (16 B of bf16 or 32 B of fp32) at element index i
+// (i must be a multiple of 8 and the row 16-byte aligned).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* p, int64_t i, float (&out)[8]) {
+  if constexpr (BF16) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    out[0] = bf16_lo(w.x); out[1] = bf16_hi(w.x);
+    out[2] = bf16_lo(w.y); out[3] = bf16_hi(w.y);
+    out[4] = bf16_lo(w.z); out[5] = bf16_hi(w.z);
+    out[6] = bf16_lo(w.w); out[7] = bf16_hi(w.w);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions inside groups of 8 / 16 lanes (DPP, no LDS)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+// Sum over aligned groups of N lanes (N = 8 or 16); every lane gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 8 || N == 16, "group size");
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N == 16) v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_isum(int v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Exclusive scan of one int per thread across a block of NT threads (NT a
+// multiple of 64, at most 1024).  `scratch` holds NT/64 + 1 ints.  Returns the
+// exclusive prefix; *total receives the block total.  Contains barriers.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < NT / 64; ++w) {
+      const int t = scratch[w];
+      scratch[w] = run;
+      run += t;
+    }
+    scratch[NT / 64] = run;
+  }
+  __syncthreads();
+  const int excl = scratch[wave] + incl - v;
+  *total = scratch[NT / 64];
+  __syncthreads();
+  return excl;
+}
+
+// ---------------------------------------------------------------------------
+// UA scalar functions
+// ---------------------------------------------------------------------------
+// log(sigmoid(z)) = -(max(-z, 0) + log1p(exp(-|z|)))
+__device__ __forceinline__ float log_sigmoid(float z) {
+  return -(fmaxf(-z, 0.0f) + log1pf(expf(-fabsf(z))));
+}
+
+__device__ __forceinline__ float sigmoid(float z) {
+  const float e = expf(-fabsf(z));
+  const float r = 1.0f / (1.0f + e);
+  return z >= 0.0f ? r : e * r;
+}
+
+// Row (query-side) and column (key-side) parts of the mean in the pair term,
+// pre-scaled to log2 units and divided by the number of enabled terms.
+struct PairCoef {
+  float inv_n2;  // log2(e) / n_terms  (0 when no term is enabled)
+  float sim_w;   // 1 / n_terms if the similarity term is on, else 0
+  bool sim;
+  bool any;
+};
+
+__device__ __forceinline__ PairCoef pair_coef(int terms) {
+  PairCoef c;
+  const int n = (terms & 1) + ((terms >> 1) & 1) + ((terms >> 2) & 1);
+  c.any = n > 0;
+  c.sim = (terms & 4) != 0;
+  c.inv_n2 = n > 0 ? kLog2e / (float)n : 0.0f;
+  c.sim_w = (n > 0 && c.sim) ? 1.0f / (float)n : 0.0f;
+  return c;
+}
+
+// A = log(1 - exp(lambda)) <= 0 for lambda <= 0, given lambda in log2 units
+// (lam2 = lambda * log2 e).  Two hardware transcendentals:
+//  * lambda > -1/8:  1 - e^lambda = -lambda (1 + lambda/2 + lambda^2/6 + ...)
+//    so A = log(-lambda) + lambda/2 + lambda^2/24 (next term is O(lambda^4));
+//  * otherwise w = e^lambda <= 0.8825, y = fl(1 - w), and the rounding error of
+//    y is recovered exactly as (1 - y) - w (Fast2Sum), so
+//    A = log(y) + ((1 - y) - w) to first order.
+// lambda = -inf gives 0; lambda = 0 gives -inf.
+__device__ __forceinline__ float log1mexp2(float lam2) {
+  const float lam = lam2 * kLn2;
+  const bool small = lam > -0.125f;
+  const float w = __builtin_amdgcn_exp2f(lam2);
+  const float y = 1.0f - w;
+  const float err = (1.0f - y) - w;
+  const float arg = small ? -lam : y;
+  const float corr = small ? lam * (0.5f + lam * (1.0f / 24.0f)) : err;
+  return __builtin_amdgcn_logf(arg) * kLn2 + corr;
+}
+
+// Pair term from the similarity s and the pre-scaled row/column parts:
+// lam2 = row2 + col2 + sim_w * log2(min(s^2, 1)).
+__device__ __forceinline__ float pair_A(const PairCoef& c, float row2, float col2, float s) {
+  if (!c.any) return 0.0f;
+  float lam2 = row2 + col2;
+  if (c.sim) lam2 += c.sim_w * __builtin_amdgcn_logf(fminf(s * s, 1.0f));
+  return log1mexp2(lam2);
+}
+
+}  // namespace ua

@@ -1,0 +1,130 @@
+"""Device-side containers for one UA layer: weights, cache and workspace.
+
+Plain torch tensors on the GPU plus the ctypes structs that point at them.
+Every call goes straight to libua.so; nothing here computes.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def _dev(a, dtype, device) -> torch.Tensor:
+    return torch.as_tensor(np.ascontiguousarray(a)).to(device=device, dtype=dtype).contiguous()
+
+
+@dataclass
+class LayerShape:
+    B: int
+    H_q: int
+    H_kv: int
+    d: int
+    D: int
+    r: int = 16
+    bf16: bool = True
+    y_bf16: bool = False
+    terms: int = L.UA_TERMS_ALL
+    rope_base: float = 10000.0
+    sm_scale: float = 0.0
+
+    def dims(self) -> L.ua_dims:
+        return L.make_dims(self.B, self.H_q, self.H_kv, self.d, self.D, self.r, self.bf16, self.y_bf16, self.terms,
+                           self.rope_base, self.sm_scale)
+
+    @property
+    def dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.bf16 else torch.float32
+
+
+class DeviceWeights:
+    def __init__(self, shape: LayerShape, W_dec, b_dec, W_dn, W_up, b_up=None, device="cuda"):
+        dt = shape.dtype
+        self.W_dec = _dev(W_dec, dt, device)
+        self.b_dec = _dev(b_dec, torch.float32, device)
+        self.W_dn = _dev(W_dn, dt, device)
+        self.W_up = _dev(W_up, dt, device)
+        self.b_up = None if b_up is None else _dev(b_up, torch.float32, device)
+        self.params = L.make_params(self.W_dec, self.b_dec, self.W_dn, self.W_up, self.b_up)
+
+
+class DeviceCache:
+    """Slot-layout cache: K/V [slots, d], logbias/kgate [slots], segment table."""
+
+    def __init__(self, shape: LayerShape, K, V, logbias, kgate, seg_off, seg_len, seg_cap, next_pos, device="cuda"):
+        dt = shape.dtype
+        self.shape = shape
+        self.K = _dev(K, dt, device)
+        self.V = _dev(V, dt, device)
+        self.logbias = _dev(logbias, torch.float32, device)
+        self.kgate = _dev(kgate, torch.float32, device)
+        self.seg_off = _dev(seg_off, torch.int64, device)
+        self.seg_len = _dev(seg_len, torch.int32, device)
+        self.seg_cap = _dev(seg_cap, torch.int32, device)
+        self.next_pos = _dev(next_pos, torch.int32, device)
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.max_seg_cap = int(np.max(seg_cap))
+        self.struct = L.make_cache(self.K, self.V, self.logbias, self.kgate, self.seg_off, self.seg_len, self.seg_cap,
+                                   self.next_pos, self.status)
+
+    @property
+    def total_slots(self) -> int:
+        return int(self.K.shape[0])
+
+
+class Workspace:
+    def __init__(self, shape: LayerShape, cache: DeviceCache, max_tokens: int = 1, device="cuda"):
+        n = L.ua_workspace_bytes(shape.dims(), max_tokens, cache.total_slots, cache.max_seg_cap)
+        if n == 0:
+            raise L.UAError("ua_workspace_bytes rejected the layer shape")
+        self.nbytes = n
+        self.buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        self.ptr = (self.buf.data_ptr() + 255) // 256 * 256  # 256-byte aligned start
+
+
+class Layer:
+    """One UA layer bound to a cache: decode / prefill / compact through the C ABI."""
+
+    def __init__(self, shape: LayerShape, weights: DeviceWeights, cache: DeviceCache, max_tokens: int = 1,
+                 device="cuda"):
+        self.shape = shape
+        self.dims = shape.dims()
+        self.w = weights
+        self.cache = cache
+        self.ws = Workspace(shape, cache, max_tokens, device)
+        self.device = device
+
+    def _tokens(self, q, k, v, x):
+        dt = self.shape.dtype
+        ts = [t if (isinstance(t, torch.Tensor) and t.device.type == "cuda" and t.dtype == dt and t.is_contiguous())
+              else _dev(t, dt, self.device) for t in (q, k, v, x)]
+        return ts, L.make_tokens(*ts)
+
+    def decode_step(self, q, k, v, x, log_p: float, y: Optional[torch.Tensor] = None, stream=None):
+        s = self.shape
+        ts, tok = self._tokens(q, k, v, x)
+        if y is None:
+            y = torch.empty((s.B, s.H_q, s.d), dtype=torch.bfloat16 if s.y_bf16 else torch.float32,
+                            device=self.device)
+        L.ua_decode_step(self.dims, self.w.params, self.cache.struct, tok, log_p, y, self.ws.ptr, self.ws.nbytes,
+                         stream)
+        return y, ts
+
+    def prefill(self, q, k, v, x, y: Optional[torch.Tensor] = None, stream=None):
+        s = self.shape
+        n = q.shape[1]
+        ts, tok = self._tokens(q, k, v, x)
+        if y is None:
+            y = torch.empty((s.B, n, s.H_q, s.d), dtype=torch.bfloat16 if s.y_bf16 else torch.float32,
+                            device=self.device)
+        L.ua_prefill(self.dims, self.w.params, self.cache.struct, tok, n, y, self.ws.ptr, self.ws.nbytes, stream)
+        return y, ts
+
+    def compact(self, log_p: float, kept: Optional[torch.Tensor] = None, stream=None):
+        L.ua_compact(self.dims, self.cache.struct, log_p, kept, self.ws.ptr, self.ws.nbytes, stream)
+        return kept

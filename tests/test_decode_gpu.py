@@ -1,0 +1,111 @@
+"""Decode-step and compaction parity: HIP path (C ABI) vs the fp64 oracle.
+
+Every step compares y, the updated log-biases, the keep masks (borderline
+entries within 1e-4 of log p adopted from the GPU and counted), segment
+lengths, positions and status; every compaction compares the kept-index list
+exactly and the moved rows bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from ua_inputs import config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_pruning_amd import load
+
+    load()  # fails loudly if libua.so is missing
+
+
+def _run(cfg, steps, p, **kw):
+    from tests.harness import run_decode_parity
+
+    print(f"[decode parity] {cfg.name} B={cfg.B} steps={steps} p={p} {kw}", flush=True)
+    run = run_decode_parity(cfg, steps, math.log(p) if p > 0 else -math.inf, **kw)
+    print(f"  max |dy| {run.max_y_err:.2e}  max rel dLambda {run.max_lam_err:.2e}  borderline {run.borderline}  "
+          f"dead {sum(r.n_dead for r in run.reports)}", flush=True)
+    return run
+
+
+def test_tiny_decode_fp32_all_steps():
+    """Tiny fp32 layer, 256 steps from an empty cache, compaction every step."""
+    cfg = config("tiny-decode-f32")
+    run = _run(cfg, cfg.steps, cfg.p)
+    assert sum(r.n_dead for r in run.reports) > 0
+
+
+def test_1b_decode_full_batch():
+    cfg = config("1b-decode")
+    _run(cfg, 12, cfg.p)
+
+
+def test_1b_decode_small_many_steps():
+    cfg = config("1b-decode", B=2)
+    _run(cfg, 40, cfg.p)
+
+
+def test_3b_decode_full_batch():
+    cfg = config("3b-decode")
+    _run(cfg, 6, cfg.p)
+
+
+def test_ragged_decode_full_batch():
+    cfg = config("ragged-decode")
+    _run(cfg, 4, cfg.p)
+
+
+def test_ragged_decode_small_many_steps():
+    cfg = config("ragged-decode", B=4)
+    _run(cfg, 24, cfg.p)
+
+
+@pytest.mark.parametrize("terms", [0, 1, 2, 4, 3, 5, 6])
+def test_term_subsets(terms):
+    cfg = config("1b-decode", B=2)
+    _run(cfg, 4, cfg.p, terms=terms)
+
+
+def test_lazy_compaction_and_p0():
+    cfg = config("1b-decode", B=2)
+    _run(cfg, 10, cfg.p, compact_every=4)
+    _run(cfg, 6, 0.0, compact_every=0)
+
+
+@pytest.mark.parametrize("G,d", [(1, 64), (2, 128), (8, 64), (4, 128), (3, 64)])
+def test_group_and_head_dims(G, d):
+    cfg = config("1b-decode", B=2, H_kv=2, H_q=2 * G, d=d, D=256, len_mean=200.0, len_max=600)
+    _run(cfg, 6, cfg.p)
+
+
+def test_fp32_cache_128():
+    cfg = config("tiny-decode-f32", B=3, H_q=6, H_kv=2, d=128, D=128, steps=40)
+    _run(cfg, 40, 0.15)
+
+
+def test_segment_full_sets_status():
+    """Capacity reached: status bit 0 set, append skipped, output still formed."""
+    cfg = config("tiny-decode-f32", B=2, H_q=2, H_kv=1, steps=8)
+    from tests import harness as H
+    import ua_inputs as G
+
+    orig = G.make_cache
+
+    def small(cfg_, w_, seed=0, extra=None):
+        c = orig(cfg_, w_, seed, extra=5)
+        return c
+
+    H.make_cache = small
+    try:
+        run = _run(cfg, 20, 0.0, compact_every=0)
+    finally:
+        H.make_cache = orig
+    assert len(run.reports) == 20
