@@ -1,0 +1,284 @@
+"""Benchmark of the UA hot path on one MI355X.
+
+Default workload: the 1B-shape decode layer (hidden 2048, 32 query / 8 KV
+heads, head dim 64, B = 8) on a pre-populated pruned cache of nominal length
+4096 (~10x compressed), one decode step + eviction + in-place compaction per
+layer instance per step, p = 0.15.  The decode working set of one layer
+(~7 MB) fits in the 256 MB Infinity Cache, so a step runs a ring of R
+independent layer instances (distinct caches, >= 1 GiB in total), as an
+R-layer model would, and throughput is counted per layer: value = B * R /
+step time.  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  See the design doc for the roofline bytes and the
+oracle baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "kv_cache_pruning_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name: str, per_launch_alg: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
+    p = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# decode workloads
+# ---------------------------------------------------------------------------
+def bench_decode(args):
+    import torch
+
+    from kv_cache_pruning_amd.layer import DeviceCache, DeviceWeights, Layer, LayerShape, Workspace
+    from ua_inputs import config, make_cache, make_step_inputs, make_weights
+
+    cfg = config(args.workload)
+    assert args.warmup + args.steps <= cfg.steps, "more steps than the cache has room for"
+    log_p = math.log(cfg.p)
+    shape = LayerShape(B=cfg.B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, D=cfg.D, r=cfg.r, bf16=cfg.bf16)
+    w = make_weights(cfg, 0)
+    dw = DeviceWeights(shape, w.W_dec, w.b_dec, w.W_dn, w.W_up, w.b_up)
+    elem = 2 if cfg.bf16 else 4
+    entry_bytes = 2 * cfg.d * elem + 12  # K + V + logbias read/write + key gate
+
+    # ring of layer instances
+    t0 = time.time()
+    caches, live0 = [], 0
+    R = args.ring
+    target = args.ring_bytes
+    i = 0
+    while True:
+        ci = make_cache(cfg, w, seed=i)
+        caches.append(DeviceCache(shape, ci.K, ci.V, ci.lam, ci.lk, ci.seg_off, ci.seg_len, ci.seg_cap,
+                                  ci.next_pos))
+        live0 += int(ci.seg_len.sum()) * entry_bytes
+        i += 1
+        if (R and i >= R) or (not R and live0 >= target) or i >= 4096:
+            break
+    R = len(caches)
+    # one workspace for the whole ring: the calls are serialised on one stream
+    ws = Workspace(shape, max(caches, key=lambda c: c.total_slots), 1)
+    insts = [Layer(shape, dw, c, workspace=ws) for c in caches]
+    nsteps = args.warmup + args.steps
+    toks = []
+    for s in range(nsteps):
+        inp = make_step_inputs(cfg, s, 1, 0)
+        dt = shape.dtype
+        toks.append([torch.from_numpy(np.ascontiguousarray(a[:, 0])).to("cuda", dt) for a in (inp.q, inp.k, inp.v, inp.x)])
+    y = torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    # snapshot for the untimed replay that counts algorithmic bytes
+    snap = [(c.K.clone(), c.V.clone(), c.logbias.clone(), c.kgate.clone(), c.seg_len.clone(), c.next_pos.clone())
+            for c in caches]
+
+    def run_step(s, events=None):
+        q, k, v, x = toks[s]
+        for j, L_ in enumerate(insts):
+            if events is not None:
+                events[j][0].record()
+            L_.decode_step(q, k, v, x, log_p, y=y)
+            if events is not None:
+                events[j][1].record()
+            L_.compact(log_p)
+            if events is not None:
+                events[j][2].record()
+
+    for s in range(args.warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in insts] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        run_step(args.warmup + s, ev[s])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    dec_ms = [e[0].elapsed_time(e[1]) for es in ev for e in es]
+    cmp_ms = [e[1].elapsed_time(e[2]) for es in ev for e in es]
+    st = int(sum(int(c.status.item()) for c in caches))
+
+    # untimed replay: live entries scanned per decode, moved entries per compaction
+    for c, sn in zip(caches, snap):
+        c.K.copy_(sn[0]); c.V.copy_(sn[1]); c.logbias.copy_(sn[2]); c.kgate.copy_(sn[3])
+        c.seg_len.copy_(sn[4]); c.next_pos.copy_(sn[5])
+    torch.cuda.synchronize()
+    scanned = 0
+    moved = 0
+    cmp_scanned = 0
+    for s in range(nsteps):
+        q, k, v, x = toks[s]
+        for L_ in insts:
+            if s >= args.warmup:
+                scanned += int(L_.cache.seg_len.sum().item())
+            L_.decode_step(q, k, v, x, log_p, y=y)
+            if s >= args.warmup:
+                lens = L_.cache.seg_len.cpu().numpy()
+                offs = L_.cache.seg_off.cpu().numpy()
+                lam = L_.cache.logbias.cpu().numpy()
+                for o, n in zip(offs, lens):
+                    seg = lam[o : o + n]
+                    dead = np.flatnonzero(seg < log_p)
+                    cmp_scanned += int(n)
+                    if dead.size:
+                        f = dead[0]
+                        moved += int(np.count_nonzero(seg[f:] >= log_p))
+            L_.compact(log_p)
+    torch.cuda.synchronize()
+
+    n_calls = args.steps * R
+    S = cfg.B * cfg.H_kv
+    per_step_extra = (S * (2 * cfg.d * elem + 8)  # appends
+                      + cfg.B * (cfg.H_q + 2 * cfg.H_kv) * cfg.d * elem + cfg.B * cfg.D * elem  # q, k, v, x
+                      + cfg.B * cfg.H_q * cfg.d * 4  # y (fp32)
+                      + (cfg.D * (3 * cfg.H_kv + cfg.r) + cfg.r * cfg.H_q * cfg.d) * elem)  # gate weights
+    dec_bytes = scanned * entry_bytes + n_calls * per_step_extra
+    cmp_bytes = cmp_scanned * 4 + moved * 2 * (2 * cfg.d * elem + 8)
+    dec_avg_ms = float(np.mean(dec_ms))
+    cmp_avg_ms = float(np.mean(cmp_ms))
+    achieved = dec_bytes / n_calls / (dec_avg_ms * 1e-3) / 1e9
+    ms_per_step = total_ms / args.steps
+    tokens = cfg.B * R  # layer-tokens per step
+    value = tokens / (ms_per_step * 1e-3)
+
+    out = {
+        "metric": "UA decode tokens/s + achieved HBM GB/s on pruned KV cache; prefill tok/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: UA decode layer B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} "
+                        f"D={cfg.D}, pruned cache nominal {cfg.nominal} (~{cfg.nominal / cfg.len_mean:.0f}x), "
+                        f"p={cfg.p}, decode + compaction every step, ring of {R} layer instances",
+            "global_batch": cfg.B,
+            "ring_instances": R,
+            "tokens_per_step": tokens,
+            "storage": "bf16" if cfg.bf16 else "f32",
+            "live_entries_per_layer_step": scanned / n_calls,
+            "decode_call_us": dec_avg_ms * 1e3,
+            "compact_call_us": cmp_avg_ms * 1e3,
+            "decode_gbs": achieved,
+            "compact_gbs": cmp_bytes / n_calls / (cmp_avg_ms * 1e-3) / 1e9,
+            "step_gbs": (dec_bytes + cmp_bytes) / (total_ms * 1e-3) / 1e9,
+            "status": st,
+            "setup_s": setup_s,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": load_traffic(f"decode_{cfg.name}", dec_bytes / n_calls),
+            "kernel": "ua_decode_step (decode_pre + decode_main)",
+            "alg_bytes_per_launch": dec_bytes / n_calls,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(cfg, args.cpu_seconds)
+    return out
+
+
+def cpu_baseline_decode(cfg, budget_s: float):
+    """The fp64 oracle, as is, on the first steps of the same workload (instance 0)."""
+    import oracle as U
+    from tests.harness import oracle_cache, oracle_dims, oracle_params
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    od, op, oc = oracle_dims(cfg), oracle_params(w), oracle_cache(cfg, c)
+    log_p = math.log(cfg.p)
+    t0 = time.time()
+    n = 0
+    while n < cfg.steps and time.time() - t0 < budget_s:
+        inp = make_step_inputs(cfg, n, 1, 0)
+        U.decode_step(od, op, oc, inp.q[:, 0], inp.k[:, 0], inp.v[:, 0], inp.x[:, 0], log_p)
+        U.compact(oc, log_p)
+        n += 1
+    dt = time.time() - t0
+    return {"value": cfg.B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{cfg.name} instance 0, first {n} decode+compaction steps ({dt:.1f} s, numpy fp64, "
+                      f"one process)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="1b-decode")
+    ap.add_argument("--ring", type=int, default=0, help="layer instances (0: enough for --ring-bytes)")
+    ap.add_argument("--ring-bytes", type=float, default=1.0 * 2**30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a "
+              f"single MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from kv_cache_pruning_amd import load
+
+    load()
+    if args.workload.endswith("prefill"):
+        out = bench_prefill(args)
+    else:
+        out = bench_decode(args)
+    print(json.dumps(out), flush=True)
+
+
+def bench_prefill(args):
+    raise SystemExit("prefill benchmark not built yet")
+
+
+if __name__ == "__main__":
+    main()

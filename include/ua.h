@@ -165,10 +165,19 @@ typedef struct ua_cache {
  * ua_decode_step, ua_prefill with up to max_tokens_per_call tokens, and
  * ua_compact, for a cache of total_slots slots whose largest segment has
  * max_seg_cap slots.  Returns 0 for invalid dims.  The workspace must be
- * 256-byte aligned; its contents need no initialisation and are scratch
- * between calls.
+ * 256-byte aligned.  Its first part holds counters and flags the kernels use
+ * to coordinate workgroups: the whole workspace must be zero-filled once
+ * before its first use (ua_workspace_init, or any zero fill), and every call
+ * leaves that part zero again.  Calls that share a workspace must be ordered
+ * on one stream; the rest of the workspace is scratch between calls.
  */
 size_t ua_workspace_bytes(const ua_dims* dims, int32_t max_tokens_per_call, int64_t total_slots, int32_t max_seg_cap);
+
+/*
+ * Zero-fill ws_bytes bytes of a workspace on `stream` (a device kernel; no
+ * memset node, so it may also be captured).  ws must be 256-byte aligned.
+ */
+ua_status ua_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /*
  * One decode step: one new token per sequence (paperlayer.ai section 4.2;

@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     UAError,
     load,
     ua_workspace_bytes,
+    ua_workspace_init,
     ua_decode_step,
     ua_prefill,
     ua_compact,

@@ -23,6 +23,7 @@ UA_STATUS_SEGMENT_FULL, UA_STATUS_WAIT_TIMEOUT = 1, 2
 
 EXPORTS = (
     "ua_workspace_bytes",
+    "ua_workspace_init",
     "ua_decode_step",
     "ua_prefill",
     "ua_compact",
@@ -92,6 +93,8 @@ def load(path: Optional[str] = None) -> C.CDLL:
     P = C.POINTER
     lib.ua_workspace_bytes.argtypes = [P(ua_dims), C.c_int32, C.c_int64, C.c_int32]
     lib.ua_workspace_bytes.restype = C.c_size_t
+    lib.ua_workspace_init.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.ua_workspace_init.restype = C.c_int
     lib.ua_decode_step.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_float, C.c_void_p,
                                    C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_decode_step.restype = C.c_int
@@ -119,6 +122,10 @@ def _check(code: int, what: str) -> None:
 # ---------------------------------------------------------------------------
 def ua_workspace_bytes(dims: ua_dims, max_tokens_per_call: int, total_slots: int, max_seg_cap: int) -> int:
     return int(load().ua_workspace_bytes(C.byref(dims), max_tokens_per_call, total_slots, max_seg_cap))
+
+
+def ua_workspace_init(ws, ws_bytes: int, stream=None) -> None:
+    _check(load().ua_workspace_init(_ptr(ws), ws_bytes, _stream(stream)), "ua_workspace_init")
 
 
 def ua_decode_step(dims, params, cache, tokens, log_p: float, y, ws, ws_bytes: int, stream=None) -> None:

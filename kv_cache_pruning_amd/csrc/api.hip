@@ -110,11 +110,15 @@ size_t ua_workspace_bytes(const ua_dims* dims, int32_t max_tokens_per_call, int6
   c.total_slots = total_slots;
   LayerArgs a = make_args(dims, nullptr, &c, nullptr, nullptr);
   size_t n = ua::decode_ws_bytes(a, ua::decode_tile_entries(a.d));
-  const size_t nc = ua::compact_ws_bytes(a);
-  if (nc > n) n = nc;
   const size_t np = ua::prefill_ws_bytes(a, max_tokens_per_call, max_seg_cap);
   if (np > n) n = np;
-  return n;
+  return ua::control_bytes(a) + n;
+}
+
+ua_status ua_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || !aligned(ws, 256) || ws_bytes == 0) return UA_ERR_INVALID_ARG;
+  const hipError_t e = ua::launch_fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
 ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
@@ -128,8 +132,10 @@ ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, params, cache, in, y);
   const int twg = ua::decode_tile_entries(a.d);
-  if (ws_bytes < ua::decode_ws_bytes(a, twg)) return UA_ERR_WORKSPACE;
-  ua::DecodeWs w = ua::decode_ws_carve(a, ws, twg);
+  const size_t cb = ua::control_bytes(a);
+  if (ws_bytes < cb + ua::decode_ws_bytes(a, twg)) return UA_ERR_WORKSPACE;
+  const ua::Control ctl = ua::control_carve(a, ws);
+  ua::DecodeWs w = ua::decode_ws_carve(a, ctl, reinterpret_cast<char*>(ws) + cb, twg);
   const hipError_t e = ua::launch_decode(a, w, log_p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
@@ -144,8 +150,11 @@ ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cach
   if (!y || !aligned(y, 16) || n_tokens < 1) return UA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, params, cache, in, y);
-  if (ws_bytes < ua::prefill_ws_bytes(a, n_tokens, 1)) return UA_ERR_WORKSPACE;
-  const hipError_t e = ua::launch_prefill(a, n_tokens, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+  const size_t cb = ua::control_bytes(a);
+  if (ws_bytes < cb) return UA_ERR_WORKSPACE;
+  const ua::Control ctl = ua::control_carve(a, ws);
+  const hipError_t e = ua::launch_prefill(a, ctl, n_tokens, 0, reinterpret_cast<char*>(ws) + cb, ws_bytes - cb,
+                                          reinterpret_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return UA_ERR_UNSUPPORTED;
   if (e == hipErrorOutOfMemory) return UA_ERR_WORKSPACE;
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
@@ -160,8 +169,9 @@ ua_status ua_compact(const ua_dims* dims, const ua_cache* cache, float log_p, in
   if (kept_idx && !aligned(kept_idx, 4)) return UA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, nullptr, cache, nullptr, nullptr);
-  if (ws_bytes < ua::compact_ws_bytes(a)) return UA_ERR_WORKSPACE;
-  const hipError_t e = ua::launch_compact(a, log_p, kept_idx, ws, reinterpret_cast<hipStream_t>(stream));
+  if (ws_bytes < ua::control_bytes(a)) return UA_ERR_WORKSPACE;
+  const ua::Control ctl = ua::control_carve(a, ws);
+  const hipError_t e = ua::launch_compact(a, ctl, log_p, kept_idx, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 

@@ -1,24 +1,27 @@
-// Stable in-place compaction of the pruned cache (gfx950).
+// Stable in-place compaction of the pruned cache (gfx950), one kernel.
 //
 // An entry whose log-bias fell below log p is evicted and never returns
 // (paperlayer.ai summary, section 4.2; ai4snews page after Figure 1).  Each
 // segment (one sequence, one KV head) is cut into chunks of CH entries and
-// every chunk gets its own workgroup, so long segments spread over many CUs:
+// every chunk gets its own workgroup, so long segments spread over many CUs.
 //
-//  compact_count -- per chunk: number of live entries (logbias >= log p);
-//                   also clears the per-call flags and the ticket counter.
-//  compact_move  -- workgroups take chunk ids from an atomic ticket, so a
-//                   chunk's predecessors in its segment are always running or
-//                   done.  A chunk's destination is the sum of its
-//                   predecessors' live counts.  It loads its live rows into
-//                   registers, publishes "loaded", waits until every earlier
-//                   chunk whose source range its destination overlaps has
-//                   loaded too, then stores.  Destinations never exceed
-//                   sources, so these waits are the only hazard.  Chunks with
-//                   no dead entry at or before them move nothing.
-//
-// Live flags come from a wave ballot; ranks inside a wave from mbcnt; the
-// block prefix from an LDS scan.
+// Workgroups take chunk ids from an atomic ticket, so a chunk's predecessors
+// in its segment always started earlier (every wait below is on a lower id,
+// which guarantees progress).  Per chunk:
+//  1. load the chunk's log-biases, count the live ones (ballot), publish the
+//     count;
+//  2. decoupled look-back over the predecessors' published counts/prefixes
+//     (one wave reads up to 64 at once) gives the destination P of the
+//     chunk's first survivor; publish the inclusive prefix;
+//  3. if anything moves (P differs from the chunk start, or the chunk has a
+//     hole): load the surviving rows into registers, publish "loaded", wait
+//     until every earlier chunk whose rows the destination range overwrites
+//     has loaded its own, then store.  Destinations never exceed sources, so
+//     this is the only hazard.
+// The last chunk of a segment to arrive writes the new length and clears the
+// segment's flags; the last workgroup overall clears the ticket.  Flags use
+// relaxed agent-scope atomics (coherent across XCDs without cache-wide
+// maintenance); waits are bounded and report a timeout in status bit 1.
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -34,259 +37,246 @@ struct CompactShape {
   static constexpr int PPT = CH * P16 / kCompactThreads;               // pieces per thread
 };
 
-struct CompactWs {
-  int* live;      // [max_chunks] live entries per chunk
-  int* loaded;    // [max_chunks] 1 once the chunk's rows are in registers
-  int* done;      // [S] finished chunks per segment
-  int* ticket;    // [1]
-  int max_chunks;
-};
-
-static int compact_max_chunks(const LayerArgs& a, int ch) {
-  return (int)(a.total_slots / ch + (int64_t)a.B * a.H_kv + 1);
+__device__ __forceinline__ int ldi_coh(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sti_coh2(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int addi_coh(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-static int compact_ch(const LayerArgs& a) {
-  const int rb = a.d * (a.bf16 ? 2 : 4);
-  return rb <= 128 ? 256 : (rb <= 256 ? 128 : 64);
-}
-
-size_t compact_ws_bytes(const LayerArgs& a) {
-  const int mc = compact_max_chunks(a, compact_ch(a));
-  const int64_t S = (int64_t)a.B * a.H_kv;
-  return align_up(sizeof(int) * mc, 256) * 2 + align_up(sizeof(int) * S, 256) + 256;
-}
-
-static CompactWs compact_carve(const LayerArgs& a, void* ws) {
-  const int mc = compact_max_chunks(a, compact_ch(a));
-  const int64_t S = (int64_t)a.B * a.H_kv;
-  char* p = reinterpret_cast<char*>(ws);
-  CompactWs w;
-  w.live = reinterpret_cast<int*>(p);
-  p += align_up(sizeof(int) * mc, 256);
-  w.loaded = reinterpret_cast<int*>(p);
-  p += align_up(sizeof(int) * mc, 256);
-  w.done = reinterpret_cast<int*>(p);
-  p += align_up(sizeof(int) * S, 256);
-  w.ticket = reinterpret_cast<int*>(p);
-  w.max_chunks = mc;
-  return w;
-}
-
-// Map a flat chunk id to (segment, chunk in segment) from the static
-// capacities: chunks of segment s are ids [first_s, first_s + ceil(cap_s/CH)).
-// Returns false if id is past the last chunk.  Block-wide (barriers inside).
-struct ChunkPos {
-  int seg, c, first, nch;
-};
-
-__device__ bool map_chunk(const int32_t* seg_cap, int S, int ch, int id, ChunkPos* out, int* s_scan, int* s_info) {
-  const int per = (S + kCompactThreads - 1) / kCompactThreads;
-  const int sb = threadIdx.x * per;
-  const int se = min(S, sb + per);
-  int mine = 0;
-  for (int s = sb; s < se; ++s) mine += max(1, (seg_cap[s] + ch - 1) / ch);
-  int total;
-  const int excl = block_exclusive_scan<kCompactThreads>(mine, s_scan, &total);
-  if (id >= total) return false;
-  int run = excl;
-  for (int s = sb; s < se; ++s) {
-    const int n = max(1, (seg_cap[s] + ch - 1) / ch);
-    if (id >= run && id < run + n) {
-      s_info[0] = s;
-      s_info[1] = id - run;
-      s_info[2] = run;
-      s_info[3] = n;
-    }
-    run += n;
-  }
-  __syncthreads();
-  out->seg = s_info[0];
-  out->c = s_info[1];
-  out->first = s_info[2];
-  out->nch = s_info[3];
-  return true;
-}
-
-template <int CH>
-__global__ __launch_bounds__(kCompactThreads) void compact_count(LayerArgs a, CompactWs w, float tau) {
-  __shared__ int s_scan[kCompactThreads / 64 + 1];
-  __shared__ int s_info[4];
-  __shared__ int s_cnt[kCompactThreads / 64];
-  const int S = a.B * a.H_kv;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *w.ticket = 0;
-  if (blockIdx.x < S && threadIdx.x == 0) w.done[blockIdx.x] = 0;
-  ChunkPos cp;
-  if (!map_chunk(a.seg_cap, S, CH, blockIdx.x, &cp, s_scan, s_info)) return;
-  const int len = a.seg_len[cp.seg];
-  const int64_t off = a.seg_off[cp.seg];
-  const int j0 = cp.c * CH;
-  int n = 0;
-  for (int t = threadIdx.x; t < CH; t += kCompactThreads) {
-    const int j = j0 + t;
-    if (j < len && a.lam[off + j] >= tau) ++n;
-  }
-  n = wave_isum(n);
-  if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = n;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int tot = 0;
-    for (int i = 0; i < kCompactThreads / 64; ++i) tot += s_cnt[i];
-    w.live[blockIdx.x] = tot;
-    w.loaded[blockIdx.x] = 0;
-  }
-}
-
-__device__ __forceinline__ int ld_acquire(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
+constexpr int kSpinLimit = 1 << 22;
 
 template <int RB>
-__global__ __launch_bounds__(kCompactThreads) void compact_move(LayerArgs a, CompactWs w, float tau, int32_t* kept) {
+__global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, Control ctl, float tau, int32_t* kept) {
   using Sh = CompactShape<RB>;
   constexpr int CH = Sh::CH, P16 = Sh::P16, PPT = Sh::PPT;
   __shared__ int s_scan[kCompactThreads / 64 + 1];
   __shared__ int s_info[4];
   __shared__ int s_ticket;
   __shared__ int s_src[CH];
+  __shared__ int s_cnt[kCompactThreads / 64];
   __shared__ int s_prefix;
   __shared__ int s_last;
   const int S = a.B * a.H_kv;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
 
-  if (tid == 0) s_ticket = atomicAdd(w.ticket, 1);
+  if (tid == 0) s_ticket = addi_coh(&ctl.cmp_glob[0], 1);
   __syncthreads();
   const int id = s_ticket;
-  ChunkPos cp;
-  if (!map_chunk(a.seg_cap, S, CH, id, &cp, s_scan, s_info)) return;
-  const int seg = cp.seg;
-  const int len = a.seg_len[seg];
-  const int64_t off = a.seg_off[seg];
-  const int j0 = cp.c * CH;
-  const int nlive = w.live[id];
 
-  // destination of this chunk = live entries in earlier chunks of the segment
-  if (tid == 0) {
-    int p = 0;
-    for (int c2 = 0; c2 < cp.c; ++c2) p += w.live[cp.first + c2];
-    s_prefix = p;
-  }
-  __syncthreads();
-  const int P = s_prefix;
-  const bool moves = (P != j0) || (nlive != min(CH, max(0, len - j0)));
-
-  if (j0 < len && moves) {
-    // compacted list of live source indices (stable)
-    int nl_before = 0;
-    for (int t0 = 0; t0 < CH; t0 += kCompactThreads) {
-      const int j = j0 + t0 + tid;
-      const bool lv = (t0 + tid < CH) && j < len && a.lam[off + j] >= tau;
-      const uint64_t mask = __ballot(lv);
-      const int lane = tid & 63;
-      const int rank_w = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-      int tot;
-      const int wbase = block_exclusive_scan<kCompactThreads>((lane == 0) ? __popcll(mask) : 0, s_scan, &tot);
-      const int wave_off = __shfl(wbase, 0, 64);
-      if (lv) s_src[nl_before + wave_off + rank_w] = t0 + tid;
-      nl_before += tot;
-      __syncthreads();
-    }
-    // load live rows (K, V pieces) and scalars into registers
-    uint4 kreg[PPT], vreg[PPT];
-    float lamr = 0.0f, lkr = 0.0f;
-    int srcr = 0;
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int piece = u * kCompactThreads + tid;
-      const int row = piece / P16;
-      const int part = piece - row * P16;
-      if (row < nlive) {
-        const int64_t src = off + j0 + s_src[row];
-        kreg[u] = reinterpret_cast<const uint4*>(a.K)[src * P16 + part];
-        vreg[u] = reinterpret_cast<const uint4*>(a.V)[src * P16 + part];
+  // ---- chunk id -> (segment, chunk) from the read-only capacities
+  bool have = false;
+  {
+    const int per = (S + kCompactThreads - 1) / kCompactThreads;
+    const int sb = tid * per;
+    const int se = min(S, sb + per);
+    int mine = 0;
+    for (int s = sb; s < se; ++s) mine += max(1, (a.seg_cap[s] + CH - 1) / CH);
+    int total;
+    const int excl = block_exclusive_scan<kCompactThreads>(mine, s_scan, &total);
+    have = id < total;
+    if (have) {
+      int run = excl;
+      for (int s = sb; s < se; ++s) {
+        const int n = max(1, (a.seg_cap[s] + CH - 1) / CH);
+        if (id >= run && id < run + n) {
+          s_info[0] = s;
+          s_info[1] = id - run;
+          s_info[2] = run;
+          s_info[3] = n;
+        }
+        run += n;
       }
     }
-    if (tid < nlive) {
-      srcr = s_src[tid];
-      lamr = a.lam[off + j0 + srcr];
-      lkr = a.lk[off + j0 + srcr];
-    }
-    // every load has returned before the chunk is declared loaded
-    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) __hip_atomic_store(&w.loaded[id], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
-    // wait for earlier chunks whose rows our destination overwrites
-    if (tid == 0) {
-      const int cfirst = P / CH;
-      for (int c2 = cfirst; c2 < cp.c; ++c2) {
+  if (have) {
+    const int seg = s_info[0];
+    const int c = s_info[1];
+    const int first = s_info[2];
+    const int nch = s_info[3];
+    const int len = a.seg_len[seg];
+    const int64_t off = a.seg_off[seg];
+    const int j0 = c * CH;
+    const int nvalid = min(CH, max(0, len - j0));
+
+    // 1. live flags and count
+    const int j = j0 + tid;
+    float lamr = 0.0f;
+    bool lv = false;
+    if (tid < CH && j < len) {
+      lamr = a.lam[off + j];
+      lv = lamr >= tau;
+    }
+    const uint64_t mask = __ballot(lv);
+    if (lane == 0) s_cnt[wv] = __popcll(mask);
+    __syncthreads();
+    int count = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kCompactThreads / 64; ++w2) count += s_cnt[w2];
+
+    // 2. publish, then look back for the destination of the first survivor
+    if (wv == 0) {
+      if (c == 0) {
+        if (lane == 0) {
+          sti_coh2(&ctl.cmp_state[id], (count << 2) | 2);
+          s_prefix = 0;
+        }
+      } else {
+        if (lane == 0) sti_coh2(&ctl.cmp_state[id], (count << 2) | 1);
+        int prefix = 0;
+        int cpos = c - 1;  // next predecessor to examine
         int spins = 0;
-        while (ld_acquire(&w.loaded[cp.first + c2]) == 0) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++spins > (1 << 24)) {  // never expected; fail loudly, not forever
-            atomicOr(a.status, 2);
+        while (true) {
+          const int pc = cpos - lane;  // lane l reads predecessor cpos - l
+          int st = (pc >= 0) ? ldi_coh(&ctl.cmp_state[first + pc]) : 2;  // chunk -1 acts as prefix 0
+          const int flag = (pc >= 0) ? (st & 3) : 2;
+          const int val = (pc >= 0) ? (st >> 2) : 0;
+          // first lane (nearest predecessor) whose prefix is complete
+          const uint64_t inc = __ballot(flag == 2);
+          const uint64_t none = __ballot(flag == 0);
+          const int stop = inc ? (int)__builtin_ctzll(inc) : 64;
+          // every lane up to `stop` must have published at least its count
+          const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1);
+          if ((none & need) == 0) {
+            int contrib = (lane <= stop) ? val : 0;
+            contrib = wave_isum(contrib);
+            prefix += contrib;
+            if (stop < 64) break;
+            cpos -= 64;
+            continue;
+          }
+          if (++spins > kSpinLimit) {
+            if (lane == 0) atomicOr(a.status, 2);
             break;
           }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) {
+          sti_coh2(&ctl.cmp_state[id], ((prefix + count) << 2) | 2);
+          s_prefix = prefix;
         }
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      const int piece = u * kCompactThreads + tid;
-      const int row = piece / P16;
-      const int part = piece - row * P16;
-      if (row < nlive) {
-        const int64_t dst = off + P + row;
-        reinterpret_cast<uint4*>(a.K)[dst * P16 + part] = kreg[u];
-        reinterpret_cast<uint4*>(a.V)[dst * P16 + part] = vreg[u];
+    const int P = s_prefix;
+    const bool moves = (P != j0) || (count != nvalid);
+
+    if (moves && nvalid > 0) {
+      // stable list of survivors (chunk-relative source indices)
+      {
+        const int rank_w = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+        int wbase = 0;
+        for (int w2 = 0; w2 < wv; ++w2) wbase += s_cnt[w2];
+        if (lv) s_src[wbase + rank_w] = tid;
       }
+      __syncthreads();
+      // unconditional loads from a clamped row (always inside this chunk) keep
+      // the rows in registers; only the stores below are predicated
+      u32x4 kreg[PPT], vreg[PPT];
+      float lkr = 0.0f, lsv = 0.0f;
+      int srcr = 0;
+      const int64_t cbase = off + j0;
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int piece = u * kCompactThreads + tid;
+        const int row = piece / P16;
+        const int part = piece - row * P16;
+        const int rsrc = (count > 0) ? s_src[row < count ? row : 0] : 0;
+        const int64_t src = cbase + rsrc;
+        kreg[u] = reinterpret_cast<const u32x4*>(a.K)[src * P16 + part];
+        vreg[u] = reinterpret_cast<const u32x4*>(a.V)[src * P16 + part];
+      }
+      if (tid < count) {
+        srcr = s_src[tid];
+        lsv = a.lam[off + j0 + srcr];
+        lkr = a.lk[off + j0 + srcr];
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // every row is in registers
+      __syncthreads();
+      if (tid == 0) sti_coh2(&ctl.cmp_loaded[id], 1);
+      // wait for the earlier chunks whose rows the destination overwrites
+      if (wv == 0) {
+        const int cfirst = P / CH;
+        int spins = 0;
+        for (int cb = cfirst; cb < c; cb += 64) {
+          const int cc = cb + lane;
+          while (true) {
+            const int ok = (cc < c) ? ldi_coh(&ctl.cmp_loaded[first + cc]) : 1;
+            if (__ballot(ok == 0) == 0) break;
+            if (++spins > kSpinLimit) {
+              if (lane == 0) atomicOr(a.status, 2);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < PPT; ++u) {
+        const int piece = u * kCompactThreads + tid;
+        const int row = piece / P16;
+        const int part = piece - row * P16;
+        if (row < count) {
+          const int64_t dst = off + P + row;
+          reinterpret_cast<u32x4*>(a.K)[dst * P16 + part] = kreg[u];
+          reinterpret_cast<u32x4*>(a.V)[dst * P16 + part] = vreg[u];
+        }
+      }
+      if (tid < count) {
+        a.lam[off + P + tid] = lsv;
+        a.lk[off + P + tid] = lkr;
+        if (kept) kept[off + P + tid] = j0 + srcr;
+      }
+    } else {
+      if (tid == 0) sti_coh2(&ctl.cmp_loaded[id], 1);
+      if (kept && tid < nvalid) kept[off + j0 + tid] = j0 + tid;
     }
-    if (tid < nlive) {
-      a.lam[off + P + tid] = lamr;
-      a.lk[off + P + tid] = lkr;
-      if (kept) kept[off + P + tid] = j0 + srcr;
-    }
-  } else {
-    if (tid == 0) __hip_atomic_store(&w.loaded[id], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    if (kept && j0 < len) {
-      for (int t = tid; t < nlive; t += kCompactThreads) kept[off + j0 + t] = j0 + t;
+
+    // 4. the last chunk of the segment to arrive sets the length, clears flags
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) s_last = (addi_coh(&ctl.cmp_done[seg], 1) == nch - 1);
+    __syncthreads();
+    if (s_last) {
+      if (tid == 0) a.seg_len[seg] = ldi_coh(&ctl.cmp_state[first + nch - 1]) >> 2;
+      __syncthreads();
+      for (int t = tid; t < nch; t += kCompactThreads) {
+        sti_coh2(&ctl.cmp_state[first + t], 0);
+        sti_coh2(&ctl.cmp_loaded[first + t], 0);
+      }
+      if (tid == 0) sti_coh2(&ctl.cmp_done[seg], 0);
     }
   }
 
-  // the last chunk of the segment sets the new length
-  __threadfence();
+  // 5. the last workgroup overall clears the ticket
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) {
-    const int old = atomicAdd(&w.done[seg], 1);
-    s_last = (old == cp.nch - 1);
-  }
-  __syncthreads();
-  if (s_last && tid == 0) {
-    __threadfence();
-    int tot = 0;
-    for (int c2 = 0; c2 < cp.nch; ++c2) tot += w.live[cp.first + c2];
-    a.seg_len[seg] = tot;
+  if (tid == 0 && addi_coh(&ctl.cmp_glob[1], 1) == (int)gridDim.x - 1) {
+    sti_coh2(&ctl.cmp_glob[0], 0);
+    sti_coh2(&ctl.cmp_glob[1], 0);
   }
 }
 
 template <int RB>
-static hipError_t launch_compact_rb(const LayerArgs& a, float tau, int32_t* kept, void* ws, hipStream_t st) {
-  using Sh = CompactShape<RB>;
-  CompactWs w = compact_carve(a, ws);
-  hipLaunchKernelGGL((compact_count<Sh::CH>), dim3(w.max_chunks), dim3(kCompactThreads), 0, st, a, w, tau);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((compact_move<RB>), dim3(w.max_chunks), dim3(kCompactThreads), 0, st, a, w, tau, kept);
+static hipError_t launch_rb(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st) {
+  hipLaunchKernelGGL((compact_kernel<RB>), dim3(ctl.max_chunks), dim3(kCompactThreads), 0, st, a, ctl, tau, kept);
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const LayerArgs& a, float tau, int32_t* kept, void* ws, hipStream_t st) {
+hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st) {
   const int rb = a.d * (a.bf16 ? 2 : 4);
   switch (rb) {
-    case 128: return launch_compact_rb<128>(a, tau, kept, ws, st);
-    case 256: return launch_compact_rb<256>(a, tau, kept, ws, st);
-    case 512: return launch_compact_rb<512>(a, tau, kept, ws, st);
+    case 128: return launch_rb<128>(a, ctl, tau, kept, st);
+    case 256: return launch_rb<256>(a, ctl, tau, kept, st);
+    case 512: return launch_rb<512>(a, ctl, tau, kept, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,7 +6,8 @@ namespace ua {
 
 size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap) { return 256; }
 
-hipError_t launch_prefill(const LayerArgs& a, int n_tokens, void* ws, size_t ws_bytes, hipStream_t st) {
+hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, int max_seg_cap, void* scratch,
+                          size_t scratch_bytes, hipStream_t st) {
   return hipErrorNotSupported;
 }
 

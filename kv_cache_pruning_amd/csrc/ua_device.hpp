@@ -6,6 +6,11 @@
 
 namespace ua {
 
+// Native 4 x 32-bit vector (a first-class LLVM vector, so arrays of it stay
+// in registers; HIP's uint4 struct is copied with memcpy and can end up in
+// scratch).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();

@@ -46,32 +46,53 @@ struct LayerArgs {
   void* y;
 };
 
-// Decode workspace regions (device pointers into the caller's workspace).
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Control block at the front of every workspace: counters and flags that
+// must be zero before the first call; every call returns them to zero.  All
+// three entry points carve it identically, so calls can share a workspace.
+struct Control {
+  int* dec_cnt;     // [S]           decode: arrivals per segment
+  int* dec_cntb;    // [B]           decode: finished segments per sequence
+  int* cmp_state;   // [max_chunks]  compaction: (count or prefix) << 2 | flag
+  int* cmp_loaded;  // [max_chunks]  compaction: chunk rows are in registers
+  int* cmp_done;    // [S]           compaction: arrivals per segment
+  int* cmp_glob;    // [2]           compaction: ticket, arrivals
+  int* pre_flag;    // [pre_blocks]  prefill: per key-block progress flags
+  int* pre_glob;    // [2]           prefill: ticket, arrivals
+  int cmp_chunk;    // entries per compaction chunk
+  int max_chunks;
+  int pre_blocks;   // flat (segment, key block) count bound for prefill
+};
+
+int compact_chunk_entries(const LayerArgs& a);
+size_t control_bytes(const LayerArgs& a);
+Control control_carve(const LayerArgs& a, void* ws);
+
+// Decode scratch (after the control block).
 struct DecodeWs {
-  float* qt;      // [B, H_q, d]   rotated queries
-  float* kt;      // [S, d]        stored new keys (cache-rounded), fp32
-  float* gates;   // [S, 4]        lq, lk, lb, unused
-  float* gamma;   // [B, H_q, d]   output gate
-  int* len_old;   // [S]           segment length before the append
-  int* cnt;       // [S]           finished tiles per segment
-  float* part_o;  // [max_tiles, G, d]
-  float* part_ml; // [max_tiles, G, 2]  running max (log2 units), sum
+  int* cnt;        // [S]  arrivals per segment (control block)
+  int* cntb;       // [B]  finished segments per sequence (control block)
+  float* gamma;    // [S, G, d]  output gate of the segment's query heads
+  float* eself;    // [S, G]     new token's own logit (log2 units)
+  float* part_o;   // [max_tiles, G, d]
+  float* part_ml;  // [max_tiles, G, 2]  max (log2 units), sum
   int max_tiles;
 };
 
 size_t decode_ws_bytes(const LayerArgs& a, int tile_entries);
 int decode_tile_entries(int d);
-DecodeWs decode_ws_carve(const LayerArgs& a, void* ws, int tile_entries);
+DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, int tile_entries);
 hipError_t launch_decode(const LayerArgs& a, const DecodeWs& w, float tau, hipStream_t st);
 
 // Compaction
-size_t compact_ws_bytes(const LayerArgs& a);
-hipError_t launch_compact(const LayerArgs& a, float tau, int32_t* kept, void* ws, hipStream_t st);
+hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st);
 
 // Prefill
 size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap);
-hipError_t launch_prefill(const LayerArgs& a, int n_tokens, void* ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, int max_seg_cap, void* scratch,
+                          size_t scratch_bytes, hipStream_t st);
 
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace ua

@@ -85,18 +85,19 @@ class Workspace:
         self.nbytes = n
         self.buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
         self.ptr = (self.buf.data_ptr() + 255) // 256 * 256  # 256-byte aligned start
+        L.ua_workspace_init(self.ptr, n)  # counters must start at zero
 
 
 class Layer:
     """One UA layer bound to a cache: decode / prefill / compact through the C ABI."""
 
     def __init__(self, shape: LayerShape, weights: DeviceWeights, cache: DeviceCache, max_tokens: int = 1,
-                 device="cuda"):
+                 device="cuda", workspace: Optional[Workspace] = None):
         self.shape = shape
         self.dims = shape.dims()
         self.w = weights
         self.cache = cache
-        self.ws = Workspace(shape, cache, max_tokens, device)
+        self.ws = workspace if workspace is not None else Workspace(shape, cache, max_tokens, device)
         self.device = device
 
     def _tokens(self, q, k, v, x):
