@@ -73,6 +73,7 @@ LayerArgs make_args(const ua_dims* d, const ua_params* p, const ua_cache* c, con
   a.y_bf16 = d->y_dtype == UA_BF16;
   a.scale = d->sm_scale != 0.0f ? d->sm_scale : (float)(1.0 / sqrt((double)d->d_head));
   a.rope_base = d->rope_base;
+  for (int i = 0; i < 64; ++i) a.inv_freq[i] = (2 * i < d->d_head) ? pow(d->rope_base, -2.0 * i / d->d_head) : 0.0;
   if (p) {
     a.W_dec = p->W_dec;
     a.b_dec = p->b_dec;

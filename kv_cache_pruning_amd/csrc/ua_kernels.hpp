@@ -20,6 +20,7 @@ struct LayerArgs {
   int y_bf16;  // y dtype is bf16 (else fp32)
   float scale;
   double rope_base;
+  double inv_freq[64];  // rope_base^(-2i/d), i < d/2, formed in fp64 on the host
   // weights
   const void* W_dec;
   const float* b_dec;
@@ -69,12 +70,16 @@ int compact_chunk_entries(const LayerArgs& a);
 size_t control_bytes(const LayerArgs& a);
 Control control_carve(const LayerArgs& a, void* ws);
 
-// Decode scratch (after the control block).
+// Decode scratch (after the control block) plus the counters it uses.
 struct DecodeWs {
   int* cnt;        // [S]  arrivals per segment (control block)
-  int* cntb;       // [B]  finished segments per sequence (control block)
-  float* gamma;    // [S, G, d]  output gate of the segment's query heads
-  float* eself;    // [S, G]     new token's own logit (log2 units)
+  int* cntb;       // [B]  finished token-kernel splits per sequence (control block)
+  float* qt;       // [B, H_q, d]  rotated queries
+  float* kt;       // [S, d]       stored new keys (cache-rounded), fp32
+  float* gates;    // [S, 4]       lq, lk, lb, unused
+  int* len_old;    // [S]          segment length before the append
+  float* eself;    // [B, H_q]     new token's own logit (log2 units)
+  float* gamma;    // [B, H_q, d]  output gate
   float* part_o;   // [max_tiles, G, d]
   float* part_ml;  // [max_tiles, G, 2]  max (log2 units), sum
   int max_tiles;
