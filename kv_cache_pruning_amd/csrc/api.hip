@@ -46,7 +46,7 @@ ua_status check_cache(const ua_cache* c) {
 
 ua_status check_params(const ua_params* p) {
   if (!p || !p->W_dec || !p->b_dec || !p->W_dn || !p->W_up) return UA_ERR_INVALID_ARG;
-  if (!aligned(p->W_dec, 4) || !aligned(p->b_dec, 4) || !aligned(p->W_dn, 4) || !aligned(p->W_up, 4) ||
+  if (!aligned(p->W_dec, 16) || !aligned(p->b_dec, 4) || !aligned(p->W_dn, 16) || !aligned(p->W_up, 16) ||
       (p->b_up && !aligned(p->b_up, 4)))
     return UA_ERR_INVALID_ARG;
   return UA_OK;

@@ -1,14 +1,792 @@
-// Chunked UA prefill (gfx950) -- kernels follow.
+// Chunked UA prefill on gfx950: three kernels per call.
+//
+// The decay bias is applied inside a fused online softmax and the L x L bias
+// matrix is never stored ("A Self-Pruning Transformer ...", paperlayer.ai
+// summary, section 4.2 and Appendix C); the three decay terms are combined by
+// a geometric mean, taken to log space and accumulated causally (ai4snews
+// page, Figure 1 caption).
+//
+// Notation.  A call appends n tokens to every segment s (one sequence b and
+// KV head h) that holds len0 entries.  Keys are indexed by their slot in the
+// segment, j in [0, len0 + n); call-local token t is key len0 + t.  Token t's
+// pair term with key j applies iff j < len0 + t, so with the stored bias
+// Lambda0_j (0 for the new keys)
+//     Lambda_tj = Lambda0_j + sum_{t' <= t, j < len0 + t'} A_{t'j},
+// and token t attends every key j <= len0 + t with that bias.  After the call
+// each key's bias is its value at the last token.
+//
+// 1. prefill_prep_kernel: clears the call's sync words and writes
+//    [W_dec | W_dn] transposed (zero-padded to 16 rows) so that the gate
+//    projections can be fed to the matrix cores with 16-byte loads.
+// 2. prefill_token_kernel: 16 tokens per workgroup.  x [W_dec | W_dn] on the
+//    matrix cores, log-sigmoid gates, the output gate sigmoid(u W_up + b_up),
+//    RoPE of the queries (bf16 copy for the matrix cores) and of the
+//    L2-normalised keys (angles in fp64), and the append of k~, v and the key
+//    gate to the cache.
+// 3. prefill_attn_kernel: one workgroup per (segment, block of 64 tokens),
+//    four waves of 16 tokens, looping over blocks of 64 keys.  Per key block,
+//    with keys as MFMA rows and the wave's tokens as columns:
+//      * <k~_j, k~_t> for the similarity term and <q~_t, k~_j> for every
+//        query head of the group come from 16x16x32 bf16 MFMA tiles;
+//      * the pair terms are scanned over the tokens: within a wave across
+//        the 16 lanes of a row (DPP), across the four waves through LDS, and
+//        across token blocks through a carry per key that the workgroup of
+//        the previous token block publishes (a chain per segment; workgroups
+//        take their ids from an atomic ticket so every wait is on a
+//        workgroup that started earlier);
+//      * logits (log2 units) feed an online softmax whose reference maximum
+//        is only raised when a block exceeds it by more than 2^8; the
+//        probabilities go to fp16 and P V runs on 16x16x32 fp16 MFMA tiles,
+//        the row sums on the same instruction with a tile of ones;
+//      * the last token block writes each key's final bias to the cache.
+//    The last workgroup to finish advances seg_len and next_pos.
+
+#include <algorithm>
+
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
 
 namespace ua {
 
-size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap) { return 256; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, int max_seg_cap, void* scratch,
+constexpr int kPTok = 16;                            // tokens per token-kernel workgroup
+constexpr int kPRows = 64;                           // tokens per attention workgroup
+constexpr int kPKeys = 64;                           // keys per block
+constexpr int kMaxZ = 3 * kMaxHkv + kMaxRank;        // gate-projection columns
+constexpr float kRescaleTh = 8.0f;                   // log2 headroom of the softmax reference
+constexpr int kPrefillSpinLimit = 1 << 22;
+
+// ---------------------------------------------------------------------------
+// workspace
+// ---------------------------------------------------------------------------
+struct PrefillWs {
+  int* sync;       // [2 + S*nrb]  ticket, arrivals, carry progress per (segment, token block)
+  uint16_t* wt;    // [cp, D_model] bf16  [W_dec | W_dn]^T, rows >= 3 H_kv + r zero
+  uint16_t* qbf;   // [B*n, H_q, d] bf16  rotated queries
+  float* gl;       // [B*n, H_kv, 2]      (lq, lb)
+  float* gam;      // [B*n, H_q*d]        output gate
+  float* carry;    // [nrb-1, total_slots] per-key carry into token block I (log2 units)
+  int n, nrb, cp;
+};
+
+static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w) {
+  const int64_t S = (int64_t)a.B * a.H_kv;
+  const int nrb = (n + kPRows - 1) / kPRows;
+  const int cp = (3 * a.H_kv + a.r + 15) / 16 * 16;
+  const int64_t NT = (int64_t)a.B * n;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes, 256);
+    return p;
+  };
+  char* sync = take(sizeof(int) * (2 + S * nrb));
+  char* wt = take(sizeof(uint16_t) * (size_t)cp * a.D_model);
+  char* qbf = take(sizeof(uint16_t) * (size_t)NT * a.H_q * a.d);
+  char* gl = take(sizeof(float) * 2 * (size_t)NT * a.H_kv);
+  char* gam = take(sizeof(float) * (size_t)NT * a.H_q * a.d);
+  char* carry = take(sizeof(float) * (size_t)(nrb - 1) * a.total_slots);
+  if (w) {
+    w->sync = reinterpret_cast<int*>(sync);
+    w->wt = reinterpret_cast<uint16_t*>(wt);
+    w->qbf = reinterpret_cast<uint16_t*>(qbf);
+    w->gl = reinterpret_cast<float*>(gl);
+    w->gam = reinterpret_cast<float*>(gam);
+    w->carry = reinterpret_cast<float*>(carry);
+    w->n = n;
+    w->nrb = nrb;
+    w->cp = cp;
+  }
+  return off;
+}
+
+size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int /*max_seg_cap*/) {
+  return prefill_layout(a, n_tokens, nullptr, nullptr);
+}
+
+__device__ __forceinline__ int ldi_coh_p(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void sti_coh_p(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int addi_coh_p(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ldf_coh_p(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stf_coh_p(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float u32x4_bf16(const u32x4& v, int e) {
+  const uint32_t wd = v[e >> 1];
+  return (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// 1. prep: clear sync words, transpose the gate projections
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_prep_kernel(LayerArgs a, PrefillWs w, int nsync) {
+  const int gt = blockIdx.x * blockDim.x + threadIdx.x;
+  const int gs = gridDim.x * blockDim.x;
+  for (int i = gt; i < nsync; i += gs) w.sync[i] = 0;
+  const int C3 = 3 * a.H_kv, nc = C3 + a.r, Dm = a.D_model;
+  const int k8 = Dm / 8;
+  const uint16_t* Wd = reinterpret_cast<const uint16_t*>(a.W_dec);
+  const uint16_t* Wn = reinterpret_cast<const uint16_t*>(a.W_dn);
+  for (int e = gt; e < w.cp * k8; e += gs) {
+    const int c = e % w.cp;  // consecutive threads read consecutive columns
+    const int kb = (e / w.cp) * 8;
+    uint32_t pk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint32_t lo = 0, hi = 0;
+      const int64_t k0 = kb + 2 * t, k1 = k0 + 1;
+      if (c < C3) {
+        lo = Wd[k0 * C3 + c];
+        hi = Wd[k1 * C3 + c];
+      } else if (c < nc) {
+        lo = Wn[k0 * a.r + c - C3];
+        hi = Wn[k1 * a.r + c - C3];
+      }
+      pk[t] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(w.wt + (int64_t)c * Dm + kb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. token kernel: gates, output gate, RoPE, append
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, PrefillWs w) {
+  constexpr int HALF = D / 2;
+  constexpr int CH = D / 8;  // 16-byte chunks per head row
+  __shared__ float s_z[kPTok][kMaxZ];
+  __shared__ __attribute__((aligned(16))) float s_ut[kMaxRank][kPTok];
+  __shared__ float s_cos[kPTok][HALF];
+  __shared__ float s_sin[kPTok][HALF];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int n = w.n;
+  const int NT = a.B * n;
+  const int tok0 = blockIdx.x * kPTok;
+  const int Hkv = a.H_kv, Hq = a.H_q;
+  const int C3 = 3 * Hkv;
+  const int Dm = a.D_model;
+
+  for (int i = tid; i < kPTok * kMaxZ; i += 256) (&s_z[0][0])[i] = 0.0f;
+  for (int e = tid; e < kPTok * HALF; e += 256) {
+    const int tt = e / HALF, i = e - tt * HALF;
+    const int tk = min(tok0 + tt, NT - 1);
+    const int b = tk / n, t = tk - b * n;
+    double sn, cn;
+    sincos((double)(a.next_pos[b] + t) * a.inv_freq[i], &sn, &cn);
+    s_cos[tt][i] = (float)cn;
+    s_sin[tt][i] = (float)sn;
+  }
+  __syncthreads();
+
+  // ---- z = x [W_dec | W_dn]: A = x rows (tokens), B = W^T rows; waves split the k range
+  {
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
+    const int nks = (Dm + 31) / 32;
+    const int64_t xrow = (int64_t)min(tok0 + c16, NT - 1) * Dm;
+    const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+    for (int nt = 0; nt < w.cp / 16; ++nt) {
+      const uint16_t* wrow = w.wt + (int64_t)(16 * nt + c16) * Dm;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k0 = wv; k0 < nks; k0 += 16) {
+        u32x4 av[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int ks = k0 + 4 * u;
+          const int kk = 32 * ks + 8 * g;
+          const bool ok = ks < nks && kk < Dm;
+          const int kc = ok ? kk : 0;
+          av[u] = *reinterpret_cast<const u32x4*>(X + xrow + kc);
+          bv[u] = *reinterpret_cast<const u32x4*>(wrow + kc);
+          if (!ok) av[u] = zero4;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc = mfma_bf16(av[u], bv[u], acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(&s_z[4 * g + i][16 * nt + c16], acc[i]);
+    }
+  }
+  __syncthreads();
+
+  // ---- gates and the append of the key gate
+  for (int e = tid; e < kPTok * a.r; e += 256) {
+    const int tt = e / a.r, rr = e - tt * a.r;
+    s_ut[rr][tt] = s_z[tt][C3 + rr];
+  }
+  for (int e = tid; e < kPTok * Hkv; e += 256) {
+    const int tt = e / Hkv, h = e - tt * Hkv;
+    const int tk = tok0 + tt;
+    if (tk >= NT) continue;
+    const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
+    const float lq = log_sigmoid(s_z[tt][h] + a.b_dec[h]);
+    const float lkk = log_sigmoid(s_z[tt][Hkv + h] + a.b_dec[Hkv + h]);
+    const float lb = log_sigmoid(s_z[tt][2 * Hkv + h] + a.b_dec[2 * Hkv + h]);
+    w.gl[2 * ((int64_t)tk * Hkv + h) + 0] = lq;
+    w.gl[2 * ((int64_t)tk * Hkv + h) + 1] = lb;
+    const int len0 = a.seg_len[s];
+    if ((int64_t)len0 + n <= a.seg_cap[s]) {
+      a.lk[a.seg_off[s] + len0 + t] = lkk;
+    } else if (t == 0) {
+      atomicOr(a.status, 1);
+    }
+  }
+
+  // ---- rotated queries (bf16 copy); chunk c pairs dims [8c, 8c+8) with [HALF+8c, HALF+8c+8)
+  {
+    const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q);
+    for (int e = tid; e < kPTok * Hq * (CH / 2); e += 256) {
+      const int c = e % (CH / 2);
+      const int rest = e / (CH / 2);
+      const int hd = rest % Hq, tt = rest / Hq;
+      const int tk = tok0 + tt;
+      if (tk >= NT) continue;
+      const int64_t base = ((int64_t)tk * Hq + hd) * D;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(Q + base + 8 * c);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(Q + base + HALF + 8 * c);
+      uint32_t olo[4], ohi[4];
+#pragma unroll
+      for (int u = 0; u < 8; u += 2) {
+        float rl[2], rh[2];
+#pragma unroll
+        for (int v2 = 0; v2 < 2; ++v2) {
+          const int i = 8 * c + u + v2;
+          const float xl = u32x4_bf16(lo, u + v2), xh = u32x4_bf16(hi, u + v2);
+          rl[v2] = fmaf(xl, s_cos[tt][i], -xh * s_sin[tt][i]);
+          rh[v2] = fmaf(xh, s_cos[tt][i], xl * s_sin[tt][i]);
+        }
+        olo[u / 2] = pack_bf16(rl[0], rl[1]);
+        ohi[u / 2] = pack_bf16(rh[0], rh[1]);
+      }
+      *reinterpret_cast<u32x4*>(w.qbf + base + 8 * c) = u32x4{olo[0], olo[1], olo[2], olo[3]};
+      *reinterpret_cast<u32x4*>(w.qbf + base + HALF + 8 * c) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
+    }
+  }
+
+  // ---- keys: normalise, rotate, round, append; values: append
+  {
+    const uint16_t* Kin = reinterpret_cast<const uint16_t*>(a.k);
+    const uint16_t* Vin = reinterpret_cast<const uint16_t*>(a.v);
+    uint16_t* Kc = reinterpret_cast<uint16_t*>(a.K);
+    uint16_t* Vc = reinterpret_cast<uint16_t*>(a.V);
+    for (int e = tid; e < kPTok * Hkv; e += 256) {
+      const int tt = e / Hkv, h = e - tt * Hkv;
+      const int tk = tok0 + tt;
+      if (tk >= NT) continue;
+      const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
+      const int len0 = a.seg_len[s];
+      if ((int64_t)len0 + n > a.seg_cap[s]) continue;
+      const int64_t base = ((int64_t)tk * Hkv + h) * D;
+      u32x4 raw[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) raw[c] = *reinterpret_cast<const u32x4*>(Kin + base + 8 * c);
+      float ss = 0.0f;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float xv = u32x4_bf16(raw[c], u);
+          ss = fmaf(xv, xv, ss);
+        }
+      const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
+      const int64_t dst = (a.seg_off[s] + len0 + t) * D;
+#pragma unroll
+      for (int c = 0; c < CH / 2; ++c) {
+        uint32_t olo[4], ohi[4];
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+          float rl[2], rh[2];
+#pragma unroll
+          for (int v2 = 0; v2 < 2; ++v2) {
+            const int i = 8 * c + u + v2;
+            const float kl = u32x4_bf16(raw[c], u + v2) * inv;
+            const float kh = u32x4_bf16(raw[c + CH / 2], u + v2) * inv;
+            rl[v2] = fmaf(kl, s_cos[tt][i], -kh * s_sin[tt][i]);
+            rh[v2] = fmaf(kh, s_cos[tt][i], kl * s_sin[tt][i]);
+          }
+          olo[u / 2] = pack_bf16(rl[0], rl[1]);
+          ohi[u / 2] = pack_bf16(rh[0], rh[1]);
+        }
+        *reinterpret_cast<u32x4*>(Kc + dst + 8 * c) = u32x4{olo[0], olo[1], olo[2], olo[3]};
+        *reinterpret_cast<u32x4*>(Kc + dst + HALF + 8 * c) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
+      }
+    }
+    for (int e = tid; e < kPTok * Hkv * CH; e += 256) {
+      const int c = e % CH;
+      const int rest = e / CH;
+      const int h = rest % Hkv, tt = rest / Hkv;
+      const int tk = tok0 + tt;
+      if (tk >= NT) continue;
+      const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
+      const int len0 = a.seg_len[s];
+      if ((int64_t)len0 + n > a.seg_cap[s]) continue;
+      *reinterpret_cast<u32x4*>(Vc + (a.seg_off[s] + len0 + t) * D + 8 * c) =
+          *reinterpret_cast<const u32x4*>(Vin + ((int64_t)tk * Hkv + h) * D + 8 * c);
+    }
+  }
+  __syncthreads();  // s_ut
+
+  // ---- output gate, four columns x 16 tokens per thread
+  {
+    const int HqD = Hq * D;
+    const uint16_t* Wu = reinterpret_cast<const uint16_t*>(a.W_up);
+    for (int cg = tid; cg < HqD / 4; cg += 256) {
+      const int c0 = 4 * cg;
+      float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (a.b_up) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bias[j] = a.b_up[c0 + j];
+      }
+      float acc[kPTok][4];
+#pragma unroll
+      for (int tt = 0; tt < kPTok; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[tt][j] = bias[j];
+      for (int rr = 0; rr < a.r; ++rr) {
+        const uint2 wr = *reinterpret_cast<const uint2*>(Wu + (int64_t)rr * HqD + c0);
+        const float w4[4] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y)};
+        const float4* u4 = reinterpret_cast<const float4*>(&s_ut[rr][0]);
+#pragma unroll
+        for (int q4 = 0; q4 < kPTok / 4; ++q4) {
+          const float4 u = u4[q4];
+          const float uu[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int z = 0; z < 4; ++z)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[4 * q4 + z][j] = fmaf(uu[z], w4[j], acc[4 * q4 + z][j]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < kPTok; ++tt) {
+        const int tk = tok0 + tt;
+        if (tk < NT)
+          *reinterpret_cast<float4*>(w.gam + (int64_t)tk * HqD + c0) =
+              make_float4(sigmoid(acc[tt][0]), sigmoid(acc[tt][1]), sigmoid(acc[tt][2]), sigmoid(acc[tt][3]));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. attention with the causal decay bias
+// ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr 1, 2, 4, 8;
+// lanes without a source read 0).
+__device__ __forceinline__ float scan16(float x) {
+  x += dpp_f<0x111>(x);
+  x += dpp_f<0x112>(x);
+  x += dpp_f<0x114>(x);
+  x += dpp_f<0x118>(x);
+  return x;
+}
+
+// Position of key k (0..63) of a block in the LDS copy of V^T: the P V product
+// takes its k index from the score tiles, where lane group q of 16 lanes holds
+// keys 4q..4q+3 of each 16-key tile; MFMA k index 8q + i of 32-key chunk c
+// maps to key 32c + 4q + i (i < 4) and 32c + 16 + 4q + (i - 4) (i >= 4).
+__device__ __forceinline__ int vt_pos(int k) {
+  const int r = k & 31;
+  return (k & 32) | (((r >> 2) & 3) << 3) | ((r >> 4) << 2) | (r & 3);
+}
+
+template <int D, int HG>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillWs w) {
+  constexpr int KC = D / 32;                        // k steps of a head-dim dot product
+  constexpr int DT = D / 16;                        // 16-wide output tiles per head
+  constexpr int KS = D + 8;                         // s_k row stride (bf16)
+  constexpr int VS = kPKeys + 8;                    // s_vt row stride (fp16)
+  constexpr int KPT = kPKeys * (D / 8) / 256;       // K pieces per thread per block
+  constexpr int VPT = (kPKeys / 2) * (D / 8) / 256; // V (key pair, 8 dims) items per thread
+  static_assert(KPT >= 1 && VPT >= 1, "tile split");
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kPKeys * KS];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][D * VS];
+  __shared__ __attribute__((aligned(16))) float s_lk[2][kPKeys];
+  __shared__ __attribute__((aligned(16))) float s_tot[2][4][kPKeys];
+  __shared__ __attribute__((aligned(16))) float s_car[2][kPKeys];
+  __shared__ int s_id;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int S = a.B * a.H_kv;
+  const int n = w.n, nrb = w.nrb;
+  const int Hq = a.H_q, Hkv = a.H_kv;
+
+  if (tid == 0) s_id = addi_coh_p(&w.sync[0], 1);
+  __syncthreads();
+  const int id = s_id;
+  const int s = id % S;  // token-block major: a chain predecessor always has a lower id
+  const int I = id / S;
+  const int b = s / Hkv, h = s - b * Hkv;
+  const int len0 = a.seg_len[s];
+  const int64_t off = a.seg_off[s];
+  const bool room = (int64_t)len0 + n <= a.seg_cap[s];
+  const int row_lo = I * kPRows + wv * 16;  // first token of this wave
+  const int tq = row_lo + c16;              // this lane's token (score column)
+  const bool row_ok = tq < n;
+  const int tqc = min(tq, n - 1);
+  const int64_t tok = (int64_t)b * n + tqc;
+  const int a0 = h * HG;
+
+  if (room) {
+    const int nkeys = len0 + n;
+    const int kend = len0 + min(n, I * kPRows + kPRows);
+    const int nJ = (kend + kPKeys - 1) / kPKeys;
+    const int64_t TS = a.total_slots;
+    const PairCoef pc = pair_coef(a.terms);
+    const float cs = a.scale * kLog2e;
+    const uint16_t* Kc = reinterpret_cast<const uint16_t*>(a.K);
+    const uint16_t* Vc = reinterpret_cast<const uint16_t*>(a.V);
+
+    // token-side constants
+    const float lq = w.gl[2 * (tok * Hkv + h) + 0];
+    const float lb = w.gl[2 * (tok * Hkv + h) + 1];
+    const float row2 = pc.inv_n2 * (((a.terms & 1) ? lq : 0.0f) + ((a.terms & 4) ? lb : 0.0f));
+    u32x4 qf[HG][KC], krf[KC];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        qf[hh][kc] = *reinterpret_cast<const u32x4*>(w.qbf + (tok * Hq + a0 + hh) * D + 32 * kc + 8 * g);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      krf[kc] = *reinterpret_cast<const u32x4*>(Kc + (off + len0 + tqc) * D + 32 * kc + 8 * g);
+
+    // staging of a key block: K rows, V rows (as key pairs), key gates
+    u32x4 kst[KPT], vst[VPT][2];
+    float lkst = 0.0f;
+    auto slot = [&](int j) -> int64_t { return off + min(j, nkeys - 1); };
+    auto load_block = [&](int J) {
+      const int j0 = J * kPKeys;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int q = tid + 256 * u, key = q / (D / 8), part = q % (D / 8);
+        kst[u] = *reinterpret_cast<const u32x4*>(Kc + slot(j0 + key) * D + 8 * part);
+      }
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int q = tid + 256 * u, p = q / (D / 8), part = q % (D / 8);
+        vst[u][0] = *reinterpret_cast<const u32x4*>(Vc + slot(j0 + 2 * p) * D + 8 * part);
+        vst[u][1] = *reinterpret_cast<const u32x4*>(Vc + slot(j0 + 2 * p + 1) * D + 8 * part);
+      }
+      lkst = a.lk[slot(j0 + lane)];
+    };
+    auto store_k = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int q = tid + 256 * u, key = q / (D / 8), part = q % (D / 8);
+        *reinterpret_cast<u32x4*>(&s_k[buf][key * KS + 8 * part]) = kst[u];
+      }
+      if (wv == 0) s_lk[buf][lane] = lkst;
+    };
+    auto store_v = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int q = tid + 256 * u, p = q / (D / 8), part = q % (D / 8);
+        const int pos = vt_pos(2 * p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const auto hv = __builtin_amdgcn_cvt_pkrtz(u32x4_bf16(vst[u][0], e), u32x4_bf16(vst[u][1], e));
+          *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
+        }
+      }
+    };
+
+    load_block(0);
+    store_k(0);
+    store_v(0);
+    __syncthreads();
+
+    float m_run[HG];
+    f32x4 cinit[HG], O[HG][DT], Lt[HG];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      m_run[hh] = 0.0f;
+      cinit[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      Lt[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) O[hh][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    f16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (c16 == 0) ? (_Float16)1.0f : (_Float16)0.0f;
+
+    for (int J = 0; J < nJ; ++J) {
+      const int cb = J & 1, nb = cb ^ 1;
+      const int j0 = J * kPKeys;
+      const bool more = J + 1 < nJ;
+      if (more) load_block(J + 1);
+
+      u32x4 kf[4][KC];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          kf[kt][kc] = *reinterpret_cast<const u32x4*>(&s_k[cb][(16 * kt + c16) * KS + 32 * kc + 8 * g]);
+      // some element of this wave's tile is masked (causal edge or tokens past n)
+      const bool edge = (j0 + kPKeys - 1 >= len0 + row_lo) || (row_lo + 15 >= n);
+
+      // ---- pair terms, scanned over this wave's 16 tokens
+      float lam[4][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        f32x4 sim = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) sim = mfma_bf16(kf[kt][kc], krf[kc], sim);
+        const float4 lk4 = *reinterpret_cast<const float4*>(&s_lk[cb][16 * kt + 4 * g]);
+        const float lkv[4] = {lk4.x, lk4.y, lk4.z, lk4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float col2 = (a.terms & 2) ? pc.inv_n2 * lkv[i] : 0.0f;
+          float A2 = pair_A2(pc, row2, col2, sim[i]);
+          if (edge) {
+            const int jg = j0 + 16 * kt + 4 * g + i;
+            A2 = (row_ok && jg < len0 + tq) ? A2 : 0.0f;
+          }
+          lam[kt][i] = scan16(A2);
+        }
+      }
+      if (c16 == 15) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          *reinterpret_cast<float4*>(&s_tot[cb][wv][16 * kt + 4 * g]) =
+              make_float4(lam[kt][0], lam[kt][1], lam[kt][2], lam[kt][3]);
+      }
+      // ---- carry into this token block for the block's keys
+      if (wv == 0) {
+        const int jg = j0 + lane;
+        const int Ist = j0 >= len0 ? (j0 - len0) / kPRows : 0;  // first token block that sees key block J
+        float v;
+        if (I == Ist) {
+          v = (jg < len0) ? a.lam[off + jg] * kLog2e : 0.0f;
+        } else {
+          const int* flag = &w.sync[2 + s * nrb + I - 1];
+          int spins = 0;
+          while (ldi_coh_p(flag) < J + 1) {
+            if (++spins > kPrefillSpinLimit) {
+              if (lane == 0) atomicOr(a.status, 2);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          v = ldf_coh_p(&w.carry[(int64_t)(I - 1) * TS + off + min(jg, nkeys - 1)]);
+        }
+        s_car[cb][lane] = v;
+      }
+      if (more) store_k(nb);
+      __syncthreads();
+
+      // ---- bias of this wave's elements (log2 units)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        float4 pre = *reinterpret_cast<const float4*>(&s_car[cb][16 * kt + 4 * g]);
+        for (int w2 = 0; w2 < wv; ++w2) {
+          const float4 t4 = *reinterpret_cast<const float4*>(&s_tot[cb][w2][16 * kt + 4 * g]);
+          pre.x += t4.x;
+          pre.y += t4.y;
+          pre.z += t4.z;
+          pre.w += t4.w;
+        }
+        lam[kt][0] += pre.x;
+        lam[kt][1] += pre.y;
+        lam[kt][2] += pre.z;
+        lam[kt][3] += pre.w;
+      }
+      // ---- carry out to the next token block, or the final bias of the call
+      if (wv == 3) {
+        const int jg = j0 + lane;
+        const float cn =
+            s_car[cb][lane] + s_tot[cb][0][lane] + s_tot[cb][1][lane] + s_tot[cb][2][lane] + s_tot[cb][3][lane];
+        if (I + 1 < nrb) {
+          if (jg < nkeys) stf_coh_p(&w.carry[(int64_t)I * TS + off + jg], cn);
+          __builtin_amdgcn_s_waitcnt(0);
+          if (lane == 0) sti_coh_p(&w.sync[2 + s * nrb + I], J + 1);
+        } else if (jg < nkeys) {
+          a.lam[off + jg] = cn * kLn2;
+        }
+      }
+
+      // ---- softmax and P V per query head
+      f16x8 vf[DT][2];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          vf[dt][c] = *reinterpret_cast<const f16x8*>(&s_vt[cb][(16 * dt + c16) * VS + 32 * c + 8 * g]);
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh) {
+        float e[4][4];
+        float bm = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          f32x4 sc = cinit[hh];
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16(kf[kt][kc], qf[hh][kc], sc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float ev = fmaf(sc[i], cs, lam[kt][i]);
+            if (edge) {
+              const int jg = j0 + 16 * kt + 4 * g + i;
+              ev = (row_ok && jg <= len0 + tq) ? ev : kNegInf;
+            }
+            e[kt][i] = ev;
+            bm = fmaxf(bm, ev);
+          }
+        }
+        if (J == 0 || __any(bm > kRescaleTh)) {
+          float bx = fmaxf(bm, __shfl_xor(bm, 16, 64));
+          bx = fmaxf(bx, __shfl_xor(bx, 32, 64));
+          float dl;
+          if (J == 0) {
+            dl = (bx > kNegInf) ? bx : 0.0f;
+          } else {
+            dl = fmaxf(bx, 0.0f);
+            const float al = __builtin_amdgcn_exp2f(-dl);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) O[hh][dt] *= al;
+            Lt[hh] *= al;
+          }
+          m_run[hh] += dl;
+          const float ci = -m_run[hh] / cs;
+          cinit[hh] = f32x4{ci, ci, ci, ci};
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[kt][i] -= dl;
+        }
+        f16x8 pk[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pk[c][i] = (_Float16)__builtin_amdgcn_exp2f(e[2 * c][i]);
+            pk[c][4 + i] = (_Float16)__builtin_amdgcn_exp2f(e[2 * c + 1][i]);
+          }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) O[hh][dt] = mfma_f16(vf[dt][c], pk[c], O[hh][dt]);
+          Lt[hh] = mfma_f16(ones, pk[c], Lt[hh]);
+        }
+      }
+      if (more) store_v(nb);
+    }
+
+    // ---- epilogue: normalise, gate, store (O^T tiles: lane holds dims 16dt + 4g + i of token c16)
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+      const float L = __shfl(Lt[hh][0], c16, 64);
+      const float inv = row_ok ? 1.0f / L : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+        const float4 gm = *reinterpret_cast<const float4*>(w.gam + yo);
+        const float y0 = gm.x * O[hh][dt][0] * inv, y1 = gm.y * O[hh][dt][1] * inv;
+        const float y2 = gm.z * O[hh][dt][2] * inv, y3 = gm.w * O[hh][dt][3] * inv;
+        if (row_ok) {
+          if (a.y_bf16) {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) =
+                make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(y0, y1, y2, y3);
+          }
+        }
+      }
+    }
+  } else if (row_ok) {
+    // the segment has no room for the call: its outputs are zero
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+        if (a.y_bf16) {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) = make_uint2(0u, 0u);
+        } else {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+  }
+
+  // ---- the last workgroup advances lengths and positions
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_id = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (s_id) {
+    for (int s2 = tid; s2 < S; s2 += 256) {
+      const int l = a.seg_len[s2];
+      if ((int64_t)l + n <= a.seg_cap[s2]) a.seg_len[s2] = l + n;
+    }
+    for (int b2 = tid; b2 < a.B; b2 += 256) a.next_pos[b2] += n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host
+// ---------------------------------------------------------------------------
+template <int D, int HG>
+static void launch_attn(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_attn_kernel<D, HG>), dim3(grid), dim3(256), 0, st, a, w);
+}
+
+hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int max_seg_cap, void* scratch,
                           size_t scratch_bytes, hipStream_t st) {
-  return hipErrorNotSupported;
+  if (!a.bf16) return hipErrorNotSupported;  // the matrix-core path is written for bf16 caches
+  const int G = a.H_q / a.H_kv;
+  if (a.d == 128 && G == 8) return hipErrorNotSupported;
+  if (prefill_ws_bytes(a, n, max_seg_cap) > scratch_bytes) return hipErrorOutOfMemory;
+  PrefillWs w;
+  prefill_layout(a, n, reinterpret_cast<char*>(scratch), &w);
+  const int S = a.B * a.H_kv;
+  const int nsync = 2 + S * w.nrb;
+  const int64_t prep_items = std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8));
+  const int prep_grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (prep_items + 255) / 256));
+  hipLaunchKernelGGL(prefill_prep_kernel, dim3(prep_grid), dim3(256), 0, st, a, w, nsync);
+  const int tok_grid = (a.B * n + kPTok - 1) / kPTok;
+  if (a.d == 64) {
+    hipLaunchKernelGGL(prefill_token_kernel<64>, dim3(tok_grid), dim3(256), 0, st, a, w);
+  } else {
+    hipLaunchKernelGGL(prefill_token_kernel<128>, dim3(tok_grid), dim3(256), 0, st, a, w);
+  }
+  const int grid = S * w.nrb;
+  switch (a.d * 16 + G) {
+    case 64 * 16 + 1: launch_attn<64, 1>(a, w, grid, st); break;
+    case 64 * 16 + 2: launch_attn<64, 2>(a, w, grid, st); break;
+    case 64 * 16 + 3: launch_attn<64, 3>(a, w, grid, st); break;
+    case 64 * 16 + 4: launch_attn<64, 4>(a, w, grid, st); break;
+    case 64 * 16 + 8: launch_attn<64, 8>(a, w, grid, st); break;
+    case 128 * 16 + 1: launch_attn<128, 1>(a, w, grid, st); break;
+    case 128 * 16 + 2: launch_attn<128, 2>(a, w, grid, st); break;
+    case 128 * 16 + 3: launch_attn<128, 3>(a, w, grid, st); break;
+    case 128 * 16 + 4: launch_attn<128, 4>(a, w, grid, st); break;
+    default: return hipErrorNotSupported;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace ua

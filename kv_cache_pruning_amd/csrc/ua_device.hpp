@@ -179,6 +179,18 @@ __device__ __forceinline__ float log1mexp2(float lam2) {
   return __builtin_amdgcn_logf(arg) * kLn2 + corr;
 }
 
+// The same in log2 units: log2(1 - 2^lam2).
+__device__ __forceinline__ float log1mexp2_b2(float lam2) {
+  const float lam = lam2 * kLn2;
+  const bool small = lam > -0.125f;
+  const float w = __builtin_amdgcn_exp2f(lam2);
+  const float y = 1.0f - w;
+  const float err = (1.0f - y) - w;
+  const float arg = small ? -lam : y;
+  const float corr = small ? lam * (0.5f + lam * (1.0f / 24.0f)) : err;
+  return __builtin_amdgcn_logf(arg) + corr * kLog2e;
+}
+
 // Pair term from the similarity s and the pre-scaled row/column parts:
 // lam2 = row2 + col2 + sim_w * log2(min(s^2, 1)).
 __device__ __forceinline__ float pair_A(const PairCoef& c, float row2, float col2, float s) {
@@ -186,6 +198,14 @@ __device__ __forceinline__ float pair_A(const PairCoef& c, float row2, float col
   float lam2 = row2 + col2;
   if (c.sim) lam2 += c.sim_w * __builtin_amdgcn_logf(fminf(s * s, 1.0f));
   return log1mexp2(lam2);
+}
+
+// pair_A in log2 units.
+__device__ __forceinline__ float pair_A2(const PairCoef& c, float row2, float col2, float s) {
+  if (!c.any) return 0.0f;
+  float lam2 = row2 + col2;
+  if (c.sim) lam2 += c.sim_w * __builtin_amdgcn_logf(fminf(s * s, 1.0f));
+  return log1mexp2_b2(lam2);
 }
 
 }  // namespace ua

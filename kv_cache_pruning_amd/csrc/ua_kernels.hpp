@@ -59,11 +59,8 @@ struct Control {
   int* cmp_loaded;  // [max_chunks]  compaction: chunk rows are in registers
   int* cmp_done;    // [S]           compaction: arrivals per segment
   int* cmp_glob;    // [2]           compaction: ticket, arrivals
-  int* pre_flag;    // [pre_blocks]  prefill: per key-block progress flags
-  int* pre_glob;    // [2]           prefill: ticket, arrivals
   int cmp_chunk;    // entries per compaction chunk
   int max_chunks;
-  int pre_blocks;   // flat (segment, key block) count bound for prefill
 };
 
 int compact_chunk_entries(const LayerArgs& a);
@@ -93,7 +90,7 @@ hipError_t launch_decode(const LayerArgs& a, const DecodeWs& w, float tau, hipSt
 // Compaction
 hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st);
 
-// Prefill
+// Prefill (its sync words live in its scratch and are cleared by the call)
 size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap);
 hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, int max_seg_cap, void* scratch,
                           size_t scratch_bytes, hipStream_t st);

@@ -1,7 +1,8 @@
-// Workspace control block: counters and flags shared by the three entry
-// points.  They are zero before the first call and every call leaves them
+// Workspace control block: counters and flags of the decode and compaction
+// kernels.  They are zero before the first call and every call leaves them
 // zero, so one workspace can serve decode, prefill and compaction calls
-// issued in order on one stream.
+// issued in order on one stream (prefill keeps its own sync words in its
+// scratch and clears them at the start of each call).
 
 #include "ua_kernels.hpp"
 
@@ -12,14 +13,10 @@ int compact_chunk_entries(const LayerArgs& a) {
   return rb <= 128 ? 256 : (rb <= 256 ? 128 : 64);
 }
 
-// Key blocks of the prefill flags: one per (segment, 64 slots of capacity).
-constexpr int kPrefillFlagBlock = 64;
-
 static size_t control_layout(const LayerArgs& a, Control* c, char* base) {
   const int64_t S = (int64_t)a.B * a.H_kv;
   const int ch = compact_chunk_entries(a);
   const int64_t mc = a.total_slots / ch + S + 1;
-  const int64_t pb = a.total_slots / kPrefillFlagBlock + S + 1;
   size_t n = 0;
   auto take = [&](size_t bytes) {
     int* q = base ? reinterpret_cast<int*>(base + n) : nullptr;
@@ -32,8 +29,6 @@ static size_t control_layout(const LayerArgs& a, Control* c, char* base) {
   int* cmp_loaded = take(sizeof(int) * mc);
   int* cmp_done = take(sizeof(int) * S);
   int* cmp_glob = take(sizeof(int) * 2);
-  int* pre_flag = take(sizeof(int) * pb);
-  int* pre_glob = take(sizeof(int) * 2);
   if (c) {
     c->dec_cnt = dec_cnt;
     c->dec_cntb = dec_cntb;
@@ -41,11 +36,8 @@ static size_t control_layout(const LayerArgs& a, Control* c, char* base) {
     c->cmp_loaded = cmp_loaded;
     c->cmp_done = cmp_done;
     c->cmp_glob = cmp_glob;
-    c->pre_flag = pre_flag;
-    c->pre_glob = pre_glob;
     c->cmp_chunk = ch;
     c->max_chunks = (int)mc;
-    c->pre_blocks = (int)pb;
   }
   return n;
 }

@@ -455,12 +455,14 @@ def dense_logbias(terms: int, Kt: np.ndarray, lq: np.ndarray, lk: np.ndarray, lb
     need = int(rows.max()) if rows.size else -1
     col = np.zeros(N)
     out = np.full((rows.size, N), -np.inf)
-    want = {int(r): i for i, r in enumerate(rows)}
+    want = {}
+    for i, r in enumerate(rows):
+        want.setdefault(int(r), []).append(i)  # a row may be asked for more than once
     for t in range(0, need + 1):
         if t > 0:
             col[:t] += pair_term(terms, Kt[t], Kt[:t], lq[t], lk[:t], lb[t])
-        if t in want:
-            out[want[t], : t + 1] = col[: t + 1]
+        for i in want.get(t, ()):
+            out[i, : t + 1] = col[: t + 1]
     return out
 
 

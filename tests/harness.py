@@ -205,3 +205,179 @@ def run_decode_parity(cfg: LayerConfig, steps: int, log_p: float, compact_every:
                     assert np.array_equal(after[name][o : o + n], before[name][src]), \
                         f"step {step} seg {s}: moved {name} rows differ"
     return run
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+def _maxabs(a, b) -> float:
+    """max |a - b|; inf if either side holds a NaN (so a NaN can never pass)."""
+    d = np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))
+    return float("inf") if np.isnan(d).any() else float(np.max(d, initial=0.0))
+
+
+def _maxrel(a, b) -> float:
+    """max |a - b| / max(|b|, 1); inf on NaN."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    d = np.abs(a - b) / np.maximum(np.abs(b), 1.0)
+    return float("inf") if np.isnan(d).any() else float(np.max(d, initial=0.0))
+
+
+def _check_new_keys(cfg, od, k_in, pos0, k_gpu):
+    """Stored new keys (R17): within one bf16 ulp of the oracle's own rounding.
+
+    k_in [B, n, H_kv, d] raw keys, pos0 [B] first positions, k_gpu [B, n, H_kv, d].
+    """
+    B, n = k_in.shape[0], k_in.shape[1]
+    k_or = np.empty_like(k_gpu)
+    for b in range(B):
+        for t in range(n):
+            k_or[b, t] = U.round_cache(od, U.rope(U.l2_normalize(np.asarray(k_in[b, t], np.float64)),
+                                                  np.full(cfg.H_kv, pos0[b] + t), od.rope_base))
+    tol = np.maximum(ulp_bf16(k_or), 2e-7) if cfg.bf16 else 2e-6
+    bad = np.abs(k_gpu - k_or) > tol * 1.0001
+    assert not bad.any(), f"stored prefill key off by more than one ulp ({int(bad.sum())} elements)"
+
+
+def _stored_new(g, c_off, len_before, cfg, n, field):
+    """Rows [len_before, len_before + n) of every segment as [B, n, H_kv, ...]."""
+    out = []
+    for b in range(cfg.B):
+        rows = []
+        for h in range(cfg.H_kv):
+            s = b * cfg.H_kv + h
+            o = int(c_off[s]) + int(len_before[s])
+            rows.append(g[field][o : o + n])
+        out.append(np.stack(rows, axis=1))
+    return np.stack(out)
+
+
+def run_prefill_parity(cfg: LayerConfig, calls: Optional[int] = None, terms: int = 7, seed: int = 0,
+                       y_bf16: bool = False) -> dict:
+    """Chunked prefill on the GPU and in the oracle, compared after every call.
+
+    ``cfg.chunk`` tokens per call, ``calls`` calls (default n_total / chunk).
+    Compares y (max-abs), every cached log-bias (relative 1e-4), the stored
+    keys (one ulp), values (exact), key gates, lengths, positions and status.
+    """
+    import torch
+
+    calls = calls if calls is not None else cfg.n_total // cfg.chunk
+    n = cfg.chunk
+    w = make_weights(cfg, seed)
+    c = make_cache(cfg, w, seed)
+    layer = device_layer(cfg, w, c, terms=terms, max_tokens=n, y_bf16=y_bf16)
+    od, op = oracle_dims(cfg, terms), oracle_params(w)
+    oc = oracle_cache(cfg, c)
+    S = cfg.B * cfg.H_kv
+    rep = {"y_err": 0.0, "lam_err": 0.0, "lk_err": 0.0, "calls": calls}
+    for call in range(calls):
+        inp = make_step_inputs(cfg, call, n, seed)
+        len_before = layer.cache.seg_len.cpu().numpy().copy()
+        pos0 = layer.cache.next_pos.cpu().numpy().copy()
+        y_gpu, _ = layer.prefill(inp.q, inp.k, inp.v, inp.x)
+        torch.cuda.synchronize()
+        g = gpu_state(layer)
+        k_gpu = _stored_new(g, c.seg_off, len_before, cfg, n, "K")
+        _check_new_keys(cfg, od, inp.k, pos0, k_gpu)
+        v_gpu = _stored_new(g, c.seg_off, len_before, cfg, n, "V")
+        assert np.array_equal(v_gpu, inp.v.astype(np.float64)), f"call {call}: appended values differ"
+        y_or = U.prefill(od, op, oc, inp.q, inp.k, inp.v, inp.x, k_override=k_gpu)
+        y_err = _maxabs(y_gpu.float().cpu().numpy(), y_or)
+        lam_err = 0.0
+        lk_err = 0.0
+        for s in range(S):
+            o, m = int(c.seg_off[s]), int(g["seg_len"][s])
+            assert m == oc.lam[s].size, f"call {call} seg {s}: length differs"
+            lg, lo = g["lam"][o : o + m], oc.lam[s]
+            assert np.array_equal(np.isneginf(lg), np.isneginf(lo)), f"call {call} seg {s}: -inf pattern differs"
+            fin = np.isfinite(lo)
+            lam_err = max(lam_err, _maxrel(lg[fin], lo[fin]))
+            lk_err = max(lk_err, _maxrel(g["lk"][o : o + m], oc.lk[s]))
+        assert np.array_equal(g["next_pos"], oc.next_pos), f"call {call}: positions differ"
+        assert g["status"] == 0, f"call {call}: status {g['status']}"
+        rep["y_err"] = max(rep["y_err"], y_err)
+        rep["lam_err"] = max(rep["lam_err"], lam_err)
+        rep["lk_err"] = max(rep["lk_err"], lk_err)
+        assert y_err <= y_tol(cfg), f"call {call}: y max-abs error {y_err:.3e}"
+        assert lam_err <= 1e-4, f"call {call}: log-bias error {lam_err:.3e}"
+        assert lk_err <= 1e-5, f"call {call}: key-gate error {lk_err:.3e}"
+    return rep
+
+
+def run_prefill_sampled(cfg: LayerConfig, segments=(0,), rows_per_call: int = 3, seed: int = 0,
+                        terms: int = 7) -> dict:
+    """Full-size prefill from an empty cache, checked on sampled outputs.
+
+    Runs every call of ``cfg`` (chunk tokens each) on the GPU in the library's
+    normal launch configuration.  For each sampled segment, the oracle's dense
+    definitions (O5 as column sums, O7 per row) give y at ``rows_per_call``
+    random rows of every call (and the last token) and the final log-bias of
+    every key; the stored keys and key gates are checked for all tokens.
+    """
+    import torch
+
+    n = cfg.chunk
+    calls = cfg.n_total // n
+    N = n * calls
+    w = make_weights(cfg, seed)
+    c = make_cache(cfg, w, seed)
+    assert int(np.max(c.seg_len)) == 0, "sampled check starts from an empty cache"
+    layer = device_layer(cfg, w, c, terms=terms, max_tokens=n)
+    od, op = oracle_dims(cfg, terms), oracle_params(w)
+    rng = np.random.default_rng(1234)
+    bs = sorted({s // cfg.H_kv for s in segments})
+    q_all = {b: np.zeros((N, cfg.H_q, cfg.d), np.float32) for b in bs}
+    k_all = {b: np.zeros((N, cfg.H_kv, cfg.d), np.float32) for b in bs}
+    x_all = {b: np.zeros((N, cfg.D), np.float32) for b in bs}
+    rows, y_rows = [], []
+    for call in range(calls):
+        inp = make_step_inputs(cfg, call, n, seed)
+        y, _ = layer.prefill(inp.q, inp.k, inp.v, inp.x)
+        pick = set(int(t) for t in rng.choice(n, rows_per_call, replace=False))
+        if call == calls - 1:
+            pick.add(n - 1)
+        pick = sorted(pick)
+        y_rows.append(y[:, pick].float().cpu().numpy().astype(np.float64))
+        rows.extend(call * n + t for t in pick)
+        for b in bs:
+            q_all[b][call * n : (call + 1) * n] = inp.q[b]
+            k_all[b][call * n : (call + 1) * n] = inp.k[b]
+            x_all[b][call * n : (call + 1) * n] = inp.x[b]
+    torch.cuda.synchronize()
+    y_gpu = np.concatenate(y_rows, axis=1)  # [B, len(rows), H_q, d]
+    g = gpu_state(layer)
+    assert g["status"] == 0 and np.all(g["seg_len"] == N)
+    rows = np.asarray(rows)
+    G = cfg.H_q // cfg.H_kv
+    rep = {"y_err": 0.0, "lam_err": 0.0, "n_rows": int(rows.size) * len(segments)}
+    for s in segments:
+        b, h = divmod(s, cfg.H_kv)
+        o = int(c.seg_off[s])
+        Kt = g["K"][o : o + N]
+        k_or = U.round_cache(od, U.rope(U.l2_normalize(np.asarray(k_all[b][:, h], np.float64)), np.arange(N),
+                                        od.rope_base))
+        tol = np.maximum(ulp_bf16(k_or), 2e-7)
+        assert not np.any(np.abs(Kt - k_or) > tol * 1.0001), f"seg {s}: stored key off by more than one ulp"
+        lq, lk, lb = U.gates(od, op, x_all[b])
+        lkg = g["lk"][o : o + N]
+        assert np.max(np.abs(lkg - lk[:, h]) / np.maximum(np.abs(lk[:, h]), 1.0)) <= 1e-5, f"seg {s}: key gates"
+        lam_rows = U.dense_logbias(terms, Kt, lq[:, h], lk[:, h], lb[:, h], rows=np.append(rows, N - 1))
+        assert np.all(np.isfinite(Kt)) and np.all(np.isfinite(g["V"][o : o + N])), f"seg {s}: non-finite cache rows"
+        lam_fin, lo = g["lam"][o : o + N], lam_rows[-1]
+        fin = np.isfinite(lo)
+        assert np.array_equal(np.isneginf(lam_fin), np.isneginf(lo)), f"seg {s}: -inf pattern differs"
+        lam_err = _maxrel(lam_fin[fin], lo[fin])
+        V = g["V"][o : o + N]
+        for ri, i in enumerate(rows):
+            qt = U.rope(np.asarray(q_all[b][i, h * G : (h + 1) * G], np.float64), np.full(G, i), od.rope_base)
+            oi = U.attend(qt, Kt[: i + 1], V[: i + 1], lam_rows[ri, : i + 1], od.scale)
+            gam = U.output_gate(od, op, x_all[b][i])[h * G : (h + 1) * G]
+            y_or = gam * oi
+            assert np.all(np.isfinite(y_or)), f"seg {s} row {i}: oracle output not finite"
+            err = _maxabs(y_gpu[b, ri, h * G : (h + 1) * G], y_or)
+            rep["y_err"] = max(rep["y_err"], err)
+        rep["lam_err"] = max(rep["lam_err"], lam_err)
+    assert rep["y_err"] <= y_tol(cfg), f"sampled y max-abs error {rep['y_err']:.3e}"
+    assert rep["lam_err"] <= 1e-4, f"final log-bias error {rep['lam_err']:.3e}"
+    return rep

@@ -568,6 +568,11 @@ def test_dense_logbias_matches_recurrence():
     Lam = U.dense_logbias(dims.terms, kt[:, 0], U.log_sigmoid(z[:, 0]), U.log_sigmoid(z[:, 1]), U.log_sigmoid(z[:, 2]), rows=[n - 1, 5])
     np.testing.assert_allclose(Lam[0], cache.lam[0], rtol=1e-13, atol=1e-14)
     assert np.all(np.isneginf(Lam[1, 6:]))
+    # a row asked for twice is filled twice (the sampled full-size checks repeat the last row)
+    rep = U.dense_logbias(dims.terms, kt[:, 0], U.log_sigmoid(z[:, 0]), U.log_sigmoid(z[:, 1]),
+                          U.log_sigmoid(z[:, 2]), rows=[n - 1, 3, n - 1])
+    np.testing.assert_array_equal(rep[0], rep[2])
+    np.testing.assert_array_equal(rep[0], Lam[0])
 
 
 def test_overflow_sets_status_and_skips_append():

@@ -1,0 +1,180 @@
+"""Chunked-prefill parity: HIP path (C ABI) vs the fp64 oracle.
+
+Small cases compare every output, every cached log-bias, the stored keys,
+values and key gates after each call against the oracle's token-by-token
+prefill.  The full 1B prefill workload (B=2, 32/8 heads, 16 calls of 1024
+tokens) is checked on sampled rows and on the final log-bias vectors of
+sampled segments, computed one by one from the oracle's dense definitions.
+Cross-path identities: chunked == one-shot prefill, and decode at p = 0
+reproduces prefill.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+from ua_inputs import config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_pruning_amd import load
+
+    load()  # fails loudly if libua.so is missing
+
+
+def _run(cfg, **kw):
+    from tests.harness import run_prefill_parity
+
+    print(f"[prefill parity] {cfg.name} B={cfg.B} H={cfg.H_q}/{cfg.H_kv} d={cfg.d} chunk={cfg.chunk} "
+          f"n_total={cfg.n_total} {kw}", flush=True)
+    rep = run_prefill_parity(cfg, **kw)
+    print(f"  max |dy| {rep['y_err']:.2e}  max rel dLambda {rep['lam_err']:.2e}  max dlk {rep['lk_err']:.2e}",
+          flush=True)
+    return rep
+
+
+SMALL = dict(B=1, H_q=8, H_kv=2, D=256, n_total=256, chunk=128)
+
+
+def test_prefill_small_two_calls():
+    _run(config("1b-prefill", **SMALL))
+
+
+def test_prefill_ragged_chunks():
+    """Calls of 100 tokens: partial token blocks, lengths off the 64-key grid."""
+    _run(config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=300, chunk=100))
+
+
+def test_prefill_single_token_calls():
+    _run(config("1b-prefill", B=1, H_q=4, H_kv=1, D=64, n_total=5, chunk=1))
+
+
+def test_prefill_on_populated_cache():
+    """Cached entries carry stored biases that the call's column sums extend."""
+    cfg = config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=192, chunk=96, len_kind="lognormal",
+                 len_mean=120.0, len_min=16, len_max=400, nominal=400, lam_p0=0.15)
+    _run(cfg)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 4), (6, 2), (16, 2)])
+def test_prefill_group_sizes_d64(hq, hkv):
+    _run(config("1b-prefill", B=1, H_q=hq, H_kv=hkv, D=128, n_total=160, chunk=80))
+
+
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (6, 2), (8, 2)])
+def test_prefill_head_dim_128(hq, hkv):
+    _run(config("1b-prefill", B=1, H_q=hq, H_kv=hkv, d=128, D=256, n_total=160, chunk=80))
+
+
+@pytest.mark.parametrize("terms", [0, 1, 2, 4, 3, 5, 6])
+def test_prefill_term_subsets(terms):
+    _run(config("1b-prefill", **SMALL), terms=terms)
+
+
+def test_prefill_bf16_output():
+    _run(config("1b-prefill", **SMALL), y_bf16=True)
+
+
+def test_prefill_1b_heads_full_batch():
+    _run(config("1b-prefill", n_total=384, chunk=192))
+
+
+def test_prefill_segment_without_room():
+    """A segment lacking room for the call: status bit, zero outputs, segment untouched."""
+    import torch
+
+    from tests.harness import device_layer, gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-prefill", B=2, H_q=4, H_kv=2, D=64, n_total=64, chunk=64)
+    w = make_weights(cfg)
+    c = make_cache(cfg, w)
+    c.seg_cap[1] = 48  # segment 1 (b=0, h=1) cannot take 64 tokens
+    layer = device_layer(cfg, w, c, max_tokens=cfg.chunk)
+    inp = make_step_inputs(cfg, 0, cfg.chunk)
+    y, _ = layer.prefill(inp.q, inp.k, inp.v, inp.x)
+    torch.cuda.synchronize()
+    g = gpu_state(layer)
+    assert g["status"] & 1
+    assert list(g["seg_len"]) == [64, 0, 64, 64]
+    assert list(g["next_pos"]) == [64, 64]
+    yy = y.cpu().numpy()
+    G = cfg.H_q // cfg.H_kv
+    assert np.all(yy[0, :, G:2 * G] == 0.0)
+    assert np.all(np.isfinite(yy)) and np.any(yy[0, :, :G] != 0.0)
+
+
+def test_chunked_equals_one_shot():
+    """Four calls of 128 tokens == one call of 512 (both on the GPU)."""
+    import torch
+
+    from tests.harness import device_layer, gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=512, chunk=128)
+    w = make_weights(cfg)
+    c = make_cache(cfg, w)
+    whole = make_step_inputs(cfg, 0, 512)
+    one = device_layer(cfg, w, c, max_tokens=512)
+    y1, _ = one.prefill(whole.q, whole.k, whole.v, whole.x)
+    many = device_layer(cfg, w, c, max_tokens=128)
+    ys = []
+    for i in range(4):
+        sl = slice(128 * i, 128 * (i + 1))
+        yi, _ = many.prefill(whole.q[:, sl], whole.k[:, sl], whole.v[:, sl], whole.x[:, sl])
+        ys.append(yi)
+    torch.cuda.synchronize()
+    y4 = torch.cat(ys, dim=1)
+    err = float((y1 - y4).abs().max())
+    g1, g4 = gpu_state(one), gpu_state(many)
+    assert np.array_equal(g1["seg_len"], g4["seg_len"])
+    l1, l4 = g1["lam"], g4["lam"]
+    lam_err = float(np.max(np.abs(l1 - l4) / np.maximum(np.abs(l1), 1.0)))
+    print(f"chunked vs one-shot: max |dy| {err:.2e}, max rel dLambda {lam_err:.2e}")
+    assert err <= 1e-2 and lam_err <= 1e-4
+
+
+def test_decode_at_p0_reproduces_prefill():
+    """Token-by-token decode with p = 0 gives the prefill's outputs and biases."""
+    import torch
+
+    from tests.harness import device_layer, gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=160, chunk=160)
+    w = make_weights(cfg)
+    c = make_cache(cfg, w)
+    inp = make_step_inputs(cfg, 0, 160)
+    pre = device_layer(cfg, w, c, max_tokens=160)
+    yp, _ = pre.prefill(inp.q, inp.k, inp.v, inp.x)
+    dec = device_layer(cfg, w, c)
+    yd = []
+    for t in range(160):
+        yt, _ = dec.decode_step(inp.q[:, t], inp.k[:, t], inp.v[:, t], inp.x[:, t], -math.inf)
+        yd.append(yt.clone())
+    torch.cuda.synchronize()
+    yd = torch.stack(yd, dim=1)
+    err = float((yp - yd).abs().max())
+    gp, gd = gpu_state(pre), gpu_state(dec)
+    assert np.array_equal(gp["seg_len"], gd["seg_len"]) and np.array_equal(gp["next_pos"], gd["next_pos"])
+    assert np.array_equal(gp["K"], gd["K"]) or np.max(np.abs(gp["K"] - gd["K"])) <= 2.0**-8
+    lam_err = float(np.max(np.abs(gp["lam"] - gd["lam"]) / np.maximum(np.abs(gd["lam"]), 1.0)))
+    print(f"decode(p=0) vs prefill: max |dy| {err:.2e}, max rel dLambda {lam_err:.2e}")
+    assert err <= 1e-2 and lam_err <= 1e-4
+
+
+def test_prefill_1b_full_workload_sampled():
+    """The full 1B prefill workload (16 calls of 1024) on sampled rows and final biases."""
+    from tests.harness import run_prefill_sampled
+
+    cfg = config("1b-prefill")
+    rep = run_prefill_sampled(cfg, segments=(0, 13), rows_per_call=3)
+    print(f"full 1b-prefill sampled: max |dy| {rep['y_err']:.2e} over {rep['n_rows']} rows, "
+          f"max rel dLambda(final) {rep['lam_err']:.2e}", flush=True)
