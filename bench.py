@@ -9,8 +9,11 @@ independent layer instances (distinct caches, >= 1 GiB in total), as an
 R-layer model would, and throughput is counted per layer: value = B * R /
 step time.  Inputs are resident in HBM before timing starts.
 
-Prints one JSON line.  See the design doc for the roofline bytes and the
-oracle baseline.
+The same line carries a "prefill" object: the 1B-shape chunked prefill
+(B = 2, 16 calls of 1024 tokens from an empty cache) in tokens/s with its
+transcendental and MFMA rooflines and the oracle's own rate.
+
+Prints one JSON line.
 """
 
 from __future__ import annotations
@@ -32,17 +35,24 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 
 
-def kernel_source_hash() -> str:
+KERNEL_FILES = {
+    "decode": ["decode.hip", "ua_device.hpp", "ua_kernels.hpp"],
+    "prefill": ["prefill.hip", "ua_device.hpp", "ua_kernels.hpp"],
+}
+
+
+def kernel_source_hash(path: str) -> str:
+    """Hash of the sources of one path's kernels (counters go stale when it changes)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "kv_cache_pruning_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in KERNEL_FILES[path]:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(name: str, per_launch_alg: float):
+def load_traffic(name: str, path: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
     p = os.path.join(ROOT, "profiles", f"{name}_counters.json")
     if not os.path.exists(p):
@@ -51,7 +61,7 @@ def load_traffic(name: str, per_launch_alg: float):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("source_hash") != kernel_source_hash():
+    if d.get("source_hash") != kernel_source_hash(path):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -245,7 +255,7 @@ def bench_decode(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": load_traffic(f"decode_{cfg.name}", dec_bytes / n_calls),
+            "traffic": load_traffic(f"decode_{cfg.name}", "decode"),
             "kernel": "ua_decode_step = decode_token_kernel + decode_main_kernel (timed together per call)",
             "alg_bytes_per_launch": dec_bytes / n_calls,
         },
@@ -288,6 +298,10 @@ def main():
     ap.add_argument("--ring-bytes", type=float, default=1.0 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 1b-prefill figure")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first run three plain device copies of MIB MiB (a known-size reference for the HBM "
+                         "byte counters of a rocprofv3 --pmc run)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a "
@@ -301,15 +315,126 @@ def main():
     from kv_cache_pruning_amd import load
 
     load()
-    if args.workload.endswith("prefill"):
-        out = bench_prefill(args)
-    else:
-        out = bench_decode(args)
+    if args.copy_probe > 0:
+        src = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    out = bench_decode(args)
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill(args)
     print(json.dumps(out), flush=True)
 
 
-def bench_prefill(args):
-    raise SystemExit("prefill benchmark not built yet")
+# ---------------------------------------------------------------------------
+# prefill workload
+# ---------------------------------------------------------------------------
+# Transcendental issue rate of the chip: 256 CUs x 4 SIMDs x 16 lanes per
+# clock at quarter rate, 2.4 GHz.
+TRANS_PEAK_TS = 256 * 4 * 16 / 4 * 2.4e9 / 1e12
+
+
+def prefill_work(cfg, len0: int, n: int):
+    """Algorithmic work of one call: causal (token, key) pairs per KV group,
+    MFMA flops (G * 4d for Q.K^T and P.V plus 2d for K.K^T per pair) and
+    transcendentals (G softmax exponentials plus 3 for the pair term)."""
+    pairs_per_seg = n * len0 + n * (n + 1) // 2
+    pairs = pairs_per_seg * cfg.B * cfg.H_kv
+    G = cfg.H_q // cfg.H_kv
+    return pairs, pairs * (G * 4 * cfg.d + 2 * cfg.d), pairs * (G + 3)
+
+
+def bench_prefill(args, name: str = "1b-prefill", passes: int = 3, warm: int = 1):
+    import torch
+
+    from tests.harness import device_layer
+    from ua_inputs import config, make_cache, make_step_inputs, make_weights
+
+    cfg = config(name)
+    n = cfg.chunk
+    calls = cfg.n_total // n
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    layer = device_layer(cfg, w, c, max_tokens=n, y_bf16=True)
+    dt = torch.bfloat16
+    toks = []
+    for i in range(calls):
+        inp = make_step_inputs(cfg, i, n, 0)
+        toks.append([torch.from_numpy(a).to("cuda", dt) for a in (inp.q, inp.k, inp.v, inp.x)])
+    y = torch.empty((cfg.B, n, cfg.H_q, cfg.d), dtype=torch.bfloat16, device="cuda")
+    seg_len0 = layer.cache.seg_len.clone()
+    pos0 = layer.cache.next_pos.clone()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    call_ms = np.zeros(calls)
+    for p in range(warm + passes):
+        # every pass starts from the empty cache (lengths and positions reset; the
+        # slots it writes are rewritten before they are read)
+        layer.cache.seg_len.copy_(seg_len0)
+        layer.cache.next_pos.copy_(pos0)
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(calls):
+            layer.prefill(*toks[i], y=y)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        if p >= warm:
+            call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(calls)])
+    call_ms /= passes
+    st = int(layer.cache.status.item())
+    total_ms = float(call_ms.sum())
+    flops = trans = 0.0
+    for i in range(calls):
+        _, f, t = prefill_work(cfg, i * n, n)
+        flops += f
+        trans += t
+    tflops = flops / (total_ms * 1e-3) / 1e12
+    tts = trans / (total_ms * 1e-3) / 1e12
+    tokens = cfg.B * calls * n
+    return {
+        "workload": f"{cfg.name}: UA chunked prefill B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} D={cfg.D}, "
+                    f"{calls} calls of {n} tokens from an empty cache (N={cfg.n_total}), bf16 storage, y bf16",
+        "value": tokens / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_pass": total_ms,
+        "passes": passes,
+        "call_ms": [round(float(x), 4) for x in call_ms],
+        "status": st,
+        "roofline": {
+            "bound": "alu",
+            "achieved": tts,
+            "peak": TRANS_PEAK_TS,
+            "unit": "T transcendentals/s",
+            "frac": tts / TRANS_PEAK_TS,
+            "traffic": load_traffic(f"prefill_{cfg.name}", "prefill"),
+            "kernel": "ua_prefill = prep + token + attention kernels (timed per call)",
+            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFS},
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_prefill(cfg, args.cpu_seconds / 2),
+    }
+
+
+def cpu_baseline_prefill(cfg, budget_s: float):
+    """The fp64 oracle's token-by-token prefill on the first tokens of the first call."""
+    import oracle as U
+    from tests.harness import oracle_cache, oracle_dims, oracle_params
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    od, op, oc = oracle_dims(cfg), oracle_params(w), oracle_cache(cfg, c)
+    inp = make_step_inputs(cfg, 0, cfg.chunk, 0)
+    t0 = time.time()
+    m = 0
+    while m < cfg.chunk and time.time() - t0 < budget_s:
+        sl = slice(m, m + 16)
+        U.prefill(od, op, oc, inp.q[:, sl], inp.k[:, sl], inp.v[:, sl], inp.x[:, sl])
+        m += 16
+    dt = time.time() - t0
+    return {"value": cfg.B * m / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{cfg.name} call 0, first {m} tokens of each of the B={cfg.B} sequences from an empty cache "
+                      f"({dt:.1f} s, numpy fp64, one process; later tokens cost more)"}
 
 
 if __name__ == "__main__":

@@ -169,7 +169,10 @@ typedef struct ua_cache {
  * to coordinate workgroups: the whole workspace must be zero-filled once
  * before its first use (ua_workspace_init, or any zero fill), and every call
  * leaves that part zero again.  Calls that share a workspace must be ordered
- * on one stream; the rest of the workspace is scratch between calls.
+ * on one stream; the rest of the workspace is scratch between calls.  A
+ * workspace may be shared by calls whose dims have the same B and H_kv (the
+ * layers of one model, say) on caches of different sizes: size it with the
+ * largest total_slots, max_tokens_per_call and max_seg_cap among them.
  */
 size_t ua_workspace_bytes(const ua_dims* dims, int32_t max_tokens_per_call, int64_t total_slots, int32_t max_seg_cap);
 

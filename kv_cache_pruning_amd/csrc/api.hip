@@ -113,7 +113,7 @@ size_t ua_workspace_bytes(const ua_dims* dims, int32_t max_tokens_per_call, int6
   size_t n = ua::decode_ws_bytes(a, ua::decode_tile_entries(a.d));
   const size_t np = ua::prefill_ws_bytes(a, max_tokens_per_call, max_seg_cap);
   if (np > n) n = np;
-  return ua::control_bytes(a) + n;
+  return ua::control_bytes(a) + n + ua::control_tail_bytes(a);
 }
 
 ua_status ua_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -134,8 +134,8 @@ ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_
   LayerArgs a = make_args(dims, params, cache, in, y);
   const int twg = ua::decode_tile_entries(a.d);
   const size_t cb = ua::control_bytes(a);
-  if (ws_bytes < cb + ua::decode_ws_bytes(a, twg)) return UA_ERR_WORKSPACE;
-  const ua::Control ctl = ua::control_carve(a, ws);
+  if (ws_bytes < cb + ua::decode_ws_bytes(a, twg) + ua::control_tail_bytes(a)) return UA_ERR_WORKSPACE;
+  const ua::Control ctl = ua::control_carve(a, ws, ws_bytes);
   ua::DecodeWs w = ua::decode_ws_carve(a, ctl, reinterpret_cast<char*>(ws) + cb, twg);
   const hipError_t e = ua::launch_decode(a, w, log_p, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
@@ -152,10 +152,12 @@ ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cach
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, params, cache, in, y);
   const size_t cb = ua::control_bytes(a);
-  if (ws_bytes < cb) return UA_ERR_WORKSPACE;
-  const ua::Control ctl = ua::control_carve(a, ws);
-  const hipError_t e = ua::launch_prefill(a, ctl, n_tokens, 0, reinterpret_cast<char*>(ws) + cb, ws_bytes - cb,
-                                          reinterpret_cast<hipStream_t>(stream));
+  const size_t tb = ua::control_tail_bytes(a);
+  if (ws_bytes < cb + tb) return UA_ERR_WORKSPACE;
+  const ua::Control ctl = ua::control_carve(a, ws, ws_bytes);
+  // the scratch ends where the compaction flags begin
+  const hipError_t e = ua::launch_prefill(a, ctl, n_tokens, 0, reinterpret_cast<char*>(ws) + cb,
+                                          ws_bytes / 256 * 256 - tb - cb, reinterpret_cast<hipStream_t>(stream));
   if (e == hipErrorNotSupported) return UA_ERR_UNSUPPORTED;
   if (e == hipErrorOutOfMemory) return UA_ERR_WORKSPACE;
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
@@ -170,8 +172,8 @@ ua_status ua_compact(const ua_dims* dims, const ua_cache* cache, float log_p, in
   if (kept_idx && !aligned(kept_idx, 4)) return UA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, nullptr, cache, nullptr, nullptr);
-  if (ws_bytes < ua::control_bytes(a)) return UA_ERR_WORKSPACE;
-  const ua::Control ctl = ua::control_carve(a, ws);
+  if (ws_bytes < ua::control_bytes(a) + ua::control_tail_bytes(a)) return UA_ERR_WORKSPACE;
+  const ua::Control ctl = ua::control_carve(a, ws, ws_bytes);
   const hipError_t e = ua::launch_compact(a, ctl, log_p, kept_idx, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
     for (int s = sb; s < se; ++s) mine += max(1, (a.seg_cap[s] + CH - 1) / CH);
     int total;
     const int excl = block_exclusive_scan<kCompactThreads>(mine, s_scan, &total);
-    have = id < total;
+    have = id >= 0 && id < total;  // ids come from the self-resetting ticket
     if (have) {
       int run = excl;
       for (int s = sb; s < se; ++s) {

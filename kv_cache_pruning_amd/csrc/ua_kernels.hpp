@@ -49,9 +49,10 @@ struct LayerArgs {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Control block at the front of every workspace: counters and flags that
-// must be zero before the first call; every call returns them to zero.  All
-// three entry points carve it identically, so calls can share a workspace.
+// Control words of a workspace: counters and flags that must be zero before
+// the first call; every call returns them to zero.  The fixed part sits at
+// the front of the workspace, the compaction flags at its end (see
+// workspace.hip), so calls on caches of different sizes can share one.
 struct Control {
   int* dec_cnt;     // [S]           decode: arrivals per segment
   int* dec_cntb;    // [B]           decode: finished segments per sequence
@@ -64,8 +65,9 @@ struct Control {
 };
 
 int compact_chunk_entries(const LayerArgs& a);
-size_t control_bytes(const LayerArgs& a);
-Control control_carve(const LayerArgs& a, void* ws);
+size_t control_bytes(const LayerArgs& a);       // fixed part at the front
+size_t control_tail_bytes(const LayerArgs& a);  // compaction flags at the end
+Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes);
 
 // Decode scratch (after the control block) plus the counters it uses.
 struct DecodeWs {

@@ -1,8 +1,16 @@
-// Workspace control block: counters and flags of the decode and compaction
-// kernels.  They are zero before the first call and every call leaves them
-// zero, so one workspace can serve decode, prefill and compaction calls
-// issued in order on one stream (prefill keeps its own sync words in its
-// scratch and clears them at the start of each call).
+// Workspace layout shared by the three entry points:
+//
+//   [ fixed control | scratch of the call ... | compaction flags ]
+//   ^ ws                                       ^ end of ws - tail
+//
+// The fixed control words (decode and compaction arrival counters, the
+// compaction ticket) depend only on B and H_kv; the compaction flags (one
+// pair per chunk, so their number depends on total_slots) are carved from
+// the END of the workspace.  Layers of one shape whose caches differ in size
+// can then share one workspace sized for the largest: no call's scratch ever
+// overlaps another call's control words.  The control words are zero before
+// the first call and every call leaves them zero; prefill keeps its own sync
+// words in its scratch and clears them at the start of each call.
 
 #include "ua_kernels.hpp"
 
@@ -13,10 +21,12 @@ int compact_chunk_entries(const LayerArgs& a) {
   return rb <= 128 ? 256 : (rb <= 256 ? 128 : 64);
 }
 
-static size_t control_layout(const LayerArgs& a, Control* c, char* base) {
+static int64_t compact_max_chunks(const LayerArgs& a) {
+  return a.total_slots / compact_chunk_entries(a) + (int64_t)a.B * a.H_kv + 1;
+}
+
+static size_t fixed_layout(const LayerArgs& a, Control* c, char* base) {
   const int64_t S = (int64_t)a.B * a.H_kv;
-  const int ch = compact_chunk_entries(a);
-  const int64_t mc = a.total_slots / ch + S + 1;
   size_t n = 0;
   auto take = [&](size_t bytes) {
     int* q = base ? reinterpret_cast<int*>(base + n) : nullptr;
@@ -25,28 +35,32 @@ static size_t control_layout(const LayerArgs& a, Control* c, char* base) {
   };
   int* dec_cnt = take(sizeof(int) * S);
   int* dec_cntb = take(sizeof(int) * a.B);
-  int* cmp_state = take(sizeof(int) * mc);
-  int* cmp_loaded = take(sizeof(int) * mc);
   int* cmp_done = take(sizeof(int) * S);
   int* cmp_glob = take(sizeof(int) * 2);
   if (c) {
     c->dec_cnt = dec_cnt;
     c->dec_cntb = dec_cntb;
-    c->cmp_state = cmp_state;
-    c->cmp_loaded = cmp_loaded;
     c->cmp_done = cmp_done;
     c->cmp_glob = cmp_glob;
-    c->cmp_chunk = ch;
-    c->max_chunks = (int)mc;
   }
   return n;
 }
 
-size_t control_bytes(const LayerArgs& a) { return control_layout(a, nullptr, nullptr); }
+size_t control_bytes(const LayerArgs& a) { return fixed_layout(a, nullptr, nullptr); }
 
-Control control_carve(const LayerArgs& a, void* ws) {
+size_t control_tail_bytes(const LayerArgs& a) { return 2 * align_up(sizeof(int) * compact_max_chunks(a), 256); }
+
+Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes) {
   Control c{};
-  control_layout(a, &c, reinterpret_cast<char*>(ws));
+  char* base = reinterpret_cast<char*>(ws);
+  fixed_layout(a, &c, base);
+  const int64_t mc = compact_max_chunks(a);
+  const size_t one = align_up(sizeof(int) * mc, 256);
+  char* tail = base + (ws_bytes / 256 * 256) - 2 * one;  // callers check ws_bytes covers every part
+  c.cmp_state = reinterpret_cast<int*>(tail);
+  c.cmp_loaded = reinterpret_cast<int*>(tail + one);
+  c.cmp_chunk = compact_chunk_entries(a);
+  c.max_chunks = (int)mc;
   return c;
 }
 

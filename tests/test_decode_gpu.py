@@ -109,3 +109,50 @@ def test_segment_full_sets_status():
     finally:
         H.make_cache = orig
     assert len(run.reports) == 20
+
+
+def test_shared_workspace_across_cache_sizes():
+    """Two layers of one shape whose caches differ in size share one workspace.
+
+    The calls interleave (decode + compaction on A, then on B) and must give
+    exactly what each layer gives with a workspace of its own.
+    """
+    import torch
+
+    from kv_cache_pruning_amd.layer import DeviceCache, DeviceWeights, Layer, LayerShape, Workspace
+    from tests.harness import gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-decode", B=2)
+    shape = LayerShape(B=cfg.B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, D=cfg.D, r=cfg.r, bf16=True)
+    w = make_weights(cfg, 0)
+    dw = DeviceWeights(shape, w.W_dec, w.b_dec, w.W_dn, w.W_up, w.b_up)
+    inits = [make_cache(cfg, w, seed=0, extra=16), make_cache(cfg, w, seed=1, extra=4096)]
+    assert inits[0].slots != inits[1].slots
+
+    def dev(ci):
+        return DeviceCache(shape, ci.K, ci.V, ci.lam, ci.lk, ci.seg_off, ci.seg_len, ci.seg_cap, ci.next_pos)
+
+    shared_caches = [dev(ci) for ci in inits]
+    ws = Workspace(shape, max(shared_caches, key=lambda c: c.total_slots), 1)
+    shared = [Layer(shape, dw, c, workspace=ws) for c in shared_caches]
+    private = [Layer(shape, dw, dev(ci)) for ci in inits]
+    log_p = math.log(cfg.p)
+    for step in range(6):
+        inp = make_step_inputs(cfg, step, 1, 0)
+        args = (inp.q[:, 0], inp.k[:, 0], inp.v[:, 0], inp.x[:, 0])
+        ys, yp = [], []
+        for L in shared:
+            ys.append(L.decode_step(*args, log_p)[0])
+            L.compact(log_p)
+        for L in private:
+            yp.append(L.decode_step(*args, log_p)[0])
+            L.compact(log_p)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(ys[i], yp[i]), f"step {step} layer {i}: y differs with a shared workspace"
+            gs, gp = gpu_state(shared[i]), gpu_state(private[i])
+            assert np.array_equal(gs["seg_len"], gp["seg_len"]) and gs["status"] == gp["status"] == 0
+            for o, n in zip(gs["seg_off"], gs["seg_len"]):
+                assert np.array_equal(gs["lam"][o : o + n], gp["lam"][o : o + n])
+                assert np.array_equal(gs["K"][o : o + n], gp["K"][o : o + n])
