@@ -42,6 +42,7 @@
 //    The last workgroup to finish advances seg_len and next_pos.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -55,6 +56,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPTok = 16;                            // tokens per token-kernel workgroup
 constexpr int kPRows = 64;                           // tokens per attention workgroup
 constexpr int kPKeys = 64;                           // keys per block
+constexpr int kPThreads = 512;                       // attention workgroup: 8 waves
 constexpr int kMaxZ = 3 * kMaxHkv + kMaxRank;        // gate-projection columns
 constexpr float kRescaleTh = 8.0f;                   // log2 headroom of the softmax reference
 constexpr int kPrefillSpinLimit = 1 << 22;
@@ -69,7 +71,8 @@ struct PrefillWs {
   float* gl;       // [B*n, H_kv, 2]      (lq, lb)
   float* gam;      // [B*n, H_q*d]        output gate
   float* carry;    // [nrb-1, total_slots] per-key carry into token block I (log2 units)
-  int n, nrb, cp;
+  uint16_t* wut;   // [H_q*d, rp] bf16  W_up^T, ranks >= r zero
+  int n, nrb, cp, rp;
 };
 
 static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w) {
@@ -89,6 +92,8 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
   char* gl = take(sizeof(float) * 2 * (size_t)NT * a.H_kv);
   char* gam = take(sizeof(float) * (size_t)NT * a.H_q * a.d);
   char* carry = take(sizeof(float) * (size_t)(nrb - 1) * a.total_slots);
+  const int rp = (a.r + 31) / 32 * 32;
+  char* wut = take(sizeof(uint16_t) * (size_t)a.H_q * a.d * rp);
   if (w) {
     w->sync = reinterpret_cast<int*>(sync);
     w->wt = reinterpret_cast<uint16_t*>(wt);
@@ -96,9 +101,11 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
     w->gl = reinterpret_cast<float*>(gl);
     w->gam = reinterpret_cast<float*>(gam);
     w->carry = reinterpret_cast<float*>(carry);
+    w->wut = reinterpret_cast<uint16_t*>(wut);
     w->n = n;
     w->nrb = nrb;
     w->cp = cp;
+    w->rp = rp;
   }
   return off;
 }
@@ -136,9 +143,7 @@ __device__ __forceinline__ float u32x4_bf16(const u32x4& v, int e) {
   return (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) { return pack2_bf16(lo, hi); }
 
 // ---------------------------------------------------------------------------
 // 1. prep: clear sync words, transpose the gate projections
@@ -170,18 +175,34 @@ __global__ __launch_bounds__(256) void prefill_prep_kernel(LayerArgs a, PrefillW
     }
     *reinterpret_cast<u32x4*>(w.wt + (int64_t)c * Dm + kb) = u32x4{pk[0], pk[1], pk[2], pk[3]};
   }
+  const int HqD = a.H_q * a.d;
+  const uint16_t* Wu = reinterpret_cast<const uint16_t*>(a.W_up);
+  for (int e = gt; e < HqD * (w.rp / 8); e += gs) {
+    const int c = e % HqD;  // consecutive threads read consecutive columns
+    const int r8 = (e / HqD) * 8;
+    uint32_t pk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r0 = r8 + 2 * t, r1 = r0 + 1;
+      const uint32_t lo = r0 < a.r ? Wu[(int64_t)r0 * HqD + c] : 0u;
+      const uint32_t hi = r1 < a.r ? Wu[(int64_t)r1 * HqD + c] : 0u;
+      pk[t] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(w.wut + (int64_t)c * w.rp + r8) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+  }
 }
 
 // ---------------------------------------------------------------------------
 // 2. token kernel: gates, output gate, RoPE, append
 // ---------------------------------------------------------------------------
+constexpr int kTT = 512;  // token-kernel workgroup: 8 waves
+
 template <int D>
-__global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, PrefillWs w) {
+__global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, PrefillWs w) {
   constexpr int HALF = D / 2;
   constexpr int CH = D / 8;  // 16-byte chunks per head row
   __shared__ float s_z[kPTok][kMaxZ];
-  __shared__ __attribute__((aligned(16))) float s_ut[kMaxRank][kPTok];
-  __shared__ float s_cos[kPTok][HALF];
+    __shared__ float s_cos[kPTok][HALF];
   __shared__ float s_sin[kPTok][HALF];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
@@ -192,8 +213,8 @@ __global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, Prefill
   const int C3 = 3 * Hkv;
   const int Dm = a.D_model;
 
-  for (int i = tid; i < kPTok * kMaxZ; i += 256) (&s_z[0][0])[i] = 0.0f;
-  for (int e = tid; e < kPTok * HALF; e += 256) {
+  for (int i = tid; i < kPTok * kMaxZ; i += kTT) (&s_z[0][0])[i] = 0.0f;
+  for (int e = tid; e < kPTok * HALF; e += kTT) {
     const int tt = e / HALF, i = e - tt * HALF;
     const int tk = min(tok0 + tt, NT - 1);
     const int b = tk / n, t = tk - b * n;
@@ -204,42 +225,47 @@ __global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, Prefill
   }
   __syncthreads();
 
-  // ---- z = x [W_dec | W_dn]: A = x rows (tokens), B = W^T rows; waves split the k range
+  // ---- z = x [W_dec | W_dn]: A = x rows (tokens), B = W^T rows.  Each wave
+  // takes chunks of 8 k steps (256 columns of x); the weight fragments of up
+  // to three 16-column tiles are loaded together with the chunk's x.
   {
+    constexpr int KCH = 8;
     const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
     const int nks = (Dm + 31) / 32;
+    const int ntile = w.cp / 16;
     const int64_t xrow = (int64_t)min(tok0 + c16, NT - 1) * Dm;
     const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-    for (int nt = 0; nt < w.cp / 16; ++nt) {
-      const uint16_t* wrow = w.wt + (int64_t)(16 * nt + c16) * Dm;
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int k0 = wv; k0 < nks; k0 += 16) {
-        u32x4 av[4], bv[4];
+    for (int k0 = wv * KCH; k0 < nks; k0 += (kTT / 64) * KCH) {
+      for (int nt0 = 0; nt0 < ntile; nt0 += 3) {
+        u32x4 av[KCH], bv[3][KCH];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int ks = k0 + 4 * u;
-          const int kk = 32 * ks + 8 * g;
-          const bool ok = ks < nks && kk < Dm;
-          const int kc = ok ? kk : 0;
+        for (int u = 0; u < KCH; ++u) {
+          const int kk = 32 * (k0 + u) + 8 * g;
+          const int kc = kk < Dm ? kk : 0;
           av[u] = *reinterpret_cast<const u32x4*>(X + xrow + kc);
-          bv[u] = *reinterpret_cast<const u32x4*>(wrow + kc);
-          if (!ok) av[u] = zero4;
+#pragma unroll
+          for (int q = 0; q < 3; ++q)
+            bv[q][u] = *reinterpret_cast<const u32x4*>(w.wt + (int64_t)(16 * min(nt0 + q, ntile - 1) + c16) * Dm + kc);
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc = mfma_bf16(av[u], bv[u], acc);
-      }
+        for (int u = 0; u < KCH; ++u)
+          if (32 * (k0 + u) + 8 * g >= Dm) av[u] = zero4;  // past the end of x (Dm is a multiple of 8)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(&s_z[4 * g + i][16 * nt + c16], acc[i]);
+        for (int q = 0; q < 3; ++q) {
+          if (nt0 + q >= ntile) break;
+          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int u = 0; u < KCH; ++u) acc = mfma_bf16(av[u], bv[q][u], acc);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) atomicAdd(&s_z[4 * g + i][16 * (nt0 + q) + c16], acc[i]);
+        }
+      }
     }
   }
   __syncthreads();
 
   // ---- gates and the append of the key gate
-  for (int e = tid; e < kPTok * a.r; e += 256) {
-    const int tt = e / a.r, rr = e - tt * a.r;
-    s_ut[rr][tt] = s_z[tt][C3 + rr];
-  }
-  for (int e = tid; e < kPTok * Hkv; e += 256) {
+  for (int e = tid; e < kPTok * Hkv; e += kTT) {
     const int tt = e / Hkv, h = e - tt * Hkv;
     const int tk = tok0 + tt;
     if (tk >= NT) continue;
@@ -257,34 +283,49 @@ __global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, Prefill
     }
   }
 
-  // ---- rotated queries (bf16 copy); chunk c pairs dims [8c, 8c+8) with [HALF+8c, HALF+8c+8)
+  // ---- rotated queries (bf16 copy); chunk c pairs dims [8c, 8c+8) with
+  // [HALF+8c, HALF+8c+8).  Items go in batches of QB per thread with every
+  // load of a batch issued before any is used.
   {
+    constexpr int QB = 8;
     const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q);
-    for (int e = tid; e < kPTok * Hq * (CH / 2); e += 256) {
-      const int c = e % (CH / 2);
-      const int rest = e / (CH / 2);
-      const int hd = rest % Hq, tt = rest / Hq;
-      const int tk = tok0 + tt;
-      if (tk >= NT) continue;
-      const int64_t base = ((int64_t)tk * Hq + hd) * D;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(Q + base + 8 * c);
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(Q + base + HALF + 8 * c);
-      uint32_t olo[4], ohi[4];
+    const int nitem = kPTok * Hq * (CH / 2);
+    for (int e0 = 0; e0 < nitem; e0 += kTT * QB) {
+      u32x4 lo[QB], hi[QB];
+      int64_t base[QB];
 #pragma unroll
-      for (int u = 0; u < 8; u += 2) {
-        float rl[2], rh[2];
-#pragma unroll
-        for (int v2 = 0; v2 < 2; ++v2) {
-          const int i = 8 * c + u + v2;
-          const float xl = u32x4_bf16(lo, u + v2), xh = u32x4_bf16(hi, u + v2);
-          rl[v2] = fmaf(xl, s_cos[tt][i], -xh * s_sin[tt][i]);
-          rh[v2] = fmaf(xh, s_cos[tt][i], xl * s_sin[tt][i]);
-        }
-        olo[u / 2] = pack_bf16(rl[0], rl[1]);
-        ohi[u / 2] = pack_bf16(rh[0], rh[1]);
+      for (int u = 0; u < QB; ++u) {
+        const int e = min(e0 + u * kTT + tid, nitem - 1);
+        const int c = e % (CH / 2);
+        const int rest = e / (CH / 2);
+        const int hd = rest % Hq, tt = rest / Hq;
+        base[u] = ((int64_t)min(tok0 + tt, NT - 1) * Hq + hd) * D + 8 * c;
+        lo[u] = *reinterpret_cast<const u32x4*>(Q + base[u]);
+        hi[u] = *reinterpret_cast<const u32x4*>(Q + base[u] + HALF);
       }
-      *reinterpret_cast<u32x4*>(w.qbf + base + 8 * c) = u32x4{olo[0], olo[1], olo[2], olo[3]};
-      *reinterpret_cast<u32x4*>(w.qbf + base + HALF + 8 * c) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
+#pragma unroll
+      for (int u = 0; u < QB; ++u) {
+        const int e = e0 + u * kTT + tid;
+        const int c = e % (CH / 2);
+        const int tt = (e / (CH / 2)) / Hq;
+        if (e >= nitem || tok0 + tt >= NT) continue;
+        uint32_t olo[4], ohi[4];
+#pragma unroll
+        for (int v = 0; v < 8; v += 2) {
+          float rl[2], rh[2];
+#pragma unroll
+          for (int v2 = 0; v2 < 2; ++v2) {
+            const int i = 8 * c + v + v2;
+            const float xl = u32x4_bf16(lo[u], v + v2), xh = u32x4_bf16(hi[u], v + v2);
+            rl[v2] = fmaf(xl, s_cos[tt][i], -xh * s_sin[tt][i]);
+            rh[v2] = fmaf(xh, s_cos[tt][i], xl * s_sin[tt][i]);
+          }
+          olo[v / 2] = pack_bf16(rl[0], rl[1]);
+          ohi[v / 2] = pack_bf16(rh[0], rh[1]);
+        }
+        *reinterpret_cast<u32x4*>(w.qbf + base[u]) = u32x4{olo[0], olo[1], olo[2], olo[3]};
+        *reinterpret_cast<u32x4*>(w.qbf + base[u] + HALF) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
+      }
     }
   }
 
@@ -294,7 +335,7 @@ __global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, Prefill
     const uint16_t* Vin = reinterpret_cast<const uint16_t*>(a.v);
     uint16_t* Kc = reinterpret_cast<uint16_t*>(a.K);
     uint16_t* Vc = reinterpret_cast<uint16_t*>(a.V);
-    for (int e = tid; e < kPTok * Hkv; e += 256) {
+    for (int e = tid; e < kPTok * Hkv; e += kTT) {
       const int tt = e / Hkv, h = e - tt * Hkv;
       const int tk = tok0 + tt;
       if (tk >= NT) continue;
@@ -336,75 +377,94 @@ __global__ __launch_bounds__(256) void prefill_token_kernel(LayerArgs a, Prefill
         *reinterpret_cast<u32x4*>(Kc + dst + HALF + 8 * c) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
       }
     }
-    for (int e = tid; e < kPTok * Hkv * CH; e += 256) {
-      const int c = e % CH;
-      const int rest = e / CH;
-      const int h = rest % Hkv, tt = rest / Hkv;
-      const int tk = tok0 + tt;
-      if (tk >= NT) continue;
-      const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
-      const int len0 = a.seg_len[s];
-      if ((int64_t)len0 + n > a.seg_cap[s]) continue;
-      *reinterpret_cast<u32x4*>(Vc + (a.seg_off[s] + len0 + t) * D + 8 * c) =
-          *reinterpret_cast<const u32x4*>(Vin + ((int64_t)tk * Hkv + h) * D + 8 * c);
+    constexpr int VB = 4;
+    const int nv = kPTok * Hkv * CH;
+    for (int e0 = 0; e0 < nv; e0 += kTT * VB) {
+      u32x4 vv[VB];
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const int e = min(e0 + u * kTT + tid, nv - 1);
+        const int c = e % CH, rest = e / CH;
+        const int h = rest % Hkv, tt = rest / Hkv;
+        vv[u] = *reinterpret_cast<const u32x4*>(Vin + ((int64_t)min(tok0 + tt, NT - 1) * Hkv + h) * D + 8 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const int e = e0 + u * kTT + tid;
+        const int c = e % CH, rest = e / CH;
+        const int h = rest % Hkv, tt = rest / Hkv;
+        const int tk = tok0 + tt;
+        if (e >= nv || tk >= NT) continue;
+        const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
+        const int len0 = a.seg_len[s];
+        if ((int64_t)len0 + n > a.seg_cap[s]) continue;
+        *reinterpret_cast<u32x4*>(Vc + (a.seg_off[s] + len0 + t) * D + 8 * c) = vv[u];
+      }
     }
   }
-  __syncthreads();  // s_ut
 
-  // ---- output gate, four columns x 16 tokens per thread
+  // ---- output gate sigmoid(u W_up + b_up) on the matrix cores: A = u (16
+  // tokens x rp ranks) as a bf16 high part plus a bf16 low part (u - high),
+  // B = rows of W_up^T (16 columns per tile)
   {
     const int HqD = Hq * D;
-    const uint16_t* Wu = reinterpret_cast<const uint16_t*>(a.W_up);
-    for (int cg = tid; cg < HqD / 4; cg += 256) {
-      const int c0 = 4 * cg;
-      float bias[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (a.b_up) {
+    const int ntile = HqD / 16;
+    u32x4 ahi[2], alo[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bias[j] = a.b_up[c0 + j];
-      }
-      float acc[kPTok][4];
+    for (int ks = 0; ks < 2; ++ks) {
+      uint32_t ph[4], pl[4];
 #pragma unroll
-      for (int tt = 0; tt < kPTok; ++tt)
+      for (int v = 0; v < 4; ++v) {
+        float x2[2], h2[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[tt][j] = bias[j];
-      for (int rr = 0; rr < a.r; ++rr) {
-        const uint2 wr = *reinterpret_cast<const uint2*>(Wu + (int64_t)rr * HqD + c0);
-        const float w4[4] = {bf16_lo(wr.x), bf16_hi(wr.x), bf16_lo(wr.y), bf16_hi(wr.y)};
-        const float4* u4 = reinterpret_cast<const float4*>(&s_ut[rr][0]);
-#pragma unroll
-        for (int q4 = 0; q4 < kPTok / 4; ++q4) {
-          const float4 u = u4[q4];
-          const float uu[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-          for (int z = 0; z < 4; ++z)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[4 * q4 + z][j] = fmaf(uu[z], w4[j], acc[4 * q4 + z][j]);
+        for (int z = 0; z < 2; ++z) {
+          const int rr = 32 * ks + 8 * g + 2 * v + z;
+          x2[z] = rr < a.r ? s_z[c16][C3 + rr] : 0.0f;
         }
+        ph[v] = pack2_bf16(x2[0], x2[1]);
+        h2[0] = bf16_lo(ph[v]);
+        h2[1] = bf16_hi(ph[v]);
+        pl[v] = pack2_bf16(x2[0] - h2[0], x2[1] - h2[1]);
       }
+      ahi[ks] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      alo[ks] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+    }
+    const int nks = w.rp / 32;
+    constexpr int TB = 4;
+    for (int nt0 = wv; nt0 < ntile; nt0 += (kTT / 64) * TB) {
+      u32x4 bv[TB][2];
 #pragma unroll
-      for (int tt = 0; tt < kPTok; ++tt) {
-        const int tk = tok0 + tt;
-        if (tk < NT)
-          *reinterpret_cast<float4*>(w.gam + (int64_t)tk * HqD + c0) =
-              make_float4(sigmoid(acc[tt][0]), sigmoid(acc[tt][1]), sigmoid(acc[tt][2]), sigmoid(acc[tt][3]));
+      for (int u = 0; u < TB; ++u)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int nt = min(nt0 + (kTT / 64) * u, ntile - 1);
+          bv[u][ks] = *reinterpret_cast<const u32x4*>(w.wut + (int64_t)(16 * nt + c16) * w.rp + 32 * min(ks, nks - 1) + 8 * g);
+        }
+#pragma unroll
+      for (int u = 0; u < TB; ++u) {
+        const int nt = nt0 + (kTT / 64) * u;
+        if (nt >= ntile) break;
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          if (ks >= nks) break;
+          acc = mfma_bf16(ahi[ks], bv[u][ks], acc);
+          acc = mfma_bf16(alo[ks], bv[u][ks], acc);
+        }
+        const int col = 16 * nt + c16;
+        const float bias = a.b_up ? a.b_up[col] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tk = tok0 + 4 * g + i;
+          if (tk < NT) w.gam[(int64_t)tk * HqD + col] = sigmoid_fast(acc[i] + bias);
+        }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------------------
 // 3. attention with the causal decay bias
 // ---------------------------------------------------------------------------
-// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr 1, 2, 4, 8;
-// lanes without a source read 0).
-__device__ __forceinline__ float scan16(float x) {
-  x += dpp_f<0x111>(x);
-  x += dpp_f<0x112>(x);
-  x += dpp_f<0x114>(x);
-  x += dpp_f<0x118>(x);
-  return x;
-}
-
 // Position of key k (0..63) of a block in the LDS copy of V^T: the P V product
 // takes its k index from the score tiles, where lane group q of 16 lanes holds
 // keys 4q..4q+3 of each 16-key tile; MFMA k index 8q + i of 32-key chunk c
@@ -415,23 +475,30 @@ __device__ __forceinline__ int vt_pos(int k) {
 }
 
 template <int D, int HG>
-__global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillWs w) {
-  constexpr int KC = D / 32;                        // k steps of a head-dim dot product
-  constexpr int DT = D / 16;                        // 16-wide output tiles per head
-  constexpr int KS = D + 8;                         // s_k row stride (bf16)
-  constexpr int VS = kPKeys + 8;                    // s_vt row stride (fp16)
-  constexpr int KPT = kPKeys * (D / 8) / 256;       // K pieces per thread per block
-  constexpr int VPT = (kPKeys / 2) * (D / 8) / 256; // V (key pair, 8 dims) items per thread
-  static_assert(KPT >= 1 && VPT >= 1, "tile split");
+__global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, PrefillWs w) {
+  constexpr int KC = D / 32;                          // k steps of a head-dim dot product
+  constexpr int DT = D / 16;                          // 16-wide output tiles per head
+  constexpr int KS = D + 8;                           // s_k row stride (bf16)
+  constexpr int VS = kPKeys + 8;                      // s_vt row stride (fp16)
+  constexpr int KPT = kPKeys * (D / 8) / kPThreads;   // K pieces per thread per block
+  constexpr int VITEMS = (kPKeys / 2) * (D / 8);      // V (key pair, 8 dims) items per block
+  constexpr int VPT = (VITEMS + kPThreads - 1) / kPThreads;
+  constexpr int XS = DT * 4 + 2;                      // floats per lane in the final merge
+  static_assert(KPT >= 1, "tile split");
+  static_assert(4 * 64 * XS * 4 <= (int)sizeof(uint16_t) * 2 * kPKeys * KS, "merge buffer fits in s_k");
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kPKeys * KS];
   __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][D * VS];
   __shared__ __attribute__((aligned(16))) float s_lk[2][kPKeys];
   __shared__ __attribute__((aligned(16))) float s_tot[2][4][kPKeys];
   __shared__ __attribute__((aligned(16))) float s_car[2][kPKeys];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kPRows * HG * D];  // rotated queries of the token block
   __shared__ int s_id;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, so branches on it stay scalar
+  const int tw = wv & 3;   // token quarter: tokens 16 tw .. 16 tw + 15 of the block
+  const int hp = wv >> 2;  // key half: keys 32 hp .. 32 hp + 31 of every key block
   const int S = a.B * a.H_kv;
   const int n = w.n, nrb = w.nrb;
   const int Hq = a.H_q, Hkv = a.H_kv;
@@ -445,7 +512,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
   const int len0 = a.seg_len[s];
   const int64_t off = a.seg_off[s];
   const bool room = (int64_t)len0 + n <= a.seg_cap[s];
-  const int row_lo = I * kPRows + wv * 16;  // first token of this wave
+  const int row_lo = I * kPRows + tw * 16;  // first token of this wave
   const int tq = row_lo + c16;              // this lane's token (score column)
   const bool row_ok = tq < n;
   const int tqc = min(tq, n - 1);
@@ -466,12 +533,15 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
     const float lq = w.gl[2 * (tok * Hkv + h) + 0];
     const float lb = w.gl[2 * (tok * Hkv + h) + 1];
     const float row2 = pc.inv_n2 * (((a.terms & 1) ? lq : 0.0f) + ((a.terms & 4) ? lb : 0.0f));
-    u32x4 qf[HG][KC], krf[KC];
-#pragma unroll
-    for (int hh = 0; hh < HG; ++hh)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        qf[hh][kc] = *reinterpret_cast<const u32x4*>(w.qbf + (tok * Hq + a0 + hh) * D + 32 * kc + 8 * g);
+    // the block's rotated queries to LDS: [token][head][dim], rows of tokens past n clamped
+    for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreads) {
+      const int tt = q / (HG * (D / 8)), rest = q - tt * (HG * (D / 8));
+      const int64_t tk = (int64_t)b * n + min(I * kPRows + tt, n - 1);
+      *reinterpret_cast<u32x4*>(&s_q[q * 8]) =
+          *reinterpret_cast<const u32x4*>(w.qbf + (tk * Hq + a0) * D + rest * 8);
+    }
+    const uint16_t* qrow = &s_q[(tw * 16 + c16) * HG * D + 8 * g];  // this lane's token, k offset 8 g
+    u32x4 krf[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
       krf[kc] = *reinterpret_cast<const u32x4*>(Kc + (off + len0 + tqc) * D + 32 * kc + 8 * g);
@@ -484,34 +554,38 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
       const int j0 = J * kPKeys;
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
-        const int q = tid + 256 * u, key = q / (D / 8), part = q % (D / 8);
+        const int q = tid + kPThreads * u, key = q / (D / 8), part = q % (D / 8);
         kst[u] = *reinterpret_cast<const u32x4*>(Kc + slot(j0 + key) * D + 8 * part);
       }
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int q = tid + 256 * u, p = q / (D / 8), part = q % (D / 8);
+        const int q = min(tid + kPThreads * u, VITEMS - 1), p = q / (D / 8), part = q % (D / 8);
         vst[u][0] = *reinterpret_cast<const u32x4*>(Vc + slot(j0 + 2 * p) * D + 8 * part);
         vst[u][1] = *reinterpret_cast<const u32x4*>(Vc + slot(j0 + 2 * p + 1) * D + 8 * part);
       }
       lkst = a.lk[slot(j0 + lane)];
     };
+    const float col_scale = (a.terms & 2) ? pc.inv_n2 : 0.0f;  // key-side part of the pair term
     auto store_k = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
-        const int q = tid + 256 * u, key = q / (D / 8), part = q % (D / 8);
+        const int q = tid + kPThreads * u, key = q / (D / 8), part = q % (D / 8);
         *reinterpret_cast<u32x4*>(&s_k[buf][key * KS + 8 * part]) = kst[u];
       }
-      if (wv == 0) s_lk[buf][lane] = lkst;
+      if (wv == 0) s_lk[buf][lane] = lkst * col_scale;
     };
     auto store_v = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int q = tid + 256 * u, p = q / (D / 8), part = q % (D / 8);
-        const int pos = vt_pos(2 * p);
+        const int q = tid + kPThreads * u;
+        if (VITEMS % kPThreads == 0 || q < VITEMS) {
+          const int p = q / (D / 8), part = q % (D / 8);
+          const int pos = vt_pos(2 * p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const auto hv = __builtin_amdgcn_cvt_pkrtz(u32x4_bf16(vst[u][0], e), u32x4_bf16(vst[u][1], e));
-          *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
+          for (int e = 0; e < 8; ++e) {
+            const auto hv = __builtin_amdgcn_cvt_pkrtz(u32x4_bf16(vst[u][0], e), u32x4_bf16(vst[u][1], e));
+            *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
+          }
         }
       }
     };
@@ -521,16 +595,27 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
     store_v(0);
     __syncthreads();
 
+    // Online softmax per (query head, token) over this wave's key halves.  P is
+    // taken relative to m_run (log2 units), which is only raised when a block
+    // exceeds it by more than 2^kRescaleTh, and set at the first block where
+    // the token has a valid key in this half (mset).
     float m_run[HG];
-    f32x4 cinit[HG], O[HG][DT], Lt[HG];
+    int mset = 0;  // bit hh: the reference of head hh is set
+    f32x4 O[HG][DT], Lt[HG];
+    const float inv_cs = 1.0f / cs;
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       m_run[hh] = 0.0f;
-      cinit[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       Lt[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) O[hh][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    // Carry into this token block for the next key block, fetched one iteration
+    // ahead (wave 0, lane = key): the stored bias for the token block that
+    // starts the key block's chain, else the previous token block's published
+    // carry if it is already there.  Raw values; scaled where used.
+    float car_cur = 0.0f, car_nxt = 0.0f;
+    bool have_cur = false, have_nxt = false, init_cur = false, init_nxt = false;
     f16x8 ones;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones[e] = (c16 == 0) ? (_Float16)1.0f : (_Float16)0.0f;
@@ -540,48 +625,103 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
       const int j0 = J * kPKeys;
       const bool more = J + 1 < nJ;
       if (more) load_block(J + 1);
-
-      u32x4 kf[4][KC];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          kf[kt][kc] = *reinterpret_cast<const u32x4*>(&s_k[cb][(16 * kt + c16) * KS + 32 * kc + 8 * g]);
-      // some element of this wave's tile is masked (causal edge or tokens past n)
-      const bool edge = (j0 + kPKeys - 1 >= len0 + row_lo) || (row_lo + 15 >= n);
-
-      // ---- pair terms, scanned over this wave's 16 tokens
-      float lam[4][4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        f32x4 sim = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) sim = mfma_bf16(kf[kt][kc], krf[kc], sim);
-        const float4 lk4 = *reinterpret_cast<const float4*>(&s_lk[cb][16 * kt + 4 * g]);
-        const float lkv[4] = {lk4.x, lk4.y, lk4.z, lk4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float col2 = (a.terms & 2) ? pc.inv_n2 * lkv[i] : 0.0f;
-          float A2 = pair_A2(pc, row2, col2, sim[i]);
-          if (edge) {
-            const int jg = j0 + 16 * kt + 4 * g + i;
-            A2 = (row_ok && jg < len0 + tq) ? A2 : 0.0f;
-          }
-          lam[kt][i] = scan16(A2);
+      const int Ist_next = (j0 + kPKeys >= len0) ? (j0 + kPKeys - len0) / kPRows : 0;
+      const bool chain_next = more && I > Ist_next;
+      int flag_next = 0;
+      have_nxt = false;
+      init_nxt = false;
+      if (wv == 0 && more) {
+        if (!chain_next) {
+          car_nxt = a.lam[off + min(j0 + kPKeys + lane, nkeys - 1)];
+          have_nxt = init_nxt = true;
+        } else {
+          flag_next = ldi_coh_p(&w.sync[2 + s * nrb + I - 1]);  // used after the barrier
         }
       }
+
+      // this wave's key fragments: 16-key tiles kt = 2 hp, 2 hp + 1
+      u32x4 kf[2][KC];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          kf[t][kc] =
+              *reinterpret_cast<const u32x4*>(&s_k[cb][(32 * hp + 16 * t + c16) * KS + 32 * kc + 8 * g]);
+      // some element of this wave's tile is masked (causal edge or tokens past n)
+      const bool edge = (j0 + 32 * hp + 31 >= len0 + row_lo) || (row_lo + 15 >= n);
+
+      // ---- pair terms, scanned over this wave's 16 tokens.  The enabled terms
+      // and the causal edge are uniform per block, so each combination is a
+      // branch-free variant and the eight pairs of a lane interleave.
+      float lam[2][4];
+      auto pair_terms = [&](auto edge_c, auto sim_c) {
+        constexpr bool EDGE = decltype(edge_c)::value, SIM = decltype(sim_c)::value;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4 sim = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (SIM) {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) sim = mfma_bf16(kf[t][kc], krf[kc], sim);
+          }
+          const float4 lk4 = *reinterpret_cast<const float4*>(&s_lk[cb][32 * hp + 16 * t + 4 * g]);
+          const float lkv[4] = {lk4.x, lk4.y, lk4.z, lk4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float lam2 = row2 + lkv[i];
+            if constexpr (SIM) lam2 = fmaf(pc.sim_w, __builtin_amdgcn_logf(fminf(sim[i] * sim[i], 1.0f)), lam2);
+            float A2 = log1mexp2_b2(lam2);
+            if constexpr (EDGE) {
+              const int jg = j0 + 32 * hp + 16 * t + 4 * g + i;
+              A2 = (row_ok && jg < len0 + tq) ? A2 : 0.0f;
+            }
+            lam[t][i] = A2;
+          }
+        }
+      };
+      if (!pc.any) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lam[t][i] = 0.0f;
+      } else if (edge) {
+        if (pc.sim) pair_terms(std::true_type{}, std::true_type{});
+        else pair_terms(std::true_type{}, std::false_type{});
+      } else {
+        if (pc.sim) pair_terms(std::false_type{}, std::true_type{});
+        else pair_terms(std::false_type{}, std::false_type{});
+      }
+      // inclusive scans over the 16 lanes of each row, step-major so the eight
+      // independent scans fill each other's DPP hazard slots
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[t][i] += dpp_f<0x111>(lam[t][i]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[t][i] += dpp_f<0x112>(lam[t][i]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[t][i] += dpp_f<0x114>(lam[t][i]);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[t][i] += dpp_f<0x118>(lam[t][i]);
       if (c16 == 15) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          *reinterpret_cast<float4*>(&s_tot[cb][wv][16 * kt + 4 * g]) =
-              make_float4(lam[kt][0], lam[kt][1], lam[kt][2], lam[kt][3]);
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<float4*>(&s_tot[cb][tw][32 * hp + 16 * t + 4 * g]) =
+              make_float4(lam[t][0], lam[t][1], lam[t][2], lam[t][3]);
       }
       // ---- carry into this token block for the block's keys
       if (wv == 0) {
         const int jg = j0 + lane;
         const int Ist = j0 >= len0 ? (j0 - len0) / kPRows : 0;  // first token block that sees key block J
         float v;
-        if (I == Ist) {
+        if (have_cur) {
+          v = init_cur ? ((jg < len0) ? car_cur * kLog2e : 0.0f) : car_cur;
+        } else if (I == Ist) {
           v = (jg < len0) ? a.lam[off + jg] * kLog2e : 0.0f;
         } else {
           const int* flag = &w.sync[2 + s * nrb + I - 1];
@@ -599,25 +739,31 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
       }
       if (more) store_k(nb);
       __syncthreads();
+      // wave 0: fetch the next block's carry now if its producer has published it
+      if (wv == 0 && chain_next && flag_next >= J + 2) {
+        car_nxt = ldf_coh_p(&w.carry[(int64_t)(I - 1) * TS + off + min(j0 + kPKeys + lane, nkeys - 1)]);
+        have_nxt = true;
+      }
 
       // ---- bias of this wave's elements (log2 units)
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float4 pre = *reinterpret_cast<const float4*>(&s_car[cb][16 * kt + 4 * g]);
-        for (int w2 = 0; w2 < wv; ++w2) {
-          const float4 t4 = *reinterpret_cast<const float4*>(&s_tot[cb][w2][16 * kt + 4 * g]);
+      for (int t = 0; t < 2; ++t) {
+        const int k4 = 32 * hp + 16 * t + 4 * g;
+        float4 pre = *reinterpret_cast<const float4*>(&s_car[cb][k4]);
+        for (int w2 = 0; w2 < tw; ++w2) {
+          const float4 t4 = *reinterpret_cast<const float4*>(&s_tot[cb][w2][k4]);
           pre.x += t4.x;
           pre.y += t4.y;
           pre.z += t4.z;
           pre.w += t4.w;
         }
-        lam[kt][0] += pre.x;
-        lam[kt][1] += pre.y;
-        lam[kt][2] += pre.z;
-        lam[kt][3] += pre.w;
+        lam[t][0] += pre.x;
+        lam[t][1] += pre.y;
+        lam[t][2] += pre.z;
+        lam[t][3] += pre.w;
       }
       // ---- carry out to the next token block, or the final bias of the call
-      if (wv == 3) {
+      if (wv == 4) {
         const int jg = j0 + lane;
         const float cn =
             s_car[cb][lane] + s_tot[cb][0][lane] + s_tot[cb][1][lane] + s_tot[cb][2][lane] + s_tot[cb][3][lane];
@@ -630,94 +776,119 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
         }
       }
 
-      // ---- softmax and P V per query head
-      f16x8 vf[DT][2];
+      // ---- softmax and P V per query head over this wave's 32 keys
+      f16x8 vf[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          vf[dt][c] = *reinterpret_cast<const f16x8*>(&s_vt[cb][(16 * dt + c16) * VS + 32 * c + 8 * g]);
+        vf[dt] = *reinterpret_cast<const f16x8*>(&s_vt[cb][(16 * dt + c16) * VS + 32 * hp + 8 * g]);
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh) {
-        float e[4][4];
+        float e[2][4];
         float bm = kNegInf;
+        u32x4 qf[KC];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          f32x4 sc = cinit[hh];
+        for (int kc = 0; kc < KC; ++kc) qf[kc] = *reinterpret_cast<const u32x4*>(qrow + hh * D + 32 * kc);
+        const float ci = -m_run[hh] * inv_cs;  // the reference folded into the accumulator's start
+        auto logits = [&](auto edge_c) {
+          constexpr bool EDGE = decltype(edge_c)::value;
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16(kf[kt][kc], qf[hh][kc], sc);
+          for (int t = 0; t < 2; ++t) {
+            f32x4 sc = f32x4{ci, ci, ci, ci};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float ev = fmaf(sc[i], cs, lam[kt][i]);
-            if (edge) {
-              const int jg = j0 + 16 * kt + 4 * g + i;
-              ev = (row_ok && jg <= len0 + tq) ? ev : kNegInf;
+            for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16(kf[t][kc], qf[kc], sc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float ev = fmaf(sc[i], cs, lam[t][i]);
+              if constexpr (EDGE) {
+                const int jg = j0 + 32 * hp + 16 * t + 4 * g + i;
+                ev = (row_ok && jg <= len0 + tq) ? ev : kNegInf;
+              }
+              e[t][i] = ev;
+              bm = fmaxf(bm, ev);
             }
-            e[kt][i] = ev;
-            bm = fmaxf(bm, ev);
           }
-        }
-        if (J == 0 || __any(bm > kRescaleTh)) {
+        };
+        if (edge) logits(std::true_type{});
+        else logits(std::false_type{});
+        const bool fresh = ((mset >> hh) & 1) == 0;
+        if (__any(bm > kRescaleTh || (fresh && bm > kNegInf))) {
           float bx = fmaxf(bm, __shfl_xor(bm, 16, 64));
           bx = fmaxf(bx, __shfl_xor(bx, 32, 64));
-          float dl;
-          if (J == 0) {
-            dl = (bx > kNegInf) ? bx : 0.0f;
-          } else {
-            dl = fmaxf(bx, 0.0f);
-            const float al = __builtin_amdgcn_exp2f(-dl);
+          const float dl = fresh ? ((bx > kNegInf) ? bx : 0.0f) : fmaxf(bx, 0.0f);
+          const float al = fresh ? 1.0f : __builtin_amdgcn_exp2f(-dl);  // nothing accumulated yet when fresh
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) O[hh][dt] *= al;
-            Lt[hh] *= al;
-          }
+          for (int dt = 0; dt < DT; ++dt) O[hh][dt] *= al;
+          Lt[hh] *= al;
           m_run[hh] += dl;
-          const float ci = -m_run[hh] / cs;
-          cinit[hh] = f32x4{ci, ci, ci, ci};
+          if (bx > kNegInf) mset |= 1 << hh;
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+          for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) e[kt][i] -= dl;
+            for (int i = 0; i < 4; ++i) e[t][i] -= dl;
         }
-        f16x8 pk[2];
+        // B operand of P V: k index 8q + i holds key 32 hp + 4q + i (i < 4) and 32 hp + 16 + 4q + i - 4
+        f16x8 pk;
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pk[c][i] = (_Float16)__builtin_amdgcn_exp2f(e[2 * c][i]);
-            pk[c][4 + i] = (_Float16)__builtin_amdgcn_exp2f(e[2 * c + 1][i]);
-          }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) O[hh][dt] = mfma_f16(vf[dt][c], pk[c], O[hh][dt]);
-          Lt[hh] = mfma_f16(ones, pk[c], Lt[hh]);
+        for (int i = 0; i < 4; ++i) {
+          pk[i] = (_Float16)__builtin_amdgcn_exp2f(e[0][i]);
+          pk[4 + i] = (_Float16)__builtin_amdgcn_exp2f(e[1][i]);
         }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) O[hh][dt] = mfma_f16(vf[dt], pk, O[hh][dt]);
+        Lt[hh] = mfma_f16(ones, pk, Lt[hh]);
       }
       if (more) store_v(nb);
+      car_cur = car_nxt;
+      have_cur = have_nxt;
+      init_cur = init_nxt;
     }
 
-    // ---- epilogue: normalise, gate, store (O^T tiles: lane holds dims 16dt + 4g + i of token c16)
+    // ---- epilogue: merge the two key halves of each token (through the K
+    // staging buffer, now free), normalise, gate, store.  O^T tiles: a lane
+    // holds dims 16 dt + 4 g + i of token c16.
+    float* xch = reinterpret_cast<float*>(&s_k[0][0]) + (tw * 64 + lane) * XS;
+    __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh) {
       const float L = __shfl(Lt[hh][0], c16, 64);
-      const float inv = row_ok ? 1.0f / L : 0.0f;
+      const float mw = (L > 0.0f) ? m_run[hh] : kNegInf;
+      if (hp == 1) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
-        const float4 gm = *reinterpret_cast<const float4*>(w.gam + yo);
-        const float y0 = gm.x * O[hh][dt][0] * inv, y1 = gm.y * O[hh][dt][1] * inv;
-        const float y2 = gm.z * O[hh][dt][2] * inv, y3 = gm.w * O[hh][dt][3] * inv;
-        if (row_ok) {
-          if (a.y_bf16) {
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) =
-                make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
-          } else {
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(y0, y1, y2, y3);
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xch[4 * dt + i] = O[hh][dt][i];
+        xch[4 * DT] = L;
+        xch[4 * DT + 1] = mw;
+      }
+      __syncthreads();
+      if (hp == 0) {
+        const float L1 = xch[4 * DT], m1 = xch[4 * DT + 1];
+        const float m = fmaxf(mw, m1);
+        const float s0 = (mw > kNegInf) ? __builtin_amdgcn_exp2f(mw - m) : 0.0f;
+        const float s1 = (m1 > kNegInf) ? __builtin_amdgcn_exp2f(m1 - m) : 0.0f;
+        const float Ls = L * s0 + L1 * s1;
+        const float inv = (row_ok && Ls > 0.0f) ? 1.0f / Ls : 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+          const float4 gm = *reinterpret_cast<const float4*>(w.gam + yo);
+          float yv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) yv[i] = (O[hh][dt][i] * s0 + xch[4 * dt + i] * s1) * inv;
+          const float y0 = gm.x * yv[0], y1 = gm.y * yv[1], y2 = gm.z * yv[2], y3 = gm.w * yv[3];
+          if (row_ok) {
+            if (a.y_bf16) {
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) =
+                  make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
+            } else {
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(y0, y1, y2, y3);
+            }
           }
         }
       }
+      __syncthreads();
     }
-  } else if (row_ok) {
+  } else if (row_ok && hp == 0) {
     // the segment has no room for the call: its outputs are zero
 #pragma unroll
     for (int hh = 0; hh < HG; ++hh)
@@ -738,11 +909,11 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
   if (tid == 0) s_id = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
   __syncthreads();
   if (s_id) {
-    for (int s2 = tid; s2 < S; s2 += 256) {
+    for (int s2 = tid; s2 < S; s2 += kPThreads) {
       const int l = a.seg_len[s2];
       if ((int64_t)l + n <= a.seg_cap[s2]) a.seg_len[s2] = l + n;
     }
-    for (int b2 = tid; b2 < a.B; b2 += 256) a.next_pos[b2] += n;
+    for (int b2 = tid; b2 < a.B; b2 += kPThreads) a.next_pos[b2] += n;
   }
 }
 
@@ -751,7 +922,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(LayerArgs a, PrefillW
 // ---------------------------------------------------------------------------
 template <int D, int HG>
 static void launch_attn(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_attn_kernel<D, HG>), dim3(grid), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL((prefill_attn_kernel<D, HG>), dim3(grid), dim3(kPThreads), 0, st, a, w);
 }
 
 hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int max_seg_cap, void* scratch,
@@ -764,14 +935,15 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int
   prefill_layout(a, n, reinterpret_cast<char*>(scratch), &w);
   const int S = a.B * a.H_kv;
   const int nsync = 2 + S * w.nrb;
-  const int64_t prep_items = std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8));
+  const int64_t prep_items = std::max<int64_t>(std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8)),
+                                               (int64_t)a.H_q * a.d * (w.rp / 8));
   const int prep_grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (prep_items + 255) / 256));
   hipLaunchKernelGGL(prefill_prep_kernel, dim3(prep_grid), dim3(256), 0, st, a, w, nsync);
   const int tok_grid = (a.B * n + kPTok - 1) / kPTok;
   if (a.d == 64) {
-    hipLaunchKernelGGL(prefill_token_kernel<64>, dim3(tok_grid), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(prefill_token_kernel<64>, dim3(tok_grid), dim3(kTT), 0, st, a, w);
   } else {
-    hipLaunchKernelGGL(prefill_token_kernel<128>, dim3(tok_grid), dim3(256), 0, st, a, w);
+    hipLaunchKernelGGL(prefill_token_kernel<128>, dim3(tok_grid), dim3(kTT), 0, st, a, w);
   }
   const int grid = S * w.nrb;
   switch (a.d * 16 + G) {

@@ -30,6 +30,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values to packed bf16 (lo in bits 0-15), round to nearest even, in
+// one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
+
 // Element load of an input that is either bf16 or fp32.
 template <bool BF16>
 __device__ __forceinline__ float load_elem(const void* p, int64_t i) {
@@ -141,6 +149,12 @@ __device__ __forceinline__ float sigmoid(float z) {
   return z >= 0.0f ? r : e * r;
 }
 
+// sigmoid through the hardware exp2 and reciprocal (about 2 ulp); 1 for large
+// z, e^z / (1 + e^z) -> 0 for very negative z.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
 // Row (query-side) and column (key-side) parts of the mean in the pair term,
 // pre-scaled to log2 units and divided by the number of enabled terms.
 struct PairCoef {
@@ -179,16 +193,20 @@ __device__ __forceinline__ float log1mexp2(float lam2) {
   return __builtin_amdgcn_logf(arg) * kLn2 + corr;
 }
 
-// The same in log2 units: log2(1 - 2^lam2).
-__device__ __forceinline__ float log1mexp2_b2(float lam2) {
-  const float lam = lam2 * kLn2;
-  const bool small = lam > -0.125f;
-  const float w = __builtin_amdgcn_exp2f(lam2);
-  const float y = 1.0f - w;
-  const float err = (1.0f - y) - w;
-  const float arg = small ? -lam : y;
-  const float corr = small ? lam * (0.5f + lam * (1.0f / 24.0f)) : err;
-  return __builtin_amdgcn_logf(arg) + corr * kLog2e;
+// The same in log2 units with one logarithm: log2(1 - 2^L) for L <= 0.
+// With lam = L ln 2 > -1/8, 1 - e^lam = -lam (1 + lam/2 + lam^2/6 + lam^3/24)
+// up to a relative 2e-6 (Taylor series of expm1); otherwise 1 - 2^L >= 0.1175
+// is formed directly, which costs at most about 1e-6 relative (the error of
+// 2^L over the result).  L = -inf gives 0, L = 0 gives -inf.
+__device__ __forceinline__ float log1mexp2_b2(float L) {
+  constexpr float l1 = kLn2;
+  constexpr float l2 = l1 * l1, l3 = l2 * l1, l4 = l3 * l1;
+  const bool small = L > -0.125f / kLn2;
+  float q = fmaf(L, -l4 / 24.0f, -l3 / 6.0f);
+  q = fmaf(L, q, -l2 / 2.0f);
+  q = fmaf(L, q, -l1);
+  const float arg = small ? L * q : 1.0f - __builtin_amdgcn_exp2f(L);
+  return __builtin_amdgcn_logf(arg);
 }
 
 // Pair term from the similarity s and the pre-scaled row/column parts:
@@ -198,14 +216,6 @@ __device__ __forceinline__ float pair_A(const PairCoef& c, float row2, float col
   float lam2 = row2 + col2;
   if (c.sim) lam2 += c.sim_w * __builtin_amdgcn_logf(fminf(s * s, 1.0f));
   return log1mexp2(lam2);
-}
-
-// pair_A in log2 units.
-__device__ __forceinline__ float pair_A2(const PairCoef& c, float row2, float col2, float s) {
-  if (!c.any) return 0.0f;
-  float lam2 = row2 + col2;
-  if (c.sim) lam2 += c.sim_w * __builtin_amdgcn_logf(fminf(s * s, 1.0f));
-  return log1mexp2_b2(lam2);
 }
 
 }  // namespace ua
