@@ -481,9 +481,11 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
   constexpr int KS = D + 8;                           // s_k row stride (bf16)
   constexpr int VS = kPKeys + 8;                      // s_vt row stride (fp16)
   constexpr int KPT = kPKeys * (D / 8) / kPThreads;   // K pieces per thread per block
-  constexpr int VITEMS = (kPKeys / 2) * (D / 8);      // V (key pair, 8 dims) items per block
-  constexpr int VPT = (VITEMS + kPThreads - 1) / kPThreads;
+  constexpr int VITEMS = (kPKeys / 2) * (D / 4);      // V (key pair, 4 dims) items per block
+  constexpr int VPT = VITEMS / kPThreads;
+  static_assert(VITEMS % kPThreads == 0, "V items per thread");
   constexpr int XS = DT * 4 + 2;                      // floats per lane in the final merge
+  constexpr int QS = HG * D + 8;                      // s_q row stride (bf16): rows shift by 16 bytes
   static_assert(KPT >= 1, "tile split");
   static_assert(4 * 64 * XS * 4 <= (int)sizeof(uint16_t) * 2 * kPKeys * KS, "merge buffer fits in s_k");
   __shared__ __attribute__((aligned(16))) uint16_t s_k[2][kPKeys * KS];
@@ -491,7 +493,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
   __shared__ __attribute__((aligned(16))) float s_lk[2][kPKeys];
   __shared__ __attribute__((aligned(16))) float s_tot[2][4][kPKeys];
   __shared__ __attribute__((aligned(16))) float s_car[2][kPKeys];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[kPRows * HG * D];  // rotated queries of the token block
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kPRows * QS];  // rotated queries of the token block
   __shared__ int s_id;
 
   const int tid = threadIdx.x;
@@ -537,20 +539,22 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
     for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreads) {
       const int tt = q / (HG * (D / 8)), rest = q - tt * (HG * (D / 8));
       const int64_t tk = (int64_t)b * n + min(I * kPRows + tt, n - 1);
-      *reinterpret_cast<u32x4*>(&s_q[q * 8]) =
+      *reinterpret_cast<u32x4*>(&s_q[tt * QS + rest * 8]) =
           *reinterpret_cast<const u32x4*>(w.qbf + (tk * Hq + a0) * D + rest * 8);
     }
-    const uint16_t* qrow = &s_q[(tw * 16 + c16) * HG * D + 8 * g];  // this lane's token, k offset 8 g
+    const uint16_t* qrow = &s_q[(tw * 16 + c16) * QS + 8 * g];  // this lane's token, k offset 8 g
     u32x4 krf[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
       krf[kc] = *reinterpret_cast<const u32x4*>(Kc + (off + len0 + tqc) * D + 32 * kc + 8 * g);
 
     // staging of a key block: K rows, V rows (as key pairs), key gates
-    u32x4 kst[KPT], vst[VPT][2];
-    float lkst = 0.0f;
+    // staging registers of the next block (kst, ...) and of the one after (kst2, ...)
+    u32x4 kst[KPT], kst2[KPT];
+    uint2 vst[VPT][2], vst2[VPT][2];
+    float lkst = 0.0f, lkst2 = 0.0f;
     auto slot = [&](int j) -> int64_t { return off + min(j, nkeys - 1); };
-    auto load_block = [&](int J) {
+    auto load_block = [&](int J, u32x4 (&kst)[KPT], uint2 (&vst)[VPT][2], float& lkst) {
       const int j0 = J * kPKeys;
 #pragma unroll
       for (int u = 0; u < KPT; ++u) {
@@ -559,9 +563,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
       }
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int q = min(tid + kPThreads * u, VITEMS - 1), p = q / (D / 8), part = q % (D / 8);
-        vst[u][0] = *reinterpret_cast<const u32x4*>(Vc + slot(j0 + 2 * p) * D + 8 * part);
-        vst[u][1] = *reinterpret_cast<const u32x4*>(Vc + slot(j0 + 2 * p + 1) * D + 8 * part);
+        const int q = tid + kPThreads * u, p = q / (D / 4), part = q % (D / 4);
+        vst[u][0] = *reinterpret_cast<const uint2*>(Vc + slot(j0 + 2 * p) * D + 4 * part);
+        vst[u][1] = *reinterpret_cast<const uint2*>(Vc + slot(j0 + 2 * p + 1) * D + 4 * part);
       }
       lkst = a.lk[slot(j0 + lane)];
     };
@@ -577,22 +581,23 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
     auto store_v = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int q = tid + kPThreads * u;
-        if (VITEMS % kPThreads == 0 || q < VITEMS) {
-          const int p = q / (D / 8), part = q % (D / 8);
-          const int pos = vt_pos(2 * p);
+        const int q = tid + kPThreads * u, p = q / (D / 4), part = q % (D / 4);
+        const int pos = vt_pos(2 * p);
+        const uint32_t k0w[2] = {vst[u][0].x, vst[u][0].y}, k1w[2] = {vst[u][1].x, vst[u][1].y};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const auto hv = __builtin_amdgcn_cvt_pkrtz(u32x4_bf16(vst[u][0], e), u32x4_bf16(vst[u][1], e));
-            *reinterpret_cast<uint32_t*>(&s_vt[buf][(8 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
-          }
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = (e & 1) ? bf16_hi(k0w[e >> 1]) : bf16_lo(k0w[e >> 1]);
+          const float v1 = (e & 1) ? bf16_hi(k1w[e >> 1]) : bf16_lo(k1w[e >> 1]);
+          const auto hv = __builtin_amdgcn_cvt_pkrtz(v0, v1);
+          *reinterpret_cast<uint32_t*>(&s_vt[buf][(4 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
         }
       }
     };
 
-    load_block(0);
+    load_block(0, kst, vst, lkst);
     store_k(0);
     store_v(0);
+    if (nJ > 1) load_block(1, kst, vst, lkst);
     __syncthreads();
 
     // Online softmax per (query head, token) over this wave's key halves.  P is
@@ -624,7 +629,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
       const int cb = J & 1, nb = cb ^ 1;
       const int j0 = J * kPKeys;
       const bool more = J + 1 < nJ;
-      if (more) load_block(J + 1);
+      if (J + 2 < nJ) load_block(J + 2, kst2, vst2, lkst2);
       const int Ist_next = (j0 + kPKeys >= len0) ? (j0 + kPKeys - len0) / kPRows : 0;
       const bool chain_next = more && I > Ist_next;
       int flag_next = 0;
@@ -838,6 +843,14 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
         Lt[hh] = mfma_f16(ones, pk, Lt[hh]);
       }
       if (more) store_v(nb);
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) kst[u] = kst2[u];
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        vst[u][0] = vst2[u][0];
+        vst[u][1] = vst2[u][1];
+      }
+      lkst = lkst2;
       car_cur = car_nxt;
       have_cur = have_nxt;
       init_cur = init_nxt;
