@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     ua_workspace_bytes,
     ua_workspace_init,
     ua_decode_step,
+    ua_decode_compact_step,
     ua_prefill,
     ua_compact,
     ua_status_string,

@@ -25,6 +25,7 @@ EXPORTS = (
     "ua_workspace_bytes",
     "ua_workspace_init",
     "ua_decode_step",
+    "ua_decode_compact_step",
     "ua_prefill",
     "ua_compact",
     "ua_status_string",
@@ -98,6 +99,9 @@ def load(path: Optional[str] = None) -> C.CDLL:
     lib.ua_decode_step.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_float, C.c_void_p,
                                    C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_decode_step.restype = C.c_int
+    lib.ua_decode_compact_step.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_float,
+                                           C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.ua_decode_compact_step.restype = C.c_int
     lib.ua_prefill.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_void_p,
                                C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_prefill.restype = C.c_int
@@ -131,6 +135,13 @@ def ua_workspace_init(ws, ws_bytes: int, stream=None) -> None:
 def ua_decode_step(dims, params, cache, tokens, log_p: float, y, ws, ws_bytes: int, stream=None) -> None:
     _check(load().ua_decode_step(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), float(log_p),
                                  _ptr(y), _ptr(ws), ws_bytes, _stream(stream)), "ua_decode_step")
+
+
+def ua_decode_compact_step(dims, params, cache, tokens, log_p: float, y, kept_idx, ws, ws_bytes: int,
+                           stream=None) -> None:
+    _check(load().ua_decode_compact_step(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens),
+                                         float(log_p), _ptr(y), _ptr(kept_idx), _ptr(ws), ws_bytes,
+                                         _stream(stream)), "ua_decode_compact_step")
 
 
 def ua_prefill(dims, params, cache, tokens, n_tokens: int, y, ws, ws_bytes: int, stream=None) -> None:

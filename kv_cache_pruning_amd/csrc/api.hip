@@ -122,14 +122,16 @@ ua_status ua_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
 }
 
-ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
-                         float log_p, void* y, void* ws, size_t ws_bytes, void* stream) {
+static ua_status decode_common(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
+                               float log_p, void* y, bool compact, int32_t* kept_idx, void* ws, size_t ws_bytes,
+                               void* stream) {
   ua_status s;
   if ((s = check_dims(dims)) != UA_OK) return s;
   if ((s = check_params(params)) != UA_OK) return s;
   if ((s = check_cache(cache)) != UA_OK) return s;
   if ((s = check_tokens(in)) != UA_OK) return s;
   if (!y || !aligned(y, 16) || bad_log_p(log_p)) return UA_ERR_INVALID_ARG;
+  if (kept_idx && !aligned(kept_idx, 4)) return UA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, params, cache, in, y);
   const int twg = ua::decode_tile_entries(a.d);
@@ -137,8 +139,19 @@ ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_
   if (ws_bytes < cb + ua::decode_ws_bytes(a, twg) + ua::control_tail_bytes(a)) return UA_ERR_WORKSPACE;
   const ua::Control ctl = ua::control_carve(a, ws, ws_bytes);
   ua::DecodeWs w = ua::decode_ws_carve(a, ctl, reinterpret_cast<char*>(ws) + cb, twg);
-  const hipError_t e = ua::launch_decode(a, w, log_p, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = ua::launch_decode(a, w, ctl, log_p, compact, kept_idx, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
+                         float log_p, void* y, void* ws, size_t ws_bytes, void* stream) {
+  return decode_common(dims, params, cache, in, log_p, y, false, nullptr, ws, ws_bytes, stream);
+}
+
+ua_status ua_decode_compact_step(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                                 const ua_tokens* in, float log_p, void* y, int32_t* kept_idx, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return decode_common(dims, params, cache, in, log_p, y, true, kept_idx, ws, ws_bytes, stream);
 }
 
 ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,

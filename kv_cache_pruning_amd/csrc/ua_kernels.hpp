@@ -55,11 +55,11 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // workspace.hip), so calls on caches of different sizes can share one.
 struct Control {
   int* dec_cnt;     // [S]           decode: arrivals per segment
-  int* dec_cntb;    // [B]           decode: finished segments per sequence
-  int* cmp_state;   // [max_chunks]  compaction: (count or prefix) << 2 | flag
-  int* cmp_loaded;  // [max_chunks]  compaction: chunk rows are in registers
+  int* dec_cntb;    // [B]           decode: finished per-token splits per sequence
+  int* cmp_state;   // [max_chunks]  compaction (also decode tiles): (count or prefix) << 2 | flag
+  int* cmp_loaded;  // [max_chunks]  compaction: the chunk's rows are in registers
   int* cmp_done;    // [S]           compaction: arrivals per segment
-  int* cmp_glob;    // [2]           compaction: ticket, arrivals
+  int* cmp_glob;    // [2]           compaction and decode: ticket, arrivals
   int cmp_chunk;    // entries per compaction chunk
   int max_chunks;
 };
@@ -72,22 +72,26 @@ Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes);
 // Decode scratch (after the control block) plus the counters it uses.
 struct DecodeWs {
   int* cnt;        // [S]  arrivals per segment (control block)
-  int* cntb;       // [B]  finished token-kernel splits per sequence (control block)
+  int* tok_done;   // [B]  finished per-token splits per sequence (control block)
   float* qt;       // [B, H_q, d]  rotated queries
   float* kt;       // [S, d]       stored new keys (cache-rounded), fp32
-  float* gates;    // [S, 4]       lq, lk, lb, unused
-  int* len_old;    // [S]          segment length before the append
+  float* zpart;    // [B, splits, zstride]  partial sums of x [W_dec | W_dn]
+  int* newlen;     // [S]          segment lengths after the step
   float* eself;    // [B, H_q]     new token's own logit (log2 units)
-  float* gamma;    // [B, H_q, d]  output gate
   float* part_o;   // [max_tiles, G, d]
   float* part_ml;  // [max_tiles, G, 2]  max (log2 units), sum
   int max_tiles;
+  int splits;      // per-token workgroups per sequence
+  int zstride;
 };
 
 size_t decode_ws_bytes(const LayerArgs& a, int tile_entries);
 int decode_tile_entries(int d);
 DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, int tile_entries);
-hipError_t launch_decode(const LayerArgs& a, const DecodeWs& w, float tau, hipStream_t st);
+// One decode step; with compact, the in-place compaction of every segment in
+// the same launch (kept: optional kept-index output).
+hipError_t launch_decode(const LayerArgs& a, const DecodeWs& w, const Control& ctl, float tau, bool compact,
+                         int32_t* kept, hipStream_t st);
 
 // Compaction
 hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st);

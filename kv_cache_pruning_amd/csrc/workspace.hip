@@ -12,6 +12,8 @@
 // the first call and every call leaves them zero; prefill keeps its own sync
 // words in its scratch and clears them at the start of each call.
 
+#include <algorithm>
+
 #include "ua_kernels.hpp"
 
 namespace ua {
@@ -21,8 +23,11 @@ int compact_chunk_entries(const LayerArgs& a) {
   return rb <= 128 ? 256 : (rb <= 256 ? 128 : 64);
 }
 
+// Flags for compaction chunks and for the tiles of a decode step that compacts
+// in the same launch (the finer of the two).
 static int64_t compact_max_chunks(const LayerArgs& a) {
-  return a.total_slots / compact_chunk_entries(a) + (int64_t)a.B * a.H_kv + 1;
+  const int unit = std::min(compact_chunk_entries(a), decode_tile_entries(a.d));
+  return a.total_slots / unit + (int64_t)a.B * a.H_kv + 1;
 }
 
 static size_t fixed_layout(const LayerArgs& a, Control* c, char* base) {

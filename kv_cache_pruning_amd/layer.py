@@ -116,6 +116,18 @@ class Layer:
                          stream)
         return y, ts
 
+    def decode_compact_step(self, q, k, v, x, log_p: float, y: Optional[torch.Tensor] = None,
+                            kept: Optional[torch.Tensor] = None, stream=None):
+        """One decode step and the compaction of every segment in one launch."""
+        s = self.shape
+        ts, tok = self._tokens(q, k, v, x)
+        if y is None:
+            y = torch.empty((s.B, s.H_q, s.d), dtype=torch.bfloat16 if s.y_bf16 else torch.float32,
+                            device=self.device)
+        L.ua_decode_compact_step(self.dims, self.w.params, self.cache.struct, tok, log_p, y, kept, self.ws.ptr,
+                                 self.ws.nbytes, stream)
+        return y, ts
+
     def prefill(self, q, k, v, x, y: Optional[torch.Tensor] = None, stream=None):
         s = self.shape
         n = q.shape[1]

@@ -381,3 +381,93 @@ def run_prefill_sampled(cfg: LayerConfig, segments=(0,), rows_per_call: int = 3,
     assert rep["y_err"] <= y_tol(cfg), f"sampled y max-abs error {rep['y_err']:.3e}"
     assert rep["lam_err"] <= 1e-4, f"final log-bias error {rep['lam_err']:.3e}"
     return rep
+
+
+# ---------------------------------------------------------------------------
+# decode step and compaction in one launch
+# ---------------------------------------------------------------------------
+def run_fused_parity(cfg: LayerConfig, steps: int, log_p: float, terms: int = 7, seed: int = 0) -> DecodeRun:
+    """ua_decode_compact_step vs the oracle's decode step followed by compaction.
+
+    Per step: y; the kept-index lists exactly; the surviving rows (K, V) bit
+    for bit; log-biases (relative 1e-4), key gates, lengths, positions and
+    status.  Entries within 1e-4 of log p take the GPU's keep decision (read
+    from its kept list) and, when kept, its log-bias.
+    """
+    import torch
+
+    w = make_weights(cfg, seed)
+    c = make_cache(cfg, w, seed)
+    layer = device_layer(cfg, w, c, terms=terms)
+    od, op = oracle_dims(cfg, terms), oracle_params(w)
+    oc = oracle_cache(cfg, c)
+    S = cfg.B * cfg.H_kv
+    run = DecodeRun()
+    kept_buf = torch.full((layer.cache.total_slots,), -1, dtype=torch.int32, device="cuda")
+    tau = log_p
+    for step in range(steps):
+        inp = make_step_inputs(cfg, step, 1, seed)
+        q, k, v, x = inp.q[:, 0], inp.k[:, 0], inp.v[:, 0], inp.x[:, 0]
+        len_before = layer.cache.seg_len.cpu().numpy().copy()
+        kept_buf.fill_(-1)
+        y_gpu, _ = layer.decode_compact_step(q, k, v, x, log_p, kept=kept_buf)
+        torch.cuda.synchronize()
+        g = gpu_state(layer)
+        kb = kept_buf.cpu().numpy()
+        y_gpu = y_gpu.float().cpu().numpy().astype(np.float64)
+        assert g["status"] == 0, f"step {step}: status {g['status']}"
+        # per segment: surviving pre-step indices and where they went
+        kept_g, where_g = {}, {}
+        k_gpu = np.zeros((cfg.B, cfg.H_kv, cfg.d))
+        for s in range(S):
+            b, h = divmod(s, cfg.H_kv)
+            o, n = int(g["seg_off"][s]), int(g["seg_len"][s])
+            kl = kb[o : o + n].astype(np.int64)
+            assert n >= 1 and kl[-1] == len_before[s], f"step {step} seg {s}: new entry missing or not last"
+            assert np.all(np.diff(kl) > 0), f"step {step} seg {s}: kept list not increasing"
+            kept_g[s] = kl
+            where_g[s] = {int(j): o + p for p, j in enumerate(kl)}
+            k_gpu[b, h] = g["K"][o + n - 1]
+        pos = oc.next_pos.copy()
+        k_or = np.stack([U.round_cache(od, U.rope(U.l2_normalize(np.asarray(k[b], np.float64)),
+                                                    np.full(cfg.H_kv, pos[b]), od.rope_base)) for b in range(cfg.B)])
+        tol = np.maximum(ulp_bf16(k_or), 2e-7) if cfg.bf16 else 2e-6
+        assert not np.any(np.abs(k_gpu - k_or) > tol * 1.0001), f"step {step}: stored key off by more than one ulp"
+
+        border_fix = {}
+
+        def decide(s, lam_new, idx):
+            live_o = lam_new >= tau
+            live_g = np.array([int(j) in where_g[s] for j in idx], bool)
+            border = np.abs(lam_new - tau) <= BORDER
+            assert not ((live_o != live_g) & ~border).any(), f"step {step} seg {s}: keep mask differs away from log p"
+            border_fix[s] = (idx[border], live_g[border])
+            return np.where(border, live_g, live_o)
+
+        y_or, info = U.decode_step(od, op, oc, q, k, v, x, log_p, decide=decide, k_override=k_gpu)
+        nb = 0
+        for s, (bidx, bl) in border_fix.items():
+            for j, lv in zip(bidx, bl):
+                oc.lam[s][j] = g["lam"][where_g[s][int(j)]] if lv else min(oc.lam[s][j], np.nextafter(tau, -np.inf))
+                nb += 1
+        kept_or = U.compact(oc, log_p)
+        y_err = _maxabs(y_gpu, y_or)
+        lam_err = 0.0
+        n_dead = 0
+        for s in range(S):
+            o, n = int(g["seg_off"][s]), int(g["seg_len"][s])
+            assert np.array_equal(kept_g[s], kept_or[s]), f"step {step} seg {s}: kept lists differ"
+            assert n == oc.lam[s].size
+            assert np.array_equal(g["K"][o : o + n], oc.K[s]), f"step {step} seg {s}: K rows differ"
+            assert np.array_equal(g["V"][o : o + n], oc.V[s]), f"step {step} seg {s}: V rows differ"
+            lg, lo = g["lam"][o : o + n], oc.lam[s]
+            assert np.array_equal(np.isneginf(lg), np.isneginf(lo)), f"step {step}: -inf pattern differs"
+            fin = np.isfinite(lo)
+            lam_err = max(lam_err, _maxrel(lg[fin], lo[fin]))
+            assert _maxrel(g["lk"][o : o + n], oc.lk[s]) <= 1e-5, f"step {step} seg {s}: key gates differ"
+            n_dead += int(len_before[s] + 1 - n)
+        assert np.array_equal(g["next_pos"], oc.next_pos), f"step {step}: positions differ"
+        run.reports.append(StepReport(step, y_err, lam_err, nb, int(np.sum(len_before)), n_dead))
+        assert y_err <= y_tol(cfg), f"step {step}: y max-abs error {y_err:.3e}"
+        assert lam_err <= 1e-4, f"step {step}: log-bias error {lam_err:.3e}"
+    return run

@@ -156,3 +156,87 @@ def test_shared_workspace_across_cache_sizes():
             for o, n in zip(gs["seg_off"], gs["seg_len"]):
                 assert np.array_equal(gs["lam"][o : o + n], gp["lam"][o : o + n])
                 assert np.array_equal(gs["K"][o : o + n], gp["K"][o : o + n])
+
+
+# ---- decode step and compaction in one launch (ua_decode_compact_step) ----
+def _run_fused(cfg, steps, p, **kw):
+    from tests.harness import run_fused_parity
+
+    print(f"[fused parity] {cfg.name} B={cfg.B} steps={steps} p={p} {kw}", flush=True)
+    run = run_fused_parity(cfg, steps, math.log(p) if p > 0 else -math.inf, **kw)
+    print(f"  max |dy| {run.max_y_err:.2e}  max rel dLambda {run.max_lam_err:.2e}  borderline {run.borderline}  "
+          f"evicted {sum(r.n_dead for r in run.reports)}", flush=True)
+    return run
+
+
+def test_fused_tiny_fp32_all_steps():
+    cfg = config("tiny-decode-f32")
+    run = _run_fused(cfg, cfg.steps, cfg.p)
+    assert sum(r.n_dead for r in run.reports) > 0
+
+
+def test_fused_1b_decode_full_batch():
+    _run_fused(config("1b-decode"), 12, 0.15)
+
+
+def test_fused_3b_decode_full_batch():
+    _run_fused(config("3b-decode"), 6, 0.15)
+
+
+def test_fused_ragged_decode():
+    _run_fused(config("ragged-decode", B=8), 4, 0.05)
+
+
+def test_fused_p0_keeps_everything():
+    _run_fused(config("1b-decode", B=2), 6, 0.0)
+
+
+@pytest.mark.parametrize("terms", [0, 1, 2, 4, 6])
+def test_fused_term_subsets(terms):
+    _run_fused(config("1b-decode", B=2), 4, 0.15, terms=terms)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (24, 8), (64, 8)])
+def test_fused_group_sizes(hq, hkv):
+    _run_fused(config("1b-decode", B=2, H_q=hq, H_kv=hkv), 4, 0.15)
+
+
+@pytest.mark.parametrize("p", [0.0, 0.02])
+def test_fused_equals_two_calls_when_segments_fill(p):
+    """Segments with room for three more entries: once full, the fused call
+    sets status bit 0 and skips the append exactly as decode_step followed by
+    ua_compact does (same outputs, rows, biases, kept lists, status)."""
+    import torch
+
+    from tests.harness import device_layer, gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-decode", B=2)
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0, extra=3)
+    fused, two = device_layer(cfg, w, c), device_layer(cfg, w, c)
+    log_p = math.log(p) if p > 0 else -math.inf
+    slots = fused.cache.total_slots
+    kf = torch.full((slots,), -1, dtype=torch.int32, device="cuda")
+    kt = torch.full((slots,), -1, dtype=torch.int32, device="cuda")
+    for step in range(8):
+        inp = make_step_inputs(cfg, step, 1, 0)
+        args = (inp.q[:, 0], inp.k[:, 0], inp.v[:, 0], inp.x[:, 0])
+        kf.fill_(-1)
+        kt.fill_(-1)
+        print(f"[fused vs two calls] p={p} step {step}", flush=True)
+        yf, _ = fused.decode_compact_step(*args, log_p, kept=kf)
+        yt, _ = two.decode_step(*args, log_p)
+        two.compact(log_p, kept=kt)
+        torch.cuda.synchronize()
+        assert torch.equal(yf, yt), f"step {step}: y differs"
+        gf, gt = gpu_state(fused), gpu_state(two)
+        assert gf["status"] == gt["status"], f"step {step}: status {gf['status']} vs {gt['status']}"
+        assert np.array_equal(gf["seg_len"], gt["seg_len"]) and np.array_equal(gf["next_pos"], gt["next_pos"])
+        kfn, ktn = kf.cpu().numpy(), kt.cpu().numpy()
+        for o, n in zip(gf["seg_off"], gf["seg_len"]):
+            for name in ("K", "V", "lam", "lk"):
+                assert np.array_equal(gf[name][o : o + n], gt[name][o : o + n]), f"step {step}: {name} differs"
+            if p > 0:
+                assert np.array_equal(kfn[o : o + n], ktn[o : o + n]), f"step {step}: kept lists differ"
+    assert gf["status"] & 1, "no segment reached its capacity"

@@ -14,7 +14,8 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("fused", [False, True], ids=["decode+compact", "decode_compact_step"])
+def test_graph_replay_matches_eager(fused):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -35,8 +36,11 @@ def test_graph_replay_matches_eager():
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        graphed.decode_step(*static, log_p, y=y_g)
-        graphed.compact(log_p)
+        if fused:
+            graphed.decode_compact_step(*static, log_p, y=y_g)
+        else:
+            graphed.decode_step(*static, log_p, y=y_g)
+            graphed.compact(log_p)
     torch.cuda.synchronize()
     for step in range(8):
         inp = make_step_inputs(cfg, step, 1, 0)
@@ -44,8 +48,11 @@ def test_graph_replay_matches_eager():
         for dst, src in zip(static, host):
             dst.copy_(torch.from_numpy(src).to(dt))
         g.replay()
-        y_e, _ = eager.decode_step(*host, log_p)
-        eager.compact(log_p)
+        if fused:
+            y_e, _ = eager.decode_compact_step(*host, log_p)
+        else:
+            y_e, _ = eager.decode_step(*host, log_p)
+            eager.compact(log_p)
         torch.cuda.synchronize()
         assert torch.equal(y_g, y_e), f"replay {step}: y differs"
         for name in ("seg_len", "next_pos", "status"):
@@ -54,7 +61,9 @@ def test_graph_replay_matches_eager():
         off = eager.cache.seg_off.cpu().numpy()
         lg, le = graphed.cache.logbias.cpu().numpy(), eager.cache.logbias.cpu().numpy()
         Kg, Ke = graphed.cache.K.cpu(), eager.cache.K.cpu()
+        Vg, Ve = graphed.cache.V.cpu(), eager.cache.V.cpu()
         for o, m in zip(off, n):
             assert np.array_equal(lg[o : o + m], le[o : o + m]), f"replay {step}: log-biases differ"
             assert torch.equal(Kg[o : o + m], Ke[o : o + m]), f"replay {step}: keys differ"
+            assert torch.equal(Vg[o : o + m], Ve[o : o + m]), f"replay {step}: values differ"
         _ = torch.ones(1000, device="cuda").sum().item()  # unrelated eager work between replays
