@@ -3,7 +3,7 @@
 Default workload: the 1B-shape decode layer (hidden 2048, 32 query / 8 KV
 heads, head dim 64, B = 8) on a pre-populated pruned cache of nominal length
 4096 (~10x compressed), one decode step + eviction + in-place compaction per
-layer instance per step, p = 0.15.  The decode working set of one layer
+layer instance per step (one fused launch), p = 0.15.  The decode working set of one layer
 (~7 MB) fits in the 256 MB Infinity Cache, so a step runs a ring of R
 independent layer instances (distinct caches, >= 1 GiB in total), as an
 R-layer model would, and throughput is counted per layer: value = B * R /
@@ -112,9 +112,10 @@ def bench_decode(args):
     torch.cuda.synchronize()
     setup_s = time.time() - t0
 
-    # One captured graph per step shape: the whole step (every instance's decode
-    # + compaction), and decode-only / compaction-only graphs for the per-call
-    # timing pass.  Inputs go through static buffers refreshed before a replay.
+    # One captured graph per step shape: the whole step (every instance's fused
+    # decode + compaction, one launch each), and for context the same step as
+    # two calls (decode-only / compaction-only graphs).  Inputs go through
+    # static buffers refreshed before a replay.
     static_in = [t.clone() for t in toks[0]]
 
     def load_inputs(s):
@@ -137,8 +138,7 @@ def bench_decode(args):
 
     def all_step():
         for L_ in insts:
-            L_.decode_step(*static_in, log_p, y=y)
-            L_.compact(log_p)
+            L_.decode_compact_step(*static_in, log_p, y=y)
 
     g_step, g_dec, g_cmp = cap(all_step), cap(all_decode), cap(all_compact)
     torch.cuda.synchronize()
@@ -156,19 +156,22 @@ def bench_decode(args):
             c.seg_len.copy_(sn[4]); c.next_pos.copy_(sn[5])
         torch.cuda.synchronize()
 
-    # ---- timed region: K steps of the whole hot path
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: K steps of the whole hot path.  Events bracket each
+    # step's graph (R fused launches back to back on this stream), which gives
+    # the launch's average duration as well.
+    ev_s = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    start.record()
     for s in range(args.steps):
         load_inputs(args.warmup + s)
+        ev_s[s][0].record()
         g_step.replay()
-    stop.record()
+        ev_s[s][1].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = ev_s[0][0].elapsed_time(ev_s[-1][1])
+    fused_ms = [e[0].elapsed_time(e[1]) / R for e in ev_s]
     st = int(sum(int(c.status.item()) for c in caches))
 
-    # ---- per-call durations: same steps from the same state, events between graphs
+    # ---- the same steps as two calls (decode, then compaction), from the same state
     restore()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for s in range(args.steps):
@@ -186,6 +189,7 @@ def bench_decode(args):
     restore()
     scanned = 0
     moved = 0
+    moved_fused = 0
     cmp_scanned = 0
     for s in range(args.steps):
         q, k, v, x = toks[args.warmup + s]
@@ -201,6 +205,8 @@ def bench_decode(args):
                 cmp_scanned += int(n)
                 if dead.size:
                     moved += int(np.count_nonzero(seg[dead[0]:] >= log_p))
+                    # the fused call writes the new (last) entry straight to its place
+                    moved_fused += int(np.count_nonzero(seg[dead[0]:-1] >= log_p))
             L_.compact(log_p)
     torch.cuda.synchronize()
 
@@ -212,9 +218,11 @@ def bench_decode(args):
                       + (cfg.D * (3 * cfg.H_kv + cfg.r) + cfg.r * cfg.H_q * cfg.d) * elem)  # gate weights
     dec_bytes = scanned * entry_bytes + n_calls * per_step_extra
     cmp_bytes = cmp_scanned * 4 + moved * 2 * (2 * cfg.d * elem + 8)
+    fused_bytes = dec_bytes + moved_fused * (2 * cfg.d * elem + 4)  # moved rows: K, V, key gate written
     dec_avg_ms = float(np.mean(dec_ms))
     cmp_avg_ms = float(np.mean(cmp_ms))
-    achieved = dec_bytes / n_calls / (dec_avg_ms * 1e-3) / 1e9
+    fused_avg_ms = float(np.mean(fused_ms))
+    achieved = fused_bytes / n_calls / (fused_avg_ms * 1e-3) / 1e9
     ms_per_step = total_ms / args.steps
     tokens = cfg.B * R  # layer-tokens per step
     value = tokens / (ms_per_step * 1e-3)
@@ -241,11 +249,14 @@ def bench_decode(args):
             "tokens_per_step": tokens,
             "storage": "bf16" if cfg.bf16 else "f32",
             "live_entries_per_layer_step": scanned / n_calls,
-            "decode_call_us": dec_avg_ms * 1e3,
-            "compact_call_us": cmp_avg_ms * 1e3,
-            "decode_gbs": achieved,
-            "compact_gbs": cmp_bytes / n_calls / (cmp_avg_ms * 1e-3) / 1e9,
-            "step_gbs": (dec_bytes + cmp_bytes) / (total_ms * 1e-3) / 1e9,
+            "fused_call_us": fused_avg_ms * 1e3,
+            "two_calls": {
+                "decode_call_us": dec_avg_ms * 1e3,
+                "compact_call_us": cmp_avg_ms * 1e3,
+                "decode_gbs": dec_bytes / n_calls / (dec_avg_ms * 1e-3) / 1e9,
+                "compact_gbs": cmp_bytes / n_calls / (cmp_avg_ms * 1e-3) / 1e9,
+            },
+            "rows_moved_per_layer_step": moved_fused / n_calls,
             "status": st,
             "setup_s": setup_s,
         },
@@ -256,8 +267,8 @@ def bench_decode(args):
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": load_traffic(f"decode_{cfg.name}", "decode"),
-            "kernel": "ua_decode_step = decode_token_kernel + decode_main_kernel (timed together per call)",
-            "alg_bytes_per_launch": dec_bytes / n_calls,
+            "kernel": "ua_decode_compact_step (decode_step_kernel, compacting), one launch per layer step",
+            "alg_bytes_per_launch": fused_bytes / n_calls,
         },
     }
     if not args.no_cpu_baseline:

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
   const int lane = tid & 63;
   const int wv = tid >> 6;
 
-  if (tid == 0) s_ticket = addi_coh(&ctl.cmp_glob[0], 1);
+  if (tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobTicket], 1);
   __syncthreads();
   const int id = s_ticket;
 
@@ -259,9 +259,9 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
   // 5. the last workgroup overall clears the ticket
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0 && addi_coh(&ctl.cmp_glob[1], 1) == (int)gridDim.x - 1) {
-    sti_coh2(&ctl.cmp_glob[0], 0);
-    sti_coh2(&ctl.cmp_glob[1], 0);
+  if (tid == 0 && addi_coh(&ctl.glob[kGlobArrive], 1) == (int)gridDim.x - 1) {
+    sti_coh2(&ctl.glob[kGlobTicket], 0);
+    sti_coh2(&ctl.glob[kGlobArrive], 0);
   }
 }
 

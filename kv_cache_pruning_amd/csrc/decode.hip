@@ -10,34 +10,42 @@
 // out of the step's softmax and are evicted; the output is the low-rank
 // sigmoid gate times the attention output; the new entry is appended.
 //
-// Workgroups take ids from an atomic ticket, so every wait below is on a
-// workgroup that started earlier.
-//  * ids [0, B*NS): per-token work of sequence b = id / NS, split NS ways over
-//    the query heads (NS = H_q d / 256): a slice of the rows of
-//    x [W_dec | W_dn] (partial sums, reduced by their consumers), the rotated
-//    queries of the split's heads, the stored key of its KV heads and the
-//    token's own logits.  The last step publishes a per-sequence counter.
-//  * later ids: one tile of TWG entries of one segment (segment = sequence and
-//    KV head), mapped from the segment lengths, which stay constant until the
-//    kernel ends.  The tile issues its cache loads, waits for its sequence's
-//    token data, and reads each entry once: the key row feeds the G query
-//    dot products and the key-similarity dot product, the pair term updates
-//    the log-bias, and an online-softmax partial (max, sum, weighted V) goes
-//    to the workspace.  With COMPACT the surviving entries then move down in
-//    place: the tile publishes its live count, looks back over the earlier
-//    tiles of its segment for its destination (decoupled look-back, up to 64
-//    predecessors per wave step), waits until every earlier tile whose rows
-//    it overwrites holds its own rows in registers, and stores.  Without
-//    COMPACT the updated log-biases are written in place.
-//  * The last tile of a segment to arrive merges the partials with the
-//    token's own term, forms the output gate for its query heads from its
-//    slice of W_up, writes y and appends the new entry (after the survivors
-//    when compacting).  The last workgroup overall commits the new lengths,
-//    advances the positions and clears the counters.
+// Work items are numbered and handed out by an atomic ticket to a persistent
+// grid (at most one workgroup per compute unit), so every wait below is on an
+// item that a running workgroup already holds.
+//  * items [0, B): per sequence, u = x W_dn and the key-gate logits of every
+//    KV head.  They are published as 64-bit words whose high half is the
+//    call's tag, so a reader checks each word on its own: no flag, no ordering
+//    between words.
+//  * later items: one tile of TWG entries of one segment (segment = sequence
+//    and KV head), numbered segment by segment from the lengths at the start
+//    of the call.  A tile issues its cache loads together with what it needs
+//    of the token (its G queries, the key, the query- and similarity-gate
+//    columns of x W_dec), forms the rotated queries and stored key itself,
+//    and reads each entry once: the key row feeds the G query dot products
+//    and the key-similarity dot product, the pair term updates the log-bias,
+//    and an online-softmax partial (max, sum, weighted V) is formed per
+//    group of lanes, merged across the wave with DPP and row swaps and across
+//    the waves in LDS.
+//  * With COMPACT the surviving entries move down in place: a tile publishes
+//    its live count once all its rows are in registers and looks back over
+//    the earlier tiles of its segment for its destination (decoupled
+//    look-back); the look-back cannot finish before every earlier tile has
+//    published, which orders the stores after the loads they overwrite.  Only
+//    rows that move are rewritten; every survivor's new log-bias is stored.
+//    Without COMPACT the log-biases are updated in place.
+//  * A segment held by one tile (the common case) combines at once from LDS.
+//    Otherwise each tile writes its partial to the workspace and the last to
+//    arrive merges them.  The combine adds the token's own term, forms the
+//    output gate from u and its slice of W_up, writes y and appends the new
+//    entry (after the survivors when compacting).
+//  * A workgroup draws its next ticket as soon as an item starts.  Drawing a
+//    ticket past the last item is its exit; the workgroup that draws the last
+//    ticket waits until every workgroup has finished and commits the new
+//    lengths and positions.
 //
-// Cross-workgroup data go through relaxed agent-scope atomics (coherent
-// across the XCDs without cache-wide write-back or invalidation); the
-// counters live in the workspace control block and return to zero.
+// Cross-workgroup data go through relaxed agent-scope atomics (coherent across
+// the XCDs without cache-wide write-back or invalidation).
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -59,11 +67,19 @@ __device__ __forceinline__ int add_coh(int* p, int v) {
 __device__ __forceinline__ void sti_coh(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st64_coh(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld64_coh(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-constexpr int kDecThreads = 256;
+constexpr int kDecThreads = 512;
+constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kSpinLimitDec = 1 << 22;
+constexpr int kWaveK = kDecWaves - 1;  // the wave that forms the stored key
 
 // Element t of a bf16 / fp32 row held as raw 16-byte chunks.
 template <bool BF16>
@@ -120,89 +136,74 @@ __device__ __forceinline__ void row_f32(const Row8<BF16>& r, float (&o)[8]) {
   }
 }
 
-template <int D>
+// Entries per lane group (rows held in registers at once; the budget of a
+// 512-thread workgroup allows four).
+template <bool BF16, int G>
+struct DecodeNB {
+  static constexpr int value = 4;
+};
+
+template <int D, int NB_>
 struct DecodeShape {
-  static constexpr int LPE = D / 8;       // lanes per entry
-  static constexpr int NGW = 64 / LPE;    // entry groups per wave
-  static constexpr int NB = 4;            // entries per group
-  static constexpr int TW = NGW * NB;     // entries per wave
-  static constexpr int NWAVE = kDecThreads / 64;
-  static constexpr int TWG = TW * NWAVE;  // entries per tile
-  static constexpr int NP = NGW * NWAVE;  // partials per tile
+  static constexpr int LPE = D / 8;     // lanes per entry (8 elements each)
+  static constexpr int NGW = 64 / LPE;  // entry groups per wave
+  static constexpr int NB = NB_;        // entries per group
+  static constexpr int TW = NGW * NB;   // entries per wave
+  static constexpr int TWG = TW * kDecWaves;
 };
 
 __device__ __forceinline__ int tiles_of(int n, int twg) { return n <= 0 ? 1 : ceil_div(n, twg); }
 
+__device__ __forceinline__ unsigned long long tag_word(float v, uint32_t tag) {
+  return ((unsigned long long)tag << 32) | __float_as_uint(v);
+}
+
 // ---------------------------------------------------------------------------
-// per-token work of one sequence, one of NS splits
+// per-sequence item: u = x W_dn (r columns) and the key-gate logits
+// log sigmoid(x W_dec[:, H_kv + h] + b) of every KV head h
 // ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__device__ void token_work(const LayerArgs& a, const DecodeWs& w, int b, int sp) {
+template <bool BF16>
+__device__ void seq_item(const LayerArgs& a, const Control& ctl, int b, uint32_t tag, float (*s_red)[8]) {
   constexpr int CW = BF16 ? 8 : 4;  // elements per 16-byte chunk
-  constexpr int HALF = D / 2;
-  constexpr int HP = kDecThreads / D;  // query heads per split
-  __shared__ float s_red[kDecThreads][8];
-  __shared__ float s_cos[HALF], s_sin[HALF];
-  __shared__ float s_q[HP * D];
-  __shared__ float s_kt[HP][D];
+  constexpr int NT = kDecThreads;
+  constexpr int KR = 16;  // rows per thread per pass, all loads in flight together
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int Hq = a.H_q, Hkv = a.H_kv, G = Hq / Hkv;
-  const int Dm = a.D_model;
-  const int C3 = 3 * Hkv, C = C3 + a.r;
-  const int NS = w.splits;
-  const int pos = a.next_pos[b];
-
-  // ---- issue the loads of the rotation part first: q element and partner, key elements
-  const int a0 = sp * HP, a1 = min(Hq, a0 + HP);
-  const int qa = a0 + tid / D, qi = tid % D;
-  const int64_t qbase = ((int64_t)b * Hq + min(qa, Hq - 1)) * D;
-  const float qx = load_elem<BF16>(a.q, qbase + qi);
-  const float qp = load_elem<BF16>(a.q, qbase + (qi < HALF ? qi + HALF : qi - HALF));
-  const int h0 = a0 / G, h1 = (a1 - 1) / G;
-  const int64_t kbase = ((int64_t)b * Hkv + min(h0 + wv, Hkv - 1)) * D;
-  const float kx0 = load_elem<BF16>(a.k, kbase + (lane % HALF));
-  const float kx1 = load_elem<BF16>(a.k, kbase + (lane % HALF) + HALF);
-
-  // ---- partial gate projections over this split's rows of x [W_dec | W_dn].
-  // Thread = (column group, row subset): a 16-byte chunk of CW columns when the
-  // rows allow it, else a single column.
-  const int RS = ceil_div(Dm, NS);
-  const int r0 = sp * RS, r1 = min(Dm, r0 + RS);
-  const bool vec = (C3 % CW == 0) && (a.r % CW == 0);
-  const int nzc = vec ? C3 / CW : 0;
-  const int nch = vec ? nzc + a.r / CW : C;  // column groups
-  const int rstep = kDecThreads / nch;
-  const int kc = tid % nch, rsub = tid / nch;
-  const bool own = rsub < rstep;
-  const bool dec_part = kc < (vec ? nzc : C3);
-  const int mcols = dec_part ? C3 : a.r;
-  const int mc0 = vec ? (dec_part ? kc : kc - nzc) * CW : (dec_part ? kc : kc - C3);
-  const void* mbase = dec_part ? a.W_dec : a.W_dn;
+  const int Hkv = a.H_kv, r = a.r, Dm = a.D_model;
+  const bool vec = (r % CW == 0) && (Hkv % CW == 0);
+  const int nu = vec ? r / CW : r;
+  const int nch = nu + (vec ? Hkv / CW : Hkv);  // column groups: W_dn chunks, then the key-gate band
+  int npow = 1;
+  while (npow < nch) npow <<= 1;
+  const int R = NT / npow;  // row subsets
+  const int kc = tid & (npow - 1), rsub = tid / npow;
+  const bool own = kc < nch;
+  const bool dn = kc < nu;
+  const void* mbase = dn ? a.W_dn : a.W_dec;
+  const int mcols = dn ? r : 3 * Hkv;
+  const int mc0 = dn ? (vec ? kc * CW : kc) : Hkv + (vec ? (kc - nu) * CW : kc - nu);
   const int64_t xb = (int64_t)b * Dm;
   float acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = 0.0f;
-  constexpr int KR = 8;  // rows per thread per pass, all loads in flight together
-  for (int rb = r0 + rsub; rb < r1; rb += KR * rstep) {
+  for (int rb = rsub; rb < Dm; rb += KR * R) {
     float xr[KR];
     u32x4 raw[KR];
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
-      const int row = min(rb + q * rstep, r1 - 1);
+      const int row = min(rb + q * R, Dm - 1);
       xr[q] = load_elem<BF16>(a.x, xb + row);
+      const int64_t e = (int64_t)row * mcols + (own ? mc0 : 0);
       if (vec) {
-        raw[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(mbase) +
-                                                  ((int64_t)row * mcols + mc0) * (BF16 ? 2 : 4));
+        raw[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(mbase) + e * (BF16 ? 2 : 4));
       } else {
-        const float e = load_elem<BF16>(mbase, (int64_t)row * mcols + mc0);
-        raw[q] = u32x4{__float_as_uint(e), 0u, 0u, 0u};
+        raw[q] = u32x4{__float_as_uint(load_elem<BF16>(mbase, e)), 0u, 0u, 0u};
       }
     }
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
-      const float xv = (own && rb + q * rstep < r1) ? xr[q] : 0.0f;
+      const float xv = (own && rb + q * R < Dm) ? xr[q] : 0.0f;
       if (vec) {
 #pragma unroll
         for (int t = 0; t < CW; ++t) acc[t] = fmaf(xv, chunk_elem<BF16>(raw[q], t), acc[t]);
@@ -211,71 +212,39 @@ __device__ void token_work(const LayerArgs& a, const DecodeWs& w, int b, int sp)
       }
     }
   }
+  // partial sums: reduced over the row subsets inside a wave when a wave holds
+  // every column group, else one slot per thread
+  int reff;
+  if (npow <= 64) {
+    for (int o = npow; o < 64; o <<= 1) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) s_red[tid][t] = acc[t];
-
-  // ---- RoPE table (fp64 angles) while the loads fly
-  if (tid < HALF) {
-    double sn, cs;
-    sincos((double)pos * a.inv_freq[tid], &sn, &cs);
-    s_cos[tid] = (float)cs;
-    s_sin[tid] = (float)sn;
+      for (int t = 0; t < 8; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
+    }
+    if (lane < npow) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) s_red[wv * npow + lane][t] = acc[t];
+    }
+    reff = kDecWaves;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) s_red[tid][t] = acc[t];
+    reff = R;
   }
   __syncthreads();
-
-  // ---- column sums of the partial projections -> workspace
-  if (tid < C) {
-    const int grp = vec ? (tid < C3 ? tid / CW : nzc + (tid - C3) / CW) : tid;
-    const int t = vec ? (tid < C3 ? tid % CW : (tid - C3) % CW) : 0;
-    float sum = 0.0f;
-    for (int q = 0; q < rstep; ++q) sum += s_red[q * nch + grp][t];
-    st_coh(w.zpart + ((int64_t)b * NS + sp) * w.zstride + tid, sum);
-  }
-
-  // ---- rotated queries of this split's heads
-  if (qa < a1) {
-    const float out =
-        (qi < HALF) ? fmaf(qx, s_cos[qi], -qp * s_sin[qi]) : fmaf(qx, s_cos[qi - HALF], qp * s_sin[qi - HALF]);
-    s_q[tid] = out;
-    st_coh(w.qt + ((int64_t)b * Hq + qa) * D + qi, out);
-  }
-  // ---- the new key of each KV head the split touches (one wave each)
-  if (wv <= h1 - h0) {
-    const int h = h0 + wv;
-    float k0 = (lane < HALF) ? kx0 : 0.0f;
-    float k1 = (lane < HALF) ? kx1 : 0.0f;
-    const float inv = 1.0f / fmaxf(sqrtf(wave_sum(k0 * k0 + k1 * k1)), 1e-12f);
-    k0 *= inv;
-    k1 *= inv;
-    if (lane < HALF) {
-      float rr0 = fmaf(k0, s_cos[lane], -k1 * s_sin[lane]);
-      float rr1 = fmaf(k1, s_cos[lane], k0 * s_sin[lane]);
-      if constexpr (BF16) {
-        rr0 = bf16_to_f32(f32_to_bf16(rr0));
-        rr1 = bf16_to_f32(f32_to_bf16(rr1));
-      }
-      s_kt[wv][lane] = rr0;
-      s_kt[wv][lane + HALF] = rr1;
-      if (h * G >= a0) {  // the split holding query head h G stores KV head h's key
-        const int64_t kb = ((int64_t)b * Hkv + h) * D;
-        st_coh(w.kt + kb + lane, rr0);
-        st_coh(w.kt + kb + lane + HALF, rr1);
-      }
+  unsigned long long* uw = ctl.uw + (int64_t)b * kUWords;
+  if (tid < r + Hkv) {
+    const bool isu = tid < r;
+    const int q = isu ? tid : tid - r;
+    const int grp = isu ? (vec ? q / CW : q) : nu + (vec ? q / CW : q);
+    const int t = vec ? q % CW : 0;
+    float z = 0.0f;
+    for (int rr = 0; rr < reff; ++rr) z += s_red[rr * npow + grp][t];
+    if (isu) {
+      st64_coh(uw + q, tag_word(z, tag));
+    } else {
+      st64_coh(uw + kMaxRank + q, tag_word(log_sigmoid(z + a.b_dec[Hkv + q]), tag));
     }
   }
-  __syncthreads();
-  // ---- the token's own logits (log2 units), one wave per query head
-  if (a0 + wv < a1) {
-    const int hw = (a0 + wv) / G - h0;
-    float e = 0.0f;
-    for (int i = lane; i < D; i += 64) e = fmaf(s_q[wv * D + i], s_kt[hw][i], e);
-    e = wave_sum(e);
-    if (lane == 0) st_coh(w.eself + b * Hq + a0 + wv, e * a.scale * kLog2e);
-  }
-  // ---- publish
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) add_coh(&w.tok_done[b], 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -284,465 +253,582 @@ __device__ void token_work(const LayerArgs& a, const DecodeWs& w, int b, int sp)
 template <int D, int G, bool BF16, bool COMPACT>
 __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(LayerArgs a, DecodeWs w, Control ctl, float tau,
                                                                   int32_t* kept) {
-  using Sh = DecodeShape<D>;
-  constexpr int LPE = Sh::LPE, NGW = Sh::NGW, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG, NP = Sh::NP;
+  using Sh = DecodeShape<D, DecodeNB<BF16, G>::value>;
+  constexpr int LPE = Sh::LPE, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
   constexpr int NT = kDecThreads;
+  constexpr int HALF = D / 2;
+  constexpr int OPT = (G * D + NT - 1) / NT;  // outputs (g, i) per thread
+  constexpr int KRG = 16;                     // gate-column rows per thread per pass
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = a.B * a.H_kv;
   const int Hkv = a.H_kv;
-  const int NS = w.splits;
-  const int ntok = a.B * NS;
+  const int Dm = a.D_model;
+  const int r = a.r;
 
   __shared__ int s_id;
   __shared__ int s_scan[NT / 64 + 1];
   __shared__ int s_info[4];
   __shared__ int s_flag;
-  __shared__ float s_po[NP * G * D];
-  __shared__ float s_pm[NP * G];
-  __shared__ float s_pl[NP * G];
-  __shared__ float s_tq[(G + 1) * D];  // the token's rotated queries of the group, then its key
-  __shared__ float s_g[2];             // query and similarity gates (log sigmoid)
-  __shared__ float s_u[kMaxRank + 1];  // x W_dn, then the new key's gate
-  __shared__ int s_cnt[NT / 64];
   __shared__ int s_pre;
+  __shared__ int s_cnt[kDecWaves];
+  __shared__ float s_red[NT][8];                              // per-sequence item: partial projections
+  __shared__ float s_cs[HALF], s_sn[HALF];                    // RoPE table of the token's position
+  __shared__ float s_tq[(G + 1) * D];                         // rotated queries of the group, then the stored key
+  __shared__ float s_gred[kDecWaves][2];                      // gate partial sums per wave
+  __shared__ float s_g[2];                                    // query and similarity gates (log sigmoid)
+  __shared__ float s_po[kDecWaves * G * D];                   // wave partials: weighted V
+  __shared__ float s_pm[kDecWaves * G], s_pl[kDecWaves * G];  // wave partials: max (log2), sum
+  __shared__ float s_es[G];                                   // the token's own logits (log2 units)
+  __shared__ float s_u[kMaxRank + 1];                         // u, then the new key's gate
 
-  if (tid == 0) s_id = add_coh(&ctl.cmp_glob[0], 1);
-  __syncthreads();
-  const int id = s_id;
+  const uint32_t tag = (uint32_t)ctl.glob[kGlobSeq] + 1u;
+  // Tickets are drawn by the first lane of the last wave (which loads no
+  // lengths below) and kept in a register until the next item starts, so the
+  // draw flies while the numbering or the current item runs.
+  constexpr int kDrawer = NT - 64;
+  int nxt = 0;
+  if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);
 
-  if (id < ntok) {
-    token_work<D, BF16>(a, w, id / NS, id - (id / NS) * NS);
-  } else {
-    // ---- (segment, tile) from the segment lengths (constant in this kernel)
-    const int tix = id - ntok;
-    bool have;
-    {
-      const int per = (S + NT - 1) / NT;
-      const int sb = tid * per;
-      const int se = min(S, sb + per);
-      int mine = 0;
-      for (int s = sb; s < se; ++s) mine += tiles_of(a.seg_len[s], TWG);
-      int total;
-      const int excl = block_exclusive_scan<NT>(mine, s_scan, &total);
-      have = tix < total;
-      if (have) {
-        int run = excl;
-        for (int s = sb; s < se; ++s) {
-          const int nt = tiles_of(a.seg_len[s], TWG);
-          if (tix >= run && tix < run + nt) {
-            s_info[0] = s;
-            s_info[1] = tix - run;
-            s_info[2] = nt;
-            s_info[3] = run;
+  // ---- tile numbering from the segment lengths (unchanged until the commit,
+  // which waits until every workgroup has finished)
+  const int per = (S + NT - 1) / NT;
+  const int sb = min(S, tid * per);
+  const int se = min(S, sb + per);
+  int mine = 0;
+  for (int s = sb; s < se; ++s) mine += tiles_of(a.seg_len[s], TWG);
+  int total_tiles;
+  const int excl = block_exclusive_scan<NT>(mine, s_scan, &total_tiles);
+  const int total_items = a.B + total_tiles;
+
+  while (true) {
+    if (tid == kDrawer) s_id = nxt;
+    __syncthreads();
+    const int id = s_id;
+
+    if (id >= total_items) {
+      // ---- exit.  Every workgroup reports that it has finished (its stores
+      // done); the one that drew the last ticket waits for all of them and
+      // commits lengths and positions.
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) add_coh(&ctl.glob[kGlobDone], 1);
+      if (id == total_items + (int)gridDim.x - 1) {
+        if (tid == 0) {
+          int spins = 0;
+          while (ldi_coh(&ctl.glob[kGlobDone]) < (int)gridDim.x) {
+            if (++spins > kSpinLimitDec) {
+              atomicOr(a.status, 2);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
           }
-          run += nt;
+        }
+        __syncthreads();
+        for (int s = tid; s < S; s += NT) a.seg_len[s] = ldi_coh(&w.newlen[s]);
+        for (int b = tid; b < a.B; b += NT) a.next_pos[b] += 1;
+        if (tid == 0) {
+          sti_coh(&ctl.glob[kGlobTicket], 0);
+          sti_coh(&ctl.glob[kGlobDone], 0);
+          sti_coh(&ctl.glob[kGlobSeq], (int)tag);
         }
       }
-      __syncthreads();
+      break;
     }
-    if (have) {
-      const int seg = s_info[0];
-      const int kt_ = s_info[1];
-      const int ntile = s_info[2];  // tiles of this segment (all arrive)
-      const int pbase = s_info[3];  // global index of its first tile
-      const int b = seg / Hkv;
-      const int h = seg - b * Hkv;
-      const int len = a.seg_len[seg];
-      const int cap = a.seg_cap[seg];
-      const int64_t off = a.seg_off[seg];
-      const float qs2 = a.scale * kLog2e;
-      const int grp = lane / LPE;
-      const int c = lane - grp * LPE;
-      const int e0 = kt_ * TWG + wv * TW + grp * NB;
+    if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);  // the next item, drawn now
+    if (id < a.B) {
+      seq_item<BF16>(a, ctl, id, tag, s_red);
+      continue;
+    }
 
-      // ---- cached entries: issue every load (from a clamped slot) before waiting for the token
-      Row8<BF16> kr[NB], vr[NB];
-      float lamv[NB], lkv[NB];
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        const int64_t j = min(off + min(e0 + bb, max(len - 1, 0)), a.total_slots - 1);
-        row_load<BF16>(kr[bb], a.K, j * D + 8 * c);
-        row_load<BF16>(vr[bb], a.V, j * D + 8 * c);
-        lamv[bb] = a.lam[j];
-        lkv[bb] = a.lk[j];
-      }
-
-      // ---- wait for the sequence's token data, then stage it in LDS
-      if (tid == 0) {
-        int spins = 0;
-        while (ldi_coh(&w.tok_done[b]) < NS) {
-          if (++spins > kSpinLimitDec) {
-            atomicOr(a.status, 2);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
+    // ---- (segment, tile) of this item
+    const int tix = id - a.B;
+    if (tix >= excl && tix < excl + mine && per == 1) {
+      s_info[0] = sb;
+      s_info[1] = tix - excl;
+      s_info[2] = mine;
+      s_info[3] = excl;
+    } else if (tix >= excl && tix < excl + mine) {
+      int run = excl;
+      for (int s = sb; s < se; ++s) {
+        const int nt = tiles_of(a.seg_len[s], TWG);
+        if (tix < run + nt) {
+          s_info[0] = s;
+          s_info[1] = tix - run;
+          s_info[2] = nt;
+          s_info[3] = run;
+          break;
         }
+        run += nt;
       }
-      __syncthreads();
-      for (int q = tid; q < (G + 1) * D; q += NT) {
-        const int g = q / D, i = q - g * D;
-        s_tq[q] = (g < G) ? ld_coh(w.qt + ((int64_t)b * a.H_q + h * G + g) * D + i)
-                          : ld_coh(w.kt + (int64_t)seg * D + i);
-      }
-      if (tid < 2) {
-        const int col = tid == 0 ? h : 2 * Hkv + h;  // query and similarity gates
-        float z = a.b_dec[col];
-        for (int sp = 0; sp < NS; ++sp) z += ld_coh(w.zpart + ((int64_t)b * NS + sp) * w.zstride + col);
-        s_g[tid] = log_sigmoid(z);
-      }
-      __syncthreads();
-      const PairCoef pc = pair_coef(a.terms);
-      const float row2 = (((a.terms & 1) ? s_g[0] : 0.0f) + ((a.terms & 4) ? s_g[1] : 0.0f)) * pc.inv_n2;
-      const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
-      float qv[G][8], ktv[8];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qv[g][i] = s_tq[g * D + 8 * c + i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ktv[i] = s_tq[G * D + 8 * c + i];
+    }
+    __syncthreads();
+    const int seg = s_info[0];
+    const int kt_ = s_info[1];
+    const int ntile = s_info[2];  // tiles of this segment
+    const int pbase = s_info[3];  // tile number of its first tile
+    const bool single = ntile == 1;
+    const int b = seg / Hkv;
+    const int h = seg - b * Hkv;
+    const int len = a.seg_len[seg];
+    const int cap = a.seg_cap[seg];
+    const int64_t off = a.seg_off[seg];
+    const float qs2 = a.scale * kLog2e;
+    const int grp = lane / LPE;
+    const int c = lane - grp * LPE;
+    const int e0 = kt_ * TWG + wv * TW + grp * NB;
 
-      // ---- dot products, pair term, bias update, logits
-      float e2[G][NB];
-      float newlam[NB];
-      bool live[NB], changed[NB];
+    // ---- cached entries: every load (from a clamped slot) issued first
+    Row8<BF16> kr[NB], vr[NB];
+    float lamv[NB], lkv[NB];
 #pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        const bool valid = e0 + bb < len;
-        row_zero_if<BF16>(kr[bb], !valid);  // slots past the end may hold anything
-        row_zero_if<BF16>(vr[bb], !valid);
-        float kf[8];
-        row_f32<BF16>(kr[bb], kf);
-        float ps = 0.0f;
-        float pq[G];
+    for (int bb = 0; bb < NB; ++bb) {
+      const int64_t j = min(off + min(e0 + bb, max(len - 1, 0)), a.total_slots - 1);
+      row_load<BF16>(kr[bb], a.K, j * D + 8 * c);
+      row_load<BF16>(vr[bb], a.V, j * D + 8 * c);
+      lamv[bb] = a.lam[j];
+      lkv[bb] = a.lk[j];
+    }
+    // ---- the token: position, query pair (g, i) / (g, i + d/2), key pair, V
+    const int pos = a.next_pos[b];
+    const int qg = min(tid / HALF, G - 1), qi = tid % HALF;
+    const int64_t qb = ((int64_t)b * a.H_q + h * G + qg) * D;
+    const float q0 = load_elem<BF16>(a.q, qb + qi);
+    const float q1 = load_elem<BF16>(a.q, qb + qi + HALF);
+    float k0 = 0.0f, k1 = 0.0f;
+    if (wv == kWaveK && lane < HALF) {
+      k0 = load_elem<BF16>(a.k, (int64_t)seg * D + lane);
+      k1 = load_elem<BF16>(a.k, (int64_t)seg * D + lane + HALF);
+    }
+    float vn[OPT];
 #pragma unroll
-        for (int g = 0; g < G; ++g) pq[g] = 0.0f;
+    for (int u = 0; u < OPT; ++u) vn[u] = load_elem<BF16>(a.v, (int64_t)seg * D + (u * NT + tid) % D);
+    // ---- query- and similarity-gate columns of x W_dec: thread = (column, row subset)
+    float gacc = 0.0f;
+    {
+      const int col = (tid & 1) ? 2 * Hkv + h : h;
+      const int rsub = tid >> 1;
+      constexpr int R = NT / 2;
+      const int64_t xb = (int64_t)b * Dm;
+      for (int rb = rsub; rb < Dm; rb += KRG * R) {
+        float xr[KRG], wr[KRG];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ps = fmaf(ktv[i], kf[i], ps);
-#pragma unroll
-          for (int g = 0; g < G; ++g) pq[g] = fmaf(qv[g][i], kf[i], pq[g]);
+        for (int q = 0; q < KRG; ++q) {
+          const int row = min(rb + q * R, Dm - 1);
+          xr[q] = load_elem<BF16>(a.x, xb + row);
+          wr[q] = load_elem<BF16>(a.W_dec, (int64_t)row * 3 * Hkv + col);
         }
-        ps = group_sum<LPE>(ps);
 #pragma unroll
-        for (int g = 0; g < G; ++g) pq[g] = group_sum<LPE>(pq[g]);
-        const float l0 = valid ? lamv[bb] : kNegInf;
-        const bool alive = valid && (l0 >= tau);
-        const float A = pair_A(pc, row2, lkv[bb] * kscale, ps);
-        const float l1 = alive ? l0 + A : l0;
-        live[bb] = alive && (l1 >= tau);
-        newlam[bb] = l1;
-        changed[bb] = alive;
-        const float lb2 = l1 * kLog2e;
-#pragma unroll
-        for (int g = 0; g < G; ++g) e2[g][bb] = live[bb] ? fmaf(pq[g], qs2, lb2) : kNegInf;
+        for (int q = 0; q < KRG; ++q) gacc = fmaf((rb + q * R < Dm) ? xr[q] : 0.0f, wr[q], gacc);
       }
+    }
+    // ---- RoPE table (fp64 angles) while the loads fly
+    if (tid < HALF) {
+      double sn, cs;
+      sincos((double)pos * a.inv_freq[tid], &sn, &cs);
+      s_cs[tid] = (float)cs;
+      s_sn[tid] = (float)sn;
+    }
+#pragma unroll
+    for (int o = 2; o < 64; o <<= 1) gacc += __shfl_xor(gacc, o, 64);
+    if (lane < 2) s_gred[wv][lane] = gacc;
+    __syncthreads();
+    // ---- rotated queries, the stored key (L2-normalised, rotated, rounded like the cache), gates
+    if (tid < G * HALF) {
+      s_tq[qg * D + qi] = fmaf(q0, s_cs[qi], -q1 * s_sn[qi]);
+      s_tq[qg * D + qi + HALF] = fmaf(q1, s_cs[qi], q0 * s_sn[qi]);
+    }
+    if (wv == kWaveK) {
+      const float inv = 1.0f / fmaxf(sqrtf(wave_sum(k0 * k0 + k1 * k1)), 1e-12f);
+      if (lane < HALF) {
+        const float n0 = k0 * inv, n1 = k1 * inv;
+        float rr0 = fmaf(n0, s_cs[lane], -n1 * s_sn[lane]);
+        float rr1 = fmaf(n1, s_cs[lane], n0 * s_sn[lane]);
+        if constexpr (BF16) {
+          rr0 = bf16_to_f32(f32_to_bf16(rr0));
+          rr1 = bf16_to_f32(f32_to_bf16(rr1));
+        }
+        s_tq[G * D + lane] = rr0;
+        s_tq[G * D + lane + HALF] = rr1;
+      }
+    }
+    if (tid < 2) {
+      float z = a.b_dec[tid == 0 ? h : 2 * Hkv + h];
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) z += s_gred[w2][tid];
+      s_g[tid] = log_sigmoid(z);
+    }
+    __syncthreads();
 
-      // ---- group partials -> LDS
-      const int pidx = wv * NGW + grp;
+    const PairCoef pc = pair_coef(a.terms);
+    const float row2 = (((a.terms & 1) ? s_g[0] : 0.0f) + ((a.terms & 4) ? s_g[1] : 0.0f)) * pc.inv_n2;
+    const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+    float qv[G][8], ktv[8];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[g][i] = s_tq[g * D + 8 * c + i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ktv[i] = s_tq[G * D + 8 * c + i];
+
+    // ---- dot products, pair term, bias update, logits
+    float e2[G][NB];
+    float newlam[NB];
+    bool live[NB], changed[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const bool valid = e0 + bb < len;
+      row_zero_if<BF16>(kr[bb], !valid);  // slots past the end may hold anything
+      row_zero_if<BF16>(vr[bb], !valid);
+      float kf[8];
+      row_f32<BF16>(kr[bb], kf);
+      float ps = 0.0f;
+      float pq[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) pq[g] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ps = fmaf(ktv[i], kf[i], ps);
+#pragma unroll
+        for (int g = 0; g < G; ++g) pq[g] = fmaf(qv[g][i], kf[i], pq[g]);
+      }
+      ps = group_sum<LPE>(ps);
+#pragma unroll
+      for (int g = 0; g < G; ++g) pq[g] = group_sum<LPE>(pq[g]);
+      const float l0 = valid ? lamv[bb] : kNegInf;
+      const bool alive = valid && (l0 >= tau);
+      const float A = pair_A(pc, row2, lkv[bb] * kscale, ps);
+      const float l1 = alive ? l0 + A : l0;
+      live[bb] = alive && (l1 >= tau);
+      newlam[bb] = l1;
+      changed[bb] = alive;
+      const float lb2 = l1 * kLog2e;
+#pragma unroll
+      for (int g = 0; g < G; ++g) e2[g][bb] = live[bb] ? fmaf(pq[g], qs2, lb2) : kNegInf;
+    }
+
+    // ---- this tile's live entries (compaction): lane grp * LPE + bb owns
+    // entry bb of its group; entries in tile order are (wave, group, entry)
+    uint64_t mask = 0;
+    if constexpr (COMPACT) {
+      bool mine_live = false;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) mine_live = (c == bb) ? live[bb] : mine_live;
+      mask = __ballot(c < NB && mine_live);
+      if (lane == 0) s_cnt[wv] = __popcll(mask);
+    }
+    // ---- issued now, used by the combine: the sequence's tagged words (u, the
+    // new key's gate)
+    const unsigned long long* uword = ctl.uw + (int64_t)b * kUWords + (tid < r ? tid : kMaxRank + h);
+    unsigned long long uwd = (tid <= r) ? ld64_coh(uword) : 0ull;
+
+    // ---- wave partial per head: max over the wave first, then sums relative to it
+    float ms[G], lw[G], o8[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = e2[g][0];
+#pragma unroll
+      for (int bb = 1; bb < NB; ++bb) m = fmaxf(m, e2[g][bb]);
+      ms[g] = across_groups_max<LPE>(m);
+      lw[g] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[g][i] = 0.0f;
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      float vf[8];
+      row_f32<BF16>(vr[bb], vf);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        float m = e2[g][0];
+        const float p = __builtin_amdgcn_exp2f(e2[g][bb] - ((ms[g] == kNegInf) ? 0.0f : ms[g]));
+        lw[g] += p;
 #pragma unroll
-        for (int bb = 1; bb < NB; ++bb) m = fmaxf(m, e2[g][bb]);
-        const float ms = (m == kNegInf) ? 0.0f : m;
-        float l = 0.0f;
-        float o[8];
+        for (int i = 0; i < 8; ++i) o8[g][i] = fmaf(p, vf[i], o8[g][i]);
+      }
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = 0.0f;
+    for (int g = 0; g < G; ++g) {
+      const float l = across_groups_sum<LPE>(lw[g]);
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const float p = __builtin_amdgcn_exp2f(e2[g][bb] - ms);
-          l += p;
-          float vf[8];
-          row_f32<BF16>(vr[bb], vf);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = fmaf(p, vf[i], o[i]);
-        }
-        float4* dst = reinterpret_cast<float4*>(s_po + (pidx * G + g) * D + 8 * c);
-        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      for (int i = 0; i < 8; ++i) o8[g][i] = across_groups_sum<LPE>(o8[g][i]);
+      if (grp == 0) {
+        float4* dst = reinterpret_cast<float4*>(s_po + (wv * G + g) * D + 8 * c);
+        dst[0] = make_float4(o8[g][0], o8[g][1], o8[g][2], o8[g][3]);
+        dst[1] = make_float4(o8[g][4], o8[g][5], o8[g][6], o8[g][7]);
         if (c == 0) {
-          s_pm[pidx * G + g] = m;
-          s_pl[pidx * G + g] = l;
+          s_pm[wv * G + g] = ms[g];
+          s_pl[wv * G + g] = l;
         }
       }
+    }
+    // the output-gate weights of this thread's outputs, for the combine
+    constexpr int kUp = 16;
+    const int Hq = a.H_q;
+    float up[OPT][kUp];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = min(u * NT + tid, G * D - 1);
+      const int col = (h * G) * D + idx;
+#pragma unroll
+      for (int q = 0; q < kUp; ++q) up[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, r - 1) * Hq * D + col);
+    }
+    __syncthreads();  // partials and live counts in LDS; every row of the tile is in registers
 
-      if constexpr (COMPACT) {
-        // ---- live count of the tile.  Entries in tile order are (wave, group,
-        // entry); lane grp * LPE + bb owns entry bb of its group.
-        bool mine_live = false;
+    int count = 0, wbase = 0;
+    if constexpr (COMPACT) {
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) mine_live = (c == bb) ? live[bb] : mine_live;
-        const uint64_t mask = __ballot(c < NB && mine_live);
-        if (lane == 0) s_cnt[wv] = __popcll(mask);
-        // this tile's rows are all in registers now (the dot products used them)
-        __syncthreads();
-        int count = 0, wbase = 0;
-#pragma unroll
-        for (int w2 = 0; w2 < NT / 64; ++w2) {
-          wbase += (w2 < wv) ? s_cnt[w2] : 0;
-          count += s_cnt[w2];
-        }
-        // ---- look back over the earlier tiles of the segment for the destination
-        if (wv == 0) {
-          int* st = ctl.cmp_state + pbase;
-          if (kt_ == 0) {
-            if (lane == 0) {
-              sti_coh(&st[0], (count << 2) | 2);
-              s_pre = 0;
-            }
-          } else {
-            if (lane == 0) sti_coh(&st[kt_], (count << 2) | 1);
-            int prefix = 0;
-            int cpos = kt_ - 1;  // next predecessor to examine
-            int spins = 0;
-            while (true) {
-              const int pc2 = cpos - lane;  // lane l reads predecessor cpos - l
-              const int sv = (pc2 >= 0) ? ldi_coh(&st[pc2]) : 2;
-              const int flag = (pc2 >= 0) ? (sv & 3) : 2;  // tile -1 acts as prefix 0
-              const int val = (pc2 >= 0) ? (sv >> 2) : 0;
-              const uint64_t inc = __ballot(flag == 2);
-              const uint64_t none = __ballot(flag == 0);
-              const int stop = inc ? (int)__builtin_ctzll(inc) : 64;
-              const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1);
-              if ((none & need) == 0) {
-                prefix += wave_isum((lane <= stop) ? val : 0);
-                if (stop < 64) break;
-                cpos -= 64;
-                continue;
-              }
-              if (++spins > kSpinLimitDec) {
-                if (lane == 0) atomicOr(a.status, 2);
-                break;
-              }
-              __builtin_amdgcn_s_sleep(1);
-            }
-            if (lane == 0) {
-              sti_coh(&st[kt_], ((prefix + count) << 2) | 2);
-              s_pre = prefix;
-            }
-          }
-          // No wait for the earlier tiles' loads is needed: a tile publishes
-          // its count only after the barrier that follows the use of all its
-          // rows, and the prefix above needed the count (or a later inclusive
-          // value) of every earlier tile.
-        }
-        __syncthreads();
-        // ---- stores of the survivors, in order
-        const int P = s_pre;
-        const int myrank =
-            wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-          const int rk = __shfl(myrank, grp * LPE + bb, 64);
-          if (live[bb]) {
-            const int64_t dst = off + P + rk;
-            row_store<BF16>(kr[bb], a.K, dst * D + 8 * c);
-            row_store<BF16>(vr[bb], a.V, dst * D + 8 * c);
-            if (c == bb) {
-              a.lam[dst] = newlam[bb];
-              a.lk[dst] = lkv[bb];
-              if (kept) kept[dst] = e0 + bb;
-            }
-          }
-        }
-      } else {
-        if (c < NB) {  // lane c of a group stores entry c's bias
-          float val = newlam[0];
-          bool ch = changed[0];
-#pragma unroll
-          for (int bb = 1; bb < NB; ++bb) {
-            val = (c == bb) ? newlam[bb] : val;
-            ch = (c == bb) ? changed[bb] : ch;
-          }
-          if (ch) a.lam[off + e0 + c] = val;
-        }
-        __syncthreads();
+      for (int w2 = 0; w2 < kDecWaves; ++w2) {
+        wbase += (w2 < wv) ? s_cnt[w2] : 0;
+        count += s_cnt[w2];
       }
+      // this tile's count (the first tile's is already its inclusive prefix)
+      if (!single && tid == 0)
+        st64_coh(&ctl.dec_state[pbase + kt_],
+                 ((unsigned long long)tag << 32) | (uint32_t)((count << 2) | (kt_ == 0 ? 2 : 1)));
+    } else {
+      if (c < NB) {  // lane c of a group stores entry c's bias
+        float val = newlam[0];
+        bool ch = changed[0];
+#pragma unroll
+        for (int bb = 1; bb < NB; ++bb) {
+          val = (c == bb) ? newlam[bb] : val;
+          ch = (c == bb) ? changed[bb] : ch;
+        }
+        if (ch) a.lam[off + e0 + c] = val;
+      }
+    }
 
-      // ---- merge the tile's partials -> workspace row pbase + kt_
+    // ---- the tile's partial per output (g, i): merge of the wave partials
+    float Mo[OPT], Lo[OPT], Oo[OPT];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = min(u * NT + tid, G * D - 1);
+      const int g = idx / D;
+      const int i = idx - g * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) M = fmaxf(M, s_pm[w2 * G + g]);
+      const float Ms = (M == kNegInf) ? 0.0f : M;
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < kDecWaves; ++w2) {
+        const float wgt = __builtin_amdgcn_exp2f(s_pm[w2 * G + g] - Ms);
+        L = fmaf(s_pl[w2 * G + g], wgt, L);
+        O = fmaf(s_po[(w2 * G + g) * D + i], wgt, O);
+      }
+      Mo[u] = M;
+      Lo[u] = L;
+      Oo[u] = O;
+    }
+
+    bool combines = single;
+    if (!single) {
+      // ---- publish the partial; the last tile of the segment to arrive merges
       const int64_t prow = (int64_t)(pbase + kt_);
-      for (int idx = tid; idx < G * D; idx += NT) {
-        const int g = idx / D;
-        const int i = idx - g * D;
-        float M = kNegInf;
 #pragma unroll
-        for (int p = 0; p < NP; ++p) M = fmaxf(M, s_pm[p * G + g]);
-        const float Ms = (M == kNegInf) ? 0.0f : M;
-        float L = 0.0f, O = 0.0f;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-          const float wgt = __builtin_amdgcn_exp2f(s_pm[p * G + g] - Ms);
-          L = fmaf(s_pl[p * G + g], wgt, L);
-          O = fmaf(s_po[(p * G + g) * D + i], wgt, O);
-        }
-        st_coh(w.part_o + (prow * G + g) * D + i, O);
-        if (i == 0) {
-          st_coh(w.part_ml + (prow * G + g) * 2 + 0, M);
-          st_coh(w.part_ml + (prow * G + g) * 2 + 1, L);
+      for (int u = 0; u < OPT; ++u) {
+        const int idx = u * NT + tid;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const int i = idx - g * D;
+          st_coh(w.part_o + (prow * G + g) * D + i, Oo[u]);
+          if (i == 0) {
+            st_coh(w.part_ml + (prow * G + g) * 2 + 0, Mo[u]);
+            st_coh(w.part_ml + (prow * G + g) * 2 + 1, Lo[u]);
+          }
         }
       }
-
-      // ---- arrival; the last tile of the segment combines
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (tid == 0) s_flag = (add_coh(&w.cnt[seg], 1) == ntile - 1);
       __syncthreads();
-      if (s_flag) {
-        // output-gate weights of this thread's outputs, issued first
-        constexpr int OPT = (G * D + NT - 1) / NT;
-        constexpr int kUp = 16;
-        const int Hq = a.H_q;
-        const int r = a.r;
-        float up[OPT][kUp];
+      combines = s_flag;
+      if (combines) {
+        constexpr int TC = 8;  // tiles per pass, loads in flight together
 #pragma unroll
         for (int u = 0; u < OPT; ++u) {
           const int idx = min(u * NT + tid, G * D - 1);
-          const int col = (h * G) * D + idx;
+          const int g = idx / D;
+          const int i = idx - g * D;
+          float M = kNegInf, L = 0.0f, O = 0.0f;
+          for (int p0 = 0; p0 < ntile; p0 += TC) {
+            float pm[TC], pl[TC], po[TC];
 #pragma unroll
-          for (int q = 0; q < kUp; ++q) up[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, r - 1) * Hq * D + col);
-        }
-        // u = x W_dn and the new key's gate, from the partial projections
-        for (int q = tid; q <= r; q += NT) {
-          const int col = q < r ? 3 * Hkv + q : Hkv + h;
-          float z = q < r ? 0.0f : a.b_dec[Hkv + h];
-          for (int sp = 0; sp < NS; ++sp) z += ld_coh(w.zpart + ((int64_t)b * NS + sp) * w.zstride + col);
-          s_u[q] = q < r ? z : log_sigmoid(z);
-        }
-        // running merge per output (g, i): the new token's own term first
-        float Mr[OPT], Lr[OPT], Or[OPT];
-#pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-          const int idx = u * NT + tid;
-          if (idx < G * D) {
-            const int g = idx / D;
-            const int i = idx - g * D;
-            Mr[u] = ld_coh(w.eself + b * Hq + h * G + g);
-            Lr[u] = 1.0f;
-            Or[u] = load_elem<BF16>(a.v, (int64_t)seg * D + i);
-          }
-        }
-        constexpr int TC = 32;        // tiles per pass
-        float* s_cm = s_po;           // [G][TC] tile maxima
-        float* s_cl = s_po + G * TC;  // [G][TC] tile sums
-        for (int p0 = 0; p0 < ntile; p0 += TC) {
-          const int np = min(TC, ntile - p0);
-          __syncthreads();
-          for (int idx = tid; idx < G * TC; idx += NT) {
-            const int g = idx / TC;
-            const int p = idx - g * TC;
-            if (p < np) {
-              const int64_t pr = (int64_t)(pbase + p0 + p);
-              s_cm[idx] = ld_coh(w.part_ml + (pr * G + g) * 2 + 0);
-              s_cl[idx] = ld_coh(w.part_ml + (pr * G + g) * 2 + 1);
+            for (int p = 0; p < TC; ++p) {
+              const int64_t pr = (int64_t)(pbase + min(p0 + p, ntile - 1));
+              pm[p] = ld_coh(w.part_ml + (pr * G + g) * 2 + 0);
+              pl[p] = ld_coh(w.part_ml + (pr * G + g) * 2 + 1);
+              po[p] = ld_coh(w.part_o + (pr * G + g) * D + i);
             }
-          }
-          __syncthreads();
+            float Mn = M;
 #pragma unroll
-          for (int u = 0; u < OPT; ++u) {
-            const int idx = u * NT + tid;
-            if (idx < G * D) {
-              const int g = idx / D;
-              const int i = idx - g * D;
-              float M = Mr[u];
-              for (int p = 0; p < np; ++p) M = fmaxf(M, s_cm[g * TC + p]);
-              const float rs = __builtin_amdgcn_exp2f(Mr[u] - M);
-              float L = Lr[u] * rs, O = Or[u] * rs;
-              float po[TC];
+            for (int p = 0; p < TC; ++p) Mn = (p0 + p < ntile) ? fmaxf(Mn, pm[p]) : Mn;
+            const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
+            const float rs = __builtin_amdgcn_exp2f(M - Ms);
+            L *= rs;
+            O *= rs;
 #pragma unroll
-              for (int p = 0; p < TC; ++p)
-                po[p] = (p < np) ? ld_coh(w.part_o + ((int64_t)(pbase + p0 + p) * G + g) * D + i) : 0.0f;
-#pragma unroll
-              for (int p = 0; p < TC; ++p) {
-                if (p < np) {
-                  const float wgt = __builtin_amdgcn_exp2f(s_cm[g * TC + p] - M);
-                  L = fmaf(s_cl[g * TC + p], wgt, L);
-                  O = fmaf(po[p], wgt, O);
-                }
+            for (int p = 0; p < TC; ++p) {
+              if (p0 + p < ntile) {
+                const float wgt = __builtin_amdgcn_exp2f(pm[p] - Ms);
+                L = fmaf(pl[p], wgt, L);
+                O = fmaf(po[p], wgt, O);
               }
-              Mr[u] = M;
-              Lr[u] = L;
-              Or[u] = O;
             }
+            M = Mn;
           }
+          Mo[u] = M;
+          Lo[u] = L;
+          Oo[u] = O;
         }
-        // ---- output gate and y (s_u was written before the barriers above)
+        if (tid == 0) sti_coh(&w.cnt[seg], 0);
+      }
+    }
+    // the tile that appends the new entry: the combining one, or with
+    // compaction the segment's last tile (it learns the final length)
+    const bool appends = COMPACT ? (kt_ == ntile - 1) : combines;
+
+    // ---- the sequence's tagged words, once they carry this call's tag
+    if ((combines || appends) && tid <= r) {
+      int spins = 0;
+      while ((uint32_t)(uwd >> 32) != tag) {
+        if (++spins > kSpinLimitDec) {
+          atomicOr(a.status, 2);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        uwd = ld64_coh(uword);
+      }
+      s_u[tid] = __uint_as_float((uint32_t)uwd);
+    }
+
+    // ---- combine: the token's own term, the output gate, y
+    if (combines) {
+      if (wv < G) {  // the token's own logit per query head (one wave each)
+        float e = 0.0f;
+        for (int i = lane; i < D; i += 64) e = fmaf(s_tq[wv * D + i], s_tq[G * D + i], e);
+        e = wave_sum(e);
+        if (lane == 0) s_es[wv] = e * qs2;
+      }
+      __syncthreads();
 #pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-          const int idx = u * NT + tid;
-          if (idx < G * D) {
-            const int col = (h * G) * D + idx;
-            float z = a.b_up ? a.b_up[col] : 0.0f;
+      for (int u = 0; u < OPT; ++u) {
+        const int idx = u * NT + tid;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const float es = s_es[g];
+          const float M = fmaxf(Mo[u], es);
+          const float rs = __builtin_amdgcn_exp2f(Mo[u] - M);  // Mo = -inf gives 0
+          const float pe = __builtin_amdgcn_exp2f(es - M);
+          const float L = fmaf(Lo[u], rs, pe);
+          const float O = fmaf(Oo[u], rs, pe * vn[u]);
+          const int col = (h * G) * D + idx;
+          float z = a.b_up ? a.b_up[col] : 0.0f;
 #pragma unroll
-            for (int q = 0; q < kUp; ++q)
-              if (q < r) z = fmaf(s_u[q], up[u][q], z);
-            for (int q = kUp; q < r; ++q) z = fmaf(s_u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
-            const int64_t yo = (int64_t)b * Hq * D + col;
-            const float yv = sigmoid(z) * (Or[u] / Lr[u]);
-            if (a.y_bf16) {
-              reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16(yv);
-            } else {
-              reinterpret_cast<float*>(a.y)[yo] = yv;
-            }
-          }
-        }
-        // ---- the new entry: after the survivors when compacting.  The final
-        // length is read once: the flags it comes from are cleared below.
-        int pos = len;
-        if constexpr (COMPACT) {
-          if (tid == 0) s_pre = ldi_coh(&ctl.cmp_state[pbase + ntile - 1]) >> 2;
-          __syncthreads();
-          pos = s_pre;
-        }
-        const bool room = len < cap;
-        if (room) {
-          for (int i = tid; i < D; i += NT) {
-            const float kv = s_tq[G * D + i];  // the key this tile staged
-            const int64_t dst = (off + pos) * D + i;
-            if constexpr (BF16) {
-              reinterpret_cast<uint16_t*>(a.K)[dst] = f32_to_bf16(kv);  // exact: kv is bf16-rounded
-              reinterpret_cast<uint16_t*>(a.V)[dst] = reinterpret_cast<const uint16_t*>(a.v)[(int64_t)seg * D + i];
-            } else {
-              reinterpret_cast<float*>(a.K)[dst] = kv;
-              reinterpret_cast<float*>(a.V)[dst] = reinterpret_cast<const float*>(a.v)[(int64_t)seg * D + i];
-            }
-          }
-        }
-        if (tid == 0) {
-          if (room) {
-            a.lam[off + pos] = 0.0f;
-            a.lk[off + pos] = s_u[r];
-            if (COMPACT && kept) kept[off + pos] = len;
+          for (int q = 0; q < kUp; ++q)
+            if (q < r) z = fmaf(s_u[q], up[u][q], z);
+          for (int q = kUp; q < r; ++q) z = fmaf(s_u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
+          const int64_t yo = (int64_t)b * Hq * D + col;
+          const float yv = sigmoid(z) * (O / L);
+          if (a.y_bf16) {
+            reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16(yv);
           } else {
-            atomicOr(a.status, 1);
+            reinterpret_cast<float*>(a.y)[yo] = yv;
           }
-          sti_coh(&w.newlen[seg], room ? pos + 1 : pos);
-          sti_coh(&w.cnt[seg], 0);
-        }
-        if constexpr (COMPACT) {
-          for (int t = tid; t < ntile; t += NT) sti_coh(&ctl.cmp_state[pbase + t], 0);
         }
       }
     }
-  }
 
-  // ---- the last workgroup overall commits lengths and positions, clears counters
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) s_flag = (add_coh(&ctl.cmp_glob[1], 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (s_flag) {
-    for (int s = tid; s < S; s += NT) a.seg_len[s] = ldi_coh(&w.newlen[s]);
-    for (int b = tid; b < a.B; b += NT) {
-      a.next_pos[b] += 1;
-      sti_coh(&w.tok_done[b], 0);
+    int npos = len;  // where the new entry goes
+    if constexpr (COMPACT) {
+      // ---- destination of the survivors: look back over the earlier tiles
+      if (single) {
+        if (tid == 0) s_pre = 0;
+      } else if (wv == 0 && kt_ == 0) {
+        if (lane == 0) s_pre = 0;
+      } else if (wv == 0) {
+        const unsigned long long* st = ctl.dec_state + pbase;
+        int prefix = 0;
+        int cpos = kt_ - 1;  // next predecessor to examine
+        int spins = 0;
+        while (true) {
+          const int pc2 = cpos - lane;  // lane l reads predecessor cpos - l
+          const unsigned long long sv = (pc2 >= 0) ? ld64_coh(&st[pc2]) : 0ull;
+          const bool cur = (pc2 < 0) || ((uint32_t)(sv >> 32) == tag);
+          const int flag = (pc2 < 0) ? 2 : (cur ? (int)(sv & 3u) : 0);  // tile -1 acts as prefix 0
+          const int val = (pc2 < 0) ? 0 : (int)((uint32_t)sv >> 2);
+          const uint64_t inc = __ballot(flag == 2);
+          const uint64_t none = __ballot(flag == 0);
+          const int stop = inc ? (int)__builtin_ctzll(inc) : 64;
+          const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1);
+          if ((none & need) == 0) {
+            prefix += wave_isum((lane <= stop) ? val : 0);
+            if (stop < 64) break;
+            cpos -= 64;
+            continue;
+          }
+          if (++spins > kSpinLimitDec) {
+            if (lane == 0) atomicOr(a.status, 2);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (lane == 0) {
+          st64_coh(&ctl.dec_state[pbase + kt_], ((unsigned long long)tag << 32) | (uint32_t)(((prefix + count) << 2) | 2));
+          s_pre = prefix;
+        }
+      }
+      __syncthreads();
+      // ---- the survivors, in order; rows already in place are not rewritten
+      const int P = s_pre;
+      const int myrank =
+          wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const int rk = __shfl(myrank, grp * LPE + bb, 64);
+        if (live[bb]) {
+          const int64_t dst = off + P + rk;
+          const bool moves = P + rk != e0 + bb;
+          if (moves) {
+            row_store<BF16>(kr[bb], a.K, dst * D + 8 * c);
+            row_store<BF16>(vr[bb], a.V, dst * D + 8 * c);
+          }
+          if (c == bb) {
+            a.lam[dst] = newlam[bb];
+            if (moves) a.lk[dst] = lkv[bb];
+            if (kept) kept[dst] = e0 + bb;
+          }
+        }
+      }
+      npos = P + count;
     }
-    if (tid == 0) {
-      sti_coh(&ctl.cmp_glob[0], 0);
-      sti_coh(&ctl.cmp_glob[1], 0);
+
+    // ---- the new entry: after the survivors when compacting
+    if (appends) {
+      if (!combines) __syncthreads();  // s_u (the combine has a barrier of its own)
+      const bool room = len < cap;
+      if (room && tid < D) {
+        const int64_t dst = (off + npos) * D + tid;
+        const float kv = s_tq[G * D + tid];
+        if constexpr (BF16) {
+          reinterpret_cast<uint16_t*>(a.K)[dst] = f32_to_bf16(kv);     // exact: kv is bf16-rounded
+          reinterpret_cast<uint16_t*>(a.V)[dst] = f32_to_bf16(vn[0]);  // exact: a bf16 input
+        } else {
+          reinterpret_cast<float*>(a.K)[dst] = kv;
+          reinterpret_cast<float*>(a.V)[dst] = vn[0];
+        }
+      }
+      if (tid == 0) {
+        if (room) {
+          a.lam[off + npos] = 0.0f;
+          a.lk[off + npos] = s_u[r];
+          if (COMPACT && kept) kept[off + npos] = len;
+        } else {
+          atomicOr(a.status, 1);
+        }
+        sti_coh(&w.newlen[seg], room ? npos + 1 : npos);
+      }
     }
   }
 }
@@ -750,9 +836,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(LayerArgs a, D
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-int decode_tile_entries(int d) { return d == 64 ? DecodeShape<64>::TWG : DecodeShape<128>::TWG; }
+static int tile_entries(int d, int nb) { return (64 / (d / 8)) * nb * kDecWaves; }
 
-static int decode_token_splits(const LayerArgs& a) { return (a.H_q * a.d + kDecThreads - 1) / kDecThreads; }
+// The finest tiling any variant uses (sizes the per-tile workspace rows and flags).
+int decode_tile_entries(int d) { return tile_entries(d, 4); }
 
 static int64_t decode_max_tiles(const LayerArgs& a, int twg) {
   const int64_t S = (int64_t)a.B * a.H_kv;
@@ -764,32 +851,20 @@ static size_t decode_layout(const LayerArgs& a, int twg, DecodeWs* w, char* base
   const int64_t S = (int64_t)a.B * a.H_kv;
   const int G = a.H_q / a.H_kv;
   const int64_t mt = decode_max_tiles(a, twg);
-  const int NS = decode_token_splits(a);
-  const int zs = (3 * a.H_kv + a.r + 3) / 4 * 4;
   size_t n = 0;
   auto take = [&](size_t bytes) {
     char* q = base ? base + n : nullptr;
     n += align_up(bytes, 256);
     return q;
   };
-  float* qt = reinterpret_cast<float*>(take(sizeof(float) * a.B * a.H_q * a.d));
-  float* kt = reinterpret_cast<float*>(take(sizeof(float) * S * a.d));
-  float* zpart = reinterpret_cast<float*>(take(sizeof(float) * a.B * NS * zs));
   int* newlen = reinterpret_cast<int*>(take(sizeof(int) * S));
-  float* eself = reinterpret_cast<float*>(take(sizeof(float) * a.B * a.H_q));
   float* part_o = reinterpret_cast<float*>(take(sizeof(float) * mt * G * a.d));
   float* part_ml = reinterpret_cast<float*>(take(sizeof(float) * mt * G * 2));
   if (w) {
-    w->qt = qt;
-    w->kt = kt;
-    w->zpart = zpart;
     w->newlen = newlen;
-    w->eself = eself;
     w->part_o = part_o;
     w->part_ml = part_ml;
     w->max_tiles = (int)mt;
-    w->splits = NS;
-    w->zstride = zs;
   }
   return n;
 }
@@ -800,14 +875,29 @@ DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, 
   DecodeWs w{};
   decode_layout(a, twg, &w, reinterpret_cast<char*>(scratch));
   w.cnt = ctl.dec_cnt;
-  w.tok_done = ctl.dec_cntb;
   return w;
+}
+
+// Compute units of the current device (the persistent grid's size), cached.
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 template <int D, int G, bool BF16>
 static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Control& ctl, float tau, bool compact,
                               int32_t* kept, hipStream_t st) {
-  const int grid = a.B * w.splits + w.max_tiles;
+  const int twg = DecodeShape<D, DecodeNB<BF16, G>::value>::TWG;
+  const int64_t items = (int64_t)a.B + decode_max_tiles(a, twg);
+  const int cus = device_cus();
+  const int grid = (int)(items < cus ? items : cus);
   if (compact) {
     hipLaunchKernelGGL((decode_step_kernel<D, G, BF16, true>), dim3(grid), dim3(kDecThreads), 0, st, a, w, ctl, tau,
                        kept);

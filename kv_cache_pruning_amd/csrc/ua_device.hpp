@@ -79,6 +79,55 @@ constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
 
+// The value of lane i ^ 8 (row_ror:8 inside each row of 16 lanes).
+constexpr int kDppRor8 = 0x128;
+
+// Combine lane i with lane i ^ X for X = 8, 16 or 32 on the VALU: DPP inside a
+// row, or the gfx950 row swaps (permlane16_swap pairs rows 0-1 and 2-3,
+// permlane32_swap the two halves; both hand every lane the even- and the
+// odd-side value).  Both lanes of a pair get bitwise the same result.
+template <int X>
+__device__ __forceinline__ float xor_sum(float v) {
+  static_assert(X == 8 || X == 16 || X == 32, "lane distance");
+  if constexpr (X == 8) {
+    return v + dpp_f<kDppRor8>(v);
+  } else {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = (X == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+template <int X>
+__device__ __forceinline__ float xor_max(float v) {
+  static_assert(X == 8 || X == 16 || X == 32, "lane distance");
+  if constexpr (X == 8) {
+    return fmaxf(v, dpp_f<kDppRor8>(v));
+  } else {
+    const uint32_t u = __float_as_uint(v);
+    const auto r = (X == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+}
+
+// Sum / max over the lanes l, l ^ N, l ^ 2N, ... of a wave (N = 8 or 16: one
+// value per group of N lanes, combined across the 64 / N groups).
+template <int N>
+__device__ __forceinline__ float across_groups_sum(float v) {
+  static_assert(N == 8 || N == 16, "group size");
+  if constexpr (N == 8) v = xor_sum<8>(v);
+  v = xor_sum<16>(v);
+  return xor_sum<32>(v);
+}
+template <int N>
+__device__ __forceinline__ float across_groups_max(float v) {
+  static_assert(N == 8 || N == 16, "group size");
+  if constexpr (N == 8) v = xor_max<8>(v);
+  v = xor_max<16>(v);
+  return xor_max<32>(v);
+}
+
 // Sum over aligned groups of N lanes (N = 8 or 16); every lane gets the sum.
 template <int N>
 __device__ __forceinline__ float group_sum(float v) {

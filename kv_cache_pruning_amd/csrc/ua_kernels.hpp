@@ -50,17 +50,27 @@ struct LayerArgs {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Control words of a workspace: counters and flags that must be zero before
-// the first call; every call returns them to zero.  The fixed part sits at
-// the front of the workspace, the compaction flags at its end (see
-// workspace.hip), so calls on caches of different sizes can share one.
+// the first call; every call returns them to zero, except the call counter at
+// glob[kGlobSeq] and the tagged words, whose stale contents carry an older
+// tag.  The fixed part sits at the front of the workspace, the compaction
+// flags at its end (see workspace.hip), so calls on caches of different
+// sizes can share one.
+constexpr int kGlobTicket = 0;   // decode and compaction: next work item
+constexpr int kGlobArrive = 32;  // compaction: workgroups done (own cache line)
+constexpr int kGlobSeq = 64;     // decode: calls made (tags the per-sequence words)
+constexpr int kGlobDone = 96;    // decode: workgroups finished
+constexpr int kGlobInts = 128;
+constexpr int kUWords = kMaxRank + kMaxHkv;  // tagged words per sequence: u, then key gates
+
 struct Control {
-  int* dec_cnt;     // [S]           decode: arrivals per segment
-  int* dec_cntb;    // [B]           decode: finished per-token splits per sequence
-  int* cmp_state;   // [max_chunks]  compaction (also decode tiles): (count or prefix) << 2 | flag
-  int* cmp_loaded;  // [max_chunks]  compaction: the chunk's rows are in registers
-  int* cmp_done;    // [S]           compaction: arrivals per segment
-  int* cmp_glob;    // [2]           compaction and decode: ticket, arrivals
-  int cmp_chunk;    // entries per compaction chunk
+  int* dec_cnt;              // [S]           decode: arrivals per segment
+  int* cmp_state;            // [max_chunks]  compaction: (count or prefix) << 2 | flag
+  int* cmp_loaded;           // [max_chunks]  compaction: the chunk's rows are in registers
+  unsigned long long* dec_state;  // [max_chunks]  decode tiles: call tag << 32 | (count or prefix) << 2 | flag
+  int* cmp_done;             // [S]           compaction: arrivals per segment
+  int* glob;                 // [kGlobInts]   ticket, arrivals, call counter, finished (one cache line each)
+  unsigned long long* uw;    // [B, kUWords]  decode: per-sequence values, call tag in the high half
+  int cmp_chunk;             // entries per compaction chunk
   int max_chunks;
 };
 
@@ -72,17 +82,10 @@ Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes);
 // Decode scratch (after the control block) plus the counters it uses.
 struct DecodeWs {
   int* cnt;        // [S]  arrivals per segment (control block)
-  int* tok_done;   // [B]  finished per-token splits per sequence (control block)
-  float* qt;       // [B, H_q, d]  rotated queries
-  float* kt;       // [S, d]       stored new keys (cache-rounded), fp32
-  float* zpart;    // [B, splits, zstride]  partial sums of x [W_dec | W_dn]
-  int* newlen;     // [S]          segment lengths after the step
-  float* eself;    // [B, H_q]     new token's own logit (log2 units)
-  float* part_o;   // [max_tiles, G, d]
-  float* part_ml;  // [max_tiles, G, 2]  max (log2 units), sum
+  int* newlen;     // [S]  segment lengths after the step
+  float* part_o;   // [max_tiles, G, d]   partials of segments held by several tiles
+  float* part_ml;  // [max_tiles, G, 2]   max (log2 units), sum
   int max_tiles;
-  int splits;      // per-token workgroups per sequence
-  int zstride;
 };
 
 size_t decode_ws_bytes(const LayerArgs& a, int tile_entries);

@@ -3,14 +3,15 @@
 //   [ fixed control | scratch of the call ... | compaction flags ]
 //   ^ ws                                       ^ end of ws - tail
 //
-// The fixed control words (decode and compaction arrival counters, the
-// compaction ticket) depend only on B and H_kv; the compaction flags (one
+// The fixed control words (arrival counters, the ticket, the decode call
+// counter and per-sequence tagged words) depend only on B and H_kv; the compaction flags (one
 // pair per chunk, so their number depends on total_slots) are carved from
 // the END of the workspace.  Layers of one shape whose caches differ in size
 // can then share one workspace sized for the largest: no call's scratch ever
 // overlaps another call's control words.  The control words are zero before
-// the first call and every call leaves them zero; prefill keeps its own sync
-// words in its scratch and clears them at the start of each call.
+// the first call and every call leaves them zero (the decode call counter and
+// the tagged words aside); prefill keeps its own sync words in its scratch and
+// clears them at the start of each call.
 
 #include <algorithm>
 
@@ -39,21 +40,24 @@ static size_t fixed_layout(const LayerArgs& a, Control* c, char* base) {
     return q;
   };
   int* dec_cnt = take(sizeof(int) * S);
-  int* dec_cntb = take(sizeof(int) * a.B);
   int* cmp_done = take(sizeof(int) * S);
-  int* cmp_glob = take(sizeof(int) * 2);
+  int* glob = take(sizeof(int) * kGlobInts);
+  int* uw = take(sizeof(unsigned long long) * a.B * kUWords);
   if (c) {
     c->dec_cnt = dec_cnt;
-    c->dec_cntb = dec_cntb;
     c->cmp_done = cmp_done;
-    c->cmp_glob = cmp_glob;
+    c->glob = glob;
+    c->uw = reinterpret_cast<unsigned long long*>(uw);
   }
   return n;
 }
 
 size_t control_bytes(const LayerArgs& a) { return fixed_layout(a, nullptr, nullptr); }
 
-size_t control_tail_bytes(const LayerArgs& a) { return 2 * align_up(sizeof(int) * compact_max_chunks(a), 256); }
+size_t control_tail_bytes(const LayerArgs& a) {
+  const int64_t mc = compact_max_chunks(a);
+  return 2 * align_up(sizeof(int) * mc, 256) + align_up(sizeof(unsigned long long) * mc, 256);
+}
 
 Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes) {
   Control c{};
@@ -61,9 +65,10 @@ Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes) {
   fixed_layout(a, &c, base);
   const int64_t mc = compact_max_chunks(a);
   const size_t one = align_up(sizeof(int) * mc, 256);
-  char* tail = base + (ws_bytes / 256 * 256) - 2 * one;  // callers check ws_bytes covers every part
+  char* tail = base + (ws_bytes / 256 * 256) - control_tail_bytes(a);  // callers check ws_bytes covers every part
   c.cmp_state = reinterpret_cast<int*>(tail);
   c.cmp_loaded = reinterpret_cast<int*>(tail + one);
+  c.dec_state = reinterpret_cast<unsigned long long*>(tail + 2 * one);
   c.cmp_chunk = compact_chunk_entries(a);
   c.max_chunks = (int)mc;
   return c;
