@@ -136,12 +136,10 @@ __device__ __forceinline__ void row_f32(const Row8<BF16>& r, float (&o)[8]) {
   }
 }
 
-// Entries per lane group (rows held in registers at once; the budget of a
-// 512-thread workgroup allows four).
-template <bool BF16, int G>
-struct DecodeNB {
-  static constexpr int value = 4;
-};
+// Entries per lane group (rows held in registers at once).  Fewer entries per
+// tile spread a step over more compute units: a tile's VALU work, not its
+// bytes, sets its time at these sizes.
+constexpr int decode_nb(int d) { return d == 64 ? 2 : 4; }
 
 template <int D, int NB_>
 struct DecodeShape {
@@ -250,10 +248,28 @@ __device__ void seq_item(const LayerArgs& a, const Control& ctl, int b, uint32_t
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
+// All kernel arguments in one struct, read through the kernel-argument
+// segment pointer where they are used: passed as separate by-value
+// parameters, every field is loaded at entry and most then spill from scalar
+// registers into vector lanes, each use costing a VALU read.  The struct is
+// the only explicit argument, so it starts the segment.
+struct DecodeKArgs {
+  LayerArgs a;
+  DecodeWs w;
+  Control ctl;
+  float tau;
+  int32_t* kept;
+};
+
 template <int D, int G, bool BF16, bool COMPACT>
-__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(LayerArgs a, DecodeWs w, Control ctl, float tau,
-                                                                  int32_t* kept) {
-  using Sh = DecodeShape<D, DecodeNB<BF16, G>::value>;
+__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs karg) {
+  const DecodeKArgs& K = *(const DecodeKArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const LayerArgs& a = K.a;
+  const DecodeWs& w = K.w;
+  const Control& ctl = K.ctl;
+  const float tau = K.tau;
+  int32_t* const kept = K.kept;
+  using Sh = DecodeShape<D, decode_nb(D)>;
   constexpr int LPE = Sh::LPE, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
   constexpr int NT = kDecThreads;
   constexpr int HALF = D / 2;
@@ -838,8 +854,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(LayerArgs a, D
 // ---------------------------------------------------------------------------
 static int tile_entries(int d, int nb) { return (64 / (d / 8)) * nb * kDecWaves; }
 
-// The finest tiling any variant uses (sizes the per-tile workspace rows and flags).
-int decode_tile_entries(int d) { return tile_entries(d, 4); }
+// Entries per tile (sizes the per-tile workspace rows and flags).
+int decode_tile_entries(int d) { return tile_entries(d, decode_nb(d)); }
 
 static int64_t decode_max_tiles(const LayerArgs& a, int twg) {
   const int64_t S = (int64_t)a.B * a.H_kv;
@@ -894,16 +910,14 @@ static int device_cus() {
 template <int D, int G, bool BF16>
 static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Control& ctl, float tau, bool compact,
                               int32_t* kept, hipStream_t st) {
-  const int twg = DecodeShape<D, DecodeNB<BF16, G>::value>::TWG;
+  const int twg = DecodeShape<D, decode_nb(D)>::TWG;
   const int64_t items = (int64_t)a.B + decode_max_tiles(a, twg);
   const int cus = device_cus();
   const int grid = (int)(items < cus ? items : cus);
   if (compact) {
-    hipLaunchKernelGGL((decode_step_kernel<D, G, BF16, true>), dim3(grid), dim3(kDecThreads), 0, st, a, w, ctl, tau,
-                       kept);
+    hipLaunchKernelGGL((decode_step_kernel<D, G, BF16, true>), dim3(grid), dim3(kDecThreads), 0, st, DecodeKArgs{a, w, ctl, tau, kept});
   } else {
-    hipLaunchKernelGGL((decode_step_kernel<D, G, BF16, false>), dim3(grid), dim3(kDecThreads), 0, st, a, w, ctl, tau,
-                       kept);
+    hipLaunchKernelGGL((decode_step_kernel<D, G, BF16, false>), dim3(grid), dim3(kDecThreads), 0, st, DecodeKArgs{a, w, ctl, tau, kept});
   }
   return hipGetLastError();
 }
