@@ -97,26 +97,29 @@ struct Row8 {
   u32x4 w[BF16 ? 1 : 2];
 };
 
+// Loads and stores at a 32-bit byte offset from a uniform base (the
+// scalar-base + vector-offset addressing form, no 64-bit address math).
+template <typename T>
+__device__ __forceinline__ T ld_at(const char* base, uint32_t boff) {
+  return *reinterpret_cast<const T*>(base + boff);
+}
 template <bool BF16>
-__device__ __forceinline__ void row_load(Row8<BF16>& r, const void* base, int64_t elem) {
+__device__ __forceinline__ float elem_at(const char* base, uint32_t boff) {
   if constexpr (BF16) {
-    r.w[0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + elem);
+    return bf16_to_f32(ld_at<uint16_t>(base, boff));
   } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(base) + elem);
-    r.w[0] = p[0];
-    r.w[1] = p[1];
+    return ld_at<float>(base, boff);
   }
 }
-
 template <bool BF16>
-__device__ __forceinline__ void row_store(const Row8<BF16>& r, void* base, int64_t elem) {
-  if constexpr (BF16) {
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + elem) = r.w[0];
-  } else {
-    u32x4* p = reinterpret_cast<u32x4*>(reinterpret_cast<float*>(base) + elem);
-    p[0] = r.w[0];
-    p[1] = r.w[1];
-  }
+__device__ __forceinline__ void row_load_at(Row8<BF16>& r, const char* base, uint32_t boff) {
+  r.w[0] = ld_at<u32x4>(base, boff);
+  if constexpr (!BF16) r.w[1] = ld_at<u32x4>(base, boff + 16);
+}
+template <bool BF16>
+__device__ __forceinline__ void row_store_at(const Row8<BF16>& r, char* base, uint32_t boff) {
+  *reinterpret_cast<u32x4*>(base + boff) = r.w[0];
+  if constexpr (!BF16) *reinterpret_cast<u32x4*>(base + boff + 16) = r.w[1];
 }
 
 template <bool BF16>
@@ -274,7 +277,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
   constexpr int NT = kDecThreads;
   constexpr int HALF = D / 2;
   constexpr int OPT = (G * D + NT - 1) / NT;  // outputs (g, i) per thread
-  constexpr int KRG = 16;                     // gate-column rows per thread per pass
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -395,48 +397,83 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
     const int c = lane - grp * LPE;
     const int e0 = kt_ * TWG + wv * TW + grp * NB;
 
-    // ---- cached entries: every load (from a clamped slot) issued first
+    // ---- cached entries: every load issued first, from the segment's base with
+    // 32-bit offsets; slots past the end read the last entry (masked below)
+    constexpr int EB = BF16 ? 2 : 4;  // bytes per element
+    char* const Kseg = reinterpret_cast<char*>(a.K) + off * (D * EB);
+    char* const Vseg = reinterpret_cast<char*>(a.V) + off * (D * EB);
+    const char* const lamseg = reinterpret_cast<const char*>(a.lam + off);
+    const char* const lkseg = reinterpret_cast<const char*>(a.lk + off);
+    const int relmax = max(len - 1, 0);
     Row8<BF16> kr[NB], vr[NB];
     float lamv[NB], lkv[NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
-      const int64_t j = min(off + min(e0 + bb, max(len - 1, 0)), a.total_slots - 1);
-      row_load<BF16>(kr[bb], a.K, j * D + 8 * c);
-      row_load<BF16>(vr[bb], a.V, j * D + 8 * c);
-      lamv[bb] = a.lam[j];
-      lkv[bb] = a.lk[j];
+      const int rel = min(e0 + bb, relmax);
+      const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+      row_load_at<BF16>(kr[bb], Kseg, ro);
+      row_load_at<BF16>(vr[bb], Vseg, ro);
+      lamv[bb] = ld_at<float>(lamseg, (uint32_t)rel * 4);
+      lkv[bb] = ld_at<float>(lkseg, (uint32_t)rel * 4);
     }
     // ---- the token: position, query pair (g, i) / (g, i + d/2), key pair, V
     const int pos = a.next_pos[b];
     const int qg = min(tid / HALF, G - 1), qi = tid % HALF;
-    const int64_t qb = ((int64_t)b * a.H_q + h * G + qg) * D;
-    const float q0 = load_elem<BF16>(a.q, qb + qi);
-    const float q1 = load_elem<BF16>(a.q, qb + qi + HALF);
+    const char* const qrow = reinterpret_cast<const char*>(a.q);
+    const uint32_t qb = (uint32_t)(((b * a.H_q + h * G + qg) * D + qi) * EB);
+    const float q0 = elem_at<BF16>(qrow, qb);
+    const float q1 = elem_at<BF16>(qrow, qb + HALF * EB);
     float k0 = 0.0f, k1 = 0.0f;
     if (wv == kWaveK && lane < HALF) {
-      k0 = load_elem<BF16>(a.k, (int64_t)seg * D + lane);
-      k1 = load_elem<BF16>(a.k, (int64_t)seg * D + lane + HALF);
+      const uint32_t kb = (uint32_t)((seg * D + lane) * EB);
+      k0 = elem_at<BF16>(reinterpret_cast<const char*>(a.k), kb);
+      k1 = elem_at<BF16>(reinterpret_cast<const char*>(a.k), kb + HALF * EB);
     }
     float vn[OPT];
 #pragma unroll
-    for (int u = 0; u < OPT; ++u) vn[u] = load_elem<BF16>(a.v, (int64_t)seg * D + (u * NT + tid) % D);
-    // ---- query- and similarity-gate columns of x W_dec: thread = (column, row subset)
-    float gacc = 0.0f;
+    for (int u = 0; u < OPT; ++u)
+      vn[u] = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + (u * NT + tid) % D) * EB));
+    // ---- query- and similarity-gate columns of x W_dec: per pass, two runs of
+    // four consecutive rows per thread (a vector load of x and eight gathered
+    // weights each), every load of the pass issued before use
+    float gq = 0.0f, gs = 0.0f;
     {
-      const int col = (tid & 1) ? 2 * Hkv + h : h;
-      const int rsub = tid >> 1;
-      constexpr int R = NT / 2;
-      const int64_t xb = (int64_t)b * Dm;
-      for (int rb = rsub; rb < Dm; rb += KRG * R) {
-        float xr[KRG], wr[KRG];
+      const char* const xrow = reinterpret_cast<const char*>(a.x) + (int64_t)b * Dm * EB;
+      const char* const wd = reinterpret_cast<const char*>(a.W_dec);
+      const uint32_t wstride = (uint32_t)(3 * Hkv * EB);
+      const uint32_t cq = (uint32_t)(h * EB), cs = (uint32_t)((2 * Hkv + h) * EB);
+      for (int p0 = 4 * tid; p0 < Dm; p0 += 8 * NT) {
+        float xv[8], wq[8], ws[8];
 #pragma unroll
-        for (int q = 0; q < KRG; ++q) {
-          const int row = min(rb + q * R, Dm - 1);
-          xr[q] = load_elem<BF16>(a.x, xb + row);
-          wr[q] = load_elem<BF16>(a.W_dec, (int64_t)row * 3 * Hkv + col);
+        for (int run = 0; run < 2; ++run) {
+          const int r0 = min(p0 + run * 4 * NT, Dm - 4);  // a run past the end repeats the last one
+          if constexpr (BF16) {
+            const uint2 xx = ld_at<uint2>(xrow, (uint32_t)r0 * 2);
+            xv[4 * run + 0] = bf16_lo(xx.x);
+            xv[4 * run + 1] = bf16_hi(xx.x);
+            xv[4 * run + 2] = bf16_lo(xx.y);
+            xv[4 * run + 3] = bf16_hi(xx.y);
+          } else {
+            const float4 xx = ld_at<float4>(xrow, (uint32_t)r0 * 4);
+            xv[4 * run + 0] = xx.x;
+            xv[4 * run + 1] = xx.y;
+            xv[4 * run + 2] = xx.z;
+            xv[4 * run + 3] = xx.w;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t ro = (uint32_t)(r0 + i) * wstride;
+            wq[4 * run + i] = elem_at<BF16>(wd, ro + cq);
+            ws[4 * run + i] = elem_at<BF16>(wd, ro + cs);
+          }
         }
+        const bool second = p0 + 4 * NT < Dm;
 #pragma unroll
-        for (int q = 0; q < KRG; ++q) gacc = fmaf((rb + q * R < Dm) ? xr[q] : 0.0f, wr[q], gacc);
+        for (int i = 0; i < 8; ++i) {
+          const float xi = (i < 4 || second) ? xv[i] : 0.0f;
+          gq = fmaf(xi, wq[i], gq);
+          gs = fmaf(xi, ws[i], gs);
+        }
       }
     }
     // ---- RoPE table (fp64 angles) while the loads fly
@@ -446,9 +483,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
       s_cs[tid] = (float)cs;
       s_sn[tid] = (float)sn;
     }
-#pragma unroll
-    for (int o = 2; o < 64; o <<= 1) gacc += __shfl_xor(gacc, o, 64);
-    if (lane < 2) s_gred[wv][lane] = gacc;
+    gq = across_groups_sum<8>(group_sum<8>(gq));
+    gs = across_groups_sum<8>(group_sum<8>(gs));
+    if (lane == 0) {
+      s_gred[wv][0] = gq;
+      s_gred[wv][1] = gs;
+    }
     __syncthreads();
     // ---- rotated queries, the stored key (L2-normalised, rotated, rounded like the cache), gates
     if (tid < G * HALF) {
@@ -804,11 +844,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
       for (int bb = 0; bb < NB; ++bb) {
         const int rk = __shfl(myrank, grp * LPE + bb, 64);
         if (live[bb]) {
-          const int64_t dst = off + P + rk;
-          const bool moves = P + rk != e0 + bb;
+          const int rel = P + rk;
+          const int64_t dst = off + rel;
+          const bool moves = rel != e0 + bb;
           if (moves) {
-            row_store<BF16>(kr[bb], a.K, dst * D + 8 * c);
-            row_store<BF16>(vr[bb], a.V, dst * D + 8 * c);
+            const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+            row_store_at<BF16>(kr[bb], Kseg, ro);
+            row_store_at<BF16>(vr[bb], Vseg, ro);
           }
           if (c == bb) {
             a.lam[dst] = newlam[bb];
