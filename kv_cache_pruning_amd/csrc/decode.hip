@@ -39,8 +39,8 @@
 //    arrive merges them.  The combine adds the token's own term, forms the
 //    output gate from u and its slice of W_up, writes y and appends the new
 //    entry (after the survivors when compacting).
-//  * A workgroup draws its next ticket as soon as an item starts.  Drawing a
-//    ticket past the last item is its exit; the workgroup that draws the last
+//  * A workgroup draws its next ticket while its current item finishes.
+//    Drawing a ticket past the last item is its exit; the workgroup that draws the last
 //    ticket waits until every workgroup has finished and commits the new
 //    lengths and positions.
 //
@@ -354,9 +354,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
       }
       break;
     }
-    if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);  // the next item, drawn now
     if (id < a.B) {
       seq_item<BF16>(a, ctl, id, tag, s_red);
+      if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);
       continue;
     }
 
@@ -629,6 +629,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
 #pragma unroll
       for (int q = 0; q < kUp; ++q) up[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, r - 1) * Hq * D + col);
     }
+    // the next item, drawn while this one finishes (not earlier: workgroups
+    // that start late must get their first items before early ones take a
+    // second)
+    if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);
     __syncthreads();  // partials and live counts in LDS; every row of the tile is in registers
 
     int count = 0, wbase = 0;
