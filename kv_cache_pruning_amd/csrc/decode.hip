@@ -25,8 +25,8 @@
 //    and reads each entry once: the key row feeds the G query dot products
 //    and the key-similarity dot product, the pair term updates the log-bias,
 //    and an online-softmax partial (max, sum, weighted V) is formed per
-//    group of lanes, merged across the wave with DPP and row swaps and across
-//    the waves in LDS.
+//    group of lanes, merged across the wave through an LDS transpose and
+//    across the waves in LDS.
 //  * With COMPACT the surviving entries move down in place: a tile publishes
 //    its live count once all its rows are in registers and looks back over
 //    the earlier tiles of its segment for its destination (decoupled
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
   const float tau = K.tau;
   int32_t* const kept = K.kept;
   using Sh = DecodeShape<D, decode_nb(D)>;
-  constexpr int LPE = Sh::LPE, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
+  constexpr int LPE = Sh::LPE, NGW = Sh::NGW, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
   constexpr int NT = kDecThreads;
   constexpr int HALF = D / 2;
   constexpr int OPT = (G * D + NT - 1) / NT;  // outputs (g, i) per thread
@@ -606,16 +606,28 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float l = across_groups_sum<LPE>(lw[g]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o8[g][i] = across_groups_sum<LPE>(o8[g][i]);
-      if (grp == 0) {
-        float4* dst = reinterpret_cast<float4*>(s_po + (wv * G + g) * D + 8 * c);
+      // the groups' weighted V summed through a per-wave LDS transpose (the
+      // per-sequence item's scratch): each lane writes its 8 sums, then lane
+      // j adds dimension j (and j + 64) over the groups.  LDS operations of
+      // one wave complete in order, so no barrier is needed.
+      float* tp = &s_red[wv * 64][0];  // [group][D]
+      {
+        float4* dst = reinterpret_cast<float4*>(tp + grp * D + 8 * c);
         dst[0] = make_float4(o8[g][0], o8[g][1], o8[g][2], o8[g][3]);
         dst[1] = make_float4(o8[g][4], o8[g][5], o8[g][6], o8[g][7]);
-        if (c == 0) {
-          s_pm[wv * G + g] = ms[g];
-          s_pl[wv * G + g] = l;
-        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int half = 0; half < D / 64; ++half) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NGW; ++q) sum += tp[q * D + half * 64 + lane];
+        s_po[(wv * G + g) * D + half * 64 + lane] = sum;
+      }
+      __builtin_amdgcn_wave_barrier();  // the next head reuses the scratch
+      if (lane == 0) {
+        s_pm[wv * G + g] = ms[g];
+        s_pl[wv * G + g] = l;
       }
     }
     // the output-gate weights of this thread's outputs, for the combine
