@@ -13,15 +13,17 @@
 // Work items are numbered and handed out by an atomic ticket to a persistent
 // grid (at most one workgroup per compute unit), so every wait below is on an
 // item that a running workgroup already holds.
-//  * items [0, B): per sequence, u = x W_dn and the key-gate logits of every
-//    KV head.  They are published as 64-bit words whose high half is the
+//  * items [0, B): per sequence, the gates log sigmoid(x W_dec + b_dec) of
+//    every KV head (query, key and similarity columns); items [B, 2B): u =
+//    x W_dn.  Results are published as 64-bit words whose high half is the
 //    call's tag, so a reader checks each word on its own: no flag, no ordering
-//    between words.
+//    between words.  Tiles read their two gate words after their loads, by
+//    which time the gate items (drawn first) have normally published.
 //  * later items: one tile of TWG entries of one segment (segment = sequence
 //    and KV head), numbered segment by segment from the lengths at the start
 //    of the call.  A tile issues its cache loads together with what it needs
-//    of the token (its G queries, the key, the query- and similarity-gate
-//    columns of x W_dec), forms the rotated queries and stored key itself,
+//    of the token (its G queries, the key, its two gate words), forms the
+//    rotated queries and stored key itself,
 //    and reads each entry once: the key row feeds the G query dot products
 //    and the key-similarity dot product, the pair term updates the log-bias,
 //    and an online-softmax partial (max, sum, weighted V) is formed per
@@ -160,31 +162,31 @@ __device__ __forceinline__ unsigned long long tag_word(float v, uint32_t tag) {
 }
 
 // ---------------------------------------------------------------------------
-// per-sequence item: u = x W_dn (r columns) and the key-gate logits
-// log sigmoid(x W_dec[:, H_kv + h] + b) of every KV head h
+// per-sequence items: the gates log sigmoid(x W_dec + b_dec) of every KV head
+// (3 H_kv columns: query, key, similarity), or u = x W_dn (r columns).  Each
+// result is published as a tagged word.
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__device__ void seq_item(const LayerArgs& a, const Control& ctl, int b, uint32_t tag, float (*s_red)[8]) {
+__device__ void seq_item(const LayerArgs& a, const Control& ctl, int b, bool gates, uint32_t tag,
+                         float (*s_red)[8]) {
   constexpr int CW = BF16 ? 8 : 4;  // elements per 16-byte chunk
   constexpr int NT = kDecThreads;
   constexpr int KR = 16;  // rows per thread per pass, all loads in flight together
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int Hkv = a.H_kv, r = a.r, Dm = a.D_model;
-  const bool vec = (r % CW == 0) && (Hkv % CW == 0);
-  const int nu = vec ? r / CW : r;
-  const int nch = nu + (vec ? Hkv / CW : Hkv);  // column groups: W_dn chunks, then the key-gate band
+  const int Dm = a.D_model;
+  const int ncols = gates ? 3 * a.H_kv : a.r;
+  const char* const mbase = reinterpret_cast<const char*>(gates ? a.W_dec : a.W_dn);
+  const bool vec = ncols % CW == 0;
+  const int nch = vec ? ncols / CW : ncols;  // column groups (16-byte chunks or single columns)
   int npow = 1;
   while (npow < nch) npow <<= 1;
   const int R = NT / npow;  // row subsets
   const int kc = tid & (npow - 1), rsub = tid / npow;
   const bool own = kc < nch;
-  const bool dn = kc < nu;
-  const void* mbase = dn ? a.W_dn : a.W_dec;
-  const int mcols = dn ? r : 3 * Hkv;
-  const int mc0 = dn ? (vec ? kc * CW : kc) : Hkv + (vec ? (kc - nu) * CW : kc - nu);
-  const int64_t xb = (int64_t)b * Dm;
+  const int mc0 = own ? (vec ? kc * CW : kc) : 0;
+  const char* const xrow = reinterpret_cast<const char*>(a.x) + (int64_t)b * Dm * (BF16 ? 2 : 4);
   float acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = 0.0f;
@@ -194,12 +196,12 @@ __device__ void seq_item(const LayerArgs& a, const Control& ctl, int b, uint32_t
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
       const int row = min(rb + q * R, Dm - 1);
-      xr[q] = load_elem<BF16>(a.x, xb + row);
-      const int64_t e = (int64_t)row * mcols + (own ? mc0 : 0);
+      xr[q] = elem_at<BF16>(xrow, (uint32_t)row * (BF16 ? 2 : 4));
+      const uint32_t e = (uint32_t)(row * ncols + mc0) * (BF16 ? 2 : 4);
       if (vec) {
-        raw[q] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(mbase) + e * (BF16 ? 2 : 4));
+        raw[q] = ld_at<u32x4>(mbase, e);
       } else {
-        raw[q] = u32x4{__float_as_uint(load_elem<BF16>(mbase, e)), 0u, 0u, 0u};
+        raw[q] = u32x4{__float_as_uint(elem_at<BF16>(mbase, e)), 0u, 0u, 0u};
       }
     }
 #pragma unroll
@@ -233,17 +235,15 @@ __device__ void seq_item(const LayerArgs& a, const Control& ctl, int b, uint32_t
   }
   __syncthreads();
   unsigned long long* uw = ctl.uw + (int64_t)b * kUWords;
-  if (tid < r + Hkv) {
-    const bool isu = tid < r;
-    const int q = isu ? tid : tid - r;
-    const int grp = isu ? (vec ? q / CW : q) : nu + (vec ? q / CW : q);
-    const int t = vec ? q % CW : 0;
+  if (tid < ncols) {
+    const int grp = vec ? tid / CW : tid;
+    const int t = vec ? tid % CW : 0;
     float z = 0.0f;
     for (int rr = 0; rr < reff; ++rr) z += s_red[rr * npow + grp][t];
-    if (isu) {
-      st64_coh(uw + q, tag_word(z, tag));
+    if (gates) {
+      st64_coh(uw + kMaxRank + tid, tag_word(log_sigmoid(z + a.b_dec[tid]), tag));
     } else {
-      st64_coh(uw + kMaxRank + q, tag_word(log_sigmoid(z + a.b_dec[Hkv + q]), tag));
+      st64_coh(uw + tid, tag_word(z, tag));
     }
   }
 }
@@ -294,7 +294,6 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
   __shared__ float s_red[NT][8];                              // per-sequence item: partial projections
   __shared__ float s_cs[HALF], s_sn[HALF];                    // RoPE table of the token's position
   __shared__ float s_tq[(G + 1) * D];                         // rotated queries of the group, then the stored key
-  __shared__ float s_gred[kDecWaves][2];                      // gate partial sums per wave
   __shared__ float s_g[2];                                    // query and similarity gates (log sigmoid)
   __shared__ float s_po[kDecWaves * G * D];                   // wave partials: weighted V
   __shared__ float s_pm[kDecWaves * G], s_pl[kDecWaves * G];  // wave partials: max (log2), sum
@@ -309,21 +308,32 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
   int nxt = 0;
   if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);
 
-  // ---- tile numbering from the segment lengths (unchanged until the commit,
-  // which waits until every workgroup has finished)
+  // Tile numbering from the segment lengths, done the first time a ticket
+  // past the per-sequence items is drawn (the lengths stay unchanged until
+  // the commit, which waits until every workgroup has finished).
   const int per = (S + NT - 1) / NT;
   const int sb = min(S, tid * per);
   const int se = min(S, sb + per);
-  int mine = 0;
-  for (int s = sb; s < se; ++s) mine += tiles_of(a.seg_len[s], TWG);
-  int total_tiles;
-  const int excl = block_exclusive_scan<NT>(mine, s_scan, &total_tiles);
-  const int total_items = a.B + total_tiles;
+  int mine = 0, excl = 0, total_items = 0;
+  bool numbered = false;
 
   while (true) {
     if (tid == kDrawer) s_id = nxt;
     __syncthreads();
     const int id = s_id;
+
+    if (id < 2 * a.B) {  // gate items first: tiles need them early
+      seq_item<BF16>(a, ctl, id % a.B, id < a.B, tag, s_red);
+      if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);
+      continue;
+    }
+    if (!numbered) {
+      for (int s = sb; s < se; ++s) mine += tiles_of(a.seg_len[s], TWG);
+      int total_tiles;
+      excl = block_exclusive_scan<NT>(mine, s_scan, &total_tiles);
+      total_items = 2 * a.B + total_tiles;
+      numbered = true;
+    }
 
     if (id >= total_items) {
       // ---- exit.  Every workgroup reports that it has finished (its stores
@@ -354,14 +364,8 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
       }
       break;
     }
-    if (id < a.B) {
-      seq_item<BF16>(a, ctl, id, tag, s_red);
-      if (tid == kDrawer) nxt = add_coh(&ctl.glob[kGlobTicket], 1);
-      continue;
-    }
-
     // ---- (segment, tile) of this item
-    const int tix = id - a.B;
+    const int tix = id - 2 * a.B;
     if (tix >= excl && tix < excl + mine && per == 1) {
       s_info[0] = sb;
       s_info[1] = tix - excl;
@@ -433,61 +437,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
 #pragma unroll
     for (int u = 0; u < OPT; ++u)
       vn[u] = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + (u * NT + tid) % D) * EB));
-    // ---- query- and similarity-gate columns of x W_dec: per pass, two runs of
-    // four consecutive rows per thread (a vector load of x and eight gathered
-    // weights each), every load of the pass issued before use
-    float gq = 0.0f, gs = 0.0f;
-    {
-      const char* const xrow = reinterpret_cast<const char*>(a.x) + (int64_t)b * Dm * EB;
-      const char* const wd = reinterpret_cast<const char*>(a.W_dec);
-      const uint32_t wstride = (uint32_t)(3 * Hkv * EB);
-      const uint32_t cq = (uint32_t)(h * EB), cs = (uint32_t)((2 * Hkv + h) * EB);
-      for (int p0 = 4 * tid; p0 < Dm; p0 += 8 * NT) {
-        float xv[8], wq[8], ws[8];
-#pragma unroll
-        for (int run = 0; run < 2; ++run) {
-          const int r0 = min(p0 + run * 4 * NT, Dm - 4);  // a run past the end repeats the last one
-          if constexpr (BF16) {
-            const uint2 xx = ld_at<uint2>(xrow, (uint32_t)r0 * 2);
-            xv[4 * run + 0] = bf16_lo(xx.x);
-            xv[4 * run + 1] = bf16_hi(xx.x);
-            xv[4 * run + 2] = bf16_lo(xx.y);
-            xv[4 * run + 3] = bf16_hi(xx.y);
-          } else {
-            const float4 xx = ld_at<float4>(xrow, (uint32_t)r0 * 4);
-            xv[4 * run + 0] = xx.x;
-            xv[4 * run + 1] = xx.y;
-            xv[4 * run + 2] = xx.z;
-            xv[4 * run + 3] = xx.w;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t ro = (uint32_t)(r0 + i) * wstride;
-            wq[4 * run + i] = elem_at<BF16>(wd, ro + cq);
-            ws[4 * run + i] = elem_at<BF16>(wd, ro + cs);
-          }
-        }
-        const bool second = p0 + 4 * NT < Dm;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float xi = (i < 4 || second) ? xv[i] : 0.0f;
-          gq = fmaf(xi, wq[i], gq);
-          gs = fmaf(xi, ws[i], gs);
-        }
-      }
-    }
+    // ---- the query and similarity gates from the sequence's gate item
+    // (tagged words; checked, and re-read if stale, after the table)
+    const unsigned long long* gword =
+        ctl.uw + (int64_t)b * kUWords + kMaxRank + (tid == 0 ? h : 2 * Hkv + h);
+    unsigned long long gwd = (tid < 2) ? ld64_coh(gword) : 0ull;
     // ---- RoPE table (fp64 angles) while the loads fly
     if (tid < HALF) {
       double sn, cs;
       sincos((double)pos * a.inv_freq[tid], &sn, &cs);
       s_cs[tid] = (float)cs;
       s_sn[tid] = (float)sn;
-    }
-    gq = across_groups_sum<8>(group_sum<8>(gq));
-    gs = across_groups_sum<8>(group_sum<8>(gs));
-    if (lane == 0) {
-      s_gred[wv][0] = gq;
-      s_gred[wv][1] = gs;
     }
     __syncthreads();
     // ---- rotated queries, the stored key (L2-normalised, rotated, rounded like the cache), gates
@@ -510,10 +470,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
       }
     }
     if (tid < 2) {
-      float z = a.b_dec[tid == 0 ? h : 2 * Hkv + h];
-#pragma unroll
-      for (int w2 = 0; w2 < kDecWaves; ++w2) z += s_gred[w2][tid];
-      s_g[tid] = log_sigmoid(z);
+      int spins = 0;
+      while ((uint32_t)(gwd >> 32) != tag) {
+        if (++spins > kSpinLimitDec) {
+          atomicOr(a.status, 2);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        gwd = ld64_coh(gword);
+      }
+      s_g[tid] = __uint_as_float((uint32_t)gwd);
     }
     __syncthreads();
 
@@ -576,7 +542,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
     }
     // ---- issued now, used by the combine: the sequence's tagged words (u, the
     // new key's gate)
-    const unsigned long long* uword = ctl.uw + (int64_t)b * kUWords + (tid < r ? tid : kMaxRank + h);
+    const unsigned long long* uword = ctl.uw + (int64_t)b * kUWords + (tid < r ? tid : kMaxRank + Hkv + h);
     unsigned long long uwd = (tid <= r) ? ld64_coh(uword) : 0ull;
 
     // ---- wave partial per head: max over the wave first, then sums relative to it

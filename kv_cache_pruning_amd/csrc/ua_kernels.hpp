@@ -60,7 +60,7 @@ constexpr int kGlobArrive = 32;  // compaction: workgroups done (own cache line)
 constexpr int kGlobSeq = 64;     // decode: calls made (tags the per-sequence words)
 constexpr int kGlobDone = 96;    // decode: workgroups finished
 constexpr int kGlobInts = 128;
-constexpr int kUWords = kMaxRank + kMaxHkv;  // tagged words per sequence: u, then key gates
+constexpr int kUWords = kMaxRank + 3 * kMaxHkv;  // tagged words per sequence: u, then the 3 H_kv gates
 
 struct Control {
   int* dec_cnt;              // [S]           decode: arrivals per segment
