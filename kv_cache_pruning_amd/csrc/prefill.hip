@@ -65,7 +65,7 @@ constexpr int kPrefillSpinLimit = 1 << 22;
 // workspace
 // ---------------------------------------------------------------------------
 struct PrefillWs {
-  int* sync;       // [2 + S*nrb]  ticket, arrivals, carry progress per (segment, token block)
+  int* sync;       // [2 + 4*S*nrb]  ticket, arrivals, carry progress per (segment, token block, wave)
   uint16_t* wt;    // [cp, D_model] bf16  [W_dec | W_dn]^T, rows >= 3 H_kv + r zero
   uint16_t* qbf;   // [B*n, H_q, d] bf16  rotated queries
   float* gl;       // [B*n, H_kv, 2]      (lq, lb)
@@ -86,7 +86,7 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
     off += align_up(bytes, 256);
     return p;
   };
-  char* sync = take(sizeof(int) * (2 + S * nrb));
+  char* sync = take(sizeof(int) * (2 + 4 * S * nrb));
   char* wt = take(sizeof(uint16_t) * (size_t)cp * a.D_model);
   char* qbf = take(sizeof(uint16_t) * (size_t)NT * a.H_q * a.d);
   char* gl = take(sizeof(float) * 2 * (size_t)NT * a.H_kv);
@@ -931,11 +931,527 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
 }
 
 // ---------------------------------------------------------------------------
+// 3b. attention for head dim 64 and up to four query heads per KV head, with
+// the waves split by role.  Waves 0-3 form the bias of the next key block, 16
+// keys each over all 64 tokens of the token block: K K^T on the matrix cores,
+// the pair terms, the scan over tokens (DPP within a 16-token tile, a
+// broadcast of the tile total across tiles) and the carry across token blocks
+// (one progress word per wave).  Waves 4-7 run the softmax and P V of the
+// current key block for 16 tokens each and stage the key blocks ahead into
+// LDS.  A SIMD holds one wave of each role, so the transcendental-heavy bias
+// work and the matrix-core-heavy softmax of the two blocks overlap; one
+// barrier per key block.
+//
+// Softmax reference.  Stored keys are unit vectors and the bias is never
+// positive, so cs |q~| bounds every logit of a (token, head) from above and
+// serves as a fixed reference: P = 2^(logit - cs |q~|) <= 1, with no running
+// maximum.  The token's own key has zero bias, so the largest P is at least
+// 2^(-2 cs |q~|); a wave whose queries have cs |q~| above kStaticRef takes the
+// running-maximum path instead, so P never leaves the fp16 normal range.
+// ---------------------------------------------------------------------------
+constexpr float kStaticRef = 6.0f;
+constexpr int kDppBcast15 = 0x15F;  // row_newbcast:15, lane 15 of each row to the whole row
+
+constexpr int kPThreadsWS = 768;  // 4 bias waves + 8 softmax waves
+
+template <int HG>
+__global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs a, PrefillWs w) {
+  constexpr int D = 64;
+  constexpr int KC = D / 32;                // k steps of a head-dim dot product
+  constexpr int DT = D / 16;                // 16-wide output tiles per head
+  constexpr int KS = D + 8;                 // s_k row stride (bf16)
+  constexpr int VS = kPKeys + 8;            // s_vt row stride (fp16)
+  constexpr int QS = HG * D + 8;            // s_q row stride (bf16)
+  constexpr int HH = (HG + 1) / 2;          // query heads of the first softmax wave of a token tile
+  constexpr int NC = kPThreadsWS - 256;     // staging threads (the softmax waves)
+  constexpr int KPT = kPKeys * (D / 8) / NC;
+  constexpr int VPT = (kPKeys / 2) * (D / 4) / NC;
+  static_assert(KPT == 1 && VPT == 1, "staging split");
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[3][kPKeys * KS];
+  __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][D * VS];
+  __shared__ __attribute__((aligned(16))) float s_lk[3][kPKeys];
+  __shared__ __attribute__((aligned(16))) float s_bias[2][16 * 64 * 4];  // [key tile][token tile][lane][4]
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[kPRows * QS];
+  __shared__ int s_id;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool bias_wave = wv < 4;
+  const int p = wv & 3;         // bias wave: key tile p of a block; softmax wave: token tile p
+  const int hf = (wv - 4) >> 2;  // softmax wave: which half of the group's query heads
+  const int S = a.B * a.H_kv;
+  const int n = w.n, nrb = w.nrb;
+  const int Hq = a.H_q, Hkv = a.H_kv;
+
+  if (tid == 0) s_id = addi_coh_p(&w.sync[0], 1);
+  __syncthreads();
+  const int id = s_id;
+  const int s = id % S;  // token-block major: a chain predecessor always has a lower id
+  const int I = id / S;
+  const int b = s / Hkv, h = s - b * Hkv;
+  const int len0 = a.seg_len[s];
+  const int64_t off = a.seg_off[s];
+  const bool room = (int64_t)len0 + n <= a.seg_cap[s];
+  const int a0 = h * HG;
+  const int t0 = I * kPRows;  // first token of the block
+
+  if (room) {
+    const int nkeys = len0 + n;
+    const int kend = len0 + min(n, t0 + kPRows);
+    const int nJ = (kend + kPKeys - 1) / kPKeys;
+    const int64_t TS = a.total_slots;
+    const PairCoef pc = pair_coef(a.terms);
+    const float cs = a.scale * kLog2e;
+    const uint16_t* Kc = reinterpret_cast<const uint16_t*>(a.K);
+    const uint16_t* Vc = reinterpret_cast<const uint16_t*>(a.V);
+    const float col_scale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+    auto slot = [&](int j) -> int64_t { return off + min(j, nkeys - 1); };
+
+    for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreadsWS) {
+      const int tt = q / (HG * (D / 8)), rest = q - tt * (HG * (D / 8));
+      const int64_t tk = (int64_t)b * n + min(t0 + tt, n - 1);
+      *reinterpret_cast<u32x4*>(&s_q[tt * QS + rest * 8]) =
+          *reinterpret_cast<const u32x4*>(w.qbf + (tk * Hq + a0) * D + rest * 8);
+    }
+
+    // ---- staging (softmax waves): K rows and key gates, V rows as key pairs
+    const int ct = tid - 256;  // after the four bias waves
+    u32x4 kst[KPT];
+    uint2 vst[VPT][2];
+    float lkst = 0.0f;
+    auto load_k = [&](int J) {
+      const int j0 = J * kPKeys;
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int q = ct + NC * u, key = q / (D / 8), part = q % (D / 8);
+        kst[u] = *reinterpret_cast<const u32x4*>(Kc + slot(j0 + key) * D + 8 * part);
+      }
+      if (ct < kPKeys) lkst = a.lk[slot(j0 + ct)];
+    };
+    auto load_v = [&](int J) {
+      const int j0 = J * kPKeys;
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int q = ct + NC * u, pp = q / (D / 4), part = q % (D / 4);
+        vst[u][0] = *reinterpret_cast<const uint2*>(Vc + slot(j0 + 2 * pp) * D + 4 * part);
+        vst[u][1] = *reinterpret_cast<const uint2*>(Vc + slot(j0 + 2 * pp + 1) * D + 4 * part);
+      }
+    };
+    auto store_k = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < KPT; ++u) {
+        const int q = ct + NC * u, key = q / (D / 8), part = q % (D / 8);
+        *reinterpret_cast<u32x4*>(&s_k[buf][key * KS + 8 * part]) = kst[u];
+      }
+      if (ct < kPKeys) s_lk[buf][ct] = lkst * col_scale;
+    };
+    auto store_v = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        const int q = ct + NC * u, pp = q / (D / 4), part = q % (D / 4);
+        const int pos = vt_pos(2 * pp);
+        const uint32_t k0w[2] = {vst[u][0].x, vst[u][0].y}, k1w[2] = {vst[u][1].x, vst[u][1].y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = (e & 1) ? bf16_hi(k0w[e >> 1]) : bf16_lo(k0w[e >> 1]);
+          const float v1 = (e & 1) ? bf16_hi(k1w[e >> 1]) : bf16_lo(k1w[e >> 1]);
+          const auto hv = __builtin_amdgcn_cvt_pkrtz(v0, v1);
+          *reinterpret_cast<uint32_t*>(&s_vt[buf][(4 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
+        }
+      }
+    };
+
+    // ---- bias wave state: this lane's tokens 16 tt + c16 of the block
+    u32x4 krf[4][KC];
+    float row2[4];
+    auto load_token_side = [&]() {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int tq = min(t0 + 16 * tt + c16, n - 1);
+        const int64_t tok = (int64_t)b * n + tq;
+        const float lq = w.gl[2 * (tok * Hkv + h) + 0];
+        const float lb = w.gl[2 * (tok * Hkv + h) + 1];
+        row2[tt] = pc.inv_n2 * (((a.terms & 1) ? lq : 0.0f) + ((a.terms & 4) ? lb : 0.0f));
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          krf[tt][kc] = *reinterpret_cast<const u32x4*>(Kc + (off + len0 + tq) * D + 32 * kc + 8 * g);
+      }
+    };
+
+    // Bias of key block JB for keys 16 p + 4 g + i and every token of the
+    // block: carry in + inclusive scan of the pair terms over the tokens.
+    // The carry in is requested first (the stored bias, or the previous token
+    // block's carry if its progress word already covers JB) and awaited after
+    // the pair terms.  The carry out is stored without waiting; its progress
+    // word is written one block later, once the stores have long completed.
+    int pending = 0;  // progress value not yet published
+    auto publish = [&]() {
+      __builtin_amdgcn_s_waitcnt(0);
+      if (lane == 0) sti_coh_p(&w.sync[2 + (s * nrb + I) * 4 + p], pending);
+      pending = 0;
+    };
+    auto bias_block = [&](int JB) {
+      const int j0 = JB * kPKeys;
+      const int kb = JB % 3;
+      const int jk = j0 + 16 * p + 4 * g;  // this lane's first key
+      const int Ist = j0 >= len0 ? (j0 - len0) / kPRows : 0;
+      const bool chain = I > Ist;
+      const int* flag = &w.sync[2 + (s * nrb + I - 1) * 4 + p];
+      float car[4];
+      bool have = !chain;
+      if (!chain) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) car[i] = (jk + i < len0) ? a.lam[slot(jk + i)] : 0.0f;
+      } else if (ldi_coh_p(flag) >= JB + 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) car[i] = ldf_coh_p(&w.carry[(int64_t)(I - 1) * TS + slot(jk + i)]);
+        have = true;
+      }
+      u32x4 kf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[kc] = *reinterpret_cast<const u32x4*>(&s_k[kb][(16 * p + c16) * KS + 32 * kc + 8 * g]);
+      const float4 lk4 = *reinterpret_cast<const float4*>(&s_lk[kb][16 * p + 4 * g]);
+      const float lkv[4] = {lk4.x, lk4.y, lk4.z, lk4.w};
+      const bool edge = (j0 + 16 * p + 15 >= len0 + t0) || (t0 + kPRows > n);
+      float lam[4][4];
+      auto pair_terms = [&](auto edge_c, auto sim_c) {
+        constexpr bool EDGE = decltype(edge_c)::value, SIM = decltype(sim_c)::value;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          f32x4 sim = {0.0f, 0.0f, 0.0f, 0.0f};
+          if constexpr (SIM) {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) sim = mfma_bf16(kf[kc], krf[tt][kc], sim);
+          }
+          const int tq = t0 + 16 * tt + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float lam2 = row2[tt] + lkv[i];
+            if constexpr (SIM) lam2 = fmaf(pc.sim_w, __builtin_amdgcn_logf(fminf(sim[i] * sim[i], 1.0f)), lam2);
+            float A2 = log1mexp2_b2(lam2);
+            if constexpr (EDGE) A2 = (tq < n && jk + i < len0 + tq) ? A2 : 0.0f;
+            lam[tt][i] = A2;
+          }
+        }
+      };
+      if (!pc.any) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lam[tt][i] = 0.0f;
+      } else if (edge) {
+        if (pc.sim) pair_terms(std::true_type{}, std::true_type{});
+        else pair_terms(std::true_type{}, std::false_type{});
+      } else {
+        if (pc.sim) pair_terms(std::false_type{}, std::true_type{});
+        else pair_terms(std::false_type{}, std::false_type{});
+      }
+      // inclusive scans over the 16 tokens of each tile, step-major
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[tt][i] += dpp_f<0x111>(lam[tt][i]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[tt][i] += dpp_f<0x112>(lam[tt][i]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[tt][i] += dpp_f<0x114>(lam[tt][i]);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lam[tt][i] += dpp_f<0x118>(lam[tt][i]);
+      // across the tiles: add the running total of the earlier tiles
+      float run[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) run[i] = dpp_f<kDppBcast15>(lam[0][i]);
+#pragma unroll
+      for (int tt = 1; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          lam[tt][i] += run[i];
+          run[i] = dpp_f<kDppBcast15>(lam[tt][i]);
+        }
+      if (pending) publish();
+      // carry into this token block (log2 units)
+      if (!chain) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) car[i] *= kLog2e;
+      } else if (!have) {
+        int spins = 0;
+        while (ldi_coh_p(flag) < JB + 1) {
+          if (++spins > kPrefillSpinLimit) {
+            if (lane == 0) atomicOr(a.status, 2);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) car[i] = ldf_coh_p(&w.carry[(int64_t)(I - 1) * TS + slot(jk + i)]);
+      }
+      // the written bias carries the attention mask: -inf where token t does
+      // not see key j (j > len0 + t, or t past the call)
+      float* ob = &s_bias[JB & 1][0];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        float bv[4];
+        const int tq = t0 + 16 * tt + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bv[i] = lam[tt][i] + car[i];
+          if (edge) bv[i] = (tq < n && jk + i <= len0 + tq) ? bv[i] : kNegInf;
+        }
+        *reinterpret_cast<float4*>(&ob[((p * 4 + tt) * 64 + lane) * 4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+      }
+      // carry out to the next token block, or the final bias of the call
+      if (I + 1 < nrb) {
+        if (c16 == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (jk + i < nkeys) stf_coh_p(&w.carry[(int64_t)I * TS + off + jk + i], car[i] + run[i]);
+        }
+        pending = JB + 1;
+      } else if (c16 == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (jk + i < nkeys) a.lam[off + jk + i] = (car[i] + run[i]) * kLn2;
+      }
+    };
+
+    // ---- prologue: blocks 0 and 1 of K, block 0 of V in LDS; the bias of block 0
+    if (!bias_wave) {
+      load_k(0);
+      load_v(0);
+      store_k(0);
+      store_v(0);
+      if (nJ > 1) {
+        load_k(1);
+        store_k(1);
+      }
+      if (nJ > 2) load_k(2);
+      if (nJ > 1) load_v(1);
+    }
+    if (bias_wave) load_token_side();
+    __syncthreads();
+    if (bias_wave) {
+      // The two roles run separate loops with the same number of barriers, so
+      // the state of one role is not live in the other.
+      bias_block(0);
+      __syncthreads();
+      for (int J = 0; J < nJ - 1; ++J) {
+        bias_block(J + 1);
+        __syncthreads();
+      }
+      if (pending) publish();
+      __syncthreads();  // the softmax loop's last barrier
+    } else {
+      // ---- softmax waves: tokens 16 p + c16, query heads hf*HH .. of the group
+      const int tq = t0 + 16 * p + c16;
+      const bool row_ok = tq < n;
+      const int64_t tok = (int64_t)b * n + min(tq, n - 1);
+      const float inv_cs = 1.0f / cs;
+      f16x8 ones;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ones[e] = (c16 == 0) ? (_Float16)1.0f : (_Float16)0.0f;
+
+      auto softmax_wave = [&](auto nh_c) {
+        constexpr int NH = decltype(nh_c)::value;  // query heads of this wave
+        const int h0 = hf * HH;                    // first of them within the group
+        float qn[NH > 0 ? NH : 1];
+        f32x4 O[NH > 0 ? NH : 1][DT], Lt[NH > 0 ? NH : 1];
+        float m_run[NH > 0 ? NH : 1];
+        int mset = 0;
+        bool stat = true;
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          float ss = 0.0f;
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            const u32x4 qv =
+                *reinterpret_cast<const u32x4*>(&s_q[(16 * p + c16) * QS + (h0 + hh) * D + 32 * kc + 8 * g]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = u32x4_bf16(qv, e);
+              ss = fmaf(x, x, ss);
+            }
+          }
+          ss += __shfl_xor(ss, 16, 64);
+          ss += __shfl_xor(ss, 32, 64);
+          qn[hh] = __builtin_sqrtf(ss);
+          stat = stat && (cs * qn[hh] <= kStaticRef);
+          m_run[hh] = 0.0f;
+          Lt[hh] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) O[hh][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        stat = __all(stat);
+        __syncthreads();
+
+        // Softmax and P V of key block J for this wave's tokens and heads, 32
+        // keys at a time.  STAT: fixed reference cs |q~| (folded into the
+        // accumulator's start); otherwise a running reference raised only when
+        // a chunk exceeds it by more than 2^kRescaleTh.
+        auto softmax_block = [&](int J, auto stat_c) {
+          constexpr bool STAT = decltype(stat_c)::value;
+          const int kb = J % 3, vb = J & 1;
+          const float* ib = &s_bias[J & 1][0];
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            u32x4 kf[2][KC];
+            float4 bias[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+              for (int kc = 0; kc < KC; ++kc)
+                kf[t][kc] =
+                    *reinterpret_cast<const u32x4*>(&s_k[kb][(32 * c2 + 16 * t + c16) * KS + 32 * kc + 8 * g]);
+              bias[t] = *reinterpret_cast<const float4*>(&ib[(((2 * c2 + t) * 4 + p) * 64 + lane) * 4]);
+            }
+            f16x8 vf[DT];
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+              vf[dt] = *reinterpret_cast<const f16x8*>(&s_vt[vb][(16 * dt + c16) * VS + 32 * c2 + 8 * g]);
+#pragma unroll
+            for (int hh = 0; hh < NH; ++hh) {
+              float e[2][4];
+              float bm = kNegInf;
+              const float ci = STAT ? -qn[hh] : -m_run[hh] * inv_cs;
+              u32x4 qf[KC];
+#pragma unroll
+              for (int kc = 0; kc < KC; ++kc)
+                qf[kc] = *reinterpret_cast<const u32x4*>(&s_q[(16 * p + c16) * QS + (h0 + hh) * D + 32 * kc + 8 * g]);
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                f32x4 sc = f32x4{ci, ci, ci, ci};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16(kf[t][kc], qf[kc], sc);
+                const float bv[4] = {bias[t].x, bias[t].y, bias[t].z, bias[t].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const float ev = fmaf(sc[i], cs, bv[i]);  // -inf where masked
+                  e[t][i] = ev;
+                  if constexpr (!STAT) bm = fmaxf(bm, ev);
+                }
+              }
+              if constexpr (!STAT) {
+                const bool fresh = ((mset >> hh) & 1) == 0;
+                if (__any(bm > kRescaleTh || (fresh && bm > kNegInf))) {
+                  float bx = fmaxf(bm, __shfl_xor(bm, 16, 64));
+                  bx = fmaxf(bx, __shfl_xor(bx, 32, 64));
+                  const float dl = fresh ? ((bx > kNegInf) ? bx : 0.0f) : fmaxf(bx, 0.0f);
+                  const float al = fresh ? 1.0f : __builtin_amdgcn_exp2f(-dl);
+#pragma unroll
+                  for (int dt = 0; dt < DT; ++dt) O[hh][dt] *= al;
+                  Lt[hh] *= al;
+                  m_run[hh] += dl;
+                  if (bx > kNegInf) mset |= 1 << hh;
+#pragma unroll
+                  for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) e[t][i] -= dl;
+                }
+              }
+              f16x8 pk;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                pk[i] = (_Float16)__builtin_amdgcn_exp2f(e[0][i]);
+                pk[4 + i] = (_Float16)__builtin_amdgcn_exp2f(e[1][i]);
+              }
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt) O[hh][dt] = mfma_f16(vf[dt], pk, O[hh][dt]);
+              Lt[hh] = mfma_f16(ones, pk, Lt[hh]);
+            }
+          }
+        };
+
+        // one loop per reference mode, so each holds only its own state
+        auto softmax_loop = [&](auto stat_c) {
+          for (int J = 0; J < nJ; ++J) {
+            if constexpr (NH > 0) softmax_block(J, stat_c);
+            // K of block J + 2 and V of block J + 1 to LDS, then the loads of the blocks after
+            if (J + 2 < nJ) store_k((J + 2) % 3);
+            if (J + 1 < nJ) store_v((J + 1) & 1);
+            if (J + 3 < nJ) load_k(J + 3);
+            if (J + 2 < nJ) load_v(J + 2);
+            __syncthreads();
+          }
+        };
+        if (stat) softmax_loop(std::true_type{});
+        else softmax_loop(std::false_type{});
+
+        // ---- epilogue: normalise, gate, store
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          const float L = __shfl(Lt[hh][0], c16, 64);
+          const float inv = (row_ok && L > 0.0f) ? 1.0f / L : 0.0f;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int64_t yo = (tok * Hq + a0 + h0 + hh) * D + 16 * dt + 4 * g;
+            const float4 gm = *reinterpret_cast<const float4*>(w.gam + yo);
+            const float y0 = gm.x * O[hh][dt][0] * inv, y1 = gm.y * O[hh][dt][1] * inv;
+            const float y2 = gm.z * O[hh][dt][2] * inv, y3 = gm.w * O[hh][dt][3] * inv;
+            if (row_ok) {
+              if (a.y_bf16) {
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) =
+                    make_uint2(pack_bf16(y0, y1), pack_bf16(y2, y3));
+              } else {
+                *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(y0, y1, y2, y3);
+              }
+            }
+          }
+        }
+      };
+      if (hf == 0) softmax_wave(std::integral_constant<int, HH>{});
+      else softmax_wave(std::integral_constant<int, HG - HH>{});
+    }
+  } else if (!bias_wave && hf == 0) {
+    // the segment has no room for the call: its outputs are zero
+    const int tq = t0 + 16 * p + c16;
+    if (tq < n) {
+      const int64_t tok = (int64_t)b * n + tq;
+#pragma unroll
+      for (int hh = 0; hh < HG; ++hh)
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+          if (a.y_bf16) {
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) = make_uint2(0u, 0u);
+          } else {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+    }
+  }
+
+  // ---- the last workgroup advances lengths and positions
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_id = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (s_id) {
+    for (int s2 = tid; s2 < S; s2 += kPThreadsWS) {
+      const int l = a.seg_len[s2];
+      if ((int64_t)l + n <= a.seg_cap[s2]) a.seg_len[s2] = l + n;
+    }
+    for (int b2 = tid; b2 < a.B; b2 += kPThreadsWS) a.next_pos[b2] += n;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host
 // ---------------------------------------------------------------------------
 template <int D, int HG>
 static void launch_attn(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
   hipLaunchKernelGGL((prefill_attn_kernel<D, HG>), dim3(grid), dim3(kPThreads), 0, st, a, w);
+}
+
+template <int HG>
+static void launch_attn_ws(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((prefill_attn_ws_kernel<HG>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
 }
 
 hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int max_seg_cap, void* scratch,
@@ -947,7 +1463,7 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int
   PrefillWs w;
   prefill_layout(a, n, reinterpret_cast<char*>(scratch), &w);
   const int S = a.B * a.H_kv;
-  const int nsync = 2 + S * w.nrb;
+  const int nsync = 2 + 4 * S * w.nrb;
   const int64_t prep_items = std::max<int64_t>(std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8)),
                                                (int64_t)a.H_q * a.d * (w.rp / 8));
   const int prep_grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (prep_items + 255) / 256));
@@ -960,10 +1476,10 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int
   }
   const int grid = S * w.nrb;
   switch (a.d * 16 + G) {
-    case 64 * 16 + 1: launch_attn<64, 1>(a, w, grid, st); break;
-    case 64 * 16 + 2: launch_attn<64, 2>(a, w, grid, st); break;
-    case 64 * 16 + 3: launch_attn<64, 3>(a, w, grid, st); break;
-    case 64 * 16 + 4: launch_attn<64, 4>(a, w, grid, st); break;
+    case 64 * 16 + 1: launch_attn_ws<1>(a, w, grid, st); break;
+    case 64 * 16 + 2: launch_attn_ws<2>(a, w, grid, st); break;
+    case 64 * 16 + 3: launch_attn_ws<3>(a, w, grid, st); break;
+    case 64 * 16 + 4: launch_attn_ws<4>(a, w, grid, st); break;
     case 64 * 16 + 8: launch_attn<64, 8>(a, w, grid, st); break;
     case 128 * 16 + 1: launch_attn<128, 1>(a, w, grid, st); break;
     case 128 * 16 + 2: launch_attn<128, 2>(a, w, grid, st); break;

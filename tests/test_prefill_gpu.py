@@ -82,6 +82,14 @@ def test_prefill_bf16_output():
     _run(config("1b-prefill", **SMALL), y_bf16=True)
 
 
+@pytest.mark.parametrize("q_scale", [4.0, 8.0])
+def test_prefill_large_query_norms(q_scale):
+    """Queries of norm ~32 and ~64: waves whose scaled norms leave the fixed
+    softmax reference's range run the running-maximum path (some waves at 4,
+    all at 8)."""
+    _run(config("1b-prefill", q_scale=q_scale, **SMALL))
+
+
 def test_prefill_1b_heads_full_batch():
     _run(config("1b-prefill", n_total=384, chunk=192))
 

@@ -75,6 +75,7 @@ class LayerConfig:
     n_total: int = 0
     chunk: int = 0
     w_var: float = 1.0 / 64.0  # variance of W_dec, W_dn, W_up entries
+    q_scale: float = 1.0  # queries are N(0, q_scale^2); a power of two keeps bf16 draws exact
 
     @property
     def G(self) -> int:
@@ -253,7 +254,7 @@ def make_step_inputs(cfg: LayerConfig, step: int, n: int = 1, seed: int = 0) -> 
     ss = _streams(seed)[2]
     child = np.random.SeedSequence(entropy=ss.entropy, spawn_key=ss.spawn_key + (step,))
     rng = np.random.Generator(np.random.PCG64(child))
-    q = _normal(rng, (cfg.B, n, cfg.H_q, cfg.d))
+    q = _normal(rng, (cfg.B, n, cfg.H_q, cfg.d)) * cfg.q_scale
     k = _normal(rng, (cfg.B, n, cfg.H_kv, cfg.d))
     v = _normal(rng, (cfg.B, n, cfg.H_kv, cfg.d))
     x = _normal(rng, (cfg.B, n, cfg.D))
