@@ -65,12 +65,14 @@ constexpr int kPrefillSpinLimit = 1 << 22;
 // workspace
 // ---------------------------------------------------------------------------
 struct PrefillWs {
-  int* sync;       // [2 + 4*S*nrb]  ticket, arrivals, carry progress per (segment, token block, wave)
+  int* sync;       // [2 + S*nrb]  ticket, arrivals, carry progress per (segment, token block)
   uint16_t* wt;    // [cp, D_model] bf16  [W_dec | W_dn]^T, rows >= 3 H_kv + r zero
   uint16_t* qbf;   // [B*n, H_q, d] bf16  rotated queries
   float* gl;       // [B*n, H_kv, 2]      (lq, lb)
   float* gam;      // [B*n, H_q*d]        output gate
   float* carry;    // [nrb-1, total_slots] per-key carry into token block I (log2 units)
+  unsigned long long* carry64;  // the same region as tagged words (call tag << 32 | carry bits)
+  int* glob;       // control words: glob[kGlobSeq] counts the calls made with the workspace
   uint16_t* wut;   // [H_q*d, rp] bf16  W_up^T, ranks >= r zero
   int n, nrb, cp, rp;
 };
@@ -86,12 +88,12 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
     off += align_up(bytes, 256);
     return p;
   };
-  char* sync = take(sizeof(int) * (2 + 4 * S * nrb));
+  char* sync = take(sizeof(int) * (2 + S * nrb));
   char* wt = take(sizeof(uint16_t) * (size_t)cp * a.D_model);
   char* qbf = take(sizeof(uint16_t) * (size_t)NT * a.H_q * a.d);
   char* gl = take(sizeof(float) * 2 * (size_t)NT * a.H_kv);
   char* gam = take(sizeof(float) * (size_t)NT * a.H_q * a.d);
-  char* carry = take(sizeof(float) * (size_t)(nrb - 1) * a.total_slots);
+  char* carry = take(sizeof(unsigned long long) * (size_t)(nrb - 1) * a.total_slots);
   const int rp = (a.r + 31) / 32 * 32;
   char* wut = take(sizeof(uint16_t) * (size_t)a.H_q * a.d * rp);
   if (w) {
@@ -101,6 +103,7 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
     w->gl = reinterpret_cast<float*>(gl);
     w->gam = reinterpret_cast<float*>(gam);
     w->carry = reinterpret_cast<float*>(carry);
+    w->carry64 = reinterpret_cast<unsigned long long*>(carry);
     w->wut = reinterpret_cast<uint16_t*>(wut);
     w->n = n;
     w->nrb = nrb;
@@ -122,6 +125,12 @@ __device__ __forceinline__ void sti_coh_p(int* p, int v) {
 }
 __device__ __forceinline__ int addi_coh_p(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long ld64_coh_p(const unsigned long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st64_coh_p(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ldf_coh_p(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -935,8 +944,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
 // the waves split by role.  Waves 0-3 form the bias of the next key block, 16
 // keys each over all 64 tokens of the token block: K K^T on the matrix cores,
 // the pair terms, the scan over tokens (DPP within a 16-token tile, a
-// broadcast of the tile total across tiles) and the carry across token blocks
-// (one progress word per wave).  Waves 4-7 run the softmax and P V of the
+// broadcast of the tile total across tiles) and the carry across token blocks.  Waves 4-7 run the softmax and P V of the
 // current key block for 16 tokens each and stage the key blocks ahead into
 // LDS.  A SIMD holds one wave of each role, so the transcendental-heavy bias
 // work and the matrix-core-heavy softmax of the two blocks overlap; one
@@ -948,11 +956,23 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
 // maximum.  The token's own key has zero bias, so the largest P is at least
 // 2^(-2 cs |q~|); a wave whose queries have cs |q~| above kStaticRef takes the
 // running-maximum path instead, so P never leaves the fp16 normal range.
+//
+// Carry words.  A carry crosses token blocks as one 64-bit word, the call's
+// tag in the high half and the value's bits in the low half, written with one
+// store and no progress word.  The next token block loads the words of a key
+// block before its pair terms and checks the tags after them, reloading only
+// the words still stale.  The tag is a signalling-NaN pattern holding the
+// call counter (glob[kGlobSeq], which decode calls advance too); arithmetic
+// never produces it, so no stale word of the workspace carries it.
 // ---------------------------------------------------------------------------
 constexpr float kStaticRef = 6.0f;
 constexpr int kDppBcast15 = 0x15F;  // row_newbcast:15, lane 15 of each row to the whole row
 
 constexpr int kPThreadsWS = 768;  // 4 bias waves + 8 softmax waves
+
+__device__ __forceinline__ uint32_t carry_tag(uint32_t seq) {
+  return 0x7F800000u | ((seq - 1u) % 0x3FFFFFu + 1u);  // exponent all ones, quiet bit clear, payload != 0
+}
 
 template <int HG>
 __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs a, PrefillWs w) {
@@ -973,6 +993,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   __shared__ __attribute__((aligned(16))) float s_bias[2][16 * 64 * 4];  // [key tile][token tile][lane][4]
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kPRows * QS];
   __shared__ int s_id;
+  __shared__ uint32_t s_seq;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -984,9 +1005,13 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   const int n = w.n, nrb = w.nrb;
   const int Hq = a.H_q, Hkv = a.H_kv;
 
-  if (tid == 0) s_id = addi_coh_p(&w.sync[0], 1);
+  if (tid == 0) {
+    s_id = addi_coh_p(&w.sync[0], 1);
+    s_seq = (uint32_t)ldi_coh_p(&w.glob[kGlobSeq]) + 1u;  // this call's number
+  }
   __syncthreads();
   const int id = s_id;
+  const uint32_t tagv = carry_tag(s_seq);
   const int s = id % S;  // token-block major: a chain predecessor always has a lower id
   const int I = id / S;
   const int b = s / Hkv, h = s - b * Hkv;
@@ -1081,32 +1106,24 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
 
     // Bias of key block JB for keys 16 p + 4 g + i and every token of the
     // block: carry in + inclusive scan of the pair terms over the tokens.
-    // The carry in is requested first (the stored bias, or the previous token
-    // block's carry if its progress word already covers JB) and awaited after
-    // the pair terms.  The carry out is stored without waiting; its progress
-    // word is written one block later, once the stores have long completed.
-    int pending = 0;  // progress value not yet published
-    auto publish = [&]() {
-      __builtin_amdgcn_s_waitcnt(0);
-      if (lane == 0) sti_coh_p(&w.sync[2 + (s * nrb + I) * 4 + p], pending);
-      pending = 0;
-    };
+    // The carry in (the stored bias where this token block starts the key
+    // block's chain, else the previous token block's carry words) is loaded
+    // before the pair terms and used after them.
     auto bias_block = [&](int JB) {
       const int j0 = JB * kPKeys;
       const int kb = JB % 3;
       const int jk = j0 + 16 * p + 4 * g;  // this lane's first key
       const int Ist = j0 >= len0 ? (j0 - len0) / kPRows : 0;
       const bool chain = I > Ist;
-      const int* flag = &w.sync[2 + (s * nrb + I - 1) * 4 + p];
+      const unsigned long long* cin = w.carry64 + (int64_t)(I - 1) * TS;
       float car[4];
-      bool have = !chain;
+      unsigned long long cw[4];
       if (!chain) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) car[i] = (jk + i < len0) ? a.lam[slot(jk + i)] : 0.0f;
-      } else if (ldi_coh_p(flag) >= JB + 1) {
+        for (int i = 0; i < 4; ++i) car[i] = (jk + i < len0) ? ldf_coh_p(&a.lam[slot(jk + i)]) : 0.0f;
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) car[i] = ldf_coh_p(&w.carry[(int64_t)(I - 1) * TS + slot(jk + i)]);
-        have = true;
+        for (int i = 0; i < 4; ++i) cw[i] = ld64_coh_p(&cin[slot(jk + i)]);
       }
       u32x4 kf[KC];
 #pragma unroll
@@ -1115,24 +1132,64 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
       const float4 lk4 = *reinterpret_cast<const float4*>(&s_lk[kb][16 * p + 4 * g]);
       const float lkv[4] = {lk4.x, lk4.y, lk4.z, lk4.w};
       const bool edge = (j0 + 16 * p + 15 >= len0 + t0) || (t0 + kPRows > n);
+      // Pair terms, step-major over the 16 (key, token) elements of the lane so
+      // that the transcendental chains of different elements interleave.  The
+      // series form of 1 - 2^L is only needed where L is near 0; a wave takes
+      // it only when one of its elements is there.
       float lam[4][4];
       auto pair_terms = [&](auto edge_c, auto sim_c) {
         constexpr bool EDGE = decltype(edge_c)::value, SIM = decltype(sim_c)::value;
+        f32x4 sim[4];
+        if constexpr (SIM) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          f32x4 sim = {0.0f, 0.0f, 0.0f, 0.0f};
-          if constexpr (SIM) {
+          for (int tt = 0; tt < 4; ++tt) {
+            sim[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) sim = mfma_bf16(kf[kc], krf[tt][kc], sim);
+            for (int kc = 0; kc < KC; ++kc) sim[tt] = mfma_bf16(kf[kc], krf[tt][kc], sim[tt]);
           }
-          const int tq = t0 + 16 * tt + c16;
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float lam2 = row2[tt] + lkv[i];
-            if constexpr (SIM) lam2 = fmaf(pc.sim_w, __builtin_amdgcn_logf(fminf(sim[i] * sim[i], 1.0f)), lam2);
-            float A2 = log1mexp2_b2(lam2);
-            if constexpr (EDGE) A2 = (tq < n && jk + i < len0 + tq) ? A2 : 0.0f;
-            lam[tt][i] = A2;
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lam[tt][i] = row2[tt] + lkv[i];
+        if constexpr (SIM) {
+          float lg[4][4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lg[tt][i] = __builtin_amdgcn_logf(fminf(sim[tt][i] * sim[tt][i], 1.0f));
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lam[tt][i] = fmaf(pc.sim_w, lg[tt][i], lam[tt][i]);
+        }
+        float lmax = kNegInf;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lmax = fmaxf(lmax, lam[tt][i]);
+        if (__any(lmax > kLog1mexpSeries)) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lam[tt][i] = log1mexp2_b2(lam[tt][i]);
+        } else {
+          float ex[4][4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ex[tt][i] = __builtin_amdgcn_exp2f(lam[tt][i]);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lam[tt][i] = __builtin_amdgcn_logf(1.0f - ex[tt][i]);
+        }
+        if constexpr (EDGE) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const int tq = t0 + 16 * tt + c16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lam[tt][i] = (tq < n && jk + i < len0 + tq) ? lam[tt][i] : 0.0f;
           }
         }
       };
@@ -1176,22 +1233,28 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
           lam[tt][i] += run[i];
           run[i] = dpp_f<kDppBcast15>(lam[tt][i]);
         }
-      if (pending) publish();
       // carry into this token block (log2 units)
       if (!chain) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) car[i] *= kLog2e;
-      } else if (!have) {
+      } else {
         int spins = 0;
-        while (ldi_coh_p(flag) < JB + 1) {
+        for (;;) {
+          bool ok = true;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ok = ok && (uint32_t)(cw[i] >> 32) == tagv;
+          if (ok) break;
           if (++spins > kPrefillSpinLimit) {
-            if (lane == 0) atomicOr(a.status, 2);
+            atomicOr(a.status, 2);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if ((uint32_t)(cw[i] >> 32) != tagv) cw[i] = ld64_coh_p(&cin[slot(jk + i)]);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) car[i] = ldf_coh_p(&w.carry[(int64_t)(I - 1) * TS + slot(jk + i)]);
+        for (int i = 0; i < 4; ++i) car[i] = __uint_as_float((uint32_t)cw[i]);
       }
       // the written bias carries the attention mask: -inf where token t does
       // not see key j (j > len0 + t, or t past the call)
@@ -1212,9 +1275,10 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         if (c16 == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (jk + i < nkeys) stf_coh_p(&w.carry[(int64_t)I * TS + off + jk + i], car[i] + run[i]);
+            if (jk + i < nkeys)
+              st64_coh_p(&w.carry64[(int64_t)I * TS + off + jk + i],
+                         (unsigned long long)tagv << 32 | __float_as_uint(car[i] + run[i]));
         }
-        pending = JB + 1;
       } else if (c16 == 0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1246,7 +1310,6 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         bias_block(J + 1);
         __syncthreads();
       }
-      if (pending) publish();
       __syncthreads();  // the softmax loop's last barrier
     } else {
       // ---- softmax waves: tokens 16 p + c16, query heads hf*HH .. of the group
@@ -1433,6 +1496,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   if (tid == 0) s_id = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
   __syncthreads();
   if (s_id) {
+    if (tid == 0) sti_coh_p(&w.glob[kGlobSeq], (int)s_seq);
     for (int s2 = tid; s2 < S; s2 += kPThreadsWS) {
       const int l = a.seg_len[s2];
       if ((int64_t)l + n <= a.seg_cap[s2]) a.seg_len[s2] = l + n;
@@ -1454,7 +1518,7 @@ static void launch_attn_ws(const LayerArgs& a, const PrefillWs& w, int grid, hip
   hipLaunchKernelGGL((prefill_attn_ws_kernel<HG>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
 }
 
-hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int max_seg_cap, void* scratch,
+hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max_seg_cap, void* scratch,
                           size_t scratch_bytes, hipStream_t st) {
   if (!a.bf16) return hipErrorNotSupported;  // the matrix-core path is written for bf16 caches
   const int G = a.H_q / a.H_kv;
@@ -1462,8 +1526,9 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& /*ctl*/, int n, int
   if (prefill_ws_bytes(a, n, max_seg_cap) > scratch_bytes) return hipErrorOutOfMemory;
   PrefillWs w;
   prefill_layout(a, n, reinterpret_cast<char*>(scratch), &w);
+  w.glob = ctl.glob;
   const int S = a.B * a.H_kv;
-  const int nsync = 2 + 4 * S * w.nrb;
+  const int nsync = 2 + S * w.nrb;
   const int64_t prep_items = std::max<int64_t>(std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8)),
                                                (int64_t)a.H_q * a.d * (w.rp / 8));
   const int prep_grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (prep_items + 255) / 256));

@@ -242,15 +242,19 @@ __device__ __forceinline__ float log1mexp2(float lam2) {
   return __builtin_amdgcn_logf(arg) * kLn2 + corr;
 }
 
+// Above this L (log2 units) log1mexp2_b2 takes its series branch.
+constexpr float kLog1mexpSeries = -0.125f / kLn2;
+
 // The same in log2 units with one logarithm: log2(1 - 2^L) for L <= 0.
 // With lam = L ln 2 > -1/8, 1 - e^lam = -lam (1 + lam/2 + lam^2/6 + lam^3/24)
 // up to a relative 2e-6 (Taylor series of expm1); otherwise 1 - 2^L >= 0.1175
 // is formed directly, which costs at most about 1e-6 relative (the error of
 // 2^L over the result).  L = -inf gives 0, L = 0 gives -inf.
+
 __device__ __forceinline__ float log1mexp2_b2(float L) {
   constexpr float l1 = kLn2;
   constexpr float l2 = l1 * l1, l3 = l2 * l1, l4 = l3 * l1;
-  const bool small = L > -0.125f / kLn2;
+  const bool small = L > kLog1mexpSeries;
   float q = fmaf(L, -l4 / 24.0f, -l3 / 6.0f);
   q = fmaf(L, q, -l2 / 2.0f);
   q = fmaf(L, q, -l1);
