@@ -343,8 +343,10 @@ def main():
 # prefill workload
 # ---------------------------------------------------------------------------
 # Transcendental issue rate of the chip: 256 CUs x 4 SIMDs x 16 lanes per
-# clock at quarter rate, 2.4 GHz.
-TRANS_PEAK_TS = 256 * 4 * 16 / 4 * 2.4e9 / 1e12
+# clock at half rate (a wave64 v_exp/v_log holds the VALU issue for two
+# 4-clock slots: SQ_ACTIVE_INST_VALU = SQ_INSTS_VALU + SQ_INSTS_VALU_TRANS_F32
+# per wave on the prefill kernels), 2.4 GHz.
+TRANS_PEAK_TS = 256 * 4 * 16 / 2 * 2.4e9 / 1e12
 
 
 def prefill_work(cfg, len0: int, n: int):
