@@ -988,7 +988,10 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   constexpr int VPT = (kPKeys / 2) * (D / 4) / NC;
   static_assert(KPT == 1 && VPT == 1, "staging split");
   __shared__ __attribute__((aligned(16))) uint16_t s_k[3][kPKeys * KS];
-  __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][D * VS];
+  // V^T rows (dims) of VS keys, 8 more halves after every 16 rows: the
+  // transposed stores of a wave then fall in 64 distinct banks
+  constexpr int VTS = D * VS + 8 * (D / 16);
+  __shared__ __attribute__((aligned(16))) _Float16 s_vt[2][VTS];
   __shared__ __attribute__((aligned(16))) float s_lk[3][kPKeys];
   __shared__ __attribute__((aligned(16))) float s_bias[2][16 * 64 * 4];  // [key tile][token tile][lane][4]
   __shared__ __attribute__((aligned(16))) uint16_t s_q[kPRows * QS];
@@ -1054,11 +1057,16 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
       }
       if (ct < kPKeys) lkst = a.lk[slot(j0 + ct)];
     };
+    // V staging: lane l of staging wave cw holds dims 4 (l & 15) .. + 3 of the
+    // key pair pp; a wave's four pairs sit at four consecutive LDS dwords of
+    // every V^T row
+    const int v_part = ct & 15, v_sub = (ct >> 4) & 3, v_cw = ct >> 6;
+    const int v_pp = (v_cw & 3) * 2 + (v_cw >> 2) * 16 + (v_sub & 1) + (v_sub >> 1) * 8;
     auto load_v = [&](int J) {
       const int j0 = J * kPKeys;
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int q = ct + NC * u, pp = q / (D / 4), part = q % (D / 4);
+        const int pp = v_pp, part = v_part;
         vst[u][0] = *reinterpret_cast<const uint2*>(Vc + slot(j0 + 2 * pp) * D + 4 * part);
         vst[u][1] = *reinterpret_cast<const uint2*>(Vc + slot(j0 + 2 * pp + 1) * D + 4 * part);
       }
@@ -1074,7 +1082,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     auto store_v = [&](int buf) {
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {
-        const int q = ct + NC * u, pp = q / (D / 4), part = q % (D / 4);
+        const int pp = v_pp, part = v_part;
         const int pos = vt_pos(2 * pp);
         const uint32_t k0w[2] = {vst[u][0].x, vst[u][0].y}, k1w[2] = {vst[u][1].x, vst[u][1].y};
 #pragma unroll
@@ -1082,7 +1090,8 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
           const float v0 = (e & 1) ? bf16_hi(k0w[e >> 1]) : bf16_lo(k0w[e >> 1]);
           const float v1 = (e & 1) ? bf16_hi(k1w[e >> 1]) : bf16_lo(k1w[e >> 1]);
           const auto hv = __builtin_amdgcn_cvt_pkrtz(v0, v1);
-          *reinterpret_cast<uint32_t*>(&s_vt[buf][(4 * part + e) * VS + pos]) = __builtin_bit_cast(uint32_t, hv);
+          const int d = 4 * part + e;
+          *reinterpret_cast<uint32_t*>(&s_vt[buf][d * VS + 8 * (d >> 4) + pos]) = __builtin_bit_cast(uint32_t, hv);
         }
       }
     };
@@ -1377,7 +1386,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
             f16x8 vf[DT];
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
-              vf[dt] = *reinterpret_cast<const f16x8*>(&s_vt[vb][(16 * dt + c16) * VS + 32 * c2 + 8 * g]);
+              vf[dt] = *reinterpret_cast<const f16x8*>(&s_vt[vb][(16 * dt + c16) * VS + 8 * dt + 32 * c2 + 8 * g]);
 #pragma unroll
             for (int hh = 0; hh < NH; ++hh) {
               float e[2][4];
