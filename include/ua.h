@@ -231,6 +231,35 @@ ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cach
                      int32_t n_tokens, void* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Pruned prefill (paperlayer.ai section 4.2: a KV pair whose effective mask
+ * falls below p is evicted per head and never returns).  As ua_prefill, but
+ * token i of the call attends a cached or earlier entry j only while its bias
+ * Lambda_ij >= log_p (the token's own entry always), and the call ends with
+ * ua_compact(log_p) on the whole cache.  Because a bias never increases, the
+ * outputs and the surviving entries equal those of n_tokens calls of
+ * ua_decode_compact_step at the same log_p, up to entries whose bias lies
+ * within rounding of log_p.  kept_idx is as for ua_compact, indices counted in
+ * the segment as it stands after the appends.  log_p as for ua_decode_step;
+ * -INFINITY makes the call ua_prefill.  A segment without room for n_tokens
+ * more entries is handled as by ua_prefill, then compacted.
+ */
+ua_status ua_prefill_pruned(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                            const ua_tokens* in, int32_t n_tokens, float log_p, void* y, int32_t* kept_idx,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Prefill with eviction at chunk boundaries (paperlayer.ai section 5: prefill
+ * pruning in chunks of 128 tokens).  Tokens [c, c + chunk) of every sequence
+ * go through ua_prefill, dense inside the chunk, and then ua_compact(log_p)
+ * runs; c = 0, chunk, 2 chunk, ... up to n_tokens (the last chunk may be
+ * shorter).  in and y hold all n_tokens tokens as for ua_prefill; the
+ * workspace needs ua_prefill's for `chunk` tokens.
+ */
+ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                             const ua_tokens* in, int32_t n_tokens, int32_t chunk, float log_p, void* y, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * Stable in-place compaction (paperlayer.ai section 4.2: an entry whose
  * effective mask falls below p is evicted and never returns).  Per segment,
  * entries with logbias < log_p are removed and the survivors (K, V, logbias,

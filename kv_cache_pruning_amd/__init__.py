@@ -13,6 +13,8 @@ from ._lib import (  # noqa: F401
     ua_decode_step,
     ua_decode_compact_step,
     ua_prefill,
+    ua_prefill_pruned,
+    ua_prefill_chunked,
     ua_compact,
     ua_status_string,
     ua_abi_version,

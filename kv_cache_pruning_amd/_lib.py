@@ -27,6 +27,8 @@ EXPORTS = (
     "ua_decode_step",
     "ua_decode_compact_step",
     "ua_prefill",
+    "ua_prefill_pruned",
+    "ua_prefill_chunked",
     "ua_compact",
     "ua_status_string",
     "ua_abi_version",
@@ -105,6 +107,12 @@ def load(path: Optional[str] = None) -> C.CDLL:
     lib.ua_prefill.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_void_p,
                                C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_prefill.restype = C.c_int
+    lib.ua_prefill_pruned.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_float,
+                                      C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.ua_prefill_pruned.restype = C.c_int
+    lib.ua_prefill_chunked.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_int32,
+                                       C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.ua_prefill_chunked.restype = C.c_int
     lib.ua_compact.argtypes = [P(ua_dims), P(ua_cache), C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_compact.restype = C.c_int
     lib.ua_status_string.argtypes = [C.c_int32]
@@ -147,6 +155,20 @@ def ua_decode_compact_step(dims, params, cache, tokens, log_p: float, y, kept_id
 def ua_prefill(dims, params, cache, tokens, n_tokens: int, y, ws, ws_bytes: int, stream=None) -> None:
     _check(load().ua_prefill(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), int(n_tokens),
                              _ptr(y), _ptr(ws), ws_bytes, _stream(stream)), "ua_prefill")
+
+
+def ua_prefill_pruned(dims, params, cache, tokens, n_tokens: int, log_p: float, y, kept_idx, ws, ws_bytes: int,
+                      stream=None) -> None:
+    _check(load().ua_prefill_pruned(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), int(n_tokens),
+                                    float(log_p), _ptr(y), _ptr(kept_idx), _ptr(ws), ws_bytes, _stream(stream)),
+           "ua_prefill_pruned")
+
+
+def ua_prefill_chunked(dims, params, cache, tokens, n_tokens: int, chunk: int, log_p: float, y, ws, ws_bytes: int,
+                       stream=None) -> None:
+    _check(load().ua_prefill_chunked(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), int(n_tokens),
+                                     int(chunk), float(log_p), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "ua_prefill_chunked")
 
 
 def ua_compact(dims, cache, log_p: float, kept_idx, ws, ws_bytes: int, stream=None) -> None:

@@ -154,26 +154,83 @@ ua_status ua_decode_compact_step(const ua_dims* dims, const ua_params* params, c
   return decode_common(dims, params, cache, in, log_p, y, true, kept_idx, ws, ws_bytes, stream);
 }
 
-ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
-                     int32_t n_tokens, void* y, void* ws, size_t ws_bytes, void* stream) {
+// Shared checks and workspace carving of the prefill entry points.
+static ua_status prefill_setup(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                               const ua_tokens* in, void* y, void* ws, size_t ws_bytes, LayerArgs* a,
+                               ua::Control* ctl, char** scratch, size_t* scratch_bytes) {
   ua_status s;
   if ((s = check_dims(dims)) != UA_OK) return s;
   if ((s = check_params(params)) != UA_OK) return s;
   if ((s = check_cache(cache)) != UA_OK) return s;
   if ((s = check_tokens(in)) != UA_OK) return s;
-  if (!y || !aligned(y, 16) || n_tokens < 1) return UA_ERR_INVALID_ARG;
+  if (!y || !aligned(y, 16)) return UA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
-  LayerArgs a = make_args(dims, params, cache, in, y);
-  const size_t cb = ua::control_bytes(a);
-  const size_t tb = ua::control_tail_bytes(a);
+  *a = make_args(dims, params, cache, in, y);
+  const size_t cb = ua::control_bytes(*a);
+  const size_t tb = ua::control_tail_bytes(*a);
   if (ws_bytes < cb + tb) return UA_ERR_WORKSPACE;
-  const ua::Control ctl = ua::control_carve(a, ws, ws_bytes);
+  *ctl = ua::control_carve(*a, ws, ws_bytes);
   // the scratch ends where the compaction flags begin
-  const hipError_t e = ua::launch_prefill(a, ctl, n_tokens, 0, reinterpret_cast<char*>(ws) + cb,
-                                          ws_bytes / 256 * 256 - tb - cb, reinterpret_cast<hipStream_t>(stream));
+  *scratch = reinterpret_cast<char*>(ws) + cb;
+  *scratch_bytes = ws_bytes / 256 * 256 - tb - cb;
+  return UA_OK;
+}
+
+static ua_status prefill_status(hipError_t e) {
   if (e == hipErrorNotSupported) return UA_ERR_UNSUPPORTED;
   if (e == hipErrorOutOfMemory) return UA_ERR_WORKSPACE;
   return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+ua_status ua_prefill(const ua_dims* dims, const ua_params* params, const ua_cache* cache, const ua_tokens* in,
+                     int32_t n_tokens, void* y, void* ws, size_t ws_bytes, void* stream) {
+  LayerArgs a;
+  ua::Control ctl;
+  char* scratch;
+  size_t sb;
+  ua_status s;
+  if (n_tokens < 1) return UA_ERR_INVALID_ARG;
+  if ((s = prefill_setup(dims, params, cache, in, y, ws, ws_bytes, &a, &ctl, &scratch, &sb)) != UA_OK) return s;
+  return prefill_status(ua::launch_prefill(a, ctl, n_tokens, 0, scratch, sb, reinterpret_cast<hipStream_t>(stream),
+                                           -__builtin_huge_valf(), n_tokens, 0));
+}
+
+ua_status ua_prefill_pruned(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                            const ua_tokens* in, int32_t n_tokens, float log_p, void* y, int32_t* kept_idx,
+                            void* ws, size_t ws_bytes, void* stream) {
+  LayerArgs a;
+  ua::Control ctl;
+  char* scratch;
+  size_t sb;
+  ua_status s;
+  if (n_tokens < 1 || bad_log_p(log_p)) return UA_ERR_INVALID_ARG;
+  if (kept_idx && !aligned(kept_idx, 4)) return UA_ERR_INVALID_ARG;
+  if ((s = prefill_setup(dims, params, cache, in, y, ws, ws_bytes, &a, &ctl, &scratch, &sb)) != UA_OK) return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if ((s = prefill_status(ua::launch_prefill(a, ctl, n_tokens, 0, scratch, sb, st, log_p, n_tokens, 0))) != UA_OK)
+    return s;
+  return ua::launch_compact(a, ctl, log_p, kept_idx, st) == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
+ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                             const ua_tokens* in, int32_t n_tokens, int32_t chunk, float log_p, void* y, void* ws,
+                             size_t ws_bytes, void* stream) {
+  LayerArgs a;
+  ua::Control ctl;
+  char* scratch;
+  size_t sb;
+  ua_status s;
+  if (n_tokens < 1 || chunk < 1 || bad_log_p(log_p)) return UA_ERR_INVALID_ARG;
+  if ((s = prefill_setup(dims, params, cache, in, y, ws, ws_bytes, &a, &ctl, &scratch, &sb)) != UA_OK) return s;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int32_t t0 = 0; t0 < n_tokens; t0 += chunk) {
+    const int32_t nc = n_tokens - t0 < chunk ? n_tokens - t0 : chunk;
+    if ((s = prefill_status(ua::launch_prefill(a, ctl, nc, 0, scratch, sb, st, -__builtin_huge_valf(), n_tokens,
+                                               t0))) != UA_OK)
+      return s;
+    if (ua::launch_compact(a, ctl, log_p, nullptr, st) != hipSuccess) return UA_ERR_HIP;
+  }
+  return UA_OK;
 }
 
 ua_status ua_compact(const ua_dims* dims, const ua_cache* cache, float log_p, int32_t* kept_idx, void* ws,

@@ -75,7 +75,15 @@ struct PrefillWs {
   int* glob;       // control words: glob[kGlobSeq] counts the calls made with the workspace
   uint16_t* wut;   // [H_q*d, rp] bf16  W_up^T, ranks >= r zero
   int n, nrb, cp, rp;
+  int ld, t0;      // token (b, t) of the call is row b * ld + t0 + t of q, k, v, x and y
+  float tau2;      // attention mask threshold in log2 units (log p * log2 e), -inf for none
 };
+
+// Row of q/k/v/x/y that holds call token tk = b * n + t.
+__device__ __forceinline__ int64_t io_row(const PrefillWs& w, int tk) {
+  const int b = tk / w.n;
+  return (int64_t)b * w.ld + w.t0 + (tk - b * w.n);
+}
 
 static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w) {
   const int64_t S = (int64_t)a.B * a.H_kv;
@@ -242,7 +250,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
     const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
     const int nks = (Dm + 31) / 32;
     const int ntile = w.cp / 16;
-    const int64_t xrow = (int64_t)min(tok0 + c16, NT - 1) * Dm;
+    const int64_t xrow = io_row(w, min(tok0 + c16, NT - 1)) * Dm;
     const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
     for (int k0 = wv * KCH; k0 < nks; k0 += (kTT / 64) * KCH) {
       for (int nt0 = 0; nt0 < ntile; nt0 += 3) {
@@ -308,9 +316,11 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
         const int c = e % (CH / 2);
         const int rest = e / (CH / 2);
         const int hd = rest % Hq, tt = rest / Hq;
-        base[u] = ((int64_t)min(tok0 + tt, NT - 1) * Hq + hd) * D + 8 * c;
-        lo[u] = *reinterpret_cast<const u32x4*>(Q + base[u]);
-        hi[u] = *reinterpret_cast<const u32x4*>(Q + base[u] + HALF);
+        const int tkc = min(tok0 + tt, NT - 1);
+        base[u] = ((int64_t)tkc * Hq + hd) * D + 8 * c;
+        const int64_t qin = (io_row(w, tkc) * Hq + hd) * D + 8 * c;
+        lo[u] = *reinterpret_cast<const u32x4*>(Q + qin);
+        hi[u] = *reinterpret_cast<const u32x4*>(Q + qin + HALF);
       }
 #pragma unroll
       for (int u = 0; u < QB; ++u) {
@@ -351,7 +361,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
       const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
       const int len0 = a.seg_len[s];
       if ((int64_t)len0 + n > a.seg_cap[s]) continue;
-      const int64_t base = ((int64_t)tk * Hkv + h) * D;
+      const int64_t base = (io_row(w, tk) * Hkv + h) * D;
       u32x4 raw[CH];
 #pragma unroll
       for (int c = 0; c < CH; ++c) raw[c] = *reinterpret_cast<const u32x4*>(Kin + base + 8 * c);
@@ -395,7 +405,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
         const int e = min(e0 + u * kTT + tid, nv - 1);
         const int c = e % CH, rest = e / CH;
         const int h = rest % Hkv, tt = rest / Hkv;
-        vv[u] = *reinterpret_cast<const u32x4*>(Vin + ((int64_t)min(tok0 + tt, NT - 1) * Hkv + h) * D + 8 * c);
+        vv[u] = *reinterpret_cast<const u32x4*>(Vin + (io_row(w, min(tok0 + tt, NT - 1)) * Hkv + h) * D + 8 * c);
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
@@ -528,6 +538,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
   const bool row_ok = tq < n;
   const int tqc = min(tq, n - 1);
   const int64_t tok = (int64_t)b * n + tqc;
+  const int64_t ytok = (int64_t)b * w.ld + w.t0 + tqc;  // the token's row of y
   const int a0 = h * HG;
 
   if (room) {
@@ -776,6 +787,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
         lam[t][2] += pre.z;
         lam[t][3] += pre.w;
       }
+      if (w.tau2 > kNegInf) {  // pruned call: entries below the threshold are not attended
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lam[t][i] = (lam[t][i] >= w.tau2) ? lam[t][i] : kNegInf;
+      }
       // ---- carry out to the next token block, or the final bias of the call
       if (wv == 4) {
         const int jg = j0 + lane;
@@ -892,8 +909,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
         const float inv = (row_ok && Ls > 0.0f) ? 1.0f / Ls : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
-          const float4 gm = *reinterpret_cast<const float4*>(w.gam + yo);
+          const int64_t go = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+          const int64_t yo = (ytok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+          const float4 gm = *reinterpret_cast<const float4*>(w.gam + go);
           float yv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) yv[i] = (O[hh][dt][i] * s0 + xch[4 * dt + i] * s1) * inv;
@@ -916,7 +934,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
     for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+        const int64_t yo = (ytok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
         if (a.y_bf16) {
           *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) = make_uint2(0u, 0u);
         } else {
@@ -1034,6 +1052,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     const uint16_t* Kc = reinterpret_cast<const uint16_t*>(a.K);
     const uint16_t* Vc = reinterpret_cast<const uint16_t*>(a.V);
     const float col_scale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+    const bool masked = w.tau2 > kNegInf;
     auto slot = [&](int j) -> int64_t { return off + min(j, nkeys - 1); };
 
     for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreadsWS) {
@@ -1266,7 +1285,8 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         for (int i = 0; i < 4; ++i) car[i] = __uint_as_float((uint32_t)cw[i]);
       }
       // the written bias carries the attention mask: -inf where token t does
-      // not see key j (j > len0 + t, or t past the call)
+      // not see key j (j > len0 + t, or t past the call), and in a pruned
+      // call where the entry's bias has fallen below the threshold
       float* ob = &s_bias[JB & 1][0];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -1276,6 +1296,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         for (int i = 0; i < 4; ++i) {
           bv[i] = lam[tt][i] + car[i];
           if (edge) bv[i] = (tq < n && jk + i <= len0 + tq) ? bv[i] : kNegInf;
+          if (masked) bv[i] = (bv[i] >= w.tau2) ? bv[i] : kNegInf;
         }
         *reinterpret_cast<float4*>(&ob[((p * 4 + tt) * 64 + lane) * 4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
       }
@@ -1325,6 +1346,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
       const int tq = t0 + 16 * p + c16;
       const bool row_ok = tq < n;
       const int64_t tok = (int64_t)b * n + min(tq, n - 1);
+      const int64_t ytok = (int64_t)b * w.ld + w.t0 + min(tq, n - 1);  // the token's row of y
       const float inv_cs = 1.0f / cs;
       f16x8 ones;
 #pragma unroll
@@ -1462,8 +1484,9 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
           const float inv = (row_ok && L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int64_t yo = (tok * Hq + a0 + h0 + hh) * D + 16 * dt + 4 * g;
-            const float4 gm = *reinterpret_cast<const float4*>(w.gam + yo);
+            const int64_t go = (tok * Hq + a0 + h0 + hh) * D + 16 * dt + 4 * g;
+            const int64_t yo = (ytok * Hq + a0 + h0 + hh) * D + 16 * dt + 4 * g;
+            const float4 gm = *reinterpret_cast<const float4*>(w.gam + go);
             const float y0 = gm.x * O[hh][dt][0] * inv, y1 = gm.y * O[hh][dt][1] * inv;
             const float y2 = gm.z * O[hh][dt][2] * inv, y3 = gm.w * O[hh][dt][3] * inv;
             if (row_ok) {
@@ -1484,12 +1507,12 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     // the segment has no room for the call: its outputs are zero
     const int tq = t0 + 16 * p + c16;
     if (tq < n) {
-      const int64_t tok = (int64_t)b * n + tq;
+      const int64_t ytok = (int64_t)b * w.ld + w.t0 + tq;
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const int64_t yo = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
+          const int64_t yo = (ytok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
           if (a.y_bf16) {
             *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) = make_uint2(0u, 0u);
           } else {
@@ -1528,7 +1551,7 @@ static void launch_attn_ws(const LayerArgs& a, const PrefillWs& w, int grid, hip
 }
 
 hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max_seg_cap, void* scratch,
-                          size_t scratch_bytes, hipStream_t st) {
+                          size_t scratch_bytes, hipStream_t st, float log_p, int ld, int t0) {
   if (!a.bf16) return hipErrorNotSupported;  // the matrix-core path is written for bf16 caches
   const int G = a.H_q / a.H_kv;
   if (a.d == 128 && G == 8) return hipErrorNotSupported;
@@ -1536,6 +1559,9 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max
   PrefillWs w;
   prefill_layout(a, n, reinterpret_cast<char*>(scratch), &w);
   w.glob = ctl.glob;
+  w.ld = ld;
+  w.t0 = t0;
+  w.tau2 = (log_p == -__builtin_huge_valf()) ? -__builtin_huge_valf() : log_p * kLog2e;
   const int S = a.B * a.H_kv;
   const int nsync = 2 + S * w.nrb;
   const int64_t prep_items = std::max<int64_t>(std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8)),

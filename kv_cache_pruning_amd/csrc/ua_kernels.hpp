@@ -101,8 +101,11 @@ hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int
 
 // Prefill (its sync words live in its scratch and are cleared by the call)
 size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap);
+// Prefill of n_tokens per sequence.  Token t of sequence b is row b * ld + t0 + t
+// of q, k, v, x and y; log_p (-inf: none) keeps entries whose bias has fallen
+// below it out of the softmax.
 hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, int max_seg_cap, void* scratch,
-                          size_t scratch_bytes, hipStream_t st);
+                          size_t scratch_bytes, hipStream_t st, float log_p, int ld, int t0);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -138,6 +138,31 @@ class Layer:
         L.ua_prefill(self.dims, self.w.params, self.cache.struct, tok, n, y, self.ws.ptr, self.ws.nbytes, stream)
         return y, ts
 
+    def prefill_pruned(self, q, k, v, x, log_p: float, y: Optional[torch.Tensor] = None,
+                       kept: Optional[torch.Tensor] = None, stream=None):
+        """Prefill that leaves entries below log_p out of the softmax, then compacts."""
+        s = self.shape
+        n = q.shape[1]
+        ts, tok = self._tokens(q, k, v, x)
+        if y is None:
+            y = torch.empty((s.B, n, s.H_q, s.d), dtype=torch.bfloat16 if s.y_bf16 else torch.float32,
+                            device=self.device)
+        L.ua_prefill_pruned(self.dims, self.w.params, self.cache.struct, tok, n, log_p, y, kept, self.ws.ptr,
+                            self.ws.nbytes, stream)
+        return y, ts
+
+    def prefill_chunked(self, q, k, v, x, chunk: int, log_p: float, y: Optional[torch.Tensor] = None, stream=None):
+        """Dense prefill in chunks of `chunk` tokens, compacting at log_p after each."""
+        s = self.shape
+        n = q.shape[1]
+        ts, tok = self._tokens(q, k, v, x)
+        if y is None:
+            y = torch.empty((s.B, n, s.H_q, s.d), dtype=torch.bfloat16 if s.y_bf16 else torch.float32,
+                            device=self.device)
+        L.ua_prefill_chunked(self.dims, self.w.params, self.cache.struct, tok, n, chunk, log_p, y, self.ws.ptr,
+                             self.ws.nbytes, stream)
+        return y, ts
+
     def compact(self, log_p: float, kept: Optional[torch.Tensor] = None, stream=None):
         L.ua_compact(self.dims, self.cache.struct, log_p, kept, self.ws.ptr, self.ws.nbytes, stream)
         return kept

@@ -471,3 +471,115 @@ def run_fused_parity(cfg: LayerConfig, steps: int, log_p: float, terms: int = 7,
         assert y_err <= y_tol(cfg), f"step {step}: y max-abs error {y_err:.3e}"
         assert lam_err <= 1e-4, f"step {step}: log-bias error {lam_err:.3e}"
     return run
+
+
+# ---------------------------------------------------------------------------
+# pruned prefill and chunk-boundary eviction
+# ---------------------------------------------------------------------------
+def _probe_layer(cfg: LayerConfig, w: Weights, c: CacheInit, terms: int, n: int):
+    """An empty cache with room for n tokens per segment at the same positions:
+    a dense prefill there stores the very key bits the tested call stores."""
+    S = cfg.B * cfg.H_kv
+    pc = CacheInit(K=np.zeros((S * n, cfg.d), np.float32), V=np.zeros((S * n, cfg.d), np.float32),
+                   lam=np.zeros(S * n, np.float32), lk=np.zeros(S * n, np.float32),
+                   seg_off=np.arange(S, dtype=np.int64) * n, seg_len=np.zeros(S, np.int32),
+                   seg_cap=np.full(S, n, np.int32), next_pos=c.next_pos.copy())
+    return device_layer(cfg, w, pc, terms=terms, max_tokens=n), pc
+
+
+def _compare_cache(layer, oc, cfg, what: str) -> float:
+    """Lengths, stored rows and biases of every segment against the oracle."""
+    g = gpu_state(layer)
+    S = cfg.B * cfg.H_kv
+    lam_err = 0.0
+    for s in range(S):
+        o, m = int(g["seg_off"][s]), int(g["seg_len"][s])
+        assert m == oc.lam[s].size, f"{what} seg {s}: {m} entries kept, oracle {oc.lam[s].size}"
+        assert np.array_equal(g["K"][o : o + m], oc.K[s]), f"{what} seg {s}: kept keys differ"
+        assert np.array_equal(g["V"][o : o + m], oc.V[s]), f"{what} seg {s}: kept values differ"
+        lam_err = max(lam_err, _maxrel(g["lam"][o : o + m], oc.lam[s]))
+        assert _maxrel(g["lk"][o : o + m], oc.lk[s]) <= 1e-5, f"{what} seg {s}: key gates differ"
+    assert np.array_equal(g["next_pos"], oc.next_pos), f"{what}: positions differ"
+    assert g["status"] == 0, f"{what}: status {g['status']}"
+    return lam_err
+
+
+def run_pruned_prefill_parity(cfg: LayerConfig, log_p: float, chunked: bool = False, terms: int = 7,
+                              seed: int = 0) -> dict:
+    """ua_prefill_pruned or ua_prefill_chunked on the GPU against the oracle.
+
+    pruned (chunked=False): n_total / chunk calls of `chunk` tokens; each equals
+    `chunk` oracle decode steps at log_p (an entry below tau is neither
+    attended nor updated again) followed by compaction.
+    chunked: one ua_prefill_chunked call over all n_total tokens with chunks of
+    `chunk`; it equals, chunk by chunk, the oracle's dense prefill followed by
+    compaction at log_p.
+    y, the kept entries (keys and values bit-exact, biases relative 1e-4) and
+    the lengths are compared after every call.  The GPU's keep decisions are
+    not visible per step here, so the run counts oracle decisions within
+    BORDER of tau ("borderline"); the caller picks inputs with none.
+    """
+    import torch
+
+    w = make_weights(cfg, seed)
+    c = make_cache(cfg, w, seed)
+    n = cfg.chunk
+    per_call = n if not chunked else cfg.n_total
+    calls = cfg.n_total // per_call
+    layer = device_layer(cfg, w, c, terms=terms, max_tokens=n)
+    probe, pc = _probe_layer(cfg, w, c, terms, cfg.n_total)
+    od, op = oracle_dims(cfg, terms), oracle_params(w)
+    oc = oracle_cache(cfg, c)
+    tau = -math.inf if log_p == -math.inf else log_p
+    rep = {"y_err": 0.0, "lam_err": 0.0, "borderline": 0, "evicted": 0, "calls": calls}
+
+    def decide(s, lam_new, idx):
+        rep["borderline"] += int(np.sum(np.abs(lam_new - tau) <= BORDER))
+        return lam_new >= tau
+
+    def compact_oracle():
+        for s in range(len(oc.lam)):
+            rep["borderline"] += int(np.sum(np.abs(oc.lam[s] - tau) <= BORDER))
+        before = sum(x.size for x in oc.lam)
+        U.compact(oc, log_p)
+        rep["evicted"] += before - sum(x.size for x in oc.lam)
+
+    for call in range(calls):
+        inp = make_step_inputs(cfg, call, per_call, seed)
+        pos0 = probe.cache.next_pos.cpu().numpy().copy()
+        plen = probe.cache.seg_len.cpu().numpy().copy()
+        probe.prefill(inp.q, inp.k, inp.v, inp.x)
+        torch.cuda.synchronize()
+        k_gpu = _stored_new(gpu_state(probe), pc.seg_off, plen, cfg, per_call, "K")
+        _check_new_keys(cfg, od, inp.k, pos0, k_gpu)
+        if chunked:
+            y_gpu, _ = layer.prefill_chunked(inp.q, inp.k, inp.v, inp.x, n, log_p)
+        else:
+            y_gpu, _ = layer.prefill_pruned(inp.q, inp.k, inp.v, inp.x, log_p)
+        torch.cuda.synchronize()
+        y_or = np.zeros((cfg.B, per_call, cfg.H_q, cfg.d))
+        if chunked:
+            for c0 in range(0, per_call, n):
+                c1 = min(per_call, c0 + n)
+                y_or[:, c0:c1] = U.prefill(od, op, oc, inp.q[:, c0:c1], inp.k[:, c0:c1], inp.v[:, c0:c1],
+                                           inp.x[:, c0:c1], k_override=k_gpu[:, c0:c1])
+                compact_oracle()
+        else:
+            for i in range(per_call):
+                y_or[:, i], _ = U.decode_step(od, op, oc, inp.q[:, i], inp.k[:, i], inp.v[:, i], inp.x[:, i], log_p,
+                                              decide=decide, k_override=k_gpu[:, i])
+            compact_oracle()
+        try:
+            rep["y_err"] = max(rep["y_err"], _maxabs(y_gpu.float().cpu().numpy(), y_or))
+            rep["lam_err"] = max(rep["lam_err"], _compare_cache(layer, oc, cfg, f"call {call}"))
+            assert rep["y_err"] <= y_tol(cfg), f"call {call}: y max-abs error {rep['y_err']:.3e}"
+            assert rep["lam_err"] <= 1e-4, f"call {call}: log-bias error {rep['lam_err']:.3e}"
+        except AssertionError as e:
+            if rep["borderline"]:
+                raise BorderlineRun(f"{e} (after {rep['borderline']} borderline decisions)") from e
+            raise
+    return rep
+
+
+class BorderlineRun(Exception):
+    """A mismatch in a run where the oracle met decisions within BORDER of tau."""

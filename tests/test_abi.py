@@ -157,6 +157,24 @@ def test_prefill_and_compact_reject():
     assert lib.ua_compact(C.byref(_dims(L)), C.byref(bad), -1.0, None, p, 1 << 40, None) == 1
 
 
+def test_pruned_and_chunked_prefill_reject():
+    """Host-side argument checks of the pruned and chunked prefill (no device work)."""
+    L = _lib()
+    lib = L.load()
+    a = _args(L)
+    p = _fake_ptr()
+    args = (C.byref(_dims(L)), C.byref(a["params"]), C.byref(a["cache"]), C.byref(a["tokens"]))
+    assert lib.ua_prefill_pruned(*args, 0, -1.0, p, None, p, 1 << 40, None) == 1       # no tokens
+    assert lib.ua_prefill_pruned(*args, 16, float("nan"), p, None, p, 1 << 40, None) == 1
+    assert lib.ua_prefill_pruned(*args, 16, 0.5, p, None, p, 1 << 40, None) == 1       # log p > 0
+    assert lib.ua_prefill_pruned(*args, 16, -1.0, p, p + 2, p, 1 << 40, None) == 1     # misaligned kept list
+    assert lib.ua_prefill_pruned(*args, 16, -1.0, p, None, p, 8, None) == 3            # workspace too small
+    assert lib.ua_prefill_chunked(*args, 16, 0, -1.0, p, p, 1 << 40, None) == 1        # empty chunk
+    assert lib.ua_prefill_chunked(*args, 0, 8, -1.0, p, p, 1 << 40, None) == 1
+    assert lib.ua_prefill_chunked(*args, 16, 8, float("nan"), p, p, 1 << 40, None) == 1
+    assert lib.ua_prefill_chunked(*args, 16, 8, -1.0, p, p, 8, None) == 3
+
+
 def test_missing_library_fails_loudly(tmp_path):
     from kv_cache_pruning_amd import _lib as L
 
