@@ -315,8 +315,8 @@ def main():
                          "byte counters of a rocprofv3 --pmc run)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this build runs on a "
-              f"single MI355X; see DESIGN.md for how the path would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the UA path here runs on "
+              f"a single MI355X", file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -336,6 +336,8 @@ def main():
     out = bench_decode(args)
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args)
+        out["prefill_pruned"] = bench_prefill_pruned(args)
+        out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
     print(json.dumps(out), flush=True)
 
 
@@ -425,6 +427,103 @@ def bench_prefill(args, name: str = "1b-prefill", passes: int = 3, warm: int = 1
             "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFS},
         },
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_prefill(cfg, args.cpu_seconds / 2),
+    }
+
+
+def bench_prefill_pruned(args, chunked: bool = False, name: str = "1b-prefill", passes: int = 3, warm: int = 1):
+    """The 1b-prefill tokens with eviction at the workload's p.
+
+    pruned: 16 calls of ua_prefill_pruned (1024 tokens each, attention masked
+    at log p, compaction at the end of each call).  chunked: one call of
+    ua_prefill_chunked over all 16384 tokens, dense inside 128-token chunks
+    with a compaction after each.  Every pass starts from the empty cache.
+    The roofline counts the (token, key) pairs of each call over the cache as
+    the call finds it (lengths read in an untimed pass), as for dense prefill.
+    """
+    import torch
+
+    from tests.harness import device_layer
+    from ua_inputs import config, make_cache, make_step_inputs, make_weights
+
+    cfg = config(name)
+    log_p = math.log(cfg.p)
+    n = 128 if chunked else cfg.chunk
+    per_call = cfg.n_total if chunked else n
+    calls = cfg.n_total // per_call
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    layer = device_layer(cfg, w, c, max_tokens=n, y_bf16=True)
+    dt = torch.bfloat16
+    inps = [make_step_inputs(cfg, i, cfg.chunk, 0) for i in range(cfg.n_total // cfg.chunk)]
+    full = [np.concatenate([getattr(x, f) for x in inps], axis=1) for f in ("q", "k", "v", "x")]
+    toks = [[torch.from_numpy(np.ascontiguousarray(a[:, i * per_call:(i + 1) * per_call])).to("cuda", dt)
+             for a in full] for i in range(calls)]
+    y = torch.empty((cfg.B, per_call, cfg.H_q, cfg.d), dtype=torch.bfloat16, device="cuda")
+    seg_len0 = layer.cache.seg_len.clone()
+    pos0 = layer.cache.next_pos.clone()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    call_ms = np.zeros(calls)
+    lens = []
+    for p in range(warm + passes + 1):
+        layer.cache.seg_len.copy_(seg_len0)
+        layer.cache.next_pos.copy_(pos0)
+        torch.cuda.synchronize()
+        if p == warm + passes:
+            # untimed: the same work as separate calls, to read the lengths each
+            # chunk (or call) finds
+            for i in range(calls):
+                for c0 in range(0, per_call, n):
+                    lens.append(layer.cache.seg_len.cpu().numpy().copy())
+                    part = [t[:, c0:c0 + n].contiguous() for t in toks[i]]
+                    if chunked:
+                        layer.prefill(*part, y=y[:, c0:c0 + n].contiguous())
+                        layer.compact(log_p)
+                    else:
+                        layer.prefill_pruned(*part, log_p, y=y)
+            torch.cuda.synchronize()
+            break
+        ev[0].record()
+        for i in range(calls):
+            if chunked:
+                layer.prefill_chunked(*toks[i], n, log_p, y=y)
+            else:
+                layer.prefill_pruned(*toks[i], log_p, y=y)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        if warm <= p < warm + passes:
+            call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(calls)])
+    call_ms /= passes
+    kept = layer.cache.seg_len.cpu().numpy()
+    st = int(layer.cache.status.item())
+    total_ms = float(call_ms.sum())
+    G = cfg.H_q // cfg.H_kv
+    pairs = float(sum(sum(n * int(l0) + n * (n + 1) // 2 for l0 in ls) for ls in lens))
+    flops, trans = pairs * (G * 4 * cfg.d + 2 * cfg.d), pairs * (G + 3)
+    tts = trans / (total_ms * 1e-3) / 1e12
+    tflops = flops / (total_ms * 1e-3) / 1e12
+    tokens = cfg.B * cfg.n_total
+    what = (f"ua_prefill_chunked, dense 128-token chunks with compaction at p={cfg.p} after each" if chunked else
+            f"{calls} calls of ua_prefill_pruned ({n} tokens, attention masked at p={cfg.p}, compaction per call)")
+    return {
+        "workload": f"{cfg.name}: {what}; B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d}, N={cfg.n_total} "
+                    f"from an empty cache, bf16 storage, y bf16",
+        "value": tokens / (total_ms * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_pass": total_ms,
+        "passes": passes,
+        "kept_entries_per_segment": float(kept.mean()),
+        "call_ms": [round(float(x), 4) for x in call_ms] if not chunked else None,
+        "status": st,
+        "roofline": {
+            "bound": "alu",
+            "achieved": tts,
+            "peak": TRANS_PEAK_TS,
+            "unit": "T transcendentals/s",
+            "frac": tts / TRANS_PEAK_TS,
+            "pairs": pairs,
+            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFS},
+        },
     }
 
 
