@@ -19,10 +19,10 @@
 //    [W_dec | W_dn] transposed (zero-padded to 16 rows) so that the gate
 //    projections can be fed to the matrix cores with 16-byte loads.
 // 2. prefill_token_kernel: 16 tokens per workgroup.  x [W_dec | W_dn] on the
-//    matrix cores, log-sigmoid gates, the output gate sigmoid(u W_up + b_up),
-//    RoPE of the queries (bf16 copy for the matrix cores) and of the
-//    L2-normalised keys (angles in fp64), and the append of k~, v and the key
-//    gate to the cache.
+//    matrix cores, log-sigmoid gates, u = x W_dn for the output gate (whose
+//    sigmoid(u W_up + b_up) the attention epilogue forms per tile), RoPE of
+//    the queries (bf16 copy for the matrix cores) and of the L2-normalised
+//    keys (angles in fp64), and the append of k~, v and the key gate.
 // 3. prefill_attn_kernel: one workgroup per (segment, block of 64 tokens),
 //    four waves of 16 tokens, looping over blocks of 64 keys.  Per key block,
 //    with keys as MFMA rows and the wave's tokens as columns:
@@ -69,7 +69,7 @@ struct PrefillWs {
   uint16_t* wt;    // [cp, D_model] bf16  [W_dec | W_dn]^T, rows >= 3 H_kv + r zero
   uint16_t* qbf;   // [B*n, H_q, d] bf16  rotated queries
   float* gl;       // [B*n, H_kv, 2]      (lq, lb)
-  float* gam;      // [B*n, H_q*d]        output gate
+  uint16_t* uf;    // [B*n, 2, rp] bf16  u = x W_dn as a high part and a low part (u - high)
   float* carry;    // [nrb-1, total_slots] per-key carry into token block I (log2 units)
   unsigned long long* carry64;  // the same region as tagged words (call tag << 32 | carry bits)
   int* glob;       // control words: glob[kGlobSeq] counts the calls made with the workspace
@@ -100,16 +100,16 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
   char* wt = take(sizeof(uint16_t) * (size_t)cp * a.D_model);
   char* qbf = take(sizeof(uint16_t) * (size_t)NT * a.H_q * a.d);
   char* gl = take(sizeof(float) * 2 * (size_t)NT * a.H_kv);
-  char* gam = take(sizeof(float) * (size_t)NT * a.H_q * a.d);
-  char* carry = take(sizeof(unsigned long long) * (size_t)(nrb - 1) * a.total_slots);
   const int rp = (a.r + 31) / 32 * 32;
+  char* uf = take(sizeof(uint16_t) * 2 * (size_t)NT * rp);
+  char* carry = take(sizeof(unsigned long long) * (size_t)(nrb - 1) * a.total_slots);
   char* wut = take(sizeof(uint16_t) * (size_t)a.H_q * a.d * rp);
   if (w) {
     w->sync = reinterpret_cast<int*>(sync);
     w->wt = reinterpret_cast<uint16_t*>(wt);
     w->qbf = reinterpret_cast<uint16_t*>(qbf);
     w->gl = reinterpret_cast<float*>(gl);
-    w->gam = reinterpret_cast<float*>(gam);
+    w->uf = reinterpret_cast<uint16_t*>(uf);
     w->carry = reinterpret_cast<float*>(carry);
     w->carry64 = reinterpret_cast<unsigned long long*>(carry);
     w->wut = reinterpret_cast<uint16_t*>(wut);
@@ -422,15 +422,14 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
     }
   }
 
-  // ---- output gate sigmoid(u W_up + b_up) on the matrix cores: A = u (16
-  // tokens x rp ranks) as a bf16 high part plus a bf16 low part (u - high),
-  // B = rows of W_up^T (16 columns per tile)
-  {
-    const int HqD = Hq * D;
-    const int ntile = HqD / 16;
-    u32x4 ahi[2], alo[2];
+  // ---- u = x W_dn for the output gate, as a bf16 high part and a bf16 low
+  // part (u - high), stored in the k layout of a matrix-core operand: the
+  // attention epilogue forms sigmoid(u W_up + b_up) for its own tokens
+  if (wv == 0) {
+    const int tk = tok0 + c16;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      if (32 * ks >= w.rp) break;
       uint32_t ph[4], pl[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
@@ -445,41 +444,35 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
         h2[1] = bf16_hi(ph[v]);
         pl[v] = pack2_bf16(x2[0] - h2[0], x2[1] - h2[1]);
       }
-      ahi[ks] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-      alo[ks] = u32x4{pl[0], pl[1], pl[2], pl[3]};
-    }
-    const int nks = w.rp / 32;
-    constexpr int TB = 4;
-    for (int nt0 = wv; nt0 < ntile; nt0 += (kTT / 64) * TB) {
-      u32x4 bv[TB][2];
-#pragma unroll
-      for (int u = 0; u < TB; ++u)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int nt = min(nt0 + (kTT / 64) * u, ntile - 1);
-          bv[u][ks] = *reinterpret_cast<const u32x4*>(w.wut + (int64_t)(16 * nt + c16) * w.rp + 32 * min(ks, nks - 1) + 8 * g);
-        }
-#pragma unroll
-      for (int u = 0; u < TB; ++u) {
-        const int nt = nt0 + (kTT / 64) * u;
-        if (nt >= ntile) break;
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          if (ks >= nks) break;
-          acc = mfma_bf16(ahi[ks], bv[u][ks], acc);
-          acc = mfma_bf16(alo[ks], bv[u][ks], acc);
-        }
-        const int col = 16 * nt + c16;
-        const float bias = a.b_up ? a.b_up[col] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tk = tok0 + 4 * g + i;
-          if (tk < NT) w.gam[(int64_t)tk * HqD + col] = sigmoid_fast(acc[i] + bias);
-        }
+      if (tk < NT) {
+        uint16_t* ut = w.uf + (int64_t)tk * 2 * w.rp + 32 * ks + 8 * g;
+        *reinterpret_cast<u32x4*>(ut) = u32x4{ph[0], ph[1], ph[2], ph[3]};
+        *reinterpret_cast<u32x4*>(ut + w.rp) = u32x4{pl[0], pl[1], pl[2], pl[3]};
       }
     }
   }
+}
+
+// Output gate sigmoid(u W_up + b_up) of call token `tok` (this lane's column
+// c16 of a 16-token tile) at output columns col0 + 4 g + i: rows of W_up^T
+// are the A operand and the token's u parts the B operand, so the result has
+// the lane layout of the O^T tiles it scales.  All 64 lanes must be active.
+__device__ __forceinline__ f32x4 out_gate(const LayerArgs& a, const PrefillWs& w, int64_t tok, int col0, int g,
+                                          int c16) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const uint16_t* ut = w.uf + tok * 2 * w.rp;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if (32 * ks >= w.rp) break;
+    const u32x4 wa = *reinterpret_cast<const u32x4*>(w.wut + (int64_t)(col0 + c16) * w.rp + 32 * ks + 8 * g);
+    const u32x4 uh = *reinterpret_cast<const u32x4*>(ut + 32 * ks + 8 * g);
+    const u32x4 ul = *reinterpret_cast<const u32x4*>(ut + w.rp + 32 * ks + 8 * g);
+    acc = mfma_bf16(wa, uh, acc);
+    acc = mfma_bf16(wa, ul, acc);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = sigmoid_fast(acc[i] + (a.b_up ? a.b_up[col0 + 4 * g + i] : 0.0f));
+  return acc;
 }
 
 // 3. attention with the causal decay bias
@@ -909,13 +902,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
         const float inv = (row_ok && Ls > 0.0f) ? 1.0f / Ls : 0.0f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const int64_t go = (tok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
           const int64_t yo = (ytok * Hq + a0 + hh) * D + 16 * dt + 4 * g;
-          const float4 gm = *reinterpret_cast<const float4*>(w.gam + go);
+          const f32x4 gm = out_gate(a, w, tok, (a0 + hh) * D + 16 * dt, g, c16);
           float yv[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) yv[i] = (O[hh][dt][i] * s0 + xch[4 * dt + i] * s1) * inv;
-          const float y0 = gm.x * yv[0], y1 = gm.y * yv[1], y2 = gm.z * yv[2], y3 = gm.w * yv[3];
+          const float y0 = gm[0] * yv[0], y1 = gm[1] * yv[1], y2 = gm[2] * yv[2], y3 = gm[3] * yv[3];
           if (row_ok) {
             if (a.y_bf16) {
               *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) =
@@ -924,6 +916,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(y0, y1, y2, y3);
             }
           }
+          __builtin_amdgcn_sched_barrier(0);  // one gate tile's operands live at a time
         }
       }
       __syncthreads();
@@ -992,7 +985,7 @@ __device__ __forceinline__ uint32_t carry_tag(uint32_t seq) {
   return 0x7F800000u | ((seq - 1u) % 0x3FFFFFu + 1u);  // exponent all ones, quiet bit clear, payload != 0
 }
 
-template <int HG>
+template <int HG, bool MASKED>
 __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs a, PrefillWs w) {
   constexpr int D = 64;
   constexpr int KC = D / 32;                // k steps of a head-dim dot product
@@ -1052,7 +1045,6 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     const uint16_t* Kc = reinterpret_cast<const uint16_t*>(a.K);
     const uint16_t* Vc = reinterpret_cast<const uint16_t*>(a.V);
     const float col_scale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
-    const bool masked = w.tau2 > kNegInf;
     auto slot = [&](int j) -> int64_t { return off + min(j, nkeys - 1); };
 
     for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreadsWS) {
@@ -1296,7 +1288,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         for (int i = 0; i < 4; ++i) {
           bv[i] = lam[tt][i] + car[i];
           if (edge) bv[i] = (tq < n && jk + i <= len0 + tq) ? bv[i] : kNegInf;
-          if (masked) bv[i] = (bv[i] >= w.tau2) ? bv[i] : kNegInf;
+          if constexpr (MASKED) bv[i] = (bv[i] >= w.tau2) ? bv[i] : kNegInf;
         }
         *reinterpret_cast<float4*>(&ob[((p * 4 + tt) * 64 + lane) * 4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
       }
@@ -1484,11 +1476,10 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
           const float inv = (row_ok && L > 0.0f) ? 1.0f / L : 0.0f;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const int64_t go = (tok * Hq + a0 + h0 + hh) * D + 16 * dt + 4 * g;
             const int64_t yo = (ytok * Hq + a0 + h0 + hh) * D + 16 * dt + 4 * g;
-            const float4 gm = *reinterpret_cast<const float4*>(w.gam + go);
-            const float y0 = gm.x * O[hh][dt][0] * inv, y1 = gm.y * O[hh][dt][1] * inv;
-            const float y2 = gm.z * O[hh][dt][2] * inv, y3 = gm.w * O[hh][dt][3] * inv;
+            const f32x4 gm = out_gate(a, w, tok, (a0 + h0 + hh) * D + 16 * dt, g, c16);
+            const float y0 = gm[0] * O[hh][dt][0] * inv, y1 = gm[1] * O[hh][dt][1] * inv;
+            const float y2 = gm[2] * O[hh][dt][2] * inv, y3 = gm[3] * O[hh][dt][3] * inv;
             if (row_ok) {
               if (a.y_bf16) {
                 *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.y) + yo) =
@@ -1497,6 +1488,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
                 *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.y) + yo) = make_float4(y0, y1, y2, y3);
               }
             }
+            __builtin_amdgcn_sched_barrier(0);  // one gate tile's operands live at a time
           }
         }
       };
@@ -1547,7 +1539,11 @@ static void launch_attn(const LayerArgs& a, const PrefillWs& w, int grid, hipStr
 
 template <int HG>
 static void launch_attn_ws(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_attn_ws_kernel<HG>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
+  if (w.tau2 > kNegInf) {
+    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, true>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
+  } else {
+    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, false>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
+  }
 }
 
 hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max_seg_cap, void* scratch,
