@@ -24,6 +24,7 @@ from .ua_ref import (  # noqa: F401
     round_cache,
     sigmoid,
     l2_normalize,
+    qk_rmsnorm,
     rope,
     log_sigmoid,
     log1mexp,

@@ -94,6 +94,12 @@ R15 positions: prefill pos = next_pos + i; decode pos = next_pos.
 R16 logsig and log1mexp are evaluated stably (Maechler 2012 for log1mexp).
 R17 for parity the harness may hand this oracle the GPU-stored k~ bits
     (after checking they are within one bf16 ulp of its own rounding).
+R18 "Qwen3-style normalized queries and keys" (paperlayer.ai summary,
+    Appendix E, ablations) = RMS normalisation over the head dimension with
+    a learned per-dimension weight shared by the heads, x / sqrt(mean(x^2) +
+    eps) * w with eps = 1e-6, applied to the projected q and k before O1-O2
+    (so the key is still L2-normalised afterwards).  It is an optional step
+    in front of the layer; the result is rounded to the token dtype.
 """
 
 from __future__ import annotations
@@ -250,6 +256,13 @@ def log1mexp(lam: np.ndarray) -> np.ndarray:
         out[near] = np.log(-np.expm1(lam[near]))
     out[~near] = np.log1p(-np.exp(lam[~near]))
     return out
+
+
+def qk_rmsnorm(x: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """R18: x / sqrt(mean(x^2) + eps) * w along the last (head) axis."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(w, np.float64)
 
 
 def sigmoid(z: np.ndarray) -> np.ndarray:

@@ -586,3 +586,38 @@ def test_overflow_sets_status_and_skips_append():
     assert cache.status & 1
     assert cache.lam[0].size == 3
     assert cache.next_pos[0] == 4
+
+
+# ---------------------------------------------------------------------------
+# R18: Qwen3-style normalized queries and keys (paperlayer.ai summary,
+# Appendix E ablations) as an RMS normalisation over the head dimension
+# ---------------------------------------------------------------------------
+def test_qk_rmsnorm_worked_example():
+    """x = (3, 4): mean square 12.5, so x / sqrt(12.5) = (0.8485..., 1.1313...); weights (1, 2)."""
+    y = U.qk_rmsnorm(np.array([3.0, 4.0]), np.array([1.0, 2.0]), eps=0.0)
+    r = math.sqrt(12.5)
+    assert np.allclose(y, [3.0 / r, 8.0 / r], rtol=0, atol=1e-15)
+
+
+def test_qk_rmsnorm_matches_torch_rms_norm():
+    """torch's RMSNorm in fp64, weights and eps included, on [B, n, H, d] heads."""
+    rng = RNG(7)
+    x = rng.normal(0, 3, (2, 5, 4, 64))
+    w = rng.normal(1, 0.2, 64)
+    ref = torch.nn.functional.rms_norm(torch.tensor(x), (64,), weight=torch.tensor(w), eps=1e-6).numpy()
+    assert np.allclose(U.qk_rmsnorm(x, w), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_qk_rmsnorm_invariants():
+    """Unit mean square with unit weights and eps = 0; invariant to a positive scale of
+    the head vector; heads are normalised independently."""
+    rng = RNG(8)
+    x = rng.normal(0, 1, (6, 3, 128))
+    one = np.ones(128)
+    y = U.qk_rmsnorm(x, one, eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, atol=1e-13)
+    assert np.allclose(U.qk_rmsnorm(7.5 * x, one, eps=0.0), y, atol=1e-13)
+    x2 = x.copy()
+    x2[:, 1] *= 100.0
+    y2 = U.qk_rmsnorm(x2, one, eps=0.0)
+    assert np.allclose(y2[:, 0], y[:, 0]) and np.allclose(y2[:, 2], y[:, 2])
