@@ -260,6 +260,19 @@ ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const
                              size_t ws_bytes, void* stream);
 
 /*
+ * Qwen3-style normalised queries and keys (paperlayer.ai summary, Appendix E:
+ * the UA ablation with normalised queries and keys), in place, before a
+ * decode or prefill call takes q and k as its inputs.  Every head vector x of
+ * q [B, n_tokens, H_q, d_head] and k [B, n_tokens, H_kv, d_head] (dims.dtype,
+ * 16-byte aligned, device) becomes x / sqrt(mean(x^2) + eps) * w over the
+ * head dimension, rounded to dims.dtype (nearest even for bf16).  w_q and w_k
+ * are fp32 [d_head] device vectors shared by the heads; a NULL weight leaves
+ * that tensor unchanged.  eps must be finite and >= 0 (1e-6 in Qwen3).
+ */
+ua_status ua_qk_norm(const ua_dims* dims, const float* w_q, const float* w_k, float eps, void* q, void* k,
+                     int32_t n_tokens, void* stream);
+
+/*
  * Stable in-place compaction (paperlayer.ai section 4.2: an entry whose
  * effective mask falls below p is evicted and never returns).  Per segment,
  * entries with logbias < log_p are removed and the survivors (K, V, logbias,

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     ua_prefill,
     ua_prefill_pruned,
     ua_prefill_chunked,
+    ua_qk_norm,
     ua_compact,
     ua_status_string,
     ua_abi_version,

@@ -29,6 +29,7 @@ EXPORTS = (
     "ua_prefill",
     "ua_prefill_pruned",
     "ua_prefill_chunked",
+    "ua_qk_norm",
     "ua_compact",
     "ua_status_string",
     "ua_abi_version",
@@ -113,6 +114,9 @@ def load(path: Optional[str] = None) -> C.CDLL:
     lib.ua_prefill_chunked.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_int32,
                                        C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_prefill_chunked.restype = C.c_int
+    lib.ua_qk_norm.argtypes = [P(ua_dims), C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_int32,
+                               C.c_void_p]
+    lib.ua_qk_norm.restype = C.c_int
     lib.ua_compact.argtypes = [P(ua_dims), P(ua_cache), C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_compact.restype = C.c_int
     lib.ua_status_string.argtypes = [C.c_int32]
@@ -169,6 +173,11 @@ def ua_prefill_chunked(dims, params, cache, tokens, n_tokens: int, chunk: int, l
     _check(load().ua_prefill_chunked(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), int(n_tokens),
                                      int(chunk), float(log_p), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
            "ua_prefill_chunked")
+
+
+def ua_qk_norm(dims, w_q, w_k, eps: float, q, k, n_tokens: int, stream=None) -> None:
+    _check(load().ua_qk_norm(C.byref(dims), _ptr(w_q), _ptr(w_k), float(eps), _ptr(q), _ptr(k), int(n_tokens),
+                             _stream(stream)), "ua_qk_norm")
 
 
 def ua_compact(dims, cache, log_p: float, kept_idx, ws, ws_bytes: int, stream=None) -> None:

@@ -233,6 +233,21 @@ ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const
   return UA_OK;
 }
 
+ua_status ua_qk_norm(const ua_dims* dims, const float* w_q, const float* w_k, float eps, void* q, void* k,
+                     int32_t n_tokens, void* stream) {
+  ua_status s;
+  if ((s = check_dims(dims)) != UA_OK) return s;
+  if (n_tokens < 1 || !(eps >= 0.0f) || !isfinite(eps)) return UA_ERR_INVALID_ARG;
+  if (w_q && (!q || !aligned(q, 16) || !aligned(w_q, 4))) return UA_ERR_INVALID_ARG;
+  if (w_k && (!k || !aligned(k, 16) || !aligned(w_k, 4))) return UA_ERR_INVALID_ARG;
+  const int64_t tok = (int64_t)dims->B * n_tokens;
+  const int64_t nq = w_q ? tok * dims->H_q : 0;
+  const int64_t nk = w_k ? tok * dims->H_kv : 0;
+  const hipError_t e = ua::launch_qk_norm(dims->d_head, dims->dtype == UA_BF16, q, w_q, nq, k, w_k, nk, eps,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
 ua_status ua_compact(const ua_dims* dims, const ua_cache* cache, float log_p, int32_t* kept_idx, void* ws,
                      size_t ws_bytes, void* stream) {
   ua_status s;

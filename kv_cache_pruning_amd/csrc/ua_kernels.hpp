@@ -101,6 +101,10 @@ hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int
 
 // Prefill (its sync words live in its scratch and are cleared by the call)
 size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap);
+// In-place RMS normalisation of nq head rows of q and nk of k (d elements each).
+hipError_t launch_qk_norm(int d, bool bf16, void* q, const float* wq, int64_t nq, void* k, const float* wk, int64_t nk,
+                          float eps, hipStream_t st);
+
 // Prefill of n_tokens per sequence.  Token t of sequence b is row b * ld + t0 + t
 // of q, k, v, x and y; log_p (-inf: none) keeps entries whose bias has fallen
 // below it out of the softmax.

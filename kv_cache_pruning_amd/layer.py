@@ -138,6 +138,19 @@ class Layer:
         L.ua_prefill(self.dims, self.w.params, self.cache.struct, tok, n, y, self.ws.ptr, self.ws.nbytes, stream)
         return y, ts
 
+    def qk_norm(self, q, k, w_q=None, w_k=None, eps: float = 1e-6, stream=None):
+        """Qwen3-style RMS normalisation of q [B, n, H_q, d] and k [B, n, H_kv, d] in place
+        (device copies in the layer's dtype are made first if needed); returns (q, k)."""
+        dt = self.shape.dtype
+        q = q if (isinstance(q, torch.Tensor) and q.device.type == "cuda" and q.dtype == dt and q.is_contiguous()) \
+            else _dev(q, dt, self.device)
+        k = k if (isinstance(k, torch.Tensor) and k.device.type == "cuda" and k.dtype == dt and k.is_contiguous()) \
+            else _dev(k, dt, self.device)
+        wq = None if w_q is None else _dev(w_q, torch.float32, self.device)
+        wk = None if w_k is None else _dev(w_k, torch.float32, self.device)
+        L.ua_qk_norm(self.dims, wq, wk, eps, q, k, q.shape[1], stream)
+        return q, k
+
     def prefill_pruned(self, q, k, v, x, log_p: float, y: Optional[torch.Tensor] = None,
                        kept: Optional[torch.Tensor] = None, stream=None):
         """Prefill that leaves entries below log_p out of the softmax, then compacts."""

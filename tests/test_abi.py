@@ -175,6 +175,21 @@ def test_pruned_and_chunked_prefill_reject():
     assert lib.ua_prefill_chunked(*args, 16, 8, -1.0, p, p, 8, None) == 3
 
 
+def test_qk_norm_rejects():
+    """Host-side argument checks of ua_qk_norm (no device work)."""
+    L = _lib()
+    lib = L.load()
+    p = _fake_ptr()
+    d = C.byref(_dims(L))
+    assert lib.ua_qk_norm(d, p, p, 1e-6, p, p, 0, None) == 1                # no tokens
+    assert lib.ua_qk_norm(d, p, p, float("nan"), p, p, 4, None) == 1
+    assert lib.ua_qk_norm(d, p, p, -1.0, p, p, 4, None) == 1
+    assert lib.ua_qk_norm(d, p, None, 1e-6, p + 2, p, 4, None) == 1         # misaligned q
+    assert lib.ua_qk_norm(d, None, p, 1e-6, p, None, 4, None) == 1          # k weight without k
+    assert lib.ua_qk_norm(d, None, None, 1e-6, None, None, 4, None) == 0    # nothing to do
+    assert lib.ua_qk_norm(C.byref(_dims(L, d_head=32)), p, p, 1e-6, p, p, 4, None) == 2
+
+
 def test_missing_library_fails_loudly(tmp_path):
     from kv_cache_pruning_amd import _lib as L
 
