@@ -94,7 +94,7 @@ R15 positions: prefill pos = next_pos + i; decode pos = next_pos.
 R16 logsig and log1mexp are evaluated stably (Maechler 2012 for log1mexp).
 R17 for parity the harness may hand this oracle the GPU-stored k~ bits
     (after checking they are within one bf16 ulp of its own rounding).
-R18 "Qwen3-style normalized queries and keys" (paperlayer.ai summary,
+R26 "Qwen3-style normalized queries and keys" (paperlayer.ai summary,
     Appendix E, ablations) = RMS normalisation over the head dimension with
     a learned per-dimension weight shared by the heads, x / sqrt(mean(x^2) +
     eps) * w with eps = 1e-6, applied to the projected q and k before O1-O2
@@ -259,7 +259,7 @@ def log1mexp(lam: np.ndarray) -> np.ndarray:
 
 
 def qk_rmsnorm(x: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:
-    """R18: x / sqrt(mean(x^2) + eps) * w along the last (head) axis."""
+    """R26: x / sqrt(mean(x^2) + eps) * w along the last (head) axis."""
     x = np.asarray(x, np.float64)
     ms = np.mean(x * x, axis=-1, keepdims=True)
     return x / np.sqrt(ms + eps) * np.asarray(w, np.float64)

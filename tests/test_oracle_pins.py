@@ -589,7 +589,7 @@ def test_overflow_sets_status_and_skips_append():
 
 
 # ---------------------------------------------------------------------------
-# R18: Qwen3-style normalized queries and keys (paperlayer.ai summary,
+# R26: Qwen3-style normalized queries and keys (paperlayer.ai summary,
 # Appendix E ablations) as an RMS normalisation over the head dimension
 # ---------------------------------------------------------------------------
 def test_qk_rmsnorm_worked_example():
