@@ -309,7 +309,9 @@ def main():
     ap.add_argument("--ring-bytes", type=float, default=1.0 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-prefill", action="store_true", help="skip the 1b-prefill figure")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the 1b-prefill figures")
+    ap.add_argument("--no-prefill-variants", action="store_true",
+                    help="skip the pruned and chunk-boundary prefill figures (profiles of the dense path)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB (a known-size reference for the HBM "
                          "byte counters of a rocprofv3 --pmc run)")
@@ -336,8 +338,9 @@ def main():
     out = bench_decode(args)
     if not args.no_prefill:
         out["prefill"] = bench_prefill(args)
-        out["prefill_pruned"] = bench_prefill_pruned(args)
-        out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
+        if not args.no_prefill_variants:
+            out["prefill_pruned"] = bench_prefill_pruned(args)
+            out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
     print(json.dumps(out), flush=True)
 
 
