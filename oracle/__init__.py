@@ -39,3 +39,5 @@ from .ua_ref import (  # noqa: F401
     dense_logbias,
     dense_attention,
 )
+
+from . import ua_grad  # noqa: F401,E402  (torch fp64 autograd reference for the backward pass)
