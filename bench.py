@@ -11,7 +11,9 @@ step time.  Inputs are resident in HBM before timing starts.
 
 The same line carries a "prefill" object: the 1B-shape chunked prefill
 (B = 2, 16 calls of 1024 tokens from an empty cache) in tokens/s with its
-transcendental and MFMA rooflines and the oracle's own rate.
+transcendental and MFMA rooflines and the oracle's own rate, and a
+"backward" object: the attention backward of one 4096-token training chunk
+per sequence (B = 2, 1B head shape) in tokens/s against the fp32 vector peak.
 
 Prints one JSON line.
 """
@@ -312,6 +314,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the 1b-prefill figures")
     ap.add_argument("--no-prefill-variants", action="store_true",
                     help="skip the pruned and chunk-boundary prefill figures (profiles of the dense path)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward figures")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB (a known-size reference for the HBM "
                          "byte counters of a rocprofv3 --pmc run)")
@@ -341,6 +344,8 @@ def main():
         if not args.no_prefill_variants:
             out["prefill_pruned"] = bench_prefill_pruned(args)
             out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
+    if not args.no_backward:
+        out["backward"] = bench_backward(args)
     print(json.dumps(out), flush=True)
 
 
@@ -550,6 +555,96 @@ def cpu_baseline_prefill(cfg, budget_s: float):
     return {"value": cfg.B * m / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{cfg.name} call 0, first {m} tokens of each of the B={cfg.B} sequences from an empty cache "
                       f"({dt:.1f} s, numpy fp64, one process; later tokens cost more)"}
+
+
+# ---------------------------------------------------------------------------
+# attention backward (one training chunk per sequence)
+# ---------------------------------------------------------------------------
+FP32_VECTOR_PEAK_TFS = 157.3
+
+
+def backward_work(B: int, N: int, H_q: int, H_kv: int, d: int):
+    """Algorithmic flops of the backward: per causal (token, key) pair and
+    query head, five length-d products (Q.K^T recomputed, dO.V^T, and the
+    dV, dQ, dK accumulations: 10d flops); per pair and KV head, the key
+    similarity and its two key gradients (6d)."""
+    pairs = B * H_kv * (N * (N + 1) // 2)
+    G = H_q // H_kv
+    return pairs * (G * 10 * d + 6 * d)
+
+
+def bench_backward(args, B: int = 2, N: int = 4096, H_q: int = 32, H_kv: int = 8, d: int = 64, passes: int = 3,
+                   warm: int = 1):
+    import torch
+
+    import kv_cache_pruning_amd as K
+    from ua_inputs import make_grad_inputs
+
+    g = make_grad_inputs(B, N, H_q, H_kv, d, True, 0)
+    dims = K.make_dims(B, H_q, H_kv, d, 2048, bf16=True)
+    dev = lambda a, t=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", t)
+    q, k, v = dev(g.q, torch.bfloat16), dev(g.k, torch.bfloat16), dev(g.v, torch.bfloat16)
+    lq, lk, lb, dO = dev(g.lq), dev(g.lk), dev(g.lb), dev(g.dO)
+    outs = [torch.empty(a.shape, dtype=torch.float32, device="cuda") for a in (g.q, g.k, g.v, g.lq, g.lk, g.lb)]
+    nb = K.ua_backward_workspace_bytes(dims, N)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for p in range(warm + passes):
+        torch.cuda.synchronize()
+        ev[0].record()
+        K.ua_attention_backward(dims, N, q, k, v, lq, lk, lb, dO, *outs, ws, nb)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if p >= warm:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    t = float(np.mean(ms))
+    flops = backward_work(B, N, H_q, H_kv, d)
+    tf = flops / (t * 1e-3) / 1e12
+    return {
+        "workload": f"UA attention backward, one training chunk per sequence: B={B} N={N} H_q={H_q} H_kv={H_kv} "
+                    f"d={d}, all three decay terms, bf16 q/k/v, fp32 gates and gradients",
+        "value": B * N / (t * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_call": t,
+        "passes": passes,
+        "roofline": {
+            "bound": "alu",
+            "achieved": tf,
+            "peak": FP32_VECTOR_PEAK_TFS,
+            "unit": "TFLOP/s (fp32 vector)",
+            "frac": tf / FP32_VECTOR_PEAK_TFS,
+            "traffic": None,
+            "kernel": "ua_attention_backward = 3 fills + bias, stats, kv, q, decay kernels (timed per call)",
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_backward(g, args.cpu_seconds / 2),
+    }
+
+
+def cpu_baseline_backward(g, budget_s: float):
+    """The fp64 oracle's backward, one (sequence, KV head) group at a time, until the budget is spent."""
+    import torch
+
+    import oracle as U
+
+    B, N, H_q, d = g.q.shape
+    H_kv = g.k.shape[2]
+    G = H_q // H_kv
+    t0 = time.time()
+    done = 0
+    while done < B * H_kv and time.time() - t0 < budget_s:
+        b, h = divmod(done, H_kv)
+        qs, hs = slice(h * G, (h + 1) * G), slice(h, h + 1)
+        U.ua_grad.attention_backward(g.q[b, :, qs].astype(np.float64), g.k[b, :, hs].astype(np.float64),
+                                     g.v[b, :, hs].astype(np.float64), g.lq[b, :, hs].astype(np.float64),
+                                     g.lk[b, :, hs].astype(np.float64), g.lb[b, :, hs].astype(np.float64),
+                                     g.dO[b, :, qs].astype(np.float64), 7, 1.0 / math.sqrt(d))
+        done += 1
+    dt = time.time() - t0
+    return {"value": B * N / (dt * B * H_kv / done), "unit": "tokens/s", "cores": torch.get_num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of the {B * H_kv} (sequence, KV head) groups ({dt:.1f} s, torch fp64 autograd on "
+                      f"the CPU), scaled to all groups"}
 
 
 if __name__ == "__main__":

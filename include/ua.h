@@ -260,6 +260,52 @@ ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const
                              size_t ws_bytes, void* stream);
 
 /*
+ * Backward pass of the decay-mask and attention kernels (paperlayer.ai summary,
+ * section 4.2 and Appendix C: training pairs a decay-mask kernel with a fused
+ * attention kernel; ai4snews Figure 1 caption: the three decays are combined
+ * by a geometric mean, taken to log space and accumulated causally).  For a
+ * training chunk of n_tokens tokens per sequence that starts from an empty
+ * cache, with o [B, n, H_q, d] the attention output before the output gate,
+ * ua_attention_backward turns dO = dL/do into the gradients of the
+ * attention's inputs:
+ *   q   [B, n, H_q, d]   rotated queries q~           (dims.dtype)
+ *   k   [B, n, H_kv, d]  stored keys k~ (normalised, rotated, cache-rounded)
+ *   v   [B, n, H_kv, d]  values                        (dims.dtype)
+ *   lq, lk, lb [B, n, H_kv] fp32  log-gates (query, key, similarity)
+ *   dO  [B, n, H_q, d] fp32
+ * Outputs (fp32, device, 16-byte aligned, written in full): dq, dk, dv of the
+ * shapes of q, k, v, and dlq, dlk, dlb of the gates'.  dk includes the
+ * similarity term's share.  The gradient of min(s^2, 1) is taken as 0 where
+ * the clamp holds.  The chain through RoPE, the key normalisation and the gate
+ * projections is elementwise or a plain GEMM and stays with the caller.  The
+ * workspace (ua_backward_workspace_bytes) holds the N x N bias and its
+ * gradient per segment; it needs no zero fill.
+ */
+typedef struct ua_grad_inputs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* lq;
+  const float* lk;
+  const float* lb;
+  const float* dO;
+} ua_grad_inputs;
+
+typedef struct ua_grads {
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dlq;
+  float* dlk;
+  float* dlb;
+} ua_grads;
+
+size_t ua_backward_workspace_bytes(const ua_dims* dims, int32_t n_tokens);
+
+ua_status ua_attention_backward(const ua_dims* dims, int32_t n_tokens, const ua_grad_inputs* in, const ua_grads* out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Qwen3-style normalised queries and keys (paperlayer.ai summary, Appendix E:
  * the UA ablation with normalised queries and keys), in place, before a
  * decode or prefill call takes q and k as its inputs.  Every head vector x of

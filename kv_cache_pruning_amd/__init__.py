@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     ua_prefill_pruned,
     ua_prefill_chunked,
     ua_qk_norm,
+    ua_backward_workspace_bytes,
+    ua_attention_backward,
     ua_compact,
     ua_status_string,
     ua_abi_version,

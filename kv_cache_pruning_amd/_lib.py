@@ -30,6 +30,8 @@ EXPORTS = (
     "ua_prefill_pruned",
     "ua_prefill_chunked",
     "ua_qk_norm",
+    "ua_backward_workspace_bytes",
+    "ua_attention_backward",
     "ua_compact",
     "ua_status_string",
     "ua_abi_version",
@@ -61,6 +63,14 @@ class ua_params(C.Structure):
 
 class ua_tokens(C.Structure):
     _fields_ = [("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p), ("x", C.c_void_p)]
+
+
+class ua_grad_inputs(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("q", "k", "v", "lq", "lk", "lb", "dO")]
+
+
+class ua_grads(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("dq", "dk", "dv", "dlq", "dlk", "dlb")]
 
 
 class ua_cache(C.Structure):
@@ -117,6 +127,11 @@ def load(path: Optional[str] = None) -> C.CDLL:
     lib.ua_qk_norm.argtypes = [P(ua_dims), C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_int32,
                                C.c_void_p]
     lib.ua_qk_norm.restype = C.c_int
+    lib.ua_backward_workspace_bytes.argtypes = [P(ua_dims), C.c_int32]
+    lib.ua_backward_workspace_bytes.restype = C.c_size_t
+    lib.ua_attention_backward.argtypes = [P(ua_dims), C.c_int32, P(ua_grad_inputs), P(ua_grads), C.c_void_p,
+                                          C.c_size_t, C.c_void_p]
+    lib.ua_attention_backward.restype = C.c_int
     lib.ua_compact.argtypes = [P(ua_dims), P(ua_cache), C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_compact.restype = C.c_int
     lib.ua_status_string.argtypes = [C.c_int32]
@@ -178,6 +193,18 @@ def ua_prefill_chunked(dims, params, cache, tokens, n_tokens: int, chunk: int, l
 def ua_qk_norm(dims, w_q, w_k, eps: float, q, k, n_tokens: int, stream=None) -> None:
     _check(load().ua_qk_norm(C.byref(dims), _ptr(w_q), _ptr(w_k), float(eps), _ptr(q), _ptr(k), int(n_tokens),
                              _stream(stream)), "ua_qk_norm")
+
+
+def ua_backward_workspace_bytes(dims, n_tokens: int) -> int:
+    return int(load().ua_backward_workspace_bytes(C.byref(dims), int(n_tokens)))
+
+
+def ua_attention_backward(dims, n_tokens: int, q, k, v, lq, lk, lb, dO, dq, dk, dv, dlq, dlk, dlb, ws, ws_bytes: int,
+                          stream=None) -> None:
+    gi = ua_grad_inputs(*(_ptr(t) for t in (q, k, v, lq, lk, lb, dO)))
+    go = ua_grads(*(_ptr(t) for t in (dq, dk, dv, dlq, dlk, dlb)))
+    _check(load().ua_attention_backward(C.byref(dims), int(n_tokens), C.byref(gi), C.byref(go), _ptr(ws), ws_bytes,
+                                        _stream(stream)), "ua_attention_backward")
 
 
 def ua_compact(dims, cache, log_p: float, kept_idx, ws, ws_bytes: int, stream=None) -> None:

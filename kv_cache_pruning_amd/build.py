@@ -18,7 +18,7 @@ OUT = os.path.join(HERE, "libua.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("UA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "workspace.hip", "decode.hip", "compact.hip", "prefill.hip", "qknorm.hip"]
+SOURCES = ["api.hip", "workspace.hip", "decode.hip", "compact.hip", "prefill.hip", "qknorm.hip", "backward.hip"]
 
 FLAGS = [
     "-O3",

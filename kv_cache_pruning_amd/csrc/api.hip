@@ -233,6 +233,35 @@ ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const
   return UA_OK;
 }
 
+size_t ua_backward_workspace_bytes(const ua_dims* dims, int32_t n_tokens) {
+  if (check_dims(dims) != UA_OK || n_tokens < 1) return 0;
+  return ua::backward_ws_bytes(dims->B, dims->H_q, dims->H_kv, n_tokens);
+}
+
+ua_status ua_attention_backward(const ua_dims* dims, int32_t n_tokens, const ua_grad_inputs* in, const ua_grads* out,
+                                void* ws, size_t ws_bytes, void* stream) {
+  ua_status s;
+  if ((s = check_dims(dims)) != UA_OK) return s;
+  if (n_tokens < 1 || !in || !out) return UA_ERR_INVALID_ARG;
+  const void* tin[3] = {in->q, in->k, in->v};
+  for (const void* p : tin)
+    if (!p || !aligned(p, 16)) return UA_ERR_INVALID_ARG;
+  const float* fin[4] = {in->lq, in->lk, in->lb, in->dO};
+  for (const float* p : fin)
+    if (!p || !aligned(p, 4)) return UA_ERR_INVALID_ARG;
+  float* fout[6] = {out->dq, out->dk, out->dv, out->dlq, out->dlk, out->dlb};
+  for (float* p : fout)
+    if (!p || !aligned(p, 16)) return UA_ERR_INVALID_ARG;
+  if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
+  if (ws_bytes < ua::backward_ws_bytes(dims->B, dims->H_q, dims->H_kv, n_tokens)) return UA_ERR_WORKSPACE;
+  const float scale = dims->sm_scale > 0.0f ? dims->sm_scale : 1.0f / sqrtf((float)dims->d_head);
+  const hipError_t e = ua::launch_backward(dims->B, dims->H_q, dims->H_kv, dims->d_head, n_tokens, dims->terms, scale,
+                                           dims->dtype == UA_BF16, in->q, in->k, in->v, in->lq, in->lk, in->lb, in->dO,
+                                           out->dq, out->dk, out->dv, out->dlq, out->dlk, out->dlb, ws,
+                                           reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? UA_OK : UA_ERR_HIP;
+}
+
 ua_status ua_qk_norm(const ua_dims* dims, const float* w_q, const float* w_k, float eps, void* q, void* k,
                      int32_t n_tokens, void* stream) {
   ua_status s;

@@ -101,6 +101,15 @@ hipError_t launch_compact(const LayerArgs& a, const Control& ctl, float tau, int
 
 // Prefill (its sync words live in its scratch and are cleared by the call)
 size_t prefill_ws_bytes(const LayerArgs& a, int n_tokens, int max_seg_cap);
+// Backward of the decay-mask and attention part for one training chunk per
+// sequence (token-major arrays, N tokens); the workspace holds Lambda and
+// dLambda (N x N fp32 per segment) and two [B, N, H_q] vectors.
+size_t backward_ws_bytes(int B, int Hq, int Hkv, int N);
+hipError_t launch_backward(int B, int Hq, int Hkv, int D, int N, int terms, float scale, bool bf16, const void* qt,
+                           const void* kt, const void* v, const float* lq, const float* lk, const float* lb,
+                           const float* dO, float* dq, float* dk, float* dv, float* dlq, float* dlk, float* dlb,
+                           void* ws, hipStream_t st);
+
 // In-place RMS normalisation of nq head rows of q and nk of k (d elements each).
 hipError_t launch_qk_norm(int d, bool bf16, void* q, const float* wq, int64_t nq, void* k, const float* wk, int64_t nk,
                           float eps, hipStream_t st);

@@ -55,6 +55,8 @@ def test_struct_layout_matches_header():
     assert C.sizeof(L.ua_cache) == 80
     assert C.sizeof(L.ua_params) == 40
     assert C.sizeof(L.ua_tokens) == 32
+    assert C.sizeof(L.ua_grad_inputs) == 56
+    assert C.sizeof(L.ua_grads) == 48
 
 
 def _dims(L, **kw):
@@ -188,6 +190,28 @@ def test_qk_norm_rejects():
     assert lib.ua_qk_norm(d, None, p, 1e-6, p, None, 4, None) == 1          # k weight without k
     assert lib.ua_qk_norm(d, None, None, 1e-6, None, None, 4, None) == 0    # nothing to do
     assert lib.ua_qk_norm(C.byref(_dims(L, d_head=32)), p, p, 1e-6, p, p, 4, None) == 2
+
+
+def test_attention_backward_rejects():
+    """Host-side checks of ua_attention_backward and its workspace size (no device work)."""
+    L = _lib()
+    lib = L.load()
+    p = _fake_ptr()
+    d = C.byref(_dims(L))
+    assert lib.ua_backward_workspace_bytes(d, 0) == 0
+    n = 100
+    want = 2 * 64 * n * n * 4 + 2 * 8 * n * 32 * 4  # two N x N fp32 per segment, two [B, N, H_q] vectors
+    assert lib.ua_backward_workspace_bytes(d, n) >= want
+    gi = L.ua_grad_inputs(*([p] * 7))
+    go = L.ua_grads(*([p] * 6))
+    ok = lib.ua_backward_workspace_bytes(d, n)
+    assert lib.ua_attention_backward(d, 0, C.byref(gi), C.byref(go), p, ok, None) == 1
+    assert lib.ua_attention_backward(d, n, C.byref(gi), C.byref(go), p, ok - 1, None) == 3
+    bad = L.ua_grad_inputs(*([p] * 6 + [None]))
+    assert lib.ua_attention_backward(d, n, C.byref(bad), C.byref(go), p, ok, None) == 1
+    bad_out = L.ua_grads(*([p] * 5 + [p + 4]))
+    assert lib.ua_attention_backward(d, n, C.byref(gi), C.byref(bad_out), p, ok, None) == 1
+    assert lib.ua_attention_backward(C.byref(_dims(L, d_head=32)), n, C.byref(gi), C.byref(go), p, ok, None) == 2
 
 
 def test_missing_library_fails_loudly(tmp_path):

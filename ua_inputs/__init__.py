@@ -16,4 +16,6 @@ from .gen import (  # noqa: F401
     make_step_inputs,
     make_layout,
     config,
+    GradInputs,
+    make_grad_inputs,
 )

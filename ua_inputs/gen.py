@@ -261,3 +261,54 @@ def make_step_inputs(cfg: LayerConfig, step: int, n: int = 1, seed: int = 0) -> 
     if cfg.bf16:
         q, k, v, x = bf16_exact(q), bf16_exact(k), bf16_exact(v), bf16_exact(x)
     return StepInputs(q=q, k=k, v=v, x=x)
+
+
+# ---------------------------------------------------------------------------
+# inputs of the attention backward (one training chunk per sequence)
+# ---------------------------------------------------------------------------
+@dataclass
+class GradInputs:
+    q: np.ndarray  # rotated queries [B, N, H_q, d]
+    k: np.ndarray  # stored keys [B, N, H_kv, d], unit norm
+    v: np.ndarray  # [B, N, H_kv, d]
+    lq: np.ndarray  # log-gates [B, N, H_kv]
+    lk: np.ndarray
+    lb: np.ndarray
+    dO: np.ndarray  # gradient of the attention output [B, N, H_q, d]
+
+    def astuple(self):
+        return self.q, self.k, self.v, self.lq, self.lk, self.lb, self.dO
+
+
+def make_grad_inputs(B: int, N: int, H_q: int, H_kv: int, d: int, bf16: bool = True, seed: int = 0,
+                     repeat_pairs: int = 0) -> GradInputs:
+    """Seeded inputs of the attention backward.
+
+    Queries, values and dO are N(0, 1); keys are Gaussian draws scaled to unit
+    norm (RoPE keeps a key's norm); each log-gate is log sigmoid(z) of a
+    pre-activation z ~ N(b_h, 32) (hidden 2048 against gate weights of variance
+    1/64) with a per-head bias b_h uniform in [-4, 0], the 1B-shape prefill's
+    gate statistics.  ``repeat_pairs`` copies that many keys onto later tokens
+    of the same head at 1.0625 times their norm (a repeated key's similarity
+    then exceeds 1).  In bf16 every q, k, v value is bf16-exact.
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    q = rng.normal(0, 1, (B, N, H_q, d)).astype(np.float32)
+    k = rng.normal(0, 1, (B, N, H_kv, d))
+    k = (k / np.linalg.norm(k, axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.normal(0, 1, (B, N, H_kv, d)).astype(np.float32)
+    if bf16:
+        q, k, v = bf16_exact(q), bf16_exact(k), bf16_exact(v)
+    for _ in range(repeat_pairs):
+        b, h = rng.integers(B), rng.integers(H_kv)
+        t, j = sorted(rng.choice(N, 2, replace=False))
+        k[b, t, h] = k[b, j, h] * np.float32(1.0625)
+        if bf16:
+            k[b, t, h] = bf16_exact(k[b, t, h])
+    bias = rng.uniform(-4, 0, (3, H_kv))
+    gates = []
+    for g in range(3):
+        z = rng.normal(0, math.sqrt(32.0), (B, N, H_kv)) + bias[g]
+        gates.append((-np.logaddexp(0.0, -z)).astype(np.float32))
+    dO = rng.normal(0, 1, (B, N, H_q, d)).astype(np.float32)
+    return GradInputs(q, k, v, gates[0], gates[1], gates[2], dO)
