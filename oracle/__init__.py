@@ -35,6 +35,7 @@ from .ua_ref import (  # noqa: F401
     preprocess_token,
     decode_step,
     prefill,
+    prefill_varlen,
     compact,
     dense_logbias,
     dense_attention,

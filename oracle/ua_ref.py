@@ -100,6 +100,10 @@ R26 "Qwen3-style normalized queries and keys" (paperlayer.ai summary,
     eps) * w with eps = 1e-6, applied to the projected q and k before O1-O2
     (so the key is still L2-normalised afterwards).  It is an optional step
     in front of the layer; the result is rounded to the token dtype.
+R31 variable-length prefill: sequence b appends its own n_b tokens (packed
+    rows cu[b] .. cu[b+1]); sequences share nothing (each KV segment belongs
+    to one sequence: paperlayer.ai section 4.2), so the call is R14's prefill
+    of each sequence on its own, n_b = 0 leaving it untouched.
 """
 
 from __future__ import annotations
@@ -433,6 +437,40 @@ def prefill(
         ko = None if k_override is None else k_override[:, i]
         yi, _ = decode_step(dims, params, cache, q[:, i], k[:, i], v[:, i], x[:, i], -math.inf, k_override=ko)
         y[:, i] = yi
+    return y
+
+
+def prefill_varlen(
+    dims: Dims,
+    params: Params,
+    cache: RefCache,
+    q: np.ndarray,
+    k: np.ndarray,
+    v: np.ndarray,
+    x: np.ndarray,
+    cu: Sequence[int],
+    k_override: Optional[np.ndarray] = None,
+) -> np.ndarray:
+    """Variable-length prefill (R31): packed rows cu[b] .. cu[b+1] of q [T, H_q, d],
+    k/v [T, H_kv, d], x [T, D] are sequence b's tokens; returns y [T, H_q, d]."""
+    T = q.shape[0]
+    y = np.zeros((T, dims.H_q, dims.d))
+    H = dims.H_kv
+    for b in range(dims.B):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        if r1 <= r0:
+            continue
+        segs = slice(b * H, (b + 1) * H)
+        one = Dims(B=1, H_q=dims.H_q, H_kv=H, d=dims.d, D=dims.D, r=dims.r, terms=dims.terms,
+                   rope_base=dims.rope_base, sm_scale=dims.sm_scale, cache_bf16=dims.cache_bf16)
+        sub = RefCache(K=cache.K[segs], V=cache.V[segs], lam=cache.lam[segs], lk=cache.lk[segs],
+                       next_pos=cache.next_pos[b : b + 1].copy(), cap=cache.cap[segs].copy())
+        ko = None if k_override is None else k_override[None, r0:r1]
+        y[r0:r1] = prefill(one, params, sub, q[None, r0:r1], k[None, r0:r1], v[None, r0:r1], x[None, r0:r1],
+                           k_override=ko)[0]
+        cache.K[segs], cache.V[segs], cache.lam[segs], cache.lk[segs] = sub.K, sub.V, sub.lam, sub.lk
+        cache.next_pos[b] = sub.next_pos[0]
+        cache.status |= sub.status
     return y
 
 

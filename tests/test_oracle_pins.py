@@ -621,3 +621,59 @@ def test_qk_rmsnorm_invariants():
     x2[:, 1] *= 100.0
     y2 = U.qk_rmsnorm(x2, one, eps=0.0)
     assert np.allclose(y2[:, 0], y[:, 0]) and np.allclose(y2[:, 2], y[:, 2])
+
+
+def test_P_varlen_prefill_is_each_sequence_on_its_own():
+    """R31 (per-sequence, per-KV-head caches: paperlayer.ai section 4.2): a packed
+    variable-length prefill gives, for each sequence, O5-O7 over that sequence's
+    own tokens alone (brute force: the dense bias and softmax written out), leaves
+    an empty sequence untouched, and advances each position by its own count."""
+    dims = _dims(B=3, H_q=4, H_kv=2, d=8, D=5)
+    rng = RNG(31)
+    p = _params(dims, rng, gate_scale=2.0)  # gamma = 1: y is the attention output
+    lens = [5, 0, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q = rng.normal(0, 1, (T, dims.H_q, dims.d))
+    k = rng.normal(0, 1, (T, dims.H_kv, dims.d))
+    v = rng.normal(0, 1, (T, dims.H_kv, dims.d))
+    x = rng.normal(0, 1, (T, dims.D))
+    cache = _fresh(dims)
+    cache.next_pos[:] = [3, 7, 0]
+    y = U.prefill_varlen(dims, p, cache, q, k, v, x, cu)
+    G = dims.G
+    for b, n in enumerate(lens):
+        r = slice(cu[b], cu[b + 1])
+        one = _dims(B=1, H_q=4, H_kv=2, d=8, D=5)
+        pos0 = [3, 7, 0][b]
+        assert cache.next_pos[b] == pos0 + n
+        for h in range(dims.H_kv):
+            assert cache.lam[b * dims.H_kv + h].shape[0] == n
+        if n == 0:
+            continue
+        qt, kt = _preprocessed(one, p, q[None, r], k[None, r], x[None, r], pos0=pos0)
+        z = x[r] @ p.W_dec + p.b_dec
+        for h in range(dims.H_kv):
+            lq, lk, lb = (U.log_sigmoid(z[:, c * dims.H_kv + h]) for c in range(3))
+            Lam = U.dense_logbias(dims.terms, kt[:, h], lq, lk, lb)
+            np.testing.assert_allclose(cache.lam[b * dims.H_kv + h], Lam[n - 1], rtol=1e-12, atol=1e-13)
+            for i in range(n):
+                e = dims.scale * (kt[: i + 1, h] @ qt[i, h * G:(h + 1) * G].T).T + Lam[i, : i + 1]
+                w = np.exp(e - e.max(axis=1, keepdims=True))
+                o = (w / w.sum(axis=1, keepdims=True)) @ v[r][: i + 1, h]
+                np.testing.assert_allclose(y[cu[b] + i, h * G:(h + 1) * G], o, rtol=1e-11, atol=1e-12)
+
+
+def test_P_varlen_equal_lengths_is_batched_prefill():
+    dims = _dims(B=2, H_q=4, H_kv=2, d=8)
+    rng = RNG(32)
+    p = _params(dims, rng, gamma_one=False)
+    n = 6
+    q, k, v, x = _tokens(dims, n, rng)
+    c1, c2 = _fresh(dims), _fresh(dims)
+    y1 = U.prefill(dims, p, c1, q, k, v, x)
+    flat = lambda a: a.reshape((-1,) + a.shape[2:])
+    y2 = U.prefill_varlen(dims, p, c2, flat(q), flat(k), flat(v), flat(x), [0, n, 2 * n])
+    np.testing.assert_array_equal(y2.reshape(y1.shape), y1)
+    for s in range(4):
+        np.testing.assert_array_equal(c2.lam[s], c1.lam[s])
