@@ -344,6 +344,7 @@ def main():
         if not args.no_prefill_variants:
             out["prefill_pruned"] = bench_prefill_pruned(args)
             out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
+            out["prefill_varlen"] = bench_prefill_varlen(args)
     if not args.no_backward:
         out["backward"] = bench_backward(args)
     print(json.dumps(out), flush=True)
@@ -521,6 +522,76 @@ def bench_prefill_pruned(args, chunked: bool = False, name: str = "1b-prefill", 
         "passes": passes,
         "kept_entries_per_segment": float(kept.mean()),
         "call_ms": [round(float(x), 4) for x in call_ms] if not chunked else None,
+        "status": st,
+        "roofline": {
+            "bound": "alu",
+            "achieved": tts,
+            "peak": TRANS_PEAK_TS,
+            "unit": "T transcendentals/s",
+            "frac": tts / TRANS_PEAK_TS,
+            "pairs": pairs,
+            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFS},
+        },
+    }
+
+
+def bench_prefill_varlen(args, B: int = 8, passes: int = 3, warm: int = 1, seed: int = 7):
+    """One ua_prefill_varlen call of B packed sequences with lengths uniform in
+    [128, 2048] (seeded), 1B head shape, from an empty cache.  The roofline
+    counts each sequence's own causal pairs."""
+    import torch
+
+    from tests.harness import device_layer
+    from ua_inputs import config, make_cache, make_step_inputs, make_weights
+
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(128, 2049, B)]
+    nmax = max(lens)
+    cfg = config("1b-prefill", B=B, n_total=nmax, chunk=nmax)
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    layer = device_layer(cfg, w, c, max_tokens=nmax, y_bf16=True)
+    inp = make_step_inputs(cfg, 0, nmax, 0)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    pack = lambda a: torch.from_numpy(np.concatenate([a[b, : lens[b]] for b in range(B)], axis=0)).to(
+        "cuda", torch.bfloat16)
+    toks = [pack(a) for a in (inp.q, inp.k, inp.v, inp.x)]
+    cu_d = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    y = torch.empty((T, cfg.H_q, cfg.d), dtype=torch.bfloat16, device="cuda")
+    import kv_cache_pruning_amd as K
+
+    _, tok = layer._tokens(*toks)
+    seg_len0 = layer.cache.seg_len.clone()
+    pos0 = layer.cache.next_pos.clone()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ms = []
+    for p in range(warm + passes):
+        layer.cache.seg_len.copy_(seg_len0)
+        layer.cache.next_pos.copy_(pos0)
+        torch.cuda.synchronize()
+        ev[0].record()
+        K.ua_prefill_varlen(layer.dims, layer.w.params, layer.cache.struct, tok, cu_d, T, nmax, y, layer.ws.ptr,
+                            layer.ws.nbytes)
+        ev[1].record()
+        torch.cuda.synchronize()
+        if p >= warm:
+            ms.append(ev[0].elapsed_time(ev[1]))
+    st = int(layer.cache.status.item())
+    t = float(np.mean(ms))
+    G = cfg.H_q // cfg.H_kv
+    pairs = float(sum(n * (n + 1) // 2 for n in lens) * cfg.H_kv)
+    flops, trans = pairs * (G * 4 * cfg.d + 2 * cfg.d), pairs * (G + 3)
+    tts = trans / (t * 1e-3) / 1e12
+    tflops = flops / (t * 1e-3) / 1e12
+    return {
+        "workload": f"ua_prefill_varlen: {B} packed sequences of {lens} tokens (1B heads H_q={cfg.H_q} "
+                    f"H_kv={cfg.H_kv} d={cfg.d}) from an empty cache, bf16 storage, y bf16",
+        "value": T / (t * 1e-3),
+        "unit": "tokens/s",
+        "ms_per_call": t,
+        "passes": passes,
         "status": st,
         "roofline": {
             "bound": "alu",

@@ -260,6 +260,26 @@ ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const
                              size_t ws_bytes, void* stream);
 
 /*
+ * Variable-length prefill: ua_prefill for a batch whose sequences append
+ * different numbers of tokens (paperlayer.ai section 4.2: the cache is kept
+ * per sequence and KV head, so sequences are independent).  Sequence b
+ * appends n_b = cu_seqlens[b + 1] - cu_seqlens[b] tokens; they are packed:
+ * token t of sequence b is row cu_seqlens[b] + t of q [total_tokens, H_q, d],
+ * k and v [total_tokens, H_kv, d], x [total_tokens, D] and y
+ * [total_tokens, H_q, d].  cu_seqlens is a device int32 array [B + 1],
+ * nondecreasing from 0 to total_tokens, with every n_b <= max_tokens (n_b = 0
+ * is allowed).  The device reads it; the host checks only its pointer.  The
+ * kernels clamp every row they touch into [0, total_tokens), so a malformed
+ * array gives wrong results but no access outside the arrays.  Everything
+ * else is as for ua_prefill with n_tokens = max_tokens, including the
+ * workspace size; segments of sequence b need room for n_b entries, and
+ * next_pos[b] advances by n_b.
+ */
+ua_status ua_prefill_varlen(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                            const ua_tokens* in, const int32_t* cu_seqlens, int32_t total_tokens, int32_t max_tokens,
+                            void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Backward pass of the decay-mask and attention kernels (paperlayer.ai summary,
  * section 4.2 and Appendix C: training pairs a decay-mask kernel with a fused
  * attention kernel; ai4snews Figure 1 caption: the three decays are combined

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     ua_prefill,
     ua_prefill_pruned,
     ua_prefill_chunked,
+    ua_prefill_varlen,
     ua_qk_norm,
     ua_backward_workspace_bytes,
     ua_attention_backward,

@@ -29,6 +29,7 @@ EXPORTS = (
     "ua_prefill",
     "ua_prefill_pruned",
     "ua_prefill_chunked",
+    "ua_prefill_varlen",
     "ua_qk_norm",
     "ua_backward_workspace_bytes",
     "ua_attention_backward",
@@ -124,6 +125,9 @@ def load(path: Optional[str] = None) -> C.CDLL:
     lib.ua_prefill_chunked.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_int32,
                                        C.c_float, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_prefill_chunked.restype = C.c_int
+    lib.ua_prefill_varlen.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_void_p, C.c_int32,
+                                      C.c_int32, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.ua_prefill_varlen.restype = C.c_int
     lib.ua_qk_norm.argtypes = [P(ua_dims), C.c_void_p, C.c_void_p, C.c_float, C.c_void_p, C.c_void_p, C.c_int32,
                                C.c_void_p]
     lib.ua_qk_norm.restype = C.c_int
@@ -181,6 +185,13 @@ def ua_prefill_pruned(dims, params, cache, tokens, n_tokens: int, log_p: float, 
     _check(load().ua_prefill_pruned(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), int(n_tokens),
                                     float(log_p), _ptr(y), _ptr(kept_idx), _ptr(ws), ws_bytes, _stream(stream)),
            "ua_prefill_pruned")
+
+
+def ua_prefill_varlen(dims, params, cache, tokens, cu_seqlens, total_tokens: int, max_tokens: int, y, ws,
+                      ws_bytes: int, stream=None) -> None:
+    _check(load().ua_prefill_varlen(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens), _ptr(cu_seqlens),
+                                    int(total_tokens), int(max_tokens), _ptr(y), _ptr(ws), ws_bytes, _stream(stream)),
+           "ua_prefill_varlen")
 
 
 def ua_prefill_chunked(dims, params, cache, tokens, n_tokens: int, chunk: int, log_p: float, y, ws, ws_bytes: int,

@@ -233,6 +233,20 @@ ua_status ua_prefill_chunked(const ua_dims* dims, const ua_params* params, const
   return UA_OK;
 }
 
+ua_status ua_prefill_varlen(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                            const ua_tokens* in, const int32_t* cu_seqlens, int32_t total_tokens, int32_t max_tokens,
+                            void* y, void* ws, size_t ws_bytes, void* stream) {
+  LayerArgs a;
+  ua::Control ctl;
+  char* scratch;
+  size_t sb;
+  ua_status s;
+  if (max_tokens < 1 || total_tokens < 1 || !cu_seqlens || !aligned(cu_seqlens, 4)) return UA_ERR_INVALID_ARG;
+  if ((s = prefill_setup(dims, params, cache, in, y, ws, ws_bytes, &a, &ctl, &scratch, &sb)) != UA_OK) return s;
+  return prefill_status(ua::launch_prefill(a, ctl, max_tokens, 0, scratch, sb, reinterpret_cast<hipStream_t>(stream),
+                                           -__builtin_huge_valf(), 0, 0, cu_seqlens, total_tokens));
+}
+
 size_t ua_backward_workspace_bytes(const ua_dims* dims, int32_t n_tokens) {
   if (check_dims(dims) != UA_OK || n_tokens < 1) return 0;
   return ua::backward_ws_bytes(dims->B, dims->H_q, dims->H_kv, n_tokens);

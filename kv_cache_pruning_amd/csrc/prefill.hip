@@ -77,12 +77,38 @@ struct PrefillWs {
   int n, nrb, cp, rp;
   int ld, t0;      // token (b, t) of the call is row b * ld + t0 + t of q, k, v, x and y
   float tau2;      // attention mask threshold in log2 units (log p * log2 e), -inf for none
+  const int* cu;   // variable-length call: [B + 1] packed row offsets (null: every sequence has n tokens)
+  int total;       // variable-length call: rows of the packed q, k, v, x and y
 };
 
-// Row of q/k/v/x/y that holds call token tk = b * n + t.
+// Tokens sequence b appends in this call (at most n).
+__device__ __forceinline__ int seq_n(const PrefillWs& w, int b) {
+  if (!w.cu) return w.n;
+  return min(max(w.cu[b + 1] - w.cu[b], 0), w.n);
+}
+
+// The same for kernels instantiated per call kind: a fixed-length call keeps
+// no offsets live (the attention kernels run at the edge of their registers).
+template <bool VARLEN>
+__device__ __forceinline__ int seq_n_k(const PrefillWs& w, int b) {
+  if constexpr (VARLEN) return min(max(w.cu[b + 1] - w.cu[b], 0), w.n);
+  else return w.n;
+}
+
+// Row of q/k/v/x/y that holds call token tk = b * n + t.  In a
+// variable-length call, row cu[b] + t, clamped into the packed arrays (rows of
+// tokens past the sequence's own count are read, never used, never written).
 __device__ __forceinline__ int64_t io_row(const PrefillWs& w, int tk) {
   const int b = tk / w.n;
+  if (w.cu) return min(max(w.cu[b] + (tk - b * w.n), 0), w.total - 1);
   return (int64_t)b * w.ld + w.t0 + (tk - b * w.n);
+}
+
+template <bool VARLEN>
+__device__ __forceinline__ int64_t io_row_k(const PrefillWs& w, int tk) {
+  const int b = tk / w.n;
+  if constexpr (VARLEN) return min(max(w.cu[b] + (tk - b * w.n), 0), w.total - 1);
+  else return (int64_t)b * w.ld + w.t0 + (tk - b * w.n);
 }
 
 static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w) {
@@ -293,8 +319,9 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
     w.gl[2 * ((int64_t)tk * Hkv + h) + 0] = lq;
     w.gl[2 * ((int64_t)tk * Hkv + h) + 1] = lb;
     const int len0 = a.seg_len[s];
-    if ((int64_t)len0 + n <= a.seg_cap[s]) {
-      a.lk[a.seg_off[s] + len0 + t] = lkk;
+    const int nq = seq_n(w, b);
+    if ((int64_t)len0 + nq <= a.seg_cap[s]) {
+      if (t < nq) a.lk[a.seg_off[s] + len0 + t] = lkk;
     } else if (t == 0) {
       atomicOr(a.status, 1);
     }
@@ -360,7 +387,8 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
       if (tk >= NT) continue;
       const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
       const int len0 = a.seg_len[s];
-      if ((int64_t)len0 + n > a.seg_cap[s]) continue;
+      const int nq = seq_n(w, b);
+      if (t >= nq || (int64_t)len0 + nq > a.seg_cap[s]) continue;
       const int64_t base = (io_row(w, tk) * Hkv + h) * D;
       u32x4 raw[CH];
 #pragma unroll
@@ -416,7 +444,8 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
         if (e >= nv || tk >= NT) continue;
         const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
         const int len0 = a.seg_len[s];
-        if ((int64_t)len0 + n > a.seg_cap[s]) continue;
+        const int nq = seq_n(w, b);
+        if (t >= nq || (int64_t)len0 + nq > a.seg_cap[s]) continue;
         *reinterpret_cast<u32x4*>(Vc + (a.seg_off[s] + len0 + t) * D + 8 * c) = vv[u];
       }
     }
@@ -486,7 +515,28 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & 32) | (((r >> 2) & 3) << 3) | ((r >> 4) << 2) | (r & 3);
 }
 
-template <int D, int HG>
+// End of an attention workgroup: after every workgroup has counted itself
+// in, the last one advances lengths and positions (and with SEQ publishes the
+// call's number, which tags the carry words).
+template <bool VARLEN, int NT, bool SEQ>
+__device__ __forceinline__ void prefill_commit(const LayerArgs& a, const PrefillWs& w, int* s_last, uint32_t seq) {
+  const int tid = threadIdx.x;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) *s_last = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (*s_last) {
+    if (SEQ && tid == 0) sti_coh_p(&w.glob[kGlobSeq], (int)seq);
+    const int S = a.B * a.H_kv;
+    for (int s2 = tid; s2 < S; s2 += NT) {
+      const int l = a.seg_len[s2], nq = seq_n_k<VARLEN>(w, s2 / a.H_kv);
+      if ((int64_t)l + nq <= a.seg_cap[s2]) a.seg_len[s2] = l + nq;
+    }
+    for (int b2 = tid; b2 < a.B; b2 += NT) a.next_pos[b2] += seq_n_k<VARLEN>(w, b2);
+  }
+}
+
+template <int D, int HG, bool VARLEN>
 __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, PrefillWs w) {
   constexpr int KC = D / 32;                          // k steps of a head-dim dot product
   constexpr int DT = D / 16;                          // 16-wide output tiles per head
@@ -525,18 +575,26 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
   const int b = s / Hkv, h = s - b * Hkv;
   const int len0 = a.seg_len[s];
   const int64_t off = a.seg_off[s];
-  const bool room = (int64_t)len0 + n <= a.seg_cap[s];
+  const int nseq = seq_n_k<VARLEN>(w, b);         // this sequence's tokens
+  const int nrbs = (nseq + kPRows - 1) / kPRows;  // and its token blocks
+  if constexpr (VARLEN) {
+    if (I >= nrbs) {  // past the sequence's tokens: no work, and no chain waits on this block
+      prefill_commit<VARLEN, kPThreads, false>(a, w, &s_id, 0u);
+      return;
+    }
+  }
+  const bool room = (int64_t)len0 + nseq <= a.seg_cap[s];
   const int row_lo = I * kPRows + tw * 16;  // first token of this wave
   const int tq = row_lo + c16;              // this lane's token (score column)
-  const bool row_ok = tq < n;
-  const int tqc = min(tq, n - 1);
+  const bool row_ok = tq < nseq;
+  const int tqc = min(tq, max(nseq, 1) - 1);
   const int64_t tok = (int64_t)b * n + tqc;
-  const int64_t ytok = (int64_t)b * w.ld + w.t0 + tqc;  // the token's row of y
+  const int64_t ytok = io_row_k<VARLEN>(w, (int)tok);  // the token's row of y
   const int a0 = h * HG;
 
   if (room) {
-    const int nkeys = len0 + n;
-    const int kend = len0 + min(n, I * kPRows + kPRows);
+    const int nkeys = len0 + nseq;
+    const int kend = len0 + min(nseq, I * kPRows + kPRows);
     const int nJ = (kend + kPKeys - 1) / kPKeys;
     const int64_t TS = a.total_slots;
     const PairCoef pc = pair_coef(a.terms);
@@ -551,7 +609,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
     // the block's rotated queries to LDS: [token][head][dim], rows of tokens past n clamped
     for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreads) {
       const int tt = q / (HG * (D / 8)), rest = q - tt * (HG * (D / 8));
-      const int64_t tk = (int64_t)b * n + min(I * kPRows + tt, n - 1);
+      const int64_t tk = (int64_t)b * n + min(I * kPRows + tt, nseq - 1);
       *reinterpret_cast<u32x4*>(&s_q[tt * QS + rest * 8]) =
           *reinterpret_cast<const u32x4*>(w.qbf + (tk * Hq + a0) * D + rest * 8);
     }
@@ -666,7 +724,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
           kf[t][kc] =
               *reinterpret_cast<const u32x4*>(&s_k[cb][(32 * hp + 16 * t + c16) * KS + 32 * kc + 8 * g]);
       // some element of this wave's tile is masked (causal edge or tokens past n)
-      const bool edge = (j0 + 32 * hp + 31 >= len0 + row_lo) || (row_lo + 15 >= n);
+      const bool edge = (j0 + 32 * hp + 31 >= len0 + row_lo) || (row_lo + 15 >= nseq);
 
       // ---- pair terms, scanned over this wave's 16 tokens.  The enabled terms
       // and the causal edge are uniform per block, so each combination is a
@@ -791,7 +849,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
         const int jg = j0 + lane;
         const float cn =
             s_car[cb][lane] + s_tot[cb][0][lane] + s_tot[cb][1][lane] + s_tot[cb][2][lane] + s_tot[cb][3][lane];
-        if (I + 1 < nrb) {
+        if (I + 1 < nrbs) {
           if (jg < nkeys) stf_coh_p(&w.carry[(int64_t)I * TS + off + jg], cn);
           __builtin_amdgcn_s_waitcnt(0);
           if (lane == 0) sti_coh_p(&w.sync[2 + s * nrb + I], J + 1);
@@ -936,18 +994,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
       }
   }
 
-  // ---- the last workgroup advances lengths and positions
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) s_id = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (s_id) {
-    for (int s2 = tid; s2 < S; s2 += kPThreads) {
-      const int l = a.seg_len[s2];
-      if ((int64_t)l + n <= a.seg_cap[s2]) a.seg_len[s2] = l + n;
-    }
-    for (int b2 = tid; b2 < a.B; b2 += kPThreads) a.next_pos[b2] += n;
-  }
+  prefill_commit<VARLEN, kPThreads, false>(a, w, &s_id, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -985,7 +1032,7 @@ __device__ __forceinline__ uint32_t carry_tag(uint32_t seq) {
   return 0x7F800000u | ((seq - 1u) % 0x3FFFFFu + 1u);  // exponent all ones, quiet bit clear, payload != 0
 }
 
-template <int HG, bool MASKED>
+template <int HG, bool MASKED, bool VARLEN>
 __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs a, PrefillWs w) {
   constexpr int D = 64;
   constexpr int KC = D / 32;                // k steps of a head-dim dot product
@@ -1031,13 +1078,21 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   const int b = s / Hkv, h = s - b * Hkv;
   const int len0 = a.seg_len[s];
   const int64_t off = a.seg_off[s];
-  const bool room = (int64_t)len0 + n <= a.seg_cap[s];
+  const int nseq = seq_n_k<VARLEN>(w, b);         // this sequence's tokens
+  const int nrbs = (nseq + kPRows - 1) / kPRows;  // and its token blocks
+  if constexpr (VARLEN) {
+    if (I >= nrbs) {  // past the sequence's tokens: no work, and no chain waits on this block
+      prefill_commit<VARLEN, kPThreadsWS, true>(a, w, &s_id, s_seq);
+      return;
+    }
+  }
+  const bool room = (int64_t)len0 + nseq <= a.seg_cap[s];
   const int a0 = h * HG;
   const int t0 = I * kPRows;  // first token of the block
 
   if (room) {
-    const int nkeys = len0 + n;
-    const int kend = len0 + min(n, t0 + kPRows);
+    const int nkeys = len0 + nseq;
+    const int kend = len0 + min(nseq, t0 + kPRows);
     const int nJ = (kend + kPKeys - 1) / kPKeys;
     const int64_t TS = a.total_slots;
     const PairCoef pc = pair_coef(a.terms);
@@ -1049,7 +1104,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
 
     for (int q = tid; q < kPRows * HG * (D / 8); q += kPThreadsWS) {
       const int tt = q / (HG * (D / 8)), rest = q - tt * (HG * (D / 8));
-      const int64_t tk = (int64_t)b * n + min(t0 + tt, n - 1);
+      const int64_t tk = (int64_t)b * n + min(t0 + tt, nseq - 1);
       *reinterpret_cast<u32x4*>(&s_q[tt * QS + rest * 8]) =
           *reinterpret_cast<const u32x4*>(w.qbf + (tk * Hq + a0) * D + rest * 8);
     }
@@ -1113,7 +1168,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     auto load_token_side = [&]() {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const int tq = min(t0 + 16 * tt + c16, n - 1);
+        const int tq = min(t0 + 16 * tt + c16, nseq - 1);
         const int64_t tok = (int64_t)b * n + tq;
         const float lq = w.gl[2 * (tok * Hkv + h) + 0];
         const float lb = w.gl[2 * (tok * Hkv + h) + 1];
@@ -1151,7 +1206,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         kf[kc] = *reinterpret_cast<const u32x4*>(&s_k[kb][(16 * p + c16) * KS + 32 * kc + 8 * g]);
       const float4 lk4 = *reinterpret_cast<const float4*>(&s_lk[kb][16 * p + 4 * g]);
       const float lkv[4] = {lk4.x, lk4.y, lk4.z, lk4.w};
-      const bool edge = (j0 + 16 * p + 15 >= len0 + t0) || (t0 + kPRows > n);
+      const bool edge = (j0 + 16 * p + 15 >= len0 + t0) || (t0 + kPRows > nseq);
       // Pair terms, step-major over the 16 (key, token) elements of the lane so
       // that the transcendental chains of different elements interleave.  The
       // series form of 1 - 2^L is only needed where L is near 0; a wave takes
@@ -1209,7 +1264,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
           for (int tt = 0; tt < 4; ++tt) {
             const int tq = t0 + 16 * tt + c16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lam[tt][i] = (tq < n && jk + i < len0 + tq) ? lam[tt][i] : 0.0f;
+            for (int i = 0; i < 4; ++i) lam[tt][i] = (tq < nseq && jk + i < len0 + tq) ? lam[tt][i] : 0.0f;
           }
         }
       };
@@ -1287,13 +1342,13 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bv[i] = lam[tt][i] + car[i];
-          if (edge) bv[i] = (tq < n && jk + i <= len0 + tq) ? bv[i] : kNegInf;
+          if (edge) bv[i] = (tq < nseq && jk + i <= len0 + tq) ? bv[i] : kNegInf;
           if constexpr (MASKED) bv[i] = (bv[i] >= w.tau2) ? bv[i] : kNegInf;
         }
         *reinterpret_cast<float4*>(&ob[((p * 4 + tt) * 64 + lane) * 4]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
       }
       // carry out to the next token block, or the final bias of the call
-      if (I + 1 < nrb) {
+      if (I + 1 < nrbs) {
         if (c16 == 0) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -1336,9 +1391,8 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     } else {
       // ---- softmax waves: tokens 16 p + c16, query heads hf*HH .. of the group
       const int tq = t0 + 16 * p + c16;
-      const bool row_ok = tq < n;
-      const int64_t tok = (int64_t)b * n + min(tq, n - 1);
-      const int64_t ytok = (int64_t)b * w.ld + w.t0 + min(tq, n - 1);  // the token's row of y
+      const bool row_ok = tq < nseq;
+      const int64_t tok = (int64_t)b * n + min(tq, nseq - 1);
       const float inv_cs = 1.0f / cs;
       f16x8 ones;
 #pragma unroll
@@ -1470,6 +1524,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         else softmax_loop(std::false_type{});
 
         // ---- epilogue: normalise, gate, store
+        const int64_t ytok = io_row_k<VARLEN>(w, (int)tok);  // the token's row of y (not live in the loop)
 #pragma unroll
         for (int hh = 0; hh < NH; ++hh) {
           const float L = __shfl(Lt[hh][0], c16, 64);
@@ -1498,8 +1553,8 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   } else if (!bias_wave && hf == 0) {
     // the segment has no room for the call: its outputs are zero
     const int tq = t0 + 16 * p + c16;
-    if (tq < n) {
-      const int64_t ytok = (int64_t)b * w.ld + w.t0 + tq;
+    if (tq < nseq) {
+      const int64_t ytok = io_row_k<VARLEN>(w, b * n + tq);
 #pragma unroll
       for (int hh = 0; hh < HG; ++hh)
 #pragma unroll
@@ -1514,19 +1569,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
     }
   }
 
-  // ---- the last workgroup advances lengths and positions
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0) s_id = (addi_coh_p(&w.sync[1], 1) == (int)gridDim.x - 1) ? 1 : 0;
-  __syncthreads();
-  if (s_id) {
-    if (tid == 0) sti_coh_p(&w.glob[kGlobSeq], (int)s_seq);
-    for (int s2 = tid; s2 < S; s2 += kPThreadsWS) {
-      const int l = a.seg_len[s2];
-      if ((int64_t)l + n <= a.seg_cap[s2]) a.seg_len[s2] = l + n;
-    }
-    for (int b2 = tid; b2 < a.B; b2 += kPThreadsWS) a.next_pos[b2] += n;
-  }
+  prefill_commit<VARLEN, kPThreadsWS, true>(a, w, &s_id, s_seq);
 }
 
 // ---------------------------------------------------------------------------
@@ -1534,20 +1577,28 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
 // ---------------------------------------------------------------------------
 template <int D, int HG>
 static void launch_attn(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((prefill_attn_kernel<D, HG>), dim3(grid), dim3(kPThreads), 0, st, a, w);
+  if (w.cu) {
+    hipLaunchKernelGGL((prefill_attn_kernel<D, HG, true>), dim3(grid), dim3(kPThreads), 0, st, a, w);
+  } else {
+    hipLaunchKernelGGL((prefill_attn_kernel<D, HG, false>), dim3(grid), dim3(kPThreads), 0, st, a, w);
+  }
 }
 
+// Instances: dense, masked (pruned prefill) and variable-length (dense).
 template <int HG>
 static void launch_attn_ws(const LayerArgs& a, const PrefillWs& w, int grid, hipStream_t st) {
-  if (w.tau2 > kNegInf) {
-    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, true>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
+  if (w.cu) {
+    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, false, true>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
+  } else if (w.tau2 > kNegInf) {
+    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, true, false>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
   } else {
-    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, false>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
+    hipLaunchKernelGGL((prefill_attn_ws_kernel<HG, false, false>), dim3(grid), dim3(kPThreadsWS), 0, st, a, w);
   }
 }
 
 hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max_seg_cap, void* scratch,
-                          size_t scratch_bytes, hipStream_t st, float log_p, int ld, int t0) {
+                          size_t scratch_bytes, hipStream_t st, float log_p, int ld, int t0, const int* cu,
+                          int total) {
   if (!a.bf16) return hipErrorNotSupported;  // the matrix-core path is written for bf16 caches
   const int G = a.H_q / a.H_kv;
   if (a.d == 128 && G == 8) return hipErrorNotSupported;
@@ -1557,6 +1608,8 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max
   w.glob = ctl.glob;
   w.ld = ld;
   w.t0 = t0;
+  w.cu = cu;
+  w.total = total;
   w.tau2 = (log_p == -__builtin_huge_valf()) ? -__builtin_huge_valf() : log_p * kLog2e;
   const int S = a.B * a.H_kv;
   const int nsync = 2 + S * w.nrb;

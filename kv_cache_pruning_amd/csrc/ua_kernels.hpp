@@ -117,8 +117,12 @@ hipError_t launch_qk_norm(int d, bool bf16, void* q, const float* wq, int64_t nq
 // Prefill of n_tokens per sequence.  Token t of sequence b is row b * ld + t0 + t
 // of q, k, v, x and y; log_p (-inf: none) keeps entries whose bias has fallen
 // below it out of the softmax.
+// cu (device, [B + 1], or null) makes the call variable-length: sequence b
+// appends cu[b + 1] - cu[b] <= n_tokens tokens, packed at rows cu[b] .. of the
+// total rows of q, k, v, x and y (ld and t0 unused).
 hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, int max_seg_cap, void* scratch,
-                          size_t scratch_bytes, hipStream_t st, float log_p, int ld, int t0);
+                          size_t scratch_bytes, hipStream_t st, float log_p, int ld, int t0,
+                          const int* cu = nullptr, int total = 0);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

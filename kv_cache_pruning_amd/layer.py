@@ -176,6 +176,23 @@ class Layer:
                              self.ws.nbytes, stream)
         return y, ts
 
+    def prefill_varlen(self, q, k, v, x, cu_seqlens, max_tokens: Optional[int] = None,
+                       y: Optional[torch.Tensor] = None, stream=None):
+        """Prefill of a packed batch: sequence b appends rows cu_seqlens[b] .. cu_seqlens[b + 1] of q [T, H_q, d],
+        k, v [T, H_kv, d] and x [T, D]; y is [T, H_q, d].  max_tokens defaults to the longest sequence."""
+        s = self.shape
+        T = q.shape[0]
+        cu_host = [int(c) for c in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens)]
+        if max_tokens is None:
+            max_tokens = max(b - a for a, b in zip(cu_host[:-1], cu_host[1:]))
+        cu = torch.tensor(cu_host, dtype=torch.int32, device=self.device)
+        ts, tok = self._tokens(q, k, v, x)
+        if y is None:
+            y = torch.empty((T, s.H_q, s.d), dtype=torch.bfloat16 if s.y_bf16 else torch.float32, device=self.device)
+        L.ua_prefill_varlen(self.dims, self.w.params, self.cache.struct, tok, cu, T, max_tokens, y, self.ws.ptr,
+                            self.ws.nbytes, stream)
+        return y, ts
+
     def compact(self, log_p: float, kept: Optional[torch.Tensor] = None, stream=None):
         L.ua_compact(self.dims, self.cache.struct, log_p, kept, self.ws.ptr, self.ws.nbytes, stream)
         return kept

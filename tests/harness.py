@@ -583,3 +583,53 @@ def run_pruned_prefill_parity(cfg: LayerConfig, log_p: float, chunked: bool = Fa
 
 class BorderlineRun(Exception):
     """A mismatch in a run where the oracle met decisions within BORDER of tau."""
+
+
+def run_varlen_parity(cfg: LayerConfig, lens_per_call, terms: int = 7, seed: int = 0) -> dict:
+    """ua_prefill_varlen on the GPU against the oracle's per-sequence prefill (R31).
+
+    Call c packs the first lens_per_call[c][b] tokens of sequence b's draw for
+    that call.  After every call: y of every packed row (max-abs), rows past
+    the packed ones untouched, the stored new keys (one ulp), and the whole
+    cache (lengths, rows, biases, key gates, positions, status).
+    """
+    import torch
+
+    nmax = max(max(l) for l in lens_per_call)
+    w = make_weights(cfg, seed)
+    c = make_cache(cfg, w, seed)
+    layer = device_layer(cfg, w, c, terms=terms, max_tokens=nmax)
+    od, op = oracle_dims(cfg, terms), oracle_params(w)
+    oc = oracle_cache(cfg, c)
+    rep = {"y_err": 0.0, "lam_err": 0.0}
+    for call, lens in enumerate(lens_per_call):
+        assert len(lens) == cfg.B
+        inp = make_step_inputs(cfg, call, nmax, seed)
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+        T = int(cu[-1])
+        pack = lambda a: np.concatenate([a[b, : lens[b]] for b in range(cfg.B)], axis=0)
+        qp, kp, vp, xp = pack(inp.q), pack(inp.k), pack(inp.v), pack(inp.x)
+        len_before = layer.cache.seg_len.cpu().numpy().copy()
+        pos0 = layer.cache.next_pos.cpu().numpy().copy()
+        y_full = torch.full((T + 8, cfg.H_q, cfg.d), float("nan"), device="cuda")
+        layer.prefill_varlen(qp, kp, vp, xp, cu, max_tokens=nmax, y=y_full[:T])
+        torch.cuda.synchronize()
+        yg = y_full.cpu().numpy()
+        assert np.isnan(yg[T:]).all(), f"call {call}: rows past the packed ones were written"
+        g = gpu_state(layer)
+        k_gpu = np.zeros((T, cfg.H_kv, cfg.d))
+        for b in range(cfg.B):
+            if lens[b] == 0:
+                continue
+            rows = np.stack([g["K"][int(c.seg_off[b * cfg.H_kv + h]) + int(len_before[b * cfg.H_kv + h]):][: lens[b]]
+                             for h in range(cfg.H_kv)], axis=1)
+            _check_new_keys(cfg, od, kp[None, cu[b]:cu[b + 1]], pos0[b:b + 1], rows[None])
+            k_gpu[cu[b]:cu[b + 1]] = rows
+        y_or = U.prefill_varlen(od, op, oc, qp, kp, vp, xp, cu, k_override=k_gpu)
+        y_err = _maxabs(yg[:T], y_or)
+        lam_err = _compare_cache(layer, oc, cfg, f"call {call}")
+        rep["y_err"] = max(rep["y_err"], y_err)
+        rep["lam_err"] = max(rep["lam_err"], lam_err)
+        assert y_err <= y_tol(cfg), f"call {call}: y max-abs error {y_err:.3e}"
+        assert lam_err <= 1e-4, f"call {call}: log-bias error {lam_err:.3e}"
+    return rep

@@ -177,6 +177,20 @@ def test_pruned_and_chunked_prefill_reject():
     assert lib.ua_prefill_chunked(*args, 16, 8, -1.0, p, p, 8, None) == 3
 
 
+def test_varlen_prefill_rejects():
+    """Host-side argument checks of ua_prefill_varlen (no device work)."""
+    L = _lib()
+    lib = L.load()
+    a = _args(L)
+    p = _fake_ptr()
+    args = (C.byref(_dims(L)), C.byref(a["params"]), C.byref(a["cache"]), C.byref(a["tokens"]))
+    assert lib.ua_prefill_varlen(*args, None, 10, 8, p, p, 1 << 40, None) == 1      # no offsets
+    assert lib.ua_prefill_varlen(*args, p + 2, 10, 8, p, p, 1 << 40, None) == 1     # misaligned offsets
+    assert lib.ua_prefill_varlen(*args, p, 0, 8, p, p, 1 << 40, None) == 1          # no rows
+    assert lib.ua_prefill_varlen(*args, p, 10, 0, p, p, 1 << 40, None) == 1         # no tokens per sequence
+    assert lib.ua_prefill_varlen(*args, p, 10, 8, p, p, 8, None) == 3               # workspace too small
+
+
 def test_qk_norm_rejects():
     """Host-side argument checks of ua_qk_norm (no device work)."""
     L = _lib()

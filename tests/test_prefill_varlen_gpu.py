@@ -1,0 +1,81 @@
+"""Variable-length prefill (ua_prefill_varlen) against the oracle (reading R31).
+
+Sequences of one call append different numbers of tokens, packed row after
+row; the oracle runs each sequence's prefill on its own.  Every output row,
+the stored keys and the whole cache are compared after each call, and the
+rows past the packed ones must stay untouched.  Cases: empty sequences,
+sequences longer than the others by several token blocks, lengths off the
+64-token grid, a populated cache, both attention kernels (head dim 64 with up
+to four query heads per KV head, and head dim 128 or eight query heads), and
+equal lengths, which must give ua_prefill's outputs bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+from ua_inputs import config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_cache_pruning_amd import load
+
+    load()
+
+
+def _run(cfg, lens, **kw):
+    from tests.harness import run_varlen_parity
+
+    print(f"[varlen] B={cfg.B} H={cfg.H_q}/{cfg.H_kv} d={cfg.d} lens={lens} {kw}", flush=True)
+    rep = run_varlen_parity(cfg, lens, **kw)
+    print(f"  max |dy| {rep['y_err']:.2e}  max rel dLambda {rep['lam_err']:.2e}", flush=True)
+
+
+def test_varlen_ragged_two_calls():
+    cfg = config("1b-prefill", B=4, H_q=8, H_kv=2, D=256, n_total=256, chunk=128)
+    _run(cfg, [[100, 37, 0, 64], [5, 128, 77, 1]])
+
+
+def test_varlen_populated_cache_group4():
+    cfg = config("1b-prefill", B=3, H_q=16, H_kv=4, D=256, n_total=192, chunk=96, len_kind="lognormal",
+                 len_mean=120.0, len_min=16, len_max=400, nominal=400, lam_p0=0.15)
+    _run(cfg, [[96, 13, 70], [31, 96, 0]])
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(8, 2, 128), (16, 2, 64)])
+def test_varlen_second_kernel(hq, hkv, d):
+    cfg = config("1b-prefill", B=3, H_q=hq, H_kv=hkv, d=d, D=256, n_total=160, chunk=80)
+    _run(cfg, [[80, 0, 65], [17, 80, 3]])
+
+
+def test_varlen_term_subset():
+    cfg = config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=128, chunk=64)
+    _run(cfg, [[64, 20]], terms=2)
+
+
+def test_varlen_equal_lengths_is_prefill():
+    """Equal lengths: the same kernels on the same rows, so y and the cache equal ua_prefill's bit for bit."""
+    import torch
+
+    from tests.harness import device_layer, gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=100, chunk=100)
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    inp = make_step_inputs(cfg, 0, 100, 0)
+    l1 = device_layer(cfg, w, c, max_tokens=100)
+    y1, _ = l1.prefill(inp.q, inp.k, inp.v, inp.x)
+    l2 = device_layer(cfg, w, c, max_tokens=100)
+    flat = lambda a: a.reshape((-1,) + a.shape[2:])
+    y2, _ = l2.prefill_varlen(flat(inp.q), flat(inp.k), flat(inp.v), flat(inp.x), [0, 100, 200])
+    torch.cuda.synchronize()
+    assert torch.equal(y1.reshape(y2.shape), y2)
+    g1, g2 = gpu_state(l1), gpu_state(l2)
+    for key in ("K", "V", "lam", "lk", "seg_len", "next_pos"):
+        assert np.array_equal(g1[key], g2[key]), key
