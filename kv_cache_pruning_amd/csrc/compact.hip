@@ -2,12 +2,16 @@
 //
 // An entry whose log-bias fell below log p is evicted and never returns
 // (paperlayer.ai summary, section 4.2; ai4snews page after Figure 1).  Each
-// segment (one sequence, one KV head) is cut into chunks of CH entries and
-// every chunk gets its own workgroup, so long segments spread over many CUs.
+// segment (one sequence, one KV head) is cut into chunks of CH entries, so
+// long segments spread over many CUs.
 //
-// Workgroups take chunk ids from an atomic ticket, so a chunk's predecessors
-// in its segment always started earlier (every wait below is on a lower id,
-// which guarantees progress).  Per chunk:
+// A persistent grid (at most one workgroup per CU) numbers the chunks of the
+// segments' current lengths, segment by segment, and hands them out by an
+// atomic ticket, so a chunk's predecessors in its segment were drawn earlier
+// by running workgroups (every wait below is on a lower id, which guarantees
+// progress).  Only chunks that hold entries are drawn: a grid sized by
+// capacity would pay a ticket and an arrival per empty chunk, and those
+// atomics on one word serialise.  Per chunk:
 //  1. load the chunk's log-biases, count the live ones (ballot), publish the
 //     count;
 //  2. decoupled look-back over the predecessors' published counts/prefixes
@@ -18,10 +22,13 @@
 //     until every earlier chunk whose rows the destination range overwrites
 //     has loaded its own, then store.  Destinations never exceed sources, so
 //     this is the only hazard.
-// The last chunk of a segment to arrive writes the new length and clears the
-// segment's flags; the last workgroup overall clears the ticket.  Flags use
-// relaxed agent-scope atomics (coherent across XCDs without cache-wide
-// maintenance); waits are bounded and report a timeout in status bit 1.
+// A workgroup draws tickets until one is past the last chunk; the one that
+// draws the last ticket waits until every workgroup has finished, writes the
+// new lengths (each segment's last inclusive prefix), clears the chunk flags
+// and resets the counters.  The lengths stay unchanged until then, so every
+// workgroup numbers the same chunks.  Flags use relaxed agent-scope atomics
+// (coherent across XCDs without cache-wide maintenance); waits are bounded
+// and report a timeout in status bit 1.
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -48,6 +55,9 @@ __device__ __forceinline__ int addi_coh(int* p, int v) {
 }
 
 constexpr int kSpinLimit = 1 << 22;
+constexpr int kCompactGrid = 256;  // persistent workgroups (one per CU)
+
+__device__ __forceinline__ int chunks_of(int len, int ch) { return len <= 0 ? 0 : (len + ch - 1) / ch; }
 
 template <int RB>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, Control ctl, float tau, int32_t* kept) {
@@ -59,52 +69,82 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
   __shared__ int s_src[CH];
   __shared__ int s_cnt[kCompactThreads / 64];
   __shared__ int s_prefix;
-  __shared__ int s_last;
   const int S = a.B * a.H_kv;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
 
-  if (tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobTicket], 1);
-  __syncthreads();
-  const int id = s_ticket;
+  // ---- numbering from the lengths at the start of the call
+  const int per = (S + kCompactThreads - 1) / kCompactThreads;
+  const int sb = min(S, tid * per);
+  const int se = min(S, sb + per);
+  int mine = 0;
+  for (int s = sb; s < se; ++s) mine += chunks_of(a.seg_len[s], CH);
+  int total;
+  const int excl = block_exclusive_scan<kCompactThreads>(mine, s_scan, &total);
 
-  // ---- chunk id -> (segment, chunk) from the read-only capacities
-  bool have = false;
-  {
-    const int per = (S + kCompactThreads - 1) / kCompactThreads;
-    const int sb = tid * per;
-    const int se = min(S, sb + per);
-    int mine = 0;
-    for (int s = sb; s < se; ++s) mine += max(1, (a.seg_cap[s] + CH - 1) / CH);
-    int total;
-    const int excl = block_exclusive_scan<kCompactThreads>(mine, s_scan, &total);
-    have = id >= 0 && id < total;  // ids come from the self-resetting ticket
-    if (have) {
+  while (true) {
+    if (tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobTicket], 1);
+    __syncthreads();
+    const int id = s_ticket;
+
+    if (id >= total) {
+      // ---- exit: report done; the workgroup with the last ticket commits
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) addi_coh(&ctl.glob[kGlobArrive], 1);
+      if (id == total + (int)gridDim.x - 1) {
+        if (tid == 0) {
+          int spins = 0;
+          while (ldi_coh(&ctl.glob[kGlobArrive]) < (int)gridDim.x) {
+            if (++spins > kSpinLimit) {
+              atomicOr(a.status, 2);
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+          }
+        }
+        __syncthreads();
+        int run = excl;
+        for (int s = sb; s < se; ++s) {
+          const int n = chunks_of(a.seg_len[s], CH);
+          if (n > 0) a.seg_len[s] = ldi_coh(&ctl.cmp_state[run + n - 1]) >> 2;
+          run += n;
+        }
+        __syncthreads();  // every prefix read before any flag is cleared
+        for (int t = tid; t < total; t += kCompactThreads) {
+          sti_coh2(&ctl.cmp_state[t], 0);
+          sti_coh2(&ctl.cmp_loaded[t], 0);
+        }
+        if (tid == 0) {
+          sti_coh2(&ctl.glob[kGlobTicket], 0);
+          sti_coh2(&ctl.glob[kGlobArrive], 0);
+        }
+      }
+      break;
+    }
+
+    // ---- chunk id -> (segment, chunk)
+    if (id >= excl && id < excl + mine) {
       int run = excl;
       for (int s = sb; s < se; ++s) {
-        const int n = max(1, (a.seg_cap[s] + CH - 1) / CH);
+        const int n = chunks_of(a.seg_len[s], CH);
         if (id >= run && id < run + n) {
           s_info[0] = s;
           s_info[1] = id - run;
           s_info[2] = run;
-          s_info[3] = n;
         }
         run += n;
       }
     }
     __syncthreads();
-  }
-
-  if (have) {
     const int seg = s_info[0];
     const int c = s_info[1];
     const int first = s_info[2];
-    const int nch = s_info[3];
     const int len = a.seg_len[seg];
     const int64_t off = a.seg_off[seg];
     const int j0 = c * CH;
-    const int nvalid = min(CH, max(0, len - j0));
+    const int nvalid = min(CH, len - j0);  // >= 1: only chunks with entries are numbered
 
     // 1. live flags and count
     const int j = j0 + tid;
@@ -168,7 +208,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
     const int P = s_prefix;
     const bool moves = (P != j0) || (count != nvalid);
 
-    if (moves && nvalid > 0) {
+    if (moves) {
       // stable list of survivors (chunk-relative source indices)
       {
         const int rank_w = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
@@ -239,35 +279,14 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
       if (tid == 0) sti_coh2(&ctl.cmp_loaded[id], 1);
       if (kept && tid < nvalid) kept[off + j0 + tid] = j0 + tid;
     }
-
-    // 4. the last chunk of the segment to arrive sets the length, clears flags
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) s_last = (addi_coh(&ctl.cmp_done[seg], 1) == nch - 1);
-    __syncthreads();
-    if (s_last) {
-      if (tid == 0) a.seg_len[seg] = ldi_coh(&ctl.cmp_state[first + nch - 1]) >> 2;
-      __syncthreads();
-      for (int t = tid; t < nch; t += kCompactThreads) {
-        sti_coh2(&ctl.cmp_state[first + t], 0);
-        sti_coh2(&ctl.cmp_loaded[first + t], 0);
-      }
-      if (tid == 0) sti_coh2(&ctl.cmp_done[seg], 0);
-    }
-  }
-
-  // 5. the last workgroup overall clears the ticket
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (tid == 0 && addi_coh(&ctl.glob[kGlobArrive], 1) == (int)gridDim.x - 1) {
-    sti_coh2(&ctl.glob[kGlobTicket], 0);
-    sti_coh2(&ctl.glob[kGlobArrive], 0);
+    __syncthreads();  // shared state is rewritten by the next chunk
   }
 }
 
 template <int RB>
 static hipError_t launch_rb(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st) {
-  hipLaunchKernelGGL((compact_kernel<RB>), dim3(ctl.max_chunks), dim3(kCompactThreads), 0, st, a, ctl, tau, kept);
+  const int grid = ctl.max_chunks < kCompactGrid ? ctl.max_chunks : kCompactGrid;
+  hipLaunchKernelGGL((compact_kernel<RB>), dim3(grid), dim3(kCompactThreads), 0, st, a, ctl, tau, kept);
   return hipGetLastError();
 }
 

@@ -67,7 +67,6 @@ struct Control {
   int* cmp_state;            // [max_chunks]  compaction: (count or prefix) << 2 | flag
   int* cmp_loaded;           // [max_chunks]  compaction: the chunk's rows are in registers
   unsigned long long* dec_state;  // [max_chunks]  decode tiles: call tag << 32 | (count or prefix) << 2 | flag
-  int* cmp_done;             // [S]           compaction: arrivals per segment
   int* glob;                 // [kGlobInts]   ticket, arrivals, call counter, finished (one cache line each)
   unsigned long long* uw;    // [B, kUWords]  decode: per-sequence values, call tag in the high half
   int cmp_chunk;             // entries per compaction chunk

@@ -40,12 +40,10 @@ static size_t fixed_layout(const LayerArgs& a, Control* c, char* base) {
     return q;
   };
   int* dec_cnt = take(sizeof(int) * S);
-  int* cmp_done = take(sizeof(int) * S);
   int* glob = take(sizeof(int) * kGlobInts);
   int* uw = take(sizeof(unsigned long long) * a.B * kUWords);
   if (c) {
     c->dec_cnt = dec_cnt;
-    c->cmp_done = cmp_done;
     c->glob = glob;
     c->uw = reinterpret_cast<unsigned long long*>(uw);
   }
