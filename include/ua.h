@@ -293,6 +293,7 @@ ua_status ua_prefill_varlen(const ua_dims* dims, const ua_params* params, const 
  *   v   [B, n, H_kv, d]  values                        (dims.dtype)
  *   lq, lk, lb [B, n, H_kv] fp32  log-gates (query, key, similarity)
  *   dO  [B, n, H_q, d] fp32
+ * q, k, v and dO must be 16-byte aligned, the gates 4-byte aligned.
  * Outputs (fp32, device, 16-byte aligned, written in full): dq, dk, dv of the
  * shapes of q, k, v, and dlq, dlk, dlb of the gates'.  dk includes the
  * similarity term's share.  The gradient of min(s^2, 1) is taken as 0 where

@@ -260,9 +260,10 @@ ua_status ua_attention_backward(const ua_dims* dims, int32_t n_tokens, const ua_
   const void* tin[3] = {in->q, in->k, in->v};
   for (const void* p : tin)
     if (!p || !aligned(p, 16)) return UA_ERR_INVALID_ARG;
-  const float* fin[4] = {in->lq, in->lk, in->lb, in->dO};
+  const float* fin[3] = {in->lq, in->lk, in->lb};
   for (const float* p : fin)
     if (!p || !aligned(p, 4)) return UA_ERR_INVALID_ARG;
+  if (!in->dO || !aligned(in->dO, 16)) return UA_ERR_INVALID_ARG;
   float* fout[6] = {out->dq, out->dk, out->dv, out->dlq, out->dlk, out->dlb};
   for (float* p : fout)
     if (!p || !aligned(p, 16)) return UA_ERR_INVALID_ARG;

@@ -20,10 +20,11 @@
 //                          sum_{i >= t} dLambda[i][j], dlambda = dA dA/dlambda,
 //                          then the gates' and the similarity term's
 //                          gradients (rows go out through atomics).
-// Threads: lane l of a 256-thread workgroup serves row or key l >> 2 and
-// quarter l & 3 of the head dimension; a dot product is four partial sums
-// combined inside the quad.  Lambda and dLambda are N x N fp32 per segment in
-// the workspace; everything is fp32 inside.
+// Kernels 1 and 5 give lane l of a 256-thread workgroup row or key l >> 2 and
+// quarter l & 3 of the head dimension (a dot product is four partial sums
+// combined inside the quad); kernels 2-4 run their products on the matrix
+// cores in fp32.  Lambda and dLambda are N x N fp32 per segment in the
+// workspace; everything is fp32 inside.
 
 #include <cmath>
 
@@ -159,217 +160,291 @@ __global__ __launch_bounds__(kBwThreads) void bwd_bias_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. LSE and D = dO . o per (token, query head)
+// 2-4 on the matrix cores: fp32 16x16x4 products (v_mfma_f32_16x16x4_f32).
+// Lane l holds A[l % 16][l / 16] and B[l / 16][l % 16] of a step and
+// D[4 (l / 16) + r][l % 16] of the 16 x 16 result (r = 0..3).  A product whose
+// reduction runs over a tile's 16 rows takes the rows in the order 4 g + st
+// (step st, lane group g = l / 16): the lane's own four result values of the
+// previous product are then its operand for the four steps, with no
+// transpose.  Tiles of 64 rows are staged in LDS as fp32 with a row stride
+// of D + 4 floats.
 // ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float expf_masked(float e) { return e == -__builtin_huge_valf() ? 0.0f : __expf(e); }
+
+// Rows r0 .. r0 + 63 (clamped to N - 1) of a [B, N, H, D] tensor at (b, head)
+// into LDS as fp32 [64][D + 4].
 template <int D, bool BF16>
-__global__ __launch_bounds__(kBwThreads) void bwd_stats_kernel(BwArgs a) {
-  constexpr int QW = D / 4;
-  __shared__ float s_k[kBwTile][D + 1];
-  __shared__ float s_v[kBwTile][D + 1];
-  __shared__ float s_l[kBwTile][kBwTile + 1];
-  const int G = a.Hq / a.Hkv;
-  const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = blockIdx.y;
-  const int b = s / a.Hkv, h = s - b * a.Hkv, hq = h * G + ga;
-  const int N = a.N;
-  const int tid = threadIdx.x, tl = tid >> 2, c = tid & 3;
-  const int t = I * kBwTile + tl, tc = min(t, N - 1);
-  float q[QW], o[QW];
+__device__ __forceinline__ void stage_rows(float* dst, const void* src, int b, int N, int H, int head, int r0) {
+  constexpr int LS = D + 4;
+  constexpr int VE = BF16 ? 8 : 4;  // elements per 16-byte load
+  for (int e = threadIdx.x; e < kBwTile * (D / VE); e += kBwThreads) {
+    const int r = e / (D / VE), c = (e - r * (D / VE)) * VE;
+    const int64_t g = (((int64_t)b * N + min(r0 + r, N - 1)) * H + head) * D + c;
+    float* o = dst + r * LS + c;
+    if constexpr (BF16) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + g);
 #pragma unroll
-  for (int e = 0; e < QW; ++e) {
-    q[e] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + c * QW + e);
-    o[e] = 0.0f;
-  }
-  float m = -__builtin_huge_valf(), l = 0.0f;
-  const float* lamS = a.lam + (int64_t)s * N * N;
-  for (int J = 0; J <= I; ++J) {
-    __syncthreads();
-    for (int e = tid; e < kBwTile * D; e += kBwThreads) {
-      const int r = e / D, col = e - r * D;
-      const int j = min(J * kBwTile + r, N - 1);
-      s_k[r][col] = ld_elem<BF16>(a.kt, (((int64_t)b * N + j) * a.Hkv + h) * D + col);
-      s_v[r][col] = ld_elem<BF16>(a.v, (((int64_t)b * N + j) * a.Hkv + h) * D + col);
-    }
-    for (int e = tid; e < kBwTile * kBwTile; e += kBwThreads) {
-      const int r = e / kBwTile, col = e - r * kBwTile;
-      const int tt = min(I * kBwTile + r, N - 1), j = min(J * kBwTile + col, N - 1);
-      s_l[r][col] = lamS[(int64_t)tt * N + j];
-    }
-    __syncthreads();
-    for (int jl = 0; jl < kBwTile; ++jl) {
-      const int j = J * kBwTile + jl;
-      if (j > t || j >= N) break;
-      float p = 0.0f;
-#pragma unroll
-      for (int e = 0; e < QW; ++e) p = fmaf(q[e], s_k[jl][c * QW + e], p);
-      const float ev = a.scale * quad_sum(p) + s_l[tl][jl];
-      const float mn = fmaxf(m, ev);
-      const float al = __expf(m - mn), pe = __expf(ev - mn);
-      l = l * al + pe;
-#pragma unroll
-      for (int e = 0; e < QW; ++e) o[e] = fmaf(pe, s_v[jl][c * QW + e], o[e] * al);
-      m = mn;
-    }
-  }
-  if (t < N) {
-    const float inv = 1.0f / l;
-    float dd = 0.0f;
-#pragma unroll
-    for (int e = 0; e < QW; ++e) dd = fmaf(a.dO[(((int64_t)b * N + t) * a.Hq + hq) * D + c * QW + e], o[e] * inv, dd);
-    dd = quad_sum(dd);
-    if (c == 0) {
-      a.lse[((int64_t)b * N + t) * a.Hq + hq] = m + __logf(l);
-      a.dd[((int64_t)b * N + t) * a.Hq + hq] = dd;
+      for (int q = 0; q < 4; ++q) {
+        o[2 * q] = __uint_as_float(w[q] << 16);
+        o[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+    } else {
+      *reinterpret_cast<float4*>(o) = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + g);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 3. dv, the attention part of dk, and dLambda (summed over the group)
+// 2. LSE and D = dO . o per (token, query head).  Wave w: tokens 16 w + c of
+// the token block (c = l % 16); per key tile S^T = K Q^T, an online softmax
+// per token, O^T += V^T P^T.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBwThreads) void bwd_stats_kernel(BwArgs a) {
+  constexpr int LS = D + 4, NS = D / 4, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) float s_k[kBwTile * LS];
+  __shared__ __attribute__((aligned(16))) float s_v[kBwTile * LS];
+  const int G = a.Hq / a.Hkv;
+  const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = blockIdx.y;
+  const int b = s / a.Hkv, h = s - b * a.Hkv, hq = h * G + ga;
+  const int N = a.N;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int t = I * kBwTile + 16 * w + c, tc = min(t, N - 1);
+  float qreg[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) qreg[st] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g);
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -__builtin_huge_valf(), lsum = 0.0f;
+  const float* lrow = a.lam + (int64_t)s * N * N + (int64_t)tc * N;
+  for (int J = 0; J <= I; ++J) {
+    __syncthreads();
+    stage_rows<D, BF16>(s_k, a.kt, b, N, a.Hkv, h, J * kBwTile);
+    stage_rows<D, BF16>(s_v, a.v, b, N, a.Hkv, h, J * kBwTile);
+    __syncthreads();
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < NS; ++st) sc = mfma4(s_k[(16 * kt + c) * LS + 4 * st + g], qreg[st], sc);
+      float e[4];
+      float mt = -__builtin_huge_valf();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = J * kBwTile + 16 * kt + 4 * g + r;
+        const bool on = j <= t && t < N;
+        e[r] = on ? fmaf(a.scale, sc[r], lrow[min(j, N - 1)]) : -__builtin_huge_valf();
+        mt = fmaxf(mt, e[r]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mn = fmaxf(m, mt);
+      const float al = (mn == -__builtin_huge_valf()) ? 1.0f : expf_masked(m - mn);
+      float p[4], ps = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = (mn == -__builtin_huge_valf()) ? 0.0f : expf_masked(e[r] - mn);
+        ps += p[r];
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      lsum = fmaf(lsum, al, ps);
+      m = mn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        oacc[dt] *= al;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) oacc[dt] = mfma4(s_v[(16 * kt + 4 * g + st) * LS + 16 * dt + c], p[st], oacc[dt]);
+      }
+    }
+  }
+  // lane holds O^T[dim 16 dt + 4 g + r][token c]
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  float dd = 0.0f;
+  const float* dorow = a.dO + (((int64_t)b * N + tc) * a.Hq + hq) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dd = fmaf(dorow[16 * dt + 4 * g + r], oacc[dt][r] * inv, dd);
+  dd += __shfl_xor(dd, 16, 64);
+  dd += __shfl_xor(dd, 32, 64);
+  if (g == 0 && t < N) {
+    a.lse[((int64_t)b * N + t) * a.Hq + hq] = m + __logf(lsum);
+    a.dd[((int64_t)b * N + t) * a.Hq + hq] = dd;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dV, the attention part of dK, and dLambda (summed over the group).  Wave
+// w: keys 16 w + c of the key block.  Per token tile S = Q K^T and dP = dO V^T
+// (tokens x keys), P and dS, then dV += P^T dO and dK += dS^T Q.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(kBwThreads) void bwd_kv_kernel(BwArgs a) {
-  constexpr int QW = D / 4;
-  __shared__ float s_q[kBwTile][D + 1];
-  __shared__ float s_do[kBwTile][D + 1];
-  __shared__ float s_l[kBwTile][kBwTile + 1];
-  __shared__ float s_dl[kBwTile][kBwTile + 1];
+  constexpr int LS = D + 4, NS = D / 4, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) float s_q[kBwTile * LS];
+  __shared__ __attribute__((aligned(16))) float s_do[kBwTile * LS];
   __shared__ float s_lse[kBwTile], s_dd[kBwTile];
   const int G = a.Hq / a.Hkv;
   const int s = blockIdx.x, J = blockIdx.y;
   const int b = s / a.Hkv, h = s - b * a.Hkv;
   const int N = a.N, nb = (N + kBwTile - 1) / kBwTile;
-  const int tid = threadIdx.x, jl = tid >> 2, c = tid & 3;
-  const int j = J * kBwTile + jl, jc = min(j, N - 1);
-  float kj[QW], vj[QW], dk[QW], dv[QW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int j = J * kBwTile + 16 * w + c, jc = min(j, N - 1);
+  float kreg[NS], vreg[NS];
 #pragma unroll
-  for (int e = 0; e < QW; ++e) {
-    kj[e] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + c * QW + e);
-    vj[e] = ld_elem<BF16>(a.v, (((int64_t)b * N + jc) * a.Hkv + h) * D + c * QW + e);
-    dk[e] = 0.0f;
-    dv[e] = 0.0f;
+  for (int st = 0; st < NS; ++st) {
+    kreg[st] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
+    vreg[st] = ld_elem<BF16>(a.v, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
+  }
+  f32x4 dv[DT], dk[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float* lamS = a.lam + (int64_t)s * N * N;
   float* dlamS = a.dlam + (int64_t)s * N * N;
   for (int I = J; I < nb; ++I) {
-    __syncthreads();
-    for (int e = tid; e < kBwTile * kBwTile; e += kBwThreads) {
-      const int r = e / kBwTile, col = e - r * kBwTile;
-      const int tt = min(I * kBwTile + r, N - 1), jj = min(J * kBwTile + col, N - 1);
-      s_l[r][col] = lamS[(int64_t)tt * N + jj];
-      s_dl[r][col] = 0.0f;
-    }
+    f32x4 dl[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) dl[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int ga = 0; ga < G; ++ga) {
       const int hq = h * G + ga;
       __syncthreads();
-      for (int e = tid; e < kBwTile * D; e += kBwThreads) {
-        const int r = e / D, col = e - r * D;
-        const int tt = min(I * kBwTile + r, N - 1);
-        s_q[r][col] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tt) * a.Hq + hq) * D + col);
-        s_do[r][col] = a.dO[(((int64_t)b * N + tt) * a.Hq + hq) * D + col];
-      }
-      for (int r = tid; r < kBwTile; r += kBwThreads) {
-        const int tt = min(I * kBwTile + r, N - 1);
-        s_lse[r] = a.lse[((int64_t)b * N + tt) * a.Hq + hq];
-        s_dd[r] = a.dd[((int64_t)b * N + tt) * a.Hq + hq];
+      stage_rows<D, BF16>(s_q, a.qt, b, N, a.Hq, hq, I * kBwTile);
+      stage_rows<D, false>(s_do, a.dO, b, N, a.Hq, hq, I * kBwTile);
+      for (int r = threadIdx.x; r < kBwTile; r += kBwThreads) {
+        const int64_t ti = ((int64_t)b * N + min(I * kBwTile + r, N - 1)) * a.Hq + hq;
+        s_lse[r] = a.lse[ti];
+        s_dd[r] = a.dd[ti];
       }
       __syncthreads();
-      for (int tl = 0; tl < kBwTile; ++tl) {
-        const int t = I * kBwTile + tl;
-        if (t >= N) break;
-        float p = 0.0f, dp = 0.0f;
+#pragma unroll 1
+      for (int tt = 0; tt < 4; ++tt) {
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < QW; ++e) {
-          p = fmaf(kj[e], s_q[tl][c * QW + e], p);
-          dp = fmaf(vj[e], s_do[tl][c * QW + e], dp);
+        for (int st = 0; st < NS; ++st) {
+          sc = mfma4(s_q[(16 * tt + c) * LS + 4 * st + g], kreg[st], sc);
+          dp = mfma4(s_do[(16 * tt + c) * LS + 4 * st + g], vreg[st], dp);
         }
-        p = quad_sum(p);
-        dp = quad_sum(dp);
-        const bool on = j <= t && j < N;
-        const float P = on ? __expf(a.scale * p + s_l[tl][jl] - s_lse[tl]) : 0.0f;
-        const float dS = P * (dp - s_dd[tl]);
+        // lane holds (token 16 tt + 4 g + r, key j)
+        float P[4], dS[4];
 #pragma unroll
-        for (int e = 0; e < QW; ++e) {
-          dv[e] = fmaf(P, s_do[tl][c * QW + e], dv[e]);
-          dk[e] = fmaf(a.scale * dS, s_q[tl][c * QW + e], dk[e]);
+        for (int r = 0; r < 4; ++r) {
+          const int tl = 16 * tt + 4 * g + r, t = I * kBwTile + tl;
+          const bool on = j <= t && t < N && j < N;
+          const float lv = lamS[(int64_t)min(t, N - 1) * N + jc];
+          P[r] = on ? __expf(fmaf(a.scale, sc[r], lv) - s_lse[tl]) : 0.0f;
+          dS[r] = P[r] * (dp[r] - s_dd[tl]);
+          dl[tt][r] += dS[r];
         }
-        if (c == 0) s_dl[tl][jl] += dS;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int row = (16 * tt + 4 * g + st) * LS + 16 * dt + c;
+            dv[dt] = mfma4(P[st], s_do[row], dv[dt]);
+            dk[dt] = mfma4(dS[st], s_q[row], dk[dt]);
+          }
       }
     }
-    __syncthreads();
-    for (int e = tid; e < kBwTile * kBwTile; e += kBwThreads) {
-      const int r = e / kBwTile, col = e - r * kBwTile;
-      const int tt = I * kBwTile + r, jj = J * kBwTile + col;
-      if (tt < N && jj < N) dlamS[(int64_t)tt * N + jj] = s_dl[r][col];
+    if (j < N) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = I * kBwTile + 16 * tt + 4 * g + r;
+          if (t < N) dlamS[(int64_t)t * N + j] = dl[tt][r];
+        }
     }
   }
-  if (j < N) {
+  // lane holds dV / dK[key 16 w + 4 g + r][dim 16 dt + c]
 #pragma unroll
-    for (int e = 0; e < QW; ++e) {
-      a.dk[(((int64_t)b * N + j) * a.Hkv + h) * D + c * QW + e] = dk[e];
-      a.dv[(((int64_t)b * N + j) * a.Hkv + h) * D + c * QW + e] = dv[e];
+  for (int r = 0; r < 4; ++r) {
+    const int jo = J * kBwTile + 16 * w + 4 * g + r;
+    if (jo < N) {
+      const int64_t o = (((int64_t)b * N + jo) * a.Hkv + h) * D + c;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        a.dv[o + 16 * dt] = dv[dt][r];
+        a.dk[o + 16 * dt] = a.scale * dk[dt][r];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 4. dq per (token block, query head)
+// 4. dQ per (token block, query head).  Wave w: tokens 16 w + c.  Per key
+// tile S^T = K Q^T and dP^T = V dO^T (keys x tokens), dS, then dQ += dS K.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(kBwThreads) void bwd_q_kernel(BwArgs a) {
-  constexpr int QW = D / 4;
-  __shared__ float s_k[kBwTile][D + 1];
-  __shared__ float s_v[kBwTile][D + 1];
-  __shared__ float s_l[kBwTile][kBwTile + 1];
+  constexpr int LS = D + 4, NS = D / 4, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) float s_k[kBwTile * LS];
+  __shared__ __attribute__((aligned(16))) float s_v[kBwTile * LS];
   const int G = a.Hq / a.Hkv;
   const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = blockIdx.y;
   const int b = s / a.Hkv, h = s - b * a.Hkv, hq = h * G + ga;
   const int N = a.N;
-  const int tid = threadIdx.x, tl = tid >> 2, c = tid & 3;
-  const int t = I * kBwTile + tl, tc = min(t, N - 1);
-  float q[QW], dO[QW], dq[QW];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int t = I * kBwTile + 16 * w + c, tc = min(t, N - 1);
+  float qreg[NS], oreg[NS];
 #pragma unroll
-  for (int e = 0; e < QW; ++e) {
-    q[e] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + c * QW + e);
-    dO[e] = a.dO[(((int64_t)b * N + tc) * a.Hq + hq) * D + c * QW + e];
-    dq[e] = 0.0f;
+  for (int st = 0; st < NS; ++st) {
+    qreg[st] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g);
+    oreg[st] = a.dO[(((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g];
   }
   const float lse = a.lse[((int64_t)b * N + tc) * a.Hq + hq];
   const float dd = a.dd[((int64_t)b * N + tc) * a.Hq + hq];
-  const float* lamS = a.lam + (int64_t)s * N * N;
+  f32x4 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* lrow = a.lam + (int64_t)s * N * N + (int64_t)tc * N;
   for (int J = 0; J <= I; ++J) {
     __syncthreads();
-    for (int e = tid; e < kBwTile * D; e += kBwThreads) {
-      const int r = e / D, col = e - r * D;
-      const int j = min(J * kBwTile + r, N - 1);
-      s_k[r][col] = ld_elem<BF16>(a.kt, (((int64_t)b * N + j) * a.Hkv + h) * D + col);
-      s_v[r][col] = ld_elem<BF16>(a.v, (((int64_t)b * N + j) * a.Hkv + h) * D + col);
-    }
-    for (int e = tid; e < kBwTile * kBwTile; e += kBwThreads) {
-      const int r = e / kBwTile, col = e - r * kBwTile;
-      const int tt = min(I * kBwTile + r, N - 1), j = min(J * kBwTile + col, N - 1);
-      s_l[r][col] = lamS[(int64_t)tt * N + j];
-    }
+    stage_rows<D, BF16>(s_k, a.kt, b, N, a.Hkv, h, J * kBwTile);
+    stage_rows<D, BF16>(s_v, a.v, b, N, a.Hkv, h, J * kBwTile);
     __syncthreads();
-    for (int jl = 0; jl < kBwTile; ++jl) {
-      const int j = J * kBwTile + jl;
-      if (j > t || j >= N) break;
-      float p = 0.0f, dp = 0.0f;
+#pragma unroll 1
+    for (int kt = 0; kt < 4; ++kt) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < QW; ++e) {
-        p = fmaf(q[e], s_k[jl][c * QW + e], p);
-        dp = fmaf(dO[e], s_v[jl][c * QW + e], dp);
+      for (int st = 0; st < NS; ++st) {
+        sc = mfma4(s_k[(16 * kt + c) * LS + 4 * st + g], qreg[st], sc);
+        dp = mfma4(s_v[(16 * kt + c) * LS + 4 * st + g], oreg[st], dp);
       }
-      p = quad_sum(p);
-      dp = quad_sum(dp);
-      const float P = __expf(a.scale * p + s_l[tl][jl] - lse);
-      const float g = a.scale * P * (dp - dd);
+      // lane holds (key 16 kt + 4 g + r, token t)
+      float dS[4];
 #pragma unroll
-      for (int e = 0; e < QW; ++e) dq[e] = fmaf(g, s_k[jl][c * QW + e], dq[e]);
+      for (int r = 0; r < 4; ++r) {
+        const int jj = J * kBwTile + 16 * kt + 4 * g + r;
+        const bool on = jj <= t && t < N;
+        const float P = on ? __expf(fmaf(a.scale, sc[r], lrow[min(jj, N - 1)]) - lse) : 0.0f;
+        dS[r] = P * (dp[r] - dd);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) dq[dt] = mfma4(dS[st], s_k[(16 * kt + 4 * g + st) * LS + 16 * dt + c], dq[dt]);
     }
   }
-  if (t < N) {
+  // lane holds dQ[token 16 w + 4 g + r][dim 16 dt + c]
 #pragma unroll
-    for (int e = 0; e < QW; ++e) a.dq[(((int64_t)b * N + t) * a.Hq + hq) * D + c * QW + e] = dq[e];
+  for (int r = 0; r < 4; ++r) {
+    const int to = I * kBwTile + 16 * w + 4 * g + r;
+    if (to < N) {
+      const int64_t o = (((int64_t)b * N + to) * a.Hq + hq) * D + c;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) a.dq[o + 16 * dt] = a.scale * dq[dt][r];
+    }
   }
 }
 

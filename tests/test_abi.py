@@ -223,6 +223,8 @@ def test_attention_backward_rejects():
     assert lib.ua_attention_backward(d, n, C.byref(gi), C.byref(go), p, ok - 1, None) == 3
     bad = L.ua_grad_inputs(*([p] * 6 + [None]))
     assert lib.ua_attention_backward(d, n, C.byref(bad), C.byref(go), p, ok, None) == 1
+    bad_do = L.ua_grad_inputs(*([p] * 6 + [p + 4]))  # dO must be 16-byte aligned
+    assert lib.ua_attention_backward(d, n, C.byref(bad_do), C.byref(go), p, ok, None) == 1
     bad_out = L.ua_grads(*([p] * 5 + [p + 4]))
     assert lib.ua_attention_backward(d, n, C.byref(gi), C.byref(bad_out), p, ok, None) == 1
     assert lib.ua_attention_backward(C.byref(_dims(L, d_head=32)), n, C.byref(gi), C.byref(go), p, ok, None) == 2

@@ -130,10 +130,11 @@ def test_backward_repeated_keys_clamp():
 
 
 def test_backward_single_token():
-    """One token: its softmax is over itself, so dq = dk = 0, dv = dO summed over the group, gates 0."""
+    """One token: its softmax is over itself, so dq = dk = 0 (dS = dO.v - dO.o, zero up to fp32
+    rounding of two equal dot products), dv = dO summed over the group, and the gates get 0."""
     q, k, v, lq, lk, lb, dO = _inputs(1, 1, 4, 1, 64, False, 9)
     got = _device_backward(q, k, v, lq, lk, lb, dO, U.TERMS_ALL, False)
-    assert not got[0].any() and not got[1].any()
+    assert np.abs(got[0]).max() <= 1e-5 and np.abs(got[1]).max() <= 1e-5
     np.testing.assert_allclose(got[2][0, 0, 0], dO[0, 0].sum(axis=0), rtol=1e-6, atol=1e-6)
     assert not got[3].any() and not got[4].any() and not got[5].any()
 
