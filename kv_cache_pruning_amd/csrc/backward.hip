@@ -10,21 +10,21 @@
 // gate), and returns dq~, dk~, dv, dlq, dlk, dlb.
 //
 // Per segment s (sequence b, KV head h) and 64 x 64 tiles of (token t, key j):
-//   1. bwd_bias_kernel     Lambda[t][j] = sum_{t' <= t} A_{t'j}: per key block a
-//                          scan down the token rows (A_{t'j} = 0 for t' <= j).
-//   2. bwd_stats_kernel    per (token, query head): LSE and D = dO . o.
-//   3. bwd_kv_kernel       per key block: dv, the attention part of dk, and
-//                          dLambda[t][j] = sum over the group's heads of dS.
-//   4. bwd_q_kernel        per (token block, query head): dq.
-//   5. bwd_decay_kernel    per key block, token rows in reverse: dA_tj =
-//                          sum_{i >= t} dLambda[i][j], dlambda = dA dA/dlambda,
-//                          then the gates' and the similarity term's
-//                          gradients (rows go out through atomics).
-// Kernels 1 and 5 give lane l of a 256-thread workgroup row or key l >> 2 and
-// quarter l & 3 of the head dimension (a dot product is four partial sums
-// combined inside the quad); kernels 2-4 run their products on the matrix
-// cores in fp32.  Lambda and dLambda are N x N fp32 per segment in the
-// workspace; everything is fp32 inside.
+//   1. bwd_bias_kernel       Lambda[t][j] = sum_{t' <= t} A_{t'j}: per key block
+//                            a scan down the token rows (A_{t'j} = 0 for t' <= j).
+//   2. bwd_stats_kernel      per (token, query head): LSE and D = dO . o.
+//   3. bwd_kv_kernel         per key block: dv, the attention part of dk, and
+//                            dLambda[t][j] = sum over the group's heads of dS.
+//   4. bwd_q_kernel          per (token block, query head): dq.
+//   5. bwd_decay_col_kernel  per key block, token rows in reverse: dA_tj =
+//                            sum_{i >= t} dLambda[i][j], the gradient g of each
+//                            pair term and ds of its similarity; dlk and the
+//                            key side of dk.
+//   6. bwd_decay_row_kernel  per token block: dlq, dlb and the token side of dk.
+// Every kernel runs its products on the matrix cores (fp32 16x16x4 tiles; the
+// decay pass's similarity in fp64) and owns the rows it writes, so no output
+// needs clearing and no atomics are used.  Lambda and dLambda are N x N fp32
+// per segment in the workspace; everything is fp32 inside.
 
 #include <cmath>
 
@@ -35,32 +35,6 @@ namespace ua {
 
 constexpr int kBwThreads = 256;
 constexpr int kBwTile = 64;
-
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp_f<kDppXor1>(v);
-  v += dpp_f<kDppXor2>(v);
-  return v;
-}
-
-// The same sum in fp64 (each half of the double moves through its own DPP).
-__device__ __forceinline__ double dpp_d_xor(double v, int which) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  int lo = (int)(u & 0xffffffffu), hi = (int)(u >> 32);
-  if (which == 1) {
-    lo = __builtin_amdgcn_update_dpp(0, lo, kDppXor1, 0xF, 0xF, false);
-    hi = __builtin_amdgcn_update_dpp(0, hi, kDppXor1, 0xF, 0xF, false);
-  } else {
-    lo = __builtin_amdgcn_update_dpp(0, lo, kDppXor2, 0xF, 0xF, false);
-    hi = __builtin_amdgcn_update_dpp(0, hi, kDppXor2, 0xF, 0xF, false);
-  }
-  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
-}
-
-__device__ __forceinline__ double quad_sum_d(double v) {
-  v += dpp_d_xor(v, 1);
-  v += dpp_d_xor(v, 2);
-  return v;
-}
 
 template <bool BF16>
 __device__ __forceinline__ float ld_elem(const void* p, int64_t i) {
@@ -110,56 +84,6 @@ __device__ __forceinline__ float log1mexp_f(float lam) {
 }
 
 // ---------------------------------------------------------------------------
-// 1. Lambda
-// ---------------------------------------------------------------------------
-template <int D, bool BF16>
-__global__ __launch_bounds__(kBwThreads) void bwd_bias_kernel(BwArgs a) {
-  constexpr int QW = D / 4;
-  __shared__ float s_k[kBwTile][D + 1];
-  __shared__ float s_lq[kBwTile], s_lb[kBwTile];
-  const int s = blockIdx.x, J = blockIdx.y;
-  const int b = s / a.Hkv, h = s - b * a.Hkv;
-  const int N = a.N, nb = (N + kBwTile - 1) / kBwTile;
-  const int tid = threadIdx.x, jl = tid >> 2, c = tid & 3;
-  const int j = J * kBwTile + jl;
-  const int jc = min(j, N - 1);
-  const int n_terms = __popc(a.terms & 7);
-  const float inv_n = n_terms ? 1.0f / n_terms : 0.0f;
-  float kj[QW];
-#pragma unroll
-  for (int e = 0; e < QW; ++e) kj[e] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + c * QW + e);
-  const float lkj = a.lk[((int64_t)b * N + jc) * a.Hkv + h];
-  float carry = 0.0f;
-  float* out = a.lam + (int64_t)s * N * N;
-  for (int I = J; I < nb; ++I) {
-    __syncthreads();
-    for (int e = tid; e < kBwTile * D; e += kBwThreads) {
-      const int r = e / D, col = e - r * D;
-      const int t = min(I * kBwTile + r, N - 1);
-      s_k[r][col] = ld_elem<BF16>(a.kt, (((int64_t)b * N + t) * a.Hkv + h) * D + col);
-    }
-    for (int r = tid; r < kBwTile; r += kBwThreads) {
-      const int t = min(I * kBwTile + r, N - 1);
-      s_lq[r] = a.lq[((int64_t)b * N + t) * a.Hkv + h];
-      s_lb[r] = a.lb[((int64_t)b * N + t) * a.Hkv + h];
-    }
-    __syncthreads();
-    for (int tl = 0; tl < kBwTile; ++tl) {
-      const int t = I * kBwTile + tl;
-      if (t >= N) break;
-      float p = 0.0f;
-#pragma unroll
-      for (int e = 0; e < QW; ++e) p = fmaf(kj[e], s_k[tl][c * QW + e], p);
-      const float sim = quad_sum(p);
-      float A = 0.0f;
-      if (n_terms && t > j) A = log1mexp_f(pair_lambda(a, sim, s_lq[tl], lkj, s_lb[tl], inv_n));
-      carry += A;
-      if (c == 0 && j < N && t >= j) out[(int64_t)t * N + j] = carry;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // 2-4 on the matrix cores: fp32 16x16x4 products (v_mfma_f32_16x16x4_f32).
 // Lane l holds A[l % 16][l / 16] and B[l / 16][l % 16] of a step and
 // D[4 (l / 16) + r][l % 16] of the 16 x 16 result (r = 0..3).  A product whose
@@ -196,6 +120,69 @@ __device__ __forceinline__ void stage_rows(float* dst, const void* src, int b, i
       }
     } else {
       *reinterpret_cast<float4*>(o) = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(src) + g);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1. Lambda[t][j] = sum_{t' <= t} A_{t'j}.  Wave w: keys 16 w + c of the key
+// block; per token tile the similarities K_t K_j^T (tokens x keys), the pair
+// terms, and an inclusive scan down the 16 tokens (within the lane, then
+// across the four lane groups) on top of the column's carry.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBwThreads) void bwd_bias_kernel(BwArgs a) {
+  constexpr int LS = D + 4, NS = D / 4;
+  __shared__ __attribute__((aligned(16))) float s_k[kBwTile * LS];
+  __shared__ float s_lq[kBwTile], s_lb[kBwTile];
+  const int s = blockIdx.x, J = blockIdx.y;
+  const int b = s / a.Hkv, h = s - b * a.Hkv;
+  const int N = a.N, nb = (N + kBwTile - 1) / kBwTile;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int j = J * kBwTile + 16 * w + c, jc = min(j, N - 1);
+  const int n_terms = __popc(a.terms & 7);
+  const float inv_n = n_terms ? 1.0f / n_terms : 0.0f;
+  float kreg[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) kreg[st] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
+  const float lkj = a.lk[((int64_t)b * N + jc) * a.Hkv + h];
+  float* out = a.lam + (int64_t)s * N * N;
+  float carry = 0.0f;
+  for (int I = J; I < nb; ++I) {
+    __syncthreads();
+    stage_rows<D, BF16>(s_k, a.kt, b, N, a.Hkv, h, I * kBwTile);
+    for (int r = threadIdx.x; r < kBwTile; r += kBwThreads) {
+      const int64_t ti = ((int64_t)b * N + min(I * kBwTile + r, N - 1)) * a.Hkv + h;
+      s_lq[r] = a.lq[ti];
+      s_lb[r] = a.lb[ti];
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int tt = 0; tt < 4; ++tt) {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      if (a.terms & 4) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) sc = mfma4(s_k[(16 * tt + c) * LS + 4 * st + g], kreg[st], sc);
+      }
+      // lane holds (token 16 tt + 4 g + r, key j): pair terms, then the scan
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 16 * tt + 4 * g + r, t = I * kBwTile + tl;
+        const bool on = n_terms && t > j && t < N && j < N;
+        const float A = on ? log1mexp_f(pair_lambda(a, sc[r], s_lq[tl], lkj, s_lb[tl], inv_n)) : 0.0f;
+        p[r] = (r ? p[r - 1] : 0.0f) + A;
+      }
+      const float T = p[3];
+      const float T0 = __shfl(T, c, 64), T1 = __shfl(T, c + 16, 64), T2 = __shfl(T, c + 32, 64),
+                  T3 = __shfl(T, c + 48, 64);
+      const float U = (g > 0 ? T0 : 0.0f) + (g > 1 ? T1 : 0.0f) + (g > 2 ? T2 : 0.0f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = I * kBwTile + 16 * tt + 4 * g + r;
+        if (j < N && t < N && t >= j) out[(int64_t)t * N + j] = carry + U + p[r];
+      }
+      carry += T0 + T1 + T2 + T3;
     }
   }
 }
@@ -449,118 +436,189 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_kernel(BwArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 5. decay backward: dLambda -> dA -> dlambda -> gates and keys
+// 5. decay gradients, column pass (key block J, token blocks in reverse).
+// dA_tj = sum_{i >= t} dLambda[i][j] is a reverse scan down the column; with
+// g_tj = dA_tj dlog(1 - e^lam)/dlam / n and, for the similarity term,
+// ds_tj = 2 g_tj / s_tj: dlk_j = sum_t g_tj and dk_j += sum_t ds_tj k_t.
+// g and ds overwrite dLambda and Lambda for the row pass.  The similarity is
+// summed in fp64 on the matrix cores: products of bf16 or fp32 keys are exact
+// there, and the factor 2/s is largest where s is near 0, where an fp32 sum's
+// absolute error would become a large relative one.  The fp64 product's
+// result rows are interleaved (lane l holds rows l / 16 + 4 r), so the token
+// rows are fed permuted and the tile lands as tokens 4 g + r, as in fp32.
 // ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(kBwThreads) void bwd_decay_kernel(BwArgs a) {
-  constexpr int QW = D / 4;
-  __shared__ float s_ki[kBwTile][D + 1];  // keys of the token block (rows)
-  __shared__ float s_kj[kBwTile][D + 1];  // keys of this key block
-  __shared__ float s_dl[kBwTile][kBwTile + 1];
-  __shared__ float s_g[kBwTile][kBwTile + 1];
-  __shared__ float s_ds[kBwTile][kBwTile + 1];
+__global__ __launch_bounds__(kBwThreads) void bwd_decay_col_kernel(BwArgs a) {
+  constexpr int LS = D + 4, NS = D / 4, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) float s_k[kBwTile * LS];
   __shared__ float s_lq[kBwTile], s_lb[kBwTile];
   const int s = blockIdx.x, J = blockIdx.y;
   const int b = s / a.Hkv, h = s - b * a.Hkv;
   const int N = a.N, nb = (N + kBwTile - 1) / kBwTile;
-  const int tid = threadIdx.x, jl = tid >> 2, c = tid & 3;
-  const int j = J * kBwTile + jl, jc = min(j, N - 1);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int j = J * kBwTile + 16 * w + c, jc = min(j, N - 1);
   const int n_terms = __popc(a.terms & 7);
-  if (n_terms == 0) return;  // no decay term: every decay gradient is zero (cleared by the caller)
+  if (n_terms == 0) {  // no decay term: every decay gradient is zero
+    if (g == 0 && j < N) a.dlk[((int64_t)b * N + j) * a.Hkv + h] = 0.0f;
+    return;
+  }
   const float inv_n = 1.0f / n_terms;
-  for (int e = tid; e < kBwTile * D; e += kBwThreads) {
-    const int r = e / D, col = e - r * D;
-    const int jj = min(J * kBwTile + r, N - 1);
-    s_kj[r][col] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jj) * a.Hkv + h) * D + col);
-  }
-  float kj[QW], dkj[QW];
+  const bool SIM = (a.terms & 4) != 0;
+  double kreg[NS];
 #pragma unroll
-  for (int e = 0; e < QW; ++e) {
-    kj[e] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + c * QW + e);
-    dkj[e] = 0.0f;
-  }
+  for (int st = 0; st < NS; ++st)
+    kreg[st] = (double)ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
   const float lkj = a.lk[((int64_t)b * N + jc) * a.Hkv + h];
-  float acc = 0.0f, dlk = 0.0f;
-  const float* dlamS = a.dlam + (int64_t)s * N * N;
+  float* dlamS = a.dlam + (int64_t)s * N * N;  // dLambda in, g out
+  float* lamS = a.lam + (int64_t)s * N * N;    // ds out
+  f32x4 dkj[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dkj[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dlk = 0.0f, carry = 0.0f;
+  const int prow = 4 * (c & 3) + (c >> 2);  // token row this lane feeds to the fp64 product
   for (int I = nb - 1; I >= J; --I) {
     __syncthreads();
-    for (int e = tid; e < kBwTile * D; e += kBwThreads) {
-      const int r = e / D, col = e - r * D;
-      const int tt = min(I * kBwTile + r, N - 1);
-      s_ki[r][col] = ld_elem<BF16>(a.kt, (((int64_t)b * N + tt) * a.Hkv + h) * D + col);
-    }
-    for (int e = tid; e < kBwTile * kBwTile; e += kBwThreads) {
-      const int r = e / kBwTile, col = e - r * kBwTile;
-      const int tt = I * kBwTile + r, jj = J * kBwTile + col;
-      s_dl[r][col] = (tt < N && jj < N && jj <= tt) ? dlamS[(int64_t)tt * N + jj] : 0.0f;
-    }
-    for (int r = tid; r < kBwTile; r += kBwThreads) {
-      const int tt = min(I * kBwTile + r, N - 1);
-      s_lq[r] = a.lq[((int64_t)b * N + tt) * a.Hkv + h];
-      s_lb[r] = a.lb[((int64_t)b * N + tt) * a.Hkv + h];
+    stage_rows<D, BF16>(s_k, a.kt, b, N, a.Hkv, h, I * kBwTile);
+    for (int r = threadIdx.x; r < kBwTile; r += kBwThreads) {
+      const int64_t ti = ((int64_t)b * N + min(I * kBwTile + r, N - 1)) * a.Hkv + h;
+      s_lq[r] = a.lq[ti];
+      s_lb[r] = a.lb[ti];
     }
     __syncthreads();
-    // (a) key lanes: reverse scan of dLambda down the rows, the gradient of
-    // each pair term, the key-side sums.  The similarity is summed in fp64:
-    // the products of bf16 or fp32 keys are exact there, and the factor 2/s
-    // of the similarity term is large where s is small, so an fp32 sum's
-    // absolute error would turn into a large relative one exactly there.
-    for (int tl = kBwTile - 1; tl >= 0; --tl) {
-      const int t = I * kBwTile + tl;
-      acc += s_dl[tl][jl];
-      double p = 0.0;
-      if (a.terms & 4) {
+#pragma unroll 1
+    for (int tt = 3; tt >= 0; --tt) {
+      f64x4 sd = {0.0, 0.0, 0.0, 0.0};
+      if (SIM) {
 #pragma unroll
-        for (int e = 0; e < QW; ++e) p = fma((double)kj[e], (double)s_ki[tl][c * QW + e], p);
-        p = quad_sum_d(p);
+        for (int st = 0; st < NS; ++st)
+          sd = __builtin_amdgcn_mfma_f64_16x16x4f64((double)s_k[(16 * tt + prow) * LS + 4 * st + g], kreg[st], sd, 0, 0,
+                                                    0);
       }
-      const float sim = (float)p;
-      float gn = 0.0f, ds = 0.0f;
-      if (t < N && j < N && t > j) {
-        const float lam = pair_lambda(a, sim, s_lq[tl], lkj, s_lb[tl], inv_n);
-        gn = acc * dlog1mexp(lam) * inv_n;
-        if ((a.terms & 4) && gn != 0.0f && p * p < 1.0) ds = 2.0f * gn / sim;
-      }
-      if (a.terms & 2) dlk += gn;
+      // lane holds (token 16 tt + 4 g + r, key j); reverse inclusive scan of dLambda
+      float x[4], q[4];
 #pragma unroll
-      for (int e = 0; e < QW; ++e) dkj[e] = fmaf(ds, s_ki[tl][c * QW + e], dkj[e]);
-      if (c == 0) {
-        s_g[tl][jl] = gn;
-        s_ds[tl][jl] = ds;
+      for (int r = 0; r < 4; ++r) {
+        const int t = I * kBwTile + 16 * tt + 4 * g + r;
+        x[r] = (t < N && j < N && t >= j) ? dlamS[(int64_t)t * N + j] : 0.0f;
+      }
+      q[3] = x[3];
+      q[2] = x[2] + q[3];
+      q[1] = x[1] + q[2];
+      q[0] = x[0] + q[1];
+      const float T = q[0];
+      const float T0 = __shfl(T, c, 64), T1 = __shfl(T, c + 16, 64), T2 = __shfl(T, c + 32, 64),
+                  T3 = __shfl(T, c + 48, 64);
+      const float V = (g < 1 ? T1 : 0.0f) + (g < 2 ? T2 : 0.0f) + (g < 3 ? T3 : 0.0f);
+      float ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 16 * tt + 4 * g + r, t = I * kBwTile + tl;
+        const float acc = carry + V + q[r];
+        float gn = 0.0f;
+        ds[r] = 0.0f;
+        if (t > j && t < N && j < N) {
+          const float sim = (float)sd[r];
+          const float lam = pair_lambda(a, sim, s_lq[tl], lkj, s_lb[tl], inv_n);
+          gn = acc * dlog1mexp(lam) * inv_n;
+          if (SIM && gn != 0.0f && sd[r] * sd[r] < 1.0) ds[r] = 2.0f * gn / sim;
+        }
+        dlk += gn;
+        if (t < N && j < N) {
+          dlamS[(int64_t)t * N + j] = gn;
+          lamS[(int64_t)t * N + j] = ds[r];
+        }
+      }
+      carry += T0 + T1 + T2 + T3;
+      if (SIM) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) dkj[dt] = mfma4(ds[st], s_k[(16 * tt + 4 * g + st) * LS + 16 * dt + c], dkj[dt]);
       }
     }
-    __syncthreads();
-    // (b) token lanes: the sums over this block's keys of the row-side terms
-    {
-      const int tl = tid >> 2, t = I * kBwTile + tl;
-      float gsum = 0.0f;
-      for (int k2 = c * 16; k2 < c * 16 + 16; ++k2) gsum += s_g[tl][k2];
-      gsum = quad_sum(gsum);
-      float dkt[QW];
+  }
+  dlk += __shfl_xor(dlk, 16, 64);
+  dlk += __shfl_xor(dlk, 32, 64);
+  if (g == 0 && j < N) a.dlk[((int64_t)b * N + j) * a.Hkv + h] = (a.terms & 2) ? dlk : 0.0f;
+  if (SIM) {  // lane holds dk[key 16 w + 4 g + r][dim 16 dt + c]; this block's keys are this workgroup's alone
 #pragma unroll
-      for (int e = 0; e < QW; ++e) dkt[e] = 0.0f;
-      for (int k2 = 0; k2 < kBwTile; ++k2) {
-        const float w = s_ds[tl][k2];
+    for (int r = 0; r < 4; ++r) {
+      const int jo = J * kBwTile + 16 * w + 4 * g + r;
+      if (jo < N) {
+        float* o = a.dk + (((int64_t)b * N + jo) * a.Hkv + h) * D + c;
 #pragma unroll
-        for (int e = 0; e < QW; ++e) dkt[e] = fmaf(w, s_kj[k2][c * QW + e], dkt[e]);
+        for (int dt = 0; dt < DT; ++dt) o[16 * dt] += dkj[dt][r];
       }
-      if (t < N) {
-        const int64_t gi = ((int64_t)b * N + t) * a.Hkv + h;
-        if (c == 0 && (a.terms & 1)) atomicAdd(&a.dlq[gi], gsum);
-        if (c == 0 && (a.terms & 4)) atomicAdd(&a.dlb[gi], gsum);
-        if (a.terms & 4) {
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 6. decay gradients, row pass (token block I, key blocks J <= I): dlq_t and
+// dlb_t = sum_j g_tj, and dk_t += sum_j ds_tj k_j on the matrix cores.  Wave
+// w: tokens 16 w + c.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(kBwThreads) void bwd_decay_row_kernel(BwArgs a) {
+  constexpr int LS = D + 4, LT = kBwTile + 4, DT = D / 16;
+  __shared__ __attribute__((aligned(16))) float s_kj[kBwTile * LS];
+  __shared__ __attribute__((aligned(16))) float s_ds[kBwTile * LT];
+  __shared__ __attribute__((aligned(16))) float s_gn[kBwTile * LT];
+  const int s = blockIdx.x, I = blockIdx.y;
+  const int b = s / a.Hkv, h = s - b * a.Hkv;
+  const int N = a.N;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const int t = I * kBwTile + 16 * w + c;
+  const int n_terms = __popc(a.terms & 7);
+  const bool SIM = (a.terms & 4) != 0;
+  f32x4 dkt[DT];
 #pragma unroll
-          for (int e = 0; e < QW; ++e) atomicAdd(&a.dk[gi * D + c * QW + e], dkt[e]);
+  for (int dt = 0; dt < DT; ++dt) dkt[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float gs = 0.0f;
+  const float* gnS = a.dlam + (int64_t)s * N * N;
+  const float* dsS = a.lam + (int64_t)s * N * N;
+  if (n_terms) {
+    for (int J = 0; J <= I; ++J) {
+      __syncthreads();
+      if (SIM) stage_rows<D, BF16>(s_kj, a.kt, b, N, a.Hkv, h, J * kBwTile);
+      for (int e = threadIdx.x; e < kBwTile * kBwTile; e += kBwThreads) {
+        const int r = e / kBwTile, col = e - r * kBwTile;
+        const int tt = I * kBwTile + r, jj = J * kBwTile + col;
+        const bool ok = tt < N && jj < N;
+        s_gn[r * LT + col] = ok ? gnS[(int64_t)tt * N + jj] : 0.0f;
+        s_ds[r * LT + col] = (ok && SIM) ? dsS[(int64_t)tt * N + jj] : 0.0f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 16; ++k) gs += s_gn[(16 * w + c) * LT + 16 * g + k];
+      if (SIM) {
+#pragma unroll 4
+        for (int st = 0; st < 16; ++st) {
+          const float av = s_ds[(16 * w + c) * LT + 4 * st + g];
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) dkt[dt] = mfma4(av, s_kj[(4 * st + g) * LS + 16 * dt + c], dkt[dt]);
         }
       }
     }
   }
-  if (j < N) {
-    const int64_t gi = ((int64_t)b * N + j) * a.Hkv + h;
-    if (c == 0 && (a.terms & 2)) atomicAdd(&a.dlk[gi], dlk);
-    if (a.terms & 4) {
+  gs += __shfl_xor(gs, 16, 64);
+  gs += __shfl_xor(gs, 32, 64);
+  if (g == 0 && t < N) {
+    const int64_t gi = ((int64_t)b * N + t) * a.Hkv + h;
+    a.dlq[gi] = (a.terms & 1) ? gs : 0.0f;
+    a.dlb[gi] = (a.terms & 4) ? gs : 0.0f;
+  }
+  if (n_terms && SIM) {  // lane holds dk[token 16 w + 4 g + r][dim 16 dt + c]; this block's tokens are ours alone
 #pragma unroll
-      for (int e = 0; e < QW; ++e) atomicAdd(&a.dk[gi * D + c * QW + e], dkj[e]);
+    for (int r = 0; r < 4; ++r) {
+      const int to = I * kBwTile + 16 * w + 4 * g + r;
+      if (to < N) {
+        float* o = a.dk + (((int64_t)b * N + to) * a.Hkv + h) * D + c;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[16 * dt] += dkt[dt][r];
+      }
     }
   }
 }
@@ -582,7 +640,8 @@ static void launch_bw(const BwArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3(S * G, nb), dim3(kBwThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_kv_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_q_kernel<D, BF16>), dim3(S * G, nb), dim3(kBwThreads), 0, st, a);
-  hipLaunchKernelGGL((bwd_decay_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_decay_col_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_decay_row_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
 }
 
 hipError_t launch_backward(int B, int Hq, int Hkv, int D, int N, int terms, float scale, bool bf16, const void* qt,
@@ -618,12 +677,6 @@ hipError_t launch_backward(int B, int Hq, int Hkv, int D, int N, int terms, floa
   a.dlam = reinterpret_cast<float*>(p + mat);
   a.lse = reinterpret_cast<float*>(p + 2 * mat);
   a.dd = reinterpret_cast<float*>(p + 2 * mat + vec);
-  // the gate gradients are sums of atomics
-  const size_t gb = sizeof(float) * (size_t)B * N * Hkv;
-  hipError_t e;
-  if ((e = launch_fill_zero(dlq, gb, st)) != hipSuccess) return e;
-  if ((e = launch_fill_zero(dlk, gb, st)) != hipSuccess) return e;
-  if ((e = launch_fill_zero(dlb, gb, st)) != hipSuccess) return e;
   if (D == 64) {
     if (bf16) launch_bw<64, true>(a, st);
     else launch_bw<64, false>(a, st);
