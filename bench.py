@@ -71,6 +71,16 @@ def load_traffic(name: str, path: str):
 # ---------------------------------------------------------------------------
 # decode workloads
 # ---------------------------------------------------------------------------
+def cache_desc(cfg) -> str:
+    """The initial cache of a decode workload, in words."""
+    if cfg.len_kind == "empty":
+        return "from an empty cache"
+    if cfg.len_kind == "ragged":
+        return (f"ragged pruned cache, nominal contexts {cfg.nom_lo}..{cfg.nom_hi}, compression "
+                f"{cfg.rho_lo:g}..{cfg.rho_hi:g}x per head")
+    return f"pruned cache nominal {cfg.nominal} (~{cfg.nominal / cfg.len_mean:.0f}x)"
+
+
 def bench_decode(args):
     import torch
 
@@ -244,8 +254,8 @@ def bench_decode(args):
         "data": "synthetic",
         "config": {
             "workload": f"{cfg.name}: UA decode layer B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} "
-                        f"D={cfg.D}, pruned cache nominal {cfg.nominal} (~{cfg.nominal / cfg.len_mean:.0f}x), "
-                        f"p={cfg.p}, decode + compaction every step, ring of {R} layer instances",
+                        f"D={cfg.D}, {cache_desc(cfg)}, p={cfg.p}, decode + compaction every step, "
+                        f"ring of {R} layer instances",
             "global_batch": cfg.B,
             "ring_instances": R,
             "tokens_per_step": tokens,
