@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
     __syncthreads();
     const int id = s_ticket;
 
-    if (id >= total) {
+    if (id >= total || id < 0) {  // (a negative id only from a corrupted ticket word: touch no chunk)
       // ---- exit: report done; the workgroup with the last ticket commits
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
