@@ -3,7 +3,7 @@
 Sequences of one call append different numbers of tokens, packed row after
 row; the oracle runs each sequence's prefill on its own.  Every output row,
 the stored keys and the whole cache are compared after each call, and the
-rows past the packed ones must stay untouched.  Cases: empty sequences,
+rows past the packed ones must stay untouched.  Cases: empty sequences, a segment without room (R21 per sequence),
 sequences longer than the others by several token blocks, lengths off the
 64-token grid, a populated cache, both attention kernels (head dim 64 with up
 to four query heads per KV head, and head dim 128 or eight query heads), and
@@ -79,3 +79,44 @@ def test_varlen_equal_lengths_is_prefill():
     g1, g2 = gpu_state(l1), gpu_state(l2)
     for key in ("K", "V", "lam", "lk", "seg_len", "next_pos"):
         assert np.array_equal(g1[key], g2[key]), key
+
+
+def test_varlen_segment_without_room():
+    """R21 per sequence: a segment without room for its own sequence's tokens is left unchanged,
+    its heads' outputs are zero and status bit 0 is set; every other segment is computed as if the
+    cap were not there (bit-identical to a run with room), and positions advance by each n_b."""
+    import torch
+
+    from tests.harness import device_layer, gpu_state
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    cfg = config("1b-prefill", B=3, H_q=4, H_kv=2, D=64, n_total=64, chunk=64)
+    lens = [40, 64, 0]
+    w = make_weights(cfg)
+    c_ok = make_cache(cfg, w)
+    c_cap = make_cache(cfg, w)
+    c_cap.seg_cap[2] = 48  # segment 2 (b=1, h=0) cannot take sequence 1's 64 tokens
+    inp = make_step_inputs(cfg, 0, 64)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pack = lambda a: np.concatenate([a[b, : lens[b]] for b in range(cfg.B)], axis=0)
+    ins = [pack(a) for a in (inp.q, inp.k, inp.v, inp.x)]
+    outs, states = [], []
+    for c in (c_ok, c_cap):
+        layer = device_layer(cfg, w, c, max_tokens=64)
+        y, _ = layer.prefill_varlen(*ins, cu)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+        states.append(gpu_state(layer))
+    ok, cap = states
+    assert ok["status"] == 0 and cap["status"] & 1
+    assert list(cap["seg_len"]) == [40, 40, 0, 64, 0, 0]
+    assert list(cap["next_pos"]) == [40, 64, 0]
+    G = cfg.H_q // cfg.H_kv
+    r1 = slice(cu[1], cu[2])
+    assert np.all(outs[1][r1, :G] == 0.0)                       # sequence 1, KV head 0: zeros
+    assert np.array_equal(outs[1][r1, G:], outs[0][r1, G:])     # its other head as with room
+    assert np.array_equal(outs[1][: cu[1]], outs[0][: cu[1]])   # sequence 0 as with room
+    for s in (0, 1, 3):
+        o, n = int(cap["seg_off"][s]), int(cap["seg_len"][s])
+        for key in ("K", "V", "lam", "lk"):
+            assert np.array_equal(cap[key][o:o + n], ok[key][o:o + n]), (s, key)
