@@ -3,10 +3,11 @@
 Sequences of one call append different numbers of tokens, packed row after
 row; the oracle runs each sequence's prefill on its own.  Every output row,
 the stored keys and the whole cache are compared after each call, and the
-rows past the packed ones must stay untouched.  Cases: empty sequences, a segment without room (R21 per sequence),
+rows past the packed ones must stay untouched.  Cases: empty sequences,
 sequences longer than the others by several token blocks, lengths off the
 64-token grid, a populated cache, both attention kernels (head dim 64 with up
-to four query heads per KV head, and head dim 128 or eight query heads), and
+to four query heads per KV head, and head dim 128 or eight query heads), a
+segment without room for its own sequence's tokens (R21 per sequence), and
 equal lengths, which must give ua_prefill's outputs bit for bit.
 """
 
