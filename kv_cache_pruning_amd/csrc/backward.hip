@@ -193,12 +193,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_bias_kernel(BwArgs a) {
 // per token, O^T += V^T P^T.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
-__global__ __launch_bounds__(kBwThreads) void bwd_stats_kernel(BwArgs a) {
+__device__ __forceinline__ void bwd_stats_block(const BwArgs& a, const int by) {
   constexpr int LS = D + 4, NS = D / 4, DT = D / 16;
   __shared__ __attribute__((aligned(16))) float s_k[kBwTile * LS];
   __shared__ __attribute__((aligned(16))) float s_v[kBwTile * LS];
   const int G = a.Hq / a.Hkv;
-  const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = blockIdx.y;
+  const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = by;
   const int b = s / a.Hkv, h = s - b * a.Hkv, hq = h * G + ga;
   const int N = a.N;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
@@ -373,12 +373,12 @@ __global__ __launch_bounds__(kBwThreads) void bwd_kv_kernel(BwArgs a) {
 // tile S^T = K Q^T and dP^T = V dO^T (keys x tokens), dS, then dQ += dS K.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
-__global__ __launch_bounds__(kBwThreads) void bwd_q_kernel(BwArgs a) {
+__device__ __forceinline__ void bwd_q_block(const BwArgs& a, const int by) {
   constexpr int LS = D + 4, NS = D / 4, DT = D / 16;
   __shared__ __attribute__((aligned(16))) float s_k[kBwTile * LS];
   __shared__ __attribute__((aligned(16))) float s_v[kBwTile * LS];
   const int G = a.Hq / a.Hkv;
-  const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = blockIdx.y;
+  const int s = blockIdx.x / G, ga = blockIdx.x - s * G, I = by;
   const int b = s / a.Hkv, h = s - b * a.Hkv, hq = h * G + ga;
   const int N = a.N;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
@@ -434,6 +434,26 @@ __global__ __launch_bounds__(kBwThreads) void bwd_q_kernel(BwArgs a) {
     }
   }
 }
+
+// Causal balance for the token-block kernels: token block I has I + 1 key
+// blocks of work, so each workgroup takes block y and block nb - 1 - y (the
+// middle one alone when nb is odd) and every workgroup does the same work.
+// (The key-block kernel keeps one block per workgroup: paired, its four
+// workgroups per CU became two and it was no faster.)
+#define UA_BW_PAIRED(NAME)                                                  \
+  template <int D, bool BF16>                                               \
+  __global__ __launch_bounds__(kBwThreads) void NAME##_kernel(BwArgs a) {   \
+    const int nb = (a.N + kBwTile - 1) / kBwTile;                           \
+    const int y0 = blockIdx.y, y1 = nb - 1 - (int)blockIdx.y;               \
+    NAME##_block<D, BF16>(a, y0);                                           \
+    if (y1 != y0) {                                                         \
+      __syncthreads();                                                      \
+      NAME##_block<D, BF16>(a, y1);                                         \
+    }                                                                       \
+  }
+UA_BW_PAIRED(bwd_stats)
+UA_BW_PAIRED(bwd_q)
+#undef UA_BW_PAIRED
 
 // ---------------------------------------------------------------------------
 // 5. decay gradients, column pass (key block J, token blocks in reverse).
@@ -637,9 +657,10 @@ template <int D, bool BF16>
 static void launch_bw(const BwArgs& a, hipStream_t st) {
   const int S = a.B * a.Hkv, G = a.Hq / a.Hkv, nb = (a.N + kBwTile - 1) / kBwTile;
   hipLaunchKernelGGL((bwd_bias_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
-  hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3(S * G, nb), dim3(kBwThreads), 0, st, a);
+  const int nh = (nb + 1) / 2;  // paired blocks
+  hipLaunchKernelGGL((bwd_stats_kernel<D, BF16>), dim3(S * G, nh), dim3(kBwThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_kv_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
-  hipLaunchKernelGGL((bwd_q_kernel<D, BF16>), dim3(S * G, nb), dim3(kBwThreads), 0, st, a);
+  hipLaunchKernelGGL((bwd_q_kernel<D, BF16>), dim3(S * G, nh), dim3(kBwThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_decay_col_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
   hipLaunchKernelGGL((bwd_decay_row_kernel<D, BF16>), dim3(S, nb), dim3(kBwThreads), 0, st, a);
 }
