@@ -99,6 +99,25 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// bf16 16x16x32 product: lane l holds A[l % 16][8 (l / 16) .. + 7] and
+// B[8 (l / 16) .. + 7][l % 16] of each 32-wide k chunk; the result has the
+// same 16 x 16 layout as the fp32 product.  Used for q~ . k~ when both are
+// bf16: the products are exact and the sum is fp32, as in the fp32 product.
+__device__ __forceinline__ f32x4 mfma_bf16x32(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// The 16-byte piece of row r (clamped to N - 1) of a bf16 [B, N, H, D] tensor
+// at (b, head) holding dims 8 q .. 8 q + 7.
+template <int D>
+__device__ __forceinline__ u32x4 bf16_piece(const void* src, int b, int N, int H, int head, int r, int q) {
+  const int64_t e = (((int64_t)b * N + min(r, N - 1)) * H + head) * D + 8 * q;
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + e);
+}
+
 __device__ __forceinline__ float expf_masked(float e) { return e == -__builtin_huge_valf() ? 0.0f : __expf(e); }
 
 // Rows r0 .. r0 + 63 (clamped to N - 1) of a [B, N, H, D] tensor at (b, head)
@@ -203,24 +222,43 @@ __device__ __forceinline__ void bwd_stats_block(const BwArgs& a, const int by) {
   const int N = a.N;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
   const int t = I * kBwTile + 16 * w + c, tc = min(t, N - 1);
-  float qreg[NS];
+  constexpr int KC = D / 32;
+  float qreg[BF16 ? 1 : NS];
+  u32x4 qb[BF16 ? KC : 1];
+  if constexpr (BF16) {
 #pragma unroll
-  for (int st = 0; st < NS; ++st) qreg[st] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g);
+    for (int kc = 0; kc < KC; ++kc) qb[kc] = bf16_piece<D>(a.qt, b, N, a.Hq, hq, tc, 4 * kc + g);
+  } else {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) qreg[st] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g);
+  }
   f32x4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -__builtin_huge_valf(), lsum = 0.0f;
   const float* lrow = a.lam + (int64_t)s * N * N + (int64_t)tc * N;
   for (int J = 0; J <= I; ++J) {
+    u32x4 kb[BF16 ? 4 : 1][KC];  // bf16: the key rows 16 kt + c of the block, straight from HBM
+    if constexpr (BF16) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) kb[kt][kc] = bf16_piece<D>(a.kt, b, N, a.Hkv, h, J * kBwTile + 16 * kt + c, 4 * kc + g);
+    }
     __syncthreads();
-    stage_rows<D, BF16>(s_k, a.kt, b, N, a.Hkv, h, J * kBwTile);
+    if constexpr (!BF16) stage_rows<D, BF16>(s_k, a.kt, b, N, a.Hkv, h, J * kBwTile);
     stage_rows<D, BF16>(s_v, a.v, b, N, a.Hkv, h, J * kBwTile);
     __syncthreads();
-#pragma unroll 1
+#pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
 #pragma unroll
-      for (int st = 0; st < NS; ++st) sc = mfma4(s_k[(16 * kt + c) * LS + 4 * st + g], qreg[st], sc);
+        for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16x32(kb[kt][kc], qb[kc], sc);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) sc = mfma4(s_k[(16 * kt + c) * LS + 4 * st + g], qreg[st], sc);
+      }
       float e[4];
       float mt = -__builtin_huge_valf();
 #pragma unroll
@@ -285,11 +323,17 @@ __global__ __launch_bounds__(kBwThreads) void bwd_kv_kernel(BwArgs a) {
   const int N = a.N, nb = (N + kBwTile - 1) / kBwTile;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
   const int j = J * kBwTile + 16 * w + c, jc = min(j, N - 1);
-  float kreg[NS], vreg[NS];
+  constexpr int KC = D / 32;
+  float kreg[BF16 ? 1 : NS], vreg[NS];
+  u32x4 kb[BF16 ? KC : 1];  // bf16: this lane's key row for the bf16 product
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    kreg[st] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
+    if constexpr (!BF16) kreg[st] = ld_elem<BF16>(a.kt, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
     vreg[st] = ld_elem<BF16>(a.v, (((int64_t)b * N + jc) * a.Hkv + h) * D + 4 * st + g);
+  }
+  if constexpr (BF16) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) kb[kc] = bf16_piece<D>(a.kt, b, N, a.Hkv, h, jc, 4 * kc + g);
   }
   f32x4 dv[DT], dk[DT];
 #pragma unroll
@@ -317,10 +361,21 @@ __global__ __launch_bounds__(kBwThreads) void bwd_kv_kernel(BwArgs a) {
 #pragma unroll 1
       for (int tt = 0; tt < 4; ++tt) {
         f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BF16) {
+          // the token rows' bf16 pieces, loaded while dP runs
+          u32x4 qa[KC];
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          sc = mfma4(s_q[(16 * tt + c) * LS + 4 * st + g], kreg[st], sc);
-          dp = mfma4(s_do[(16 * tt + c) * LS + 4 * st + g], vreg[st], dp);
+          for (int kc = 0; kc < KC; ++kc) qa[kc] = bf16_piece<D>(a.qt, b, N, a.Hq, hq, I * kBwTile + 16 * tt + c, 4 * kc + g);
+#pragma unroll
+          for (int st = 0; st < NS; ++st) dp = mfma4(s_do[(16 * tt + c) * LS + 4 * st + g], vreg[st], dp);
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16x32(qa[kc], kb[kc], sc);
+        } else {
+#pragma unroll
+          for (int st = 0; st < NS; ++st) {
+            sc = mfma4(s_q[(16 * tt + c) * LS + 4 * st + g], kreg[st], sc);
+            dp = mfma4(s_do[(16 * tt + c) * LS + 4 * st + g], vreg[st], dp);
+          }
         }
         // lane holds (token 16 tt + 4 g + r, key j)
         float P[4], dS[4];
@@ -383,11 +438,17 @@ __device__ __forceinline__ void bwd_q_block(const BwArgs& a, const int by) {
   const int N = a.N;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
   const int t = I * kBwTile + 16 * w + c, tc = min(t, N - 1);
-  float qreg[NS], oreg[NS];
+  constexpr int KC = D / 32;
+  float qreg[BF16 ? 1 : NS], oreg[NS];
+  u32x4 qb[BF16 ? KC : 1];  // bf16: this lane's token row for the bf16 product
 #pragma unroll
   for (int st = 0; st < NS; ++st) {
-    qreg[st] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g);
+    if constexpr (!BF16) qreg[st] = ld_elem<BF16>(a.qt, (((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g);
     oreg[st] = a.dO[(((int64_t)b * N + tc) * a.Hq + hq) * D + 4 * st + g];
+  }
+  if constexpr (BF16) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) qb[kc] = bf16_piece<D>(a.qt, b, N, a.Hq, hq, tc, 4 * kc + g);
   }
   const float lse = a.lse[((int64_t)b * N + tc) * a.Hq + hq];
   const float dd = a.dd[((int64_t)b * N + tc) * a.Hq + hq];
@@ -403,10 +464,21 @@ __device__ __forceinline__ void bwd_q_block(const BwArgs& a, const int by) {
 #pragma unroll 1
     for (int kt = 0; kt < 4; ++kt) {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+        // the key rows' bf16 pieces, loaded while dP^T runs
+        u32x4 ka[KC];
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        sc = mfma4(s_k[(16 * kt + c) * LS + 4 * st + g], qreg[st], sc);
-        dp = mfma4(s_v[(16 * kt + c) * LS + 4 * st + g], oreg[st], dp);
+        for (int kc = 0; kc < KC; ++kc) ka[kc] = bf16_piece<D>(a.kt, b, N, a.Hkv, h, J * kBwTile + 16 * kt + c, 4 * kc + g);
+#pragma unroll
+        for (int st = 0; st < NS; ++st) dp = mfma4(s_v[(16 * kt + c) * LS + 4 * st + g], oreg[st], dp);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) sc = mfma_bf16x32(ka[kc], qb[kc], sc);
+      } else {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          sc = mfma4(s_k[(16 * kt + c) * LS + 4 * st + g], qreg[st], sc);
+          dp = mfma4(s_v[(16 * kt + c) * LS + 4 * st + g], oreg[st], dp);
+        }
       }
       // lane holds (key 16 kt + 4 g + r, token t)
       float dS[4];
