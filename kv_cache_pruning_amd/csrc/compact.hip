@@ -35,13 +35,15 @@
 
 namespace ua {
 
-constexpr int kCompactThreads = 256;
-
-template <int RB>  // row bytes of K / V
+// Two workgroup sizes: 256 threads for caches whose chunks are about as many
+// as the grid's workgroups, 512 threads (chunks twice as long) for larger
+// caches, where a workgroup walks several chunks in turn and fewer, longer
+// chunks shorten that walk.
+template <int RB, int NT>  // row bytes of K / V, threads per workgroup
 struct CompactShape {
-  static constexpr int CH = RB <= 128 ? 256 : (RB <= 256 ? 128 : 64);  // entries per chunk
-  static constexpr int P16 = RB / 16;                                  // 16-byte pieces per row
-  static constexpr int PPT = CH * P16 / kCompactThreads;               // pieces per thread
+  static constexpr int CH = (RB <= 128 ? 256 : (RB <= 256 ? 128 : 64)) * NT / 256;  // entries per chunk
+  static constexpr int P16 = RB / 16;                                                // 16-byte pieces per row
+  static constexpr int PPT = CH * P16 / NT;                                          // pieces per thread
 };
 
 __device__ __forceinline__ int ldi_coh(const int* p) {
@@ -59,9 +61,9 @@ constexpr int kCompactGrid = 256;  // persistent workgroups (one per CU)
 
 __device__ __forceinline__ int chunks_of(int len, int ch) { return len <= 0 ? 0 : (len + ch - 1) / ch; }
 
-template <int RB>
+template <int RB, int kCompactThreads>
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, Control ctl, float tau, int32_t* kept) {
-  using Sh = CompactShape<RB>;
+  using Sh = CompactShape<RB, kCompactThreads>;
   constexpr int CH = Sh::CH, P16 = Sh::P16, PPT = Sh::PPT;
   __shared__ int s_scan[kCompactThreads / 64 + 1];
   __shared__ int s_info[4];
@@ -286,7 +288,13 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
 template <int RB>
 static hipError_t launch_rb(const LayerArgs& a, const Control& ctl, float tau, int32_t* kept, hipStream_t st) {
   const int grid = ctl.max_chunks < kCompactGrid ? ctl.max_chunks : kCompactGrid;
-  hipLaunchKernelGGL((compact_kernel<RB>), dim3(grid), dim3(kCompactThreads), 0, st, a, ctl, tau, kept);
+  // chunks of 256-thread workgroups the capacity allows, against the grid
+  const int64_t cap_chunks = a.total_slots / CompactShape<RB, 256>::CH;
+  if (cap_chunks > 2 * (int64_t)kCompactGrid) {
+    hipLaunchKernelGGL((compact_kernel<RB, 512>), dim3(grid), dim3(512), 0, st, a, ctl, tau, kept);
+  } else {
+    hipLaunchKernelGGL((compact_kernel<RB, 256>), dim3(grid), dim3(256), 0, st, a, ctl, tau, kept);
+  }
   return hipGetLastError();
 }
 
