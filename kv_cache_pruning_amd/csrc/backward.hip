@@ -22,8 +22,9 @@
 //                            key side of dk.
 //   6. bwd_decay_row_kernel  per token block: dlq, dlb and the token side of dk.
 // Every kernel runs its products on the matrix cores (fp32 16x16x4 tiles; the
-// decay pass's similarity in fp64) and owns the rows it writes, so no output
-// needs clearing and no atomics are used.  Lambda and dLambda are N x N fp32
+// decay pass's similarity in fp64; q~ . k~ in bf16 when the inputs are bf16)
+// and owns the rows it writes, so no output needs clearing and no atomics are
+// used.  Lambda and dLambda are N x N fp32
 // per segment in the workspace; everything is fp32 inside.
 
 #include <cmath>
