@@ -300,7 +300,12 @@ ua_status ua_prefill_varlen(const ua_dims* dims, const ua_params* params, const 
  * the clamp holds.  The chain through RoPE, the key normalisation and the gate
  * projections is elementwise or a plain GEMM and stays with the caller.  The
  * workspace (ua_backward_workspace_bytes) holds the N x N bias and its
- * gradient per segment; it needs no zero fill.
+ * gradient per segment (2 N^2 fp32 per (sequence, KV head), 256-byte
+ * aligned); it needs no zero fill, and ua_backward_workspace_bytes returns 0
+ * for dims it rejects.  Errors: UA_ERR_INVALID_ARG (n_tokens < 1, a null or
+ * misaligned pointer), UA_ERR_UNSUPPORTED (head dim other than 64 or 128),
+ * UA_ERR_WORKSPACE (ws_bytes too small), UA_ERR_HIP (launch failure).  The
+ * call is asynchronous on `stream`.
  */
 typedef struct ua_grad_inputs {
   const void* q;
