@@ -143,3 +143,32 @@ def test_backward_1b_chunk():
     """The 1B-shape training chunk (32 / 8 heads, d 64, N 1024): one sequence against the oracle in full."""
     B, N, Hq, Hkv, d = 1, 1024, 32, 8, 64
     _check(B, N, Hq, Hkv, d, True, U.TERMS_ALL, seed=123)
+
+
+def test_backward_bench_size_sampled():
+    """The bench's workload (B = 2, N = 4096, 32 / 8 heads, d = 64, bf16): the device backward of the
+    whole batch, and one (sequence, KV head) group of it against the oracle in full."""
+    import torch
+
+    import kv_cache_pruning_amd as K
+
+    B, N, Hq, Hkv, d = 2, 4096, 32, 8, 64
+    G = Hq // Hkv
+    print(f"[backward] bench size B={B} N={N} Hq={Hq} Hkv={Hkv} d={d}", flush=True)
+    q, k, v, lq, lk, lb, dO = _inputs(B, N, Hq, Hkv, d, True, 0)
+    got = _device_backward(q, k, v, lq, lk, lb, dO, U.TERMS_ALL, True)
+    b, h = 1, 5
+    qs, hs = slice(h * G, (h + 1) * G), slice(h, h + 1)
+    ref = U.ua_grad.attention_backward(q[b, :, qs].astype(np.float64), k[b, :, hs].astype(np.float64),
+                                       v[b, :, hs].astype(np.float64), lq[b, :, hs].astype(np.float64),
+                                       lk[b, :, hs].astype(np.float64), lb[b, :, hs].astype(np.float64),
+                                       dO[b, :, qs].astype(np.float64), U.TERMS_ALL, 1.0 / math.sqrt(d))
+    parts = (got[0][b, :, qs], got[1][b, :, hs], got[2][b, :, hs], got[3][b, :, hs], got[4][b, :, hs],
+             got[5][b, :, hs])
+    for name, g, r in zip(NAMES, parts, ref):
+        assert np.isfinite(g).all(), name
+        e = float(np.abs(g - r).max() / np.abs(r).max())
+        print(f"  {name} scaled error {e:.2e}", flush=True)
+        assert e <= TOL, (name, e)
+    for a in got:  # every other group is finite too
+        assert np.isfinite(a).all()
