@@ -121,3 +121,57 @@ def test_varlen_segment_without_room():
         o, n = int(cap["seg_off"][s]), int(cap["seg_len"][s])
         for key in ("K", "V", "lam", "lk"):
             assert np.array_equal(cap[key][o:o + n], ok[key][o:o + n]), (s, key)
+
+
+def test_varlen_bench_size_sampled():
+    """The bench's variable-length workload (8 packed sequences of 128..2048 tokens, 1B heads, from an
+    empty cache) in one call: for sampled segments, the final log-bias of every key and y at sampled
+    rows against the oracle's dense definitions (O5 as column sums, O7 per row)."""
+    import torch
+
+    import oracle as U
+    from tests.harness import _maxabs, _maxrel, device_layer, gpu_state, oracle_dims, oracle_params, ulp_bf16, y_tol
+    from ua_inputs import make_cache, make_step_inputs, make_weights
+
+    B = 8
+    lens = [int(x) for x in np.random.default_rng(7).integers(128, 2049, B)]
+    nmax = max(lens)
+    cfg = config("1b-prefill", B=B, n_total=nmax, chunk=nmax)
+    print(f"[varlen] bench size lens={lens}", flush=True)
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    layer = device_layer(cfg, w, c, max_tokens=nmax)
+    inp = make_step_inputs(cfg, 0, nmax, 0)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pack = lambda a: np.concatenate([a[b, : lens[b]] for b in range(B)], axis=0)
+    y, _ = layer.prefill_varlen(pack(inp.q), pack(inp.k), pack(inp.v), pack(inp.x), cu)
+    torch.cuda.synchronize()
+    yg = y.float().cpu().numpy().astype(np.float64)
+    g = gpu_state(layer)
+    assert g["status"] == 0 and list(g["seg_len"]) == [lens[s // cfg.H_kv] for s in range(B * cfg.H_kv)]
+    od, op = oracle_dims(cfg), oracle_params(w)
+    G = cfg.H_q // cfg.H_kv
+    rng = np.random.default_rng(99)
+    y_err = lam_err = 0.0
+    for s in (0, 13, 42, 63):
+        b, h = divmod(s, cfg.H_kv)
+        n = lens[b]
+        o = int(c.seg_off[s])
+        Kt = g["K"][o:o + n]
+        k_or = U.round_cache(od, U.rope(U.l2_normalize(inp.k[b, :n, h].astype(np.float64)), np.arange(n), od.rope_base))
+        assert not np.any(np.abs(Kt - k_or) > np.maximum(ulp_bf16(k_or), 2e-7) * 1.0001), f"seg {s}: stored keys"
+        lq, lk, lb = U.gates(od, op, inp.x[b, :n].astype(np.float64))
+        rows = np.unique(np.append(rng.choice(n, 4, replace=False), n - 1))
+        lam_rows = U.dense_logbias(od.terms, Kt, lq[:, h], lk[:, h], lb[:, h], rows=rows)
+        lam_fin, lo = g["lam"][o:o + n], lam_rows[-1]
+        fin = np.isfinite(lo)
+        assert np.array_equal(np.isneginf(lam_fin), np.isneginf(lo)), f"seg {s}: -inf pattern"
+        lam_err = max(lam_err, _maxrel(lam_fin[fin], lo[fin]))
+        V = g["V"][o:o + n]
+        for ri, i in enumerate(rows):
+            qt = U.rope(inp.q[b, i, h * G:(h + 1) * G].astype(np.float64), np.full(G, i), od.rope_base)
+            oi = U.attend(qt, Kt[:i + 1], V[:i + 1], lam_rows[ri, :i + 1], od.scale)
+            gam = U.output_gate(od, op, inp.x[b, i].astype(np.float64))[h * G:(h + 1) * G]
+            y_err = max(y_err, _maxabs(yg[cu[b] + i, h * G:(h + 1) * G], gam * oi))
+    print(f"  max |dy| {y_err:.2e}  max rel dLambda {lam_err:.2e}", flush=True)
+    assert y_err <= y_tol(cfg) and lam_err <= 1e-4
