@@ -141,10 +141,11 @@ __device__ __forceinline__ void row_f32(const Row8<BF16>& r, float (&o)[8]) {
   }
 }
 
-// Entries per lane group (rows held in registers at once).  Fewer entries per
-// tile spread a step over more compute units: a tile's VALU work, not its
-// bytes, sets its time at these sizes.
-constexpr int decode_nb(int d) { return d == 64 ? 2 : 4; }
+// Entries per lane group (rows held in registers at once).  Four keeps every
+// load of a tile in flight together without spilling at group sizes up to 4;
+// two left the tiles' fixed costs (the combine, the per-tile partials) to
+// dominate at large batches, eight spills.
+constexpr int decode_nb(int) { return 4; }
 
 template <int D, int NB_>
 struct DecodeShape {
@@ -153,6 +154,7 @@ struct DecodeShape {
   static constexpr int NB = NB_;        // entries per group
   static constexpr int TW = NGW * NB;   // entries per wave
   static constexpr int TWG = TW * kDecWaves;
+  static_assert(NB <= LPE, "lane c < NB of a group holds entry c's flags");
 };
 
 __device__ __forceinline__ int tiles_of(int n, int twg) { return n <= 0 ? 1 : ceil_div(n, twg); }
