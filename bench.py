@@ -87,7 +87,12 @@ def bench_decode(args):
     from kv_cache_pruning_amd.layer import DeviceCache, DeviceWeights, Layer, LayerShape, Workspace
     from ua_inputs import config, make_cache, make_step_inputs, make_weights
 
-    cfg = config(args.workload, **({"B": args.batch} if args.batch else {}))
+    over = {}
+    if args.batch:
+        over["B"] = args.batch
+    if args.q_heads:
+        over["H_q"] = args.q_heads
+    cfg = config(args.workload, **over)
     assert args.warmup + args.steps <= cfg.steps, "more steps than the cache has room for"
     log_p = math.log(cfg.p)
     shape = LayerShape(B=cfg.B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, D=cfg.D, r=cfg.r, bf16=cfg.bf16)
@@ -319,6 +324,8 @@ def main():
     ap.add_argument("--workload", default="1b-decode")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the decode workload's batch (a sweep; the default line uses the workload's own)")
+    ap.add_argument("--q-heads", type=int, default=0,
+                    help="override the decode workload's query heads (a multiple of its KV heads: the group size)")
     ap.add_argument("--ring", type=int, default=0, help="layer instances (0: enough for --ring-bytes)")
     ap.add_argument("--ring-bytes", type=float, default=1.0 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -141,11 +141,12 @@ __device__ __forceinline__ void row_f32(const Row8<BF16>& r, float (&o)[8]) {
   }
 }
 
-// Entries per lane group (rows held in registers at once).  Four keeps every
-// load of a tile in flight together without spilling at group sizes up to 4;
-// two left the tiles' fixed costs (the combine, the per-tile partials) to
-// dominate at large batches, eight spills.
-constexpr int decode_nb(int) { return 4; }
+// Entries per lane group (rows held in registers at once), by head dim and
+// query heads per KV head.  Four keeps every load of a tile in flight together
+// without spilling at group sizes up to 4; two leaves the tiles' fixed costs
+// (the combine, the per-tile partials) to dominate at large batches, eight
+// spills.  At group size 8 and head dim 64, four spills and two is faster.
+constexpr int decode_nb(int d, int g) { return (d == 64 && g >= 8) ? 2 : 4; }
 
 template <int D, int NB_>
 struct DecodeShape {
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
   const Control& ctl = K.ctl;
   const float tau = K.tau;
   int32_t* const kept = K.kept;
-  using Sh = DecodeShape<D, decode_nb(D)>;
+  using Sh = DecodeShape<D, decode_nb(D, G)>;
   constexpr int LPE = Sh::LPE, NGW = Sh::NGW, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
   constexpr int NT = kDecThreads;
   constexpr int HALF = D / 2;
@@ -881,7 +882,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
 static int tile_entries(int d, int nb) { return (64 / (d / 8)) * nb * kDecWaves; }
 
 // Entries per tile (sizes the per-tile workspace rows and flags).
-int decode_tile_entries(int d) { return tile_entries(d, decode_nb(d)); }
+int decode_tile_entries(int d, int g) { return tile_entries(d, decode_nb(d, g)); }
 
 static int64_t decode_max_tiles(const LayerArgs& a, int twg) {
   const int64_t S = (int64_t)a.B * a.H_kv;
@@ -936,7 +937,7 @@ static int device_cus() {
 template <int D, int G, bool BF16>
 static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Control& ctl, float tau, bool compact,
                               int32_t* kept, hipStream_t st) {
-  const int twg = DecodeShape<D, decode_nb(D)>::TWG;
+  const int twg = DecodeShape<D, decode_nb(D, G)>::TWG;
   const int64_t items = (int64_t)a.B + decode_max_tiles(a, twg);
   const int cus = device_cus();
   const int grid = (int)(items < cus ? items : cus);

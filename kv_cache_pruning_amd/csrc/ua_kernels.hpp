@@ -88,7 +88,7 @@ struct DecodeWs {
 };
 
 size_t decode_ws_bytes(const LayerArgs& a, int tile_entries);
-int decode_tile_entries(int d);
+int decode_tile_entries(int d, int g);  // g: query heads per KV head
 DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, int tile_entries);
 // One decode step; with compact, the in-place compaction of every segment in
 // the same launch (kept: optional kept-index output).
