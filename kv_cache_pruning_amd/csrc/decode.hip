@@ -447,15 +447,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(DecodeKArgs ka
     unsigned long long gwd = (tid < 2) ? ld64_coh(gword) : 0ull;
     // ---- RoPE table (fp64 angles) while the loads fly
     if (tid < HALF) {
-      // the fp64 angle reduced to [-pi, pi] in fp64 (2 pi in two parts), then
-      // evaluated in fp32, the table's precision
-      const double ang = (double)pos * a.inv_freq[tid];
-      const double t = rint(ang * 0.15915494309189535);
-      const float rr = (float)fma(-t, 2.4492935982947064e-16, fma(-t, 6.283185307179586, ang));
-      float sn, cs;
-      sincosf(rr, &sn, &cs);
-      s_cs[tid] = cs;
-      s_sn[tid] = sn;
+      double sn, cs;
+      sincos((double)pos * a.inv_freq[tid], &sn, &cs);
+      s_cs[tid] = (float)cs;
+      s_sn[tid] = (float)sn;
     }
     __syncthreads();
     // ---- rotated queries, the stored key (L2-normalised, rotated, rounded like the cache), gates
