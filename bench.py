@@ -1,19 +1,20 @@
 """Benchmark of the UA hot path on one MI355X.
 
-Default workload: the 1B-shape decode layer (hidden 2048, 32 query / 8 KV
-heads, head dim 64, B = 8) on a pre-populated pruned cache of nominal length
-4096 (~10x compressed), one decode step + eviction + in-place compaction per
-layer instance per step (one fused launch), p = 0.15.  The decode working set of one layer
-(~7 MB) fits in the 256 MB Infinity Cache, so a step runs a ring of R
-independent layer instances (distinct caches, >= 1 GiB in total), as an
-R-layer model would, and throughput is counted per layer: value = B * R /
-step time.  Inputs are resident in HBM before timing starts.
+Headline: the ragged-stress decode layer (1B shape: hidden 2048, 32 query / 8
+KV heads, head dim 64; B = 64 sequences with nominal contexts 1k..32k and
+per-head compression 2..114x), the largest single-GPU decode workload: one
+decode step + eviction + in-place compaction per layer instance per step (one
+fused launch), p = 0.05.  A layer's decode working set fits in the 256 MB
+Infinity Cache, so a step runs a ring of R independent layer instances
+(distinct caches, >= 1 GiB in total), as an R-layer model would, and
+throughput is counted per layer: value = B * R / step time.  Inputs are
+resident in HBM before timing starts.
 
-The same line carries a "prefill" object: the 1B-shape chunked prefill
-(B = 2, 16 calls of 1024 tokens from an empty cache) in tokens/s with its
-transcendental and MFMA rooflines and the oracle's own rate, and a
-"backward" object: the attention backward of one 4096-token training chunk
-per sequence (B = 2, 1B head shape) in tokens/s against the fp32 peak.
+The same line carries the other decode workloads (3B-shape long context, 1B
+shape, tiny fp32) as objects of their own, each with its roofline and the
+oracle's rate on the host cores; the 1B-shape chunked prefill with the final
+eviction at p = 0.05 inside its timed region; the prefill variants; and the
+attention backward of one training chunk.
 
 Prints one JSON line.
 """
@@ -69,6 +70,114 @@ def load_traffic(name: str, path: str):
 
 
 # ---------------------------------------------------------------------------
+# the oracle on the host cores: one (sequence, KV head) unit per task
+# ---------------------------------------------------------------------------
+def host_cores() -> int:
+    """Cores this process may use (the GPU machine gives one GPU's share: at most 16)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def oracle_unit(cfg, w, c, b: int, h: int):
+    """The oracle's problem for one (sequence b, KV head h) unit: dims with one
+    sequence and one KV head, the parameters' columns of that head, and a cache
+    holding its one segment.  Units share nothing (the decay gates, the bias
+    and eviction are per KV head), so running them apart is the same work."""
+    import oracle as U
+
+    G = cfg.H_q // cfg.H_kv
+    cols = [h, cfg.H_kv + h, 2 * cfg.H_kv + h]
+    qs = slice(h * G * cfg.d, (h + 1) * G * cfg.d)
+    f = lambda a: np.asarray(a, np.float64)
+    od = U.Dims(B=1, H_q=G, H_kv=1, d=cfg.d, D=cfg.D, r=cfg.r, terms=U.TERMS_ALL, rope_base=10000.0,
+                cache_bf16=cfg.bf16)
+    op = U.Params(W_dec=f(w.W_dec)[:, cols], b_dec=f(w.b_dec)[cols], W_dn=f(w.W_dn), W_up=f(w.W_up)[:, qs],
+                  b_up=f(w.b_up)[qs])
+    s = b * cfg.H_kv + h
+    o, n = int(c.seg_off[s]), int(c.seg_len[s])
+    oc = U.RefCache(K=[f(c.K[o : o + n])], V=[f(c.V[o : o + n])], lam=[f(c.lam[o : o + n])], lk=[f(c.lk[o : o + n])],
+                    next_pos=np.array([int(c.next_pos[b])], np.int64), cap=np.array([int(c.seg_cap[s])], np.int64))
+    return od, op, oc
+
+
+def _oracle_decode_units(job):
+    """Worker: ``k`` decode + compaction steps of each unit; returns its compute seconds."""
+    name, over, units, k = job
+    import oracle as U
+    from ua_inputs import config, make_cache, make_step_inputs, make_weights
+
+    cfg = config(name, **over)
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    probs = [oracle_unit(cfg, w, c, b, h) for b, h in units]
+    inps = [make_step_inputs(cfg, t, 1, 0) for t in range(k)]
+    G = cfg.H_q // cfg.H_kv
+    log_p = math.log(cfg.p)
+    t0 = time.perf_counter()
+    for (b, h), (od, op, oc) in zip(units, probs):
+        for inp in inps:
+            U.decode_step(od, op, oc, inp.q[b : b + 1, 0, h * G : (h + 1) * G], inp.k[b : b + 1, 0, h : h + 1],
+                          inp.v[b : b + 1, 0, h : h + 1], inp.x[b : b + 1, 0], log_p)
+            U.compact(oc, log_p)
+    return time.perf_counter() - t0
+
+
+def _oracle_prefill_units(job):
+    """Worker: the first ``m`` tokens of call 0 of each unit, token by token."""
+    name, over, units, m = job
+    import oracle as U
+    from ua_inputs import config, make_cache, make_step_inputs, make_weights
+
+    cfg = config(name, **over)
+    w = make_weights(cfg, 0)
+    c = make_cache(cfg, w, 0)
+    probs = [oracle_unit(cfg, w, c, b, h) for b, h in units]
+    inp = make_step_inputs(cfg, 0, m, 0)
+    G = cfg.H_q // cfg.H_kv
+    t0 = time.perf_counter()
+    for (b, h), (od, op, oc) in zip(units, probs):
+        U.prefill(od, op, oc, inp.q[b : b + 1, :, h * G : (h + 1) * G], inp.k[b : b + 1, :, h : h + 1],
+                  inp.v[b : b + 1, :, h : h + 1], inp.x[b : b + 1])
+    return time.perf_counter() - t0
+
+
+def _pool_run(fn, cfg, over, per_unit, budget_s: float, probe_arg, max_arg, granule: int = 1):
+    """Run ``fn`` over every unit of ``cfg`` on the host cores.
+
+    A one-unit probe times ``probe_arg`` of work; the amount per unit is then
+    chosen so the whole pool takes about ``budget_s`` of wall time.  Returns
+    (amount per unit, wall seconds of the slowest worker's compute, cores).
+    """
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    units = [(b, h) for b in range(cfg.B) for h in range(cfg.H_kv)]
+    cores = min(host_cores(), len(units))
+    t1 = fn((cfg.name, over, units[:1], probe_arg)) / probe_arg
+    amount = int(budget_s * cores / (len(units) * t1 * per_unit))
+    amount = max(granule, min(max_arg, amount // granule * granule))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"  # one BLAS thread per worker process
+    jobs = [(cfg.name, over, units[i::cores], amount) for i in range(cores)]
+    with cf.ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as ex:
+        times = list(ex.map(fn, jobs))
+    return amount, max(times), cores
+
+
+def cpu_baseline_decode(cfg, over, budget_s: float):
+    """The fp64 oracle, as is, on the first steps of the same workload (instance 0),
+    its (sequence, KV head) units spread over the host cores."""
+    k, wall, cores = _pool_run(_oracle_decode_units, cfg, over, 1.0, budget_s, 4, cfg.steps)
+    return {"value": cfg.B * k / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cfg.name} instance 0: the first {k} decode + compaction steps of all {cfg.B * cfg.H_kv} "
+                      f"(sequence, KV head) units, numpy fp64, {cores} worker processes, one BLAS thread each "
+                      f"({wall:.1f} s of the slowest worker's compute)"}
+
+
+# ---------------------------------------------------------------------------
 # decode workloads
 # ---------------------------------------------------------------------------
 def cache_desc(cfg) -> str:
@@ -81,19 +190,21 @@ def cache_desc(cfg) -> str:
     return f"pruned cache nominal {cfg.nominal} (~{cfg.nominal / cfg.len_mean:.0f}x)"
 
 
-def bench_decode(args):
+def bench_decode(args, name: str, over=None, cpu: bool = True):
+    """One decode workload: a ring of R layer instances (>= ring-bytes of live
+    cache), each step one fused decode + eviction + compaction launch per
+    instance, captured in a HIP graph and timed with events around every step.
+    The same steps are replayed as two calls (decode, then ua_compact) from the
+    same state, and once more untimed to count live entries and moved rows."""
     import torch
 
     from kv_cache_pruning_amd.layer import DeviceCache, DeviceWeights, Layer, LayerShape, Workspace
     from ua_inputs import config, make_cache, make_step_inputs, make_weights
 
-    over = {}
-    if args.batch:
-        over["B"] = args.batch
-    if args.q_heads:
-        over["H_q"] = args.q_heads
-    cfg = config(args.workload, **over)
-    assert args.warmup + args.steps <= cfg.steps, "more steps than the cache has room for"
+    over = dict(over or {})
+    cfg = config(name, **over)
+    steps = min(args.steps, cfg.steps - args.warmup)
+    assert steps > 0, "more warmup steps than the cache has room for"
     log_p = math.log(cfg.p)
     shape = LayerShape(B=cfg.B, H_q=cfg.H_q, H_kv=cfg.H_kv, d=cfg.d, D=cfg.D, r=cfg.r, bf16=cfg.bf16)
     w = make_weights(cfg, 0)
@@ -101,11 +212,8 @@ def bench_decode(args):
     elem = 2 if cfg.bf16 else 4
     entry_bytes = 2 * cfg.d * elem + 12  # K + V + logbias read/write + key gate
 
-    # ring of layer instances
     t0 = time.time()
     caches, live0 = [], 0
-    R = args.ring
-    target = args.ring_bytes
     i = 0
     while True:
         ci = make_cache(cfg, w, seed=i)
@@ -113,26 +221,20 @@ def bench_decode(args):
                                   ci.next_pos))
         live0 += int(ci.seg_len.sum()) * entry_bytes
         i += 1
-        if (R and i >= R) or (not R and live0 >= target) or i >= 4096:
+        if (args.ring and i >= args.ring) or (not args.ring and live0 >= args.ring_bytes) or i >= 4096:
             break
     R = len(caches)
-    # one workspace for the whole ring: the calls are serialised on one stream
-    ws = Workspace(shape, max(caches, key=lambda c: c.total_slots), 1)
+    ws = Workspace(shape, max(caches, key=lambda c: c.total_slots), 1)  # calls are serialised on one stream
     insts = [Layer(shape, dw, c, workspace=ws) for c in caches]
-    nsteps = args.warmup + args.steps
+    nsteps = args.warmup + steps
+    dt = shape.dtype
     toks = []
     for s in range(nsteps):
         inp = make_step_inputs(cfg, s, 1, 0)
-        dt = shape.dtype
         toks.append([torch.from_numpy(np.ascontiguousarray(a[:, 0])).to("cuda", dt) for a in (inp.q, inp.k, inp.v, inp.x)])
     y = torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     setup_s = time.time() - t0
-
-    # One captured graph per step shape: the whole step (every instance's fused
-    # decode + compaction, one launch each), and for context the same step as
-    # two calls (decode-only / compaction-only graphs).  Inputs go through
-    # static buffers refreshed before a replay.
     static_in = [t.clone() for t in toks[0]]
 
     def load_inputs(s):
@@ -159,7 +261,6 @@ def bench_decode(args):
 
     g_step, g_dec, g_cmp = cap(all_step), cap(all_decode), cap(all_compact)
     torch.cuda.synchronize()
-
     for s in range(args.warmup):
         load_inputs(s)
         g_step.replay()
@@ -173,12 +274,12 @@ def bench_decode(args):
             c.seg_len.copy_(sn[4]); c.next_pos.copy_(sn[5])
         torch.cuda.synchronize()
 
-    # ---- timed region: K steps of the whole hot path.  Events bracket each
-    # step's graph (R fused launches back to back on this stream), which gives
-    # the launch's average duration as well.
-    ev_s = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # ---- timed region: `steps` steps of the whole hot path.  Events bracket
+    # each step's graph (R fused launches back to back on this stream), which
+    # gives the launch's average duration as well.
+    ev_s = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
-    for s in range(args.steps):
+    for s in range(steps):
         load_inputs(args.warmup + s)
         ev_s[s][0].record()
         g_step.replay()
@@ -190,8 +291,8 @@ def bench_decode(args):
 
     # ---- the same steps as two calls (decode, then compaction), from the same state
     restore()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for s in range(args.steps):
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for s in range(steps):
         load_inputs(args.warmup + s)
         ev[s][0].record()
         g_dec.replay()
@@ -204,17 +305,14 @@ def bench_decode(args):
 
     # ---- untimed replay of the same steps: live entries scanned, rows moved
     restore()
-    scanned = 0
-    moved = 0
-    moved_fused = 0
-    cmp_scanned = 0
-    for s in range(args.steps):
+    scanned = moved = moved_fused = cmp_scanned = 0
+    for s in range(steps):
         q, k, v, x = toks[args.warmup + s]
         for L_ in insts:
+            offs = L_.cache.seg_off.cpu().numpy()
             scanned += int(L_.cache.seg_len.sum().item())
             L_.decode_step(q, k, v, x, log_p, y=y)
             lens = L_.cache.seg_len.cpu().numpy()
-            offs = L_.cache.seg_off.cpu().numpy()
             lam = L_.cache.logbias.cpu().numpy()
             for o, n in zip(offs, lens):
                 seg = lam[o : o + n]
@@ -222,61 +320,44 @@ def bench_decode(args):
                 cmp_scanned += int(n)
                 if dead.size:
                     moved += int(np.count_nonzero(seg[dead[0]:] >= log_p))
-                    # the fused call writes the new (last) entry straight to its place
-                    moved_fused += int(np.count_nonzero(seg[dead[0]:-1] >= log_p))
+                    moved_fused += int(np.count_nonzero(seg[dead[0]:-1] >= log_p))  # the new entry lands in place
             L_.compact(log_p)
     torch.cuda.synchronize()
+    del g_step, g_dec, g_cmp, snap
 
-    n_calls = args.steps * R
+    n_calls = steps * R
     S = cfg.B * cfg.H_kv
     per_step_extra = (S * (2 * cfg.d * elem + 8)  # appends
                       + cfg.B * (cfg.H_q + 2 * cfg.H_kv) * cfg.d * elem + cfg.B * cfg.D * elem  # q, k, v, x
                       + cfg.B * cfg.H_q * cfg.d * 4  # y (fp32)
                       + (cfg.D * (3 * cfg.H_kv + cfg.r) + cfg.r * cfg.H_q * cfg.d) * elem)  # gate weights
+    row_bytes = 2 * cfg.d * elem + 8  # K, V, log-bias, key gate of one moved row
     dec_bytes = scanned * entry_bytes + n_calls * per_step_extra
-    cmp_bytes = cmp_scanned * 4 + moved * 2 * (2 * cfg.d * elem + 8)
-    fused_bytes = dec_bytes + moved_fused * (2 * cfg.d * elem + 4)  # moved rows: K, V, key gate written
-    dec_avg_ms = float(np.mean(dec_ms))
-    cmp_avg_ms = float(np.mean(cmp_ms))
+    # compaction: 4 B per entry scanned, plus each moved row read and written
+    cmp_bytes = cmp_scanned * 4 + moved * 2 * row_bytes
+    fused_bytes = dec_bytes + moved_fused * (row_bytes - 4)  # moved rows: K, V, key gate written
+    dec_avg_ms, cmp_avg_ms = float(np.mean(dec_ms)), float(np.mean(cmp_ms))
     fused_avg_ms = float(np.mean(fused_ms))
     achieved = fused_bytes / n_calls / (fused_avg_ms * 1e-3) / 1e9
-    ms_per_step = total_ms / args.steps
+    ms_per_step = total_ms / steps
     tokens = cfg.B * R  # layer-tokens per step
-    value = tokens / (ms_per_step * 1e-3)
-
-    out = {
-        "metric": "UA decode tokens/s + achieved HBM GB/s on pruned KV cache; prefill tok/s",
-        "value": value,
+    cmp_gbs = cmp_bytes / n_calls / (cmp_avg_ms * 1e-3) / 1e9
+    res = {
+        "value": tokens / (ms_per_step * 1e-3),
         "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
         "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{cfg.name}: UA decode layer B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} "
-                        f"D={cfg.D}, {cache_desc(cfg)}, p={cfg.p}, decode + compaction every step, "
-                        f"ring of {R} layer instances",
-            "global_batch": cfg.B,
-            "ring_instances": R,
-            "tokens_per_step": tokens,
-            "storage": "bf16" if cfg.bf16 else "f32",
-            "live_entries_per_layer_step": scanned / n_calls,
-            "fused_call_us": fused_avg_ms * 1e3,
-            "two_calls": {
-                "decode_call_us": dec_avg_ms * 1e3,
-                "compact_call_us": cmp_avg_ms * 1e3,
-                "decode_gbs": dec_bytes / n_calls / (dec_avg_ms * 1e-3) / 1e9,
-                "compact_gbs": cmp_bytes / n_calls / (cmp_avg_ms * 1e-3) / 1e9,
-            },
-            "rows_moved_per_layer_step": moved_fused / n_calls,
-            "status": st,
-            "setup_s": setup_s,
-        },
+        "dtype": "bf16" if cfg.bf16 else "f32",
+        "workload": f"{cfg.name}: UA decode layer B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} D={cfg.D}, "
+                    f"{cache_desc(cfg)}, p={cfg.p}, decode + eviction + compaction every step (one fused launch), "
+                    f"ring of {R} layer instances",
+        "ring_instances": R,
+        "tokens_per_step": tokens,
+        "live_entries_per_layer_step": scanned / n_calls,
+        "rows_moved_per_layer_step": moved_fused / n_calls,
+        "fused_call_us": fused_avg_ms * 1e3,
+        "status": st,
+        "setup_s": setup_s,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
@@ -284,36 +365,31 @@ def bench_decode(args):
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": load_traffic(f"decode_{cfg.name}", "decode"),
-            "kernel": "ua_decode_compact_step (decode_step_kernel, compacting), one launch per layer step",
+            "kernel": "ua_decode_compact_step, one launch per layer step (average launch from events around "
+                      "the R launches of each step)",
             "alg_bytes_per_launch": fused_bytes / n_calls,
         },
+        "two_calls": {
+            "decode_call_us": dec_avg_ms * 1e3,
+            "decode_gbs": dec_bytes / n_calls / (dec_avg_ms * 1e-3) / 1e9,
+        },
+        "compact": {
+            "what": "standalone ua_compact after ua_decode_step (the lazy-eviction path), same steps and state",
+            "call_us": cmp_avg_ms * 1e3,
+            "alg_bytes_per_call": cmp_bytes / n_calls,
+            "achieved": cmp_gbs,
+            "unit": "GB/s",
+            "frac": cmp_gbs / HBM_PEAK_GBS,
+        },
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_decode(cfg, args.cpu_seconds)
-    return out
+    if cpu and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(cfg, over, args.cpu_seconds)
+    del insts, caches, ws, toks
+    torch.cuda.empty_cache()
+    return res
 
 
-def cpu_baseline_decode(cfg, budget_s: float):
-    """The fp64 oracle, as is, on the first steps of the same workload (instance 0)."""
-    import oracle as U
-    from tests.harness import oracle_cache, oracle_dims, oracle_params
-    from ua_inputs import make_cache, make_step_inputs, make_weights
-
-    w = make_weights(cfg, 0)
-    c = make_cache(cfg, w, 0)
-    od, op, oc = oracle_dims(cfg), oracle_params(w), oracle_cache(cfg, c)
-    log_p = math.log(cfg.p)
-    t0 = time.time()
-    n = 0
-    while n < cfg.steps and time.time() - t0 < budget_s:
-        inp = make_step_inputs(cfg, n, 1, 0)
-        U.decode_step(od, op, oc, inp.q[:, 0], inp.k[:, 0], inp.v[:, 0], inp.x[:, 0], log_p)
-        U.compact(oc, log_p)
-        n += 1
-    dt = time.time() - t0
-    return {"value": cfg.B * n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{cfg.name} instance 0, first {n} decode+compaction steps ({dt:.1f} s, numpy fp64, "
-                      f"one process)"}
+DECODE_WORKLOADS = ["ragged-decode", "3b-decode", "1b-decode", "tiny-decode-f32"]
 
 
 def main():
@@ -321,7 +397,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="1b-decode")
+    ap.add_argument("--workload", default="ragged-decode",
+                    help="the headline decode workload (the largest single-GPU one by default)")
+    ap.add_argument("--only", action="store_true",
+                    help="time the headline decode workload only (profiles, sweeps)")
     ap.add_argument("--batch", type=int, default=0,
                     help="override the decode workload's batch (a sweep; the default line uses the workload's own)")
     ap.add_argument("--q-heads", type=int, default=0,
@@ -329,10 +408,10 @@ def main():
     ap.add_argument("--ring", type=int, default=0, help="layer instances (0: enough for --ring-bytes)")
     ap.add_argument("--ring-bytes", type=float, default=1.0 * 2**30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-prefill", action="store_true", help="skip the 1b-prefill figures")
     ap.add_argument("--no-prefill-variants", action="store_true",
-                    help="skip the pruned and chunk-boundary prefill figures (profiles of the dense path)")
+                    help="skip the pruned, chunk-boundary and variable-length prefill figures")
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward figures")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB (a known-size reference for the HBM "
@@ -357,27 +436,52 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    out = bench_decode(args)
-    if not args.no_prefill:
-        out["prefill"] = bench_prefill(args)
-        if not args.no_prefill_variants:
-            out["prefill_pruned"] = bench_prefill_pruned(args)
-            out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
-            out["prefill_varlen"] = bench_prefill_varlen(args)
-    if not args.no_backward:
-        out["backward"] = bench_backward(args)
+    over = {}
+    if args.batch:
+        over["B"] = args.batch
+    if args.q_heads:
+        over["H_q"] = args.q_heads
+    head = bench_decode(args, args.workload, over)
+    out = {
+        "metric": "UA decode tokens/s + achieved HBM GB/s on pruned KV cache; prefill tok/s",
+        "value": head["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head["dtype"],
+        "data": "synthetic",
+        "config": {k: head[k] for k in ("workload", "ring_instances", "tokens_per_step",
+                                         "live_entries_per_layer_step", "rows_moved_per_layer_step",
+                                         "fused_call_us", "status", "setup_s", "two_calls", "compact")},
+        "roofline": head["roofline"],
+    }
+    out["config"]["global_batch"] = head["tokens_per_step"] // head["ring_instances"]
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if not args.only:
+        out["decode_configs"] = {}
+        for name in DECODE_WORKLOADS:
+            if name != args.workload:
+                out["decode_configs"][name] = bench_decode(args, name)
+        if not args.no_prefill:
+            out["prefill"] = bench_prefill(args)
+            if not args.no_prefill_variants:
+                out["prefill_pruned"] = bench_prefill_pruned(args)
+                out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
+                out["prefill_varlen"] = bench_prefill_varlen(args)
+        if not args.no_backward:
+            out["backward"] = bench_backward(args)
     print(json.dumps(out), flush=True)
 
 
 # ---------------------------------------------------------------------------
 # prefill workload
 # ---------------------------------------------------------------------------
-# Transcendental issue rate of the chip: 256 CUs x 4 SIMDs x 16 lanes per
-# clock at half rate (a wave64 v_exp/v_log holds the VALU issue for two
-# 4-clock slots: SQ_ACTIVE_INST_VALU = SQ_INSTS_VALU + SQ_INSTS_VALU_TRANS_F32
-# per wave on the prefill kernels), 2.4 GHz.
-TRANS_PEAK_TS = 256 * 4 * 16 / 2 * 2.4e9 / 1e12
-
 
 def prefill_work(cfg, len0: int, n: int):
     """Algorithmic work of one call: causal (token, key) pairs per KV group,
@@ -390,17 +494,22 @@ def prefill_work(cfg, len0: int, n: int):
 
 
 def bench_prefill(args, name: str = "1b-prefill", passes: int = 3, warm: int = 1):
+    """The 1B-shape chunked prefill: 16 calls of 1024 tokens from an empty cache,
+    then the eviction of the final log-biases at p = 0.05 (one ua_compact), all
+    inside the timed region.  Events bracket every call."""
     import torch
 
-    from tests.harness import device_layer
+    from kv_cache_pruning_amd.layer import layer_from_arrays
     from ua_inputs import config, make_cache, make_step_inputs, make_weights
 
     cfg = config(name)
     n = cfg.chunk
     calls = cfg.n_total // n
+    log_p = math.log(cfg.p)
     w = make_weights(cfg, 0)
     c = make_cache(cfg, w, 0)
-    layer = device_layer(cfg, w, c, max_tokens=n, y_bf16=True)
+    layer = layer_from_arrays(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, cfg.D, cfg.r, cfg.bf16, w, c, max_tokens=n,
+                              y_bf16=True)
     dt = torch.bfloat16
     toks = []
     for i in range(calls):
@@ -409,8 +518,8 @@ def bench_prefill(args, name: str = "1b-prefill", passes: int = 3, warm: int = 1
     y = torch.empty((cfg.B, n, cfg.H_q, cfg.d), dtype=torch.bfloat16, device="cuda")
     seg_len0 = layer.cache.seg_len.clone()
     pos0 = layer.cache.next_pos.clone()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
-    call_ms = np.zeros(calls)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 2)]
+    call_ms = np.zeros(calls + 1)
     for p in range(warm + passes):
         # every pass starts from the empty cache (lengths and positions reset; the
         # slots it writes are rewritten before they are read)
@@ -421,40 +530,51 @@ def bench_prefill(args, name: str = "1b-prefill", passes: int = 3, warm: int = 1
         for i in range(calls):
             layer.prefill(*toks[i], y=y)
             ev[i + 1].record()
+        layer.compact(log_p)
+        ev[calls + 1].record()
         torch.cuda.synchronize()
         if p >= warm:
-            call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(calls)])
+            call_ms += np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(calls + 1)])
     call_ms /= passes
+    kept = layer.cache.seg_len.cpu().numpy()
     st = int(layer.cache.status.item())
     total_ms = float(call_ms.sum())
+    prefill_ms = float(call_ms[:calls].sum())
     flops = trans = 0.0
     for i in range(calls):
         _, f, t = prefill_work(cfg, i * n, n)
         flops += f
         trans += t
     tflops = flops / (total_ms * 1e-3) / 1e12
-    tts = trans / (total_ms * 1e-3) / 1e12
+    tflops_calls = flops / (prefill_ms * 1e-3) / 1e12
+    tts = trans / (prefill_ms * 1e-3) / 1e12
     tokens = cfg.B * calls * n
     return {
         "workload": f"{cfg.name}: UA chunked prefill B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} D={cfg.D}, "
-                    f"{calls} calls of {n} tokens from an empty cache (N={cfg.n_total}), bf16 storage, y bf16",
+                    f"{calls} calls of {n} tokens from an empty cache (N={cfg.n_total}), then eviction of the final "
+                    f"log-biases at p={cfg.p} (ua_compact), bf16 storage, y bf16",
         "value": tokens / (total_ms * 1e-3),
         "unit": "tokens/s",
         "ms_per_pass": total_ms,
         "passes": passes,
-        "call_ms": [round(float(x), 4) for x in call_ms],
+        "call_ms": [round(float(x), 4) for x in call_ms[:calls]],
+        "eviction_ms": float(call_ms[calls]),
+        "kept_entries_per_segment": float(kept.mean()),
         "status": st,
         "roofline": {
-            "bound": "alu",
-            "achieved": tts,
-            "peak": TRANS_PEAK_TS,
-            "unit": "T transcendentals/s",
-            "frac": tts / TRANS_PEAK_TS,
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFS,
             "traffic": load_traffic(f"prefill_{cfg.name}", "prefill"),
-            "kernel": "ua_prefill = prep + token + attention kernels (timed per call)",
-            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFS},
+            "kernel": "ua_prefill = prep + token + attention kernels, timed per call with events (the attention "
+                      "kernel dominates); the eviction is inside the time",
+            "alg_flops": flops,
+            "calls_only_frac": tflops_calls / MFMA_BF16_PEAK_TFS,
+            "transcendentals_per_s": tts * 1e12,
         },
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_prefill(cfg, args.cpu_seconds / 2),
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_prefill(cfg, args.cpu_seconds),
     }
 
 
@@ -470,7 +590,7 @@ def bench_prefill_pruned(args, chunked: bool = False, name: str = "1b-prefill", 
     """
     import torch
 
-    from tests.harness import device_layer
+    from kv_cache_pruning_amd.layer import layer_from_arrays
     from ua_inputs import config, make_cache, make_step_inputs, make_weights
 
     cfg = config(name)
@@ -480,7 +600,8 @@ def bench_prefill_pruned(args, chunked: bool = False, name: str = "1b-prefill", 
     calls = cfg.n_total // per_call
     w = make_weights(cfg, 0)
     c = make_cache(cfg, w, 0)
-    layer = device_layer(cfg, w, c, max_tokens=n, y_bf16=True)
+    layer = layer_from_arrays(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, cfg.D, cfg.r, cfg.bf16, w, c, max_tokens=n,
+                              y_bf16=True)
     dt = torch.bfloat16
     inps = [make_step_inputs(cfg, i, cfg.chunk, 0) for i in range(cfg.n_total // cfg.chunk)]
     full = [np.concatenate([getattr(x, f) for x in inps], axis=1) for f in ("q", "k", "v", "x")]
@@ -543,14 +664,13 @@ def bench_prefill_pruned(args, chunked: bool = False, name: str = "1b-prefill", 
         "call_ms": [round(float(x), 4) for x in call_ms] if not chunked else None,
         "status": st,
         "roofline": {
-            "bound": "alu",
-            "achieved": tts,
-            "peak": TRANS_PEAK_TS,
-            "unit": "T transcendentals/s",
-            "frac": tts / TRANS_PEAK_TS,
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFS,
             "pairs": pairs,
-            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_BF16_PEAK_TFS},
+            "transcendentals_per_s": tts * 1e12,
         },
     }
 
@@ -561,7 +681,7 @@ def bench_prefill_varlen(args, B: int = 8, passes: int = 3, warm: int = 1, seed:
     counts each sequence's own causal pairs."""
     import torch
 
-    from tests.harness import device_layer
+    from kv_cache_pruning_amd.layer import layer_from_arrays
     from ua_inputs import config, make_cache, make_step_inputs, make_weights
 
     rng = np.random.default_rng(seed)
@@ -570,7 +690,8 @@ def bench_prefill_varlen(args, B: int = 8, passes: int = 3, warm: int = 1, seed:
     cfg = config("1b-prefill", B=B, n_total=nmax, chunk=nmax)
     w = make_weights(cfg, 0)
     c = make_cache(cfg, w, 0)
-    layer = device_layer(cfg, w, c, max_tokens=nmax, y_bf16=True)
+    layer = layer_from_arrays(cfg.B, cfg.H_q, cfg.H_kv, cfg.d, cfg.D, cfg.r, cfg.bf16, w, c, max_tokens=nmax,
+                              y_bf16=True)
     inp = make_step_inputs(cfg, 0, nmax, 0)
     cu = np.concatenate([[0], np.cumsum(lens)])
     T = int(cu[-1])
@@ -613,38 +734,25 @@ def bench_prefill_varlen(args, B: int = 8, passes: int = 3, warm: int = 1, seed:
         "passes": passes,
         "status": st,
         "roofline": {
-            "bound": "alu",
-            "achieved": tts,
-            "peak": TRANS_PEAK_TS,
-            "unit": "T transcendentals/s",
-            "frac": tts / TRANS_PEAK_TS,
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": MFMA_BF16_PEAK_TFS,
+            "unit": "TFLOP/s",
+            "frac": tflops / MFMA_BF16_PEAK_TFS,
             "pairs": pairs,
-            "mfma": {"achieved": tflops, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": tflops / MFMA_BF16_PEAK_TFS},
+            "transcendentals_per_s": tts * 1e12,
         },
     }
 
 
 def cpu_baseline_prefill(cfg, budget_s: float):
-    """The fp64 oracle's token-by-token prefill on the first tokens of the first call."""
-    import oracle as U
-    from tests.harness import oracle_cache, oracle_dims, oracle_params
-    from ua_inputs import make_cache, make_step_inputs, make_weights
-
-    w = make_weights(cfg, 0)
-    c = make_cache(cfg, w, 0)
-    od, op, oc = oracle_dims(cfg), oracle_params(w), oracle_cache(cfg, c)
-    inp = make_step_inputs(cfg, 0, cfg.chunk, 0)
-    t0 = time.time()
-    m = 0
-    while m < cfg.chunk and time.time() - t0 < budget_s:
-        sl = slice(m, m + 16)
-        U.prefill(od, op, oc, inp.q[:, sl], inp.k[:, sl], inp.v[:, sl], inp.x[:, sl])
-        m += 16
-    dt = time.time() - t0
-    return {"value": cfg.B * m / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{cfg.name} call 0, first {m} tokens of each of the B={cfg.B} sequences from an empty cache "
-                      f"({dt:.1f} s, numpy fp64, one process; later tokens cost more)"}
+    """The fp64 oracle's token-by-token prefill on the first tokens of call 0,
+    its (sequence, KV head) units spread over the host cores."""
+    m, wall, cores = _pool_run(_oracle_prefill_units, cfg, {}, 1.0, budget_s, 32, cfg.chunk, granule=32)
+    return {"value": cfg.B * m / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cfg.name} call 0: the first {m} tokens of each of the {cfg.B * cfg.H_kv} (sequence, KV "
+                      f"head) units from an empty cache, numpy fp64, {cores} worker processes ({wall:.1f} s of the "
+                      f"slowest worker's compute; later tokens cost more)"}
 
 
 # ---------------------------------------------------------------------------

@@ -67,8 +67,10 @@ enum { UA_TERM_Q = 1, UA_TERM_K = 2, UA_TERM_SIM = 4, UA_TERMS_ALL = 7 };
 /* Sticky device status bits (ua_cache.status). */
 /* bit 0: an append or a prefill found its segment full (that segment was left
  * unchanged); bit 1: a wait on another workgroup of the same call timed out
- * (never expected; the outputs and the cache contents are then undefined). */
-enum { UA_STATUS_SEGMENT_FULL = 1, UA_STATUS_WAIT_TIMEOUT = 2 };
+ * (never expected; the outputs and the cache contents are then undefined);
+ * bit 2: a decode step found a segment length above its capacity (a broken
+ * cache table; the step changed nothing but next_pos, and y is undefined). */
+enum { UA_STATUS_SEGMENT_FULL = 1, UA_STATUS_WAIT_TIMEOUT = 2, UA_STATUS_BAD_LENGTH = 4 };
 
 /*
  * Layer shape and numeric options.
@@ -201,13 +203,13 @@ ua_status ua_decode_step(const ua_dims* dims, const ua_params* params, const ua_
                          float log_p, void* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * One decode step followed, in the same launch, by the compaction of every
- * segment: the result equals ua_decode_step(log_p) then ua_compact(log_p) on
- * the same cache (paperlayer.ai section 4.2: evicted entries never return;
- * the new entry, when appended, lands after the survivors).  kept_idx is as
- * for ua_compact, with the new entry's index given as the segment's length
- * before the step.  The cached entries of a segment are read once: the
- * survivors move down from registers.
+ * One decode step followed, in the same pass over the cache, by the
+ * compaction of every segment: the result equals ua_decode_step(log_p) then
+ * ua_compact(log_p) on the same cache (paperlayer.ai section 4.2: evicted
+ * entries never return; the new entry, when appended, lands after the
+ * survivors).  kept_idx is as for ua_compact, with the new entry's index
+ * given as the segment's length before the step.  The cached entries of a
+ * segment are read once: the survivors move down from registers.
  */
 ua_status ua_decode_compact_step(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
                                  const ua_tokens* in, float log_p, void* y, int32_t* kept_idx, void* ws,

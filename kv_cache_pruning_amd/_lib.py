@@ -19,7 +19,7 @@ LIB_PATH = os.environ.get("UA_LIB", os.path.join(HERE, "libua.so"))
 UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = range(5)
 UA_F32, UA_BF16 = 0, 1
 UA_TERM_Q, UA_TERM_K, UA_TERM_SIM, UA_TERMS_ALL = 1, 2, 4, 7
-UA_STATUS_SEGMENT_FULL, UA_STATUS_WAIT_TIMEOUT = 1, 2
+UA_STATUS_SEGMENT_FULL, UA_STATUS_WAIT_TIMEOUT, UA_STATUS_BAD_LENGTH = 1, 2, 4
 
 EXPORTS = (
     "ua_workspace_bytes",

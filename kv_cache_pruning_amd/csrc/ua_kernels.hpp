@@ -51,24 +51,21 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Control words of a workspace: counters and flags that must be zero before
 // the first call; every call returns them to zero, except the call counter at
-// glob[kGlobSeq] and the tagged words, whose stale contents carry an older
-// tag.  The fixed part sits at the front of the workspace, the compaction
-// flags at its end (see workspace.hip), so calls on caches of different
-// sizes can share one.
-constexpr int kGlobTicket = 0;   // decode and compaction: next work item
+// glob[kGlobSeq] (prefill tags its carry words with it) and the decode words
+// that the decode step's first launch clears itself.  The fixed part sits at
+// the front of the workspace, the compaction flags at its end (see
+// workspace.hip), so calls on caches of different sizes can share one.
+constexpr int kGlobTicket = 0;   // compaction: next work item
 constexpr int kGlobArrive = 32;  // compaction: workgroups done (own cache line)
-constexpr int kGlobSeq = 64;     // decode: calls made (tags the per-sequence words)
-constexpr int kGlobDone = 96;    // decode: workgroups finished
+constexpr int kGlobSeq = 64;     // prefill: calls made (tags the carry words)
 constexpr int kGlobInts = 128;
-constexpr int kUWords = kMaxRank + 3 * kMaxHkv;  // tagged words per sequence: u, then the 3 H_kv gates
 
 struct Control {
   int* dec_cnt;              // [S]           decode: arrivals per segment
   int* cmp_state;            // [max_chunks]  compaction: (count or prefix) << 2 | flag
   int* cmp_loaded;           // [max_chunks]  compaction: the chunk's rows are in registers
-  unsigned long long* dec_state;  // [max_chunks]  decode tiles: call tag << 32 | (count or prefix) << 2 | flag
-  int* glob;                 // [kGlobInts]   ticket, arrivals, call counter, finished (one cache line each)
-  unsigned long long* uw;    // [B, kUWords]  decode: per-sequence values, call tag in the high half
+  unsigned long long* dec_state;  // [max_chunks]  decode tiles: (count or prefix) << 2 | flag
+  int* glob;                 // [kGlobInts]   ticket, arrivals, call counter (one cache line each)
   int cmp_chunk;             // entries per compaction chunk
   int max_chunks;
 };
@@ -78,10 +75,20 @@ size_t control_bytes(const LayerArgs& a);       // fixed part at the front
 size_t control_tail_bytes(const LayerArgs& a);  // compaction flags at the end
 Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes);
 
-// Decode scratch (after the control block) plus the counters it uses.
+// Decode scratch (after the control block) plus the counters it uses.  The
+// token launch writes the per-sequence quantities and the tile records, and
+// clears the per-segment counters and look-back words the tile launch uses.
 struct DecodeWs {
   int* cnt;        // [S]  arrivals per segment (control block)
-  int* newlen;     // [S]  segment lengths after the step
+  int* segtk;      // [S]  tile tickets per segment
+  int* ntiles;     // [1]  tiles of the step
+  int4* map;       // [max_tiles, 2]  per tile: {segment, unused, length, tiles of the segment},
+                   //                 {record of the segment's first tile, offset low, offset high, 0}
+  float* tq;       // [B, H_q, d]  rotated queries
+  float* tkey;     // [B * H_kv, d]  stored new keys (rounded like the cache)
+  float* gam;      // [B, H_q * d]  output gate
+  float* tokf;     // [B * H_kv, 2]  query/similarity part of the pair term (log2 units / terms), new key gate
+  float* es;       // [B, H_q]  the token's logit against its own key (log2 units)
   float* part_o;   // [max_tiles, G, d]   partials of segments held by several tiles
   float* part_ml;  // [max_tiles, G, 2]   max (log2 units), sum
   int max_tiles;

@@ -3,15 +3,16 @@
 //   [ fixed control | scratch of the call ... | compaction flags ]
 //   ^ ws                                       ^ end of ws - tail
 //
-// The fixed control words (arrival counters, the ticket, the decode call
-// counter and per-sequence tagged words) depend only on B and H_kv; the compaction flags (one
+// The fixed control words (arrival counters, the ticket, the call counter)
+// depend only on B and H_kv; the compaction flags (one
 // pair per chunk, so their number depends on total_slots) are carved from
 // the END of the workspace.  Layers of one shape whose caches differ in size
 // can then share one workspace sized for the largest: no call's scratch ever
 // overlaps another call's control words.  The control words are zero before
-// the first call and every call leaves them zero (the decode call counter and
-// the tagged words aside); prefill keeps its own sync words in its scratch and
-// clears them at the start of each call.
+// the first call and every call leaves them zero (the call counter aside; the
+// decode step clears its own counters and look-back words in its first
+// launch); prefill keeps its own sync words in its scratch and clears them at
+// the start of each call.
 
 #include <algorithm>
 
@@ -41,11 +42,9 @@ static size_t fixed_layout(const LayerArgs& a, Control* c, char* base) {
   };
   int* dec_cnt = take(sizeof(int) * S);
   int* glob = take(sizeof(int) * kGlobInts);
-  int* uw = take(sizeof(unsigned long long) * a.B * kUWords);
   if (c) {
     c->dec_cnt = dec_cnt;
     c->glob = glob;
-    c->uw = reinterpret_cast<unsigned long long*>(uw);
   }
   return n;
 }

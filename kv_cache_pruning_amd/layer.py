@@ -196,3 +196,19 @@ class Layer:
     def compact(self, log_p: float, kept: Optional[torch.Tensor] = None, stream=None):
         L.ua_compact(self.dims, self.cache.struct, log_p, kept, self.ws.ptr, self.ws.nbytes, stream)
         return kept
+
+
+def layer_from_arrays(B: int, H_q: int, H_kv: int, d: int, D: int, r: int, bf16: bool, weights, cache,
+                      terms: int = L.UA_TERMS_ALL, max_tokens: int = 1, y_bf16: bool = False,
+                      workspace: Optional[Workspace] = None, device="cuda") -> Layer:
+    """A Layer from host arrays.
+
+    ``weights`` holds W_dec, b_dec, W_dn, W_up, b_up; ``cache`` holds K, V,
+    lam (log-biases), lk (key gates), seg_off, seg_len, seg_cap, next_pos
+    (attributes of plain objects, e.g. dataclasses).  Copies go to the device.
+    """
+    shape = LayerShape(B=B, H_q=H_q, H_kv=H_kv, d=d, D=D, r=r, bf16=bf16, y_bf16=y_bf16, terms=terms)
+    w, c = weights, cache
+    dw = DeviceWeights(shape, w.W_dec, w.b_dec, w.W_dn, w.W_up, w.b_up, device=device)
+    dc = DeviceCache(shape, c.K, c.V, c.lam, c.lk, c.seg_off, c.seg_len, c.seg_cap, c.next_pos, device=device)
+    return Layer(shape, dw, dc, max_tokens=max_tokens, device=device, workspace=workspace)

@@ -19,9 +19,9 @@ form below is a reading, listed at the end of this docstring):
 * same page, section 4.2: at inference a KV pair is evicted once its effective
   mask falls below p, per head; the bias only decreases.
 * ai4snews page, Figure 1 caption: keys are L2-normalised, RoPE is kept, a
-  low-rank sigmoid gate multiplies the attention output, and the three terms
-  are "combined via a geometric mean, transformed to log-space, and
-  accumulated causally" into the bias matrix Lambda.
+  low-rank sigmoid gate multiplies the attention output, and the bias matrix
+  Lambda comes from the three terms in three moves: their geometric mean,
+  then its logarithm, then a causal running sum.
 * ai4snews page, paragraph after Figure 1: the geometric mean vetoes (one term
   saying "no decay" zeroes the combined decay); f_q alone is FoX-style; one
   scalar bias is kept per KV pair and eviction is monotone.

@@ -31,8 +31,8 @@ def _run(cfg, steps, p, **kw):
 
     print(f"[decode parity] {cfg.name} B={cfg.B} steps={steps} p={p} {kw}", flush=True)
     run = run_decode_parity(cfg, steps, math.log(p) if p > 0 else -math.inf, **kw)
-    print(f"  max |dy| {run.max_y_err:.2e}  max rel dLambda {run.max_lam_err:.2e}  borderline {run.borderline}  "
-          f"dead {sum(r.n_dead for r in run.reports)}", flush=True)
+    print(f"  max |dy| {run.max_y_err:.2e}  max rel dLambda {run.max_lam_err:.2e} (floor 1e-6: "
+          f"{run.max_lam_err_strict:.2e})  borderline {run.borderline}  dead {sum(r.n_dead for r in run.reports)}", flush=True)
     return run
 
 
@@ -80,7 +80,7 @@ def test_lazy_compaction_and_p0():
     _run(cfg, 6, 0.0, compact_every=0)
 
 
-@pytest.mark.parametrize("G,d", [(1, 64), (2, 128), (8, 64), (4, 128), (3, 64)])
+@pytest.mark.parametrize("G,d", [(1, 64), (2, 128), (8, 64), (4, 128), (3, 64), (8, 128)])
 def test_group_and_head_dims(G, d):
     cfg = config("1b-decode", B=2, H_kv=2, H_q=2 * G, d=d, D=256, len_mean=200.0, len_max=600)
     _run(cfg, 6, cfg.p)
@@ -164,8 +164,8 @@ def _run_fused(cfg, steps, p, **kw):
 
     print(f"[fused parity] {cfg.name} B={cfg.B} steps={steps} p={p} {kw}", flush=True)
     run = run_fused_parity(cfg, steps, math.log(p) if p > 0 else -math.inf, **kw)
-    print(f"  max |dy| {run.max_y_err:.2e}  max rel dLambda {run.max_lam_err:.2e}  borderline {run.borderline}  "
-          f"evicted {sum(r.n_dead for r in run.reports)}", flush=True)
+    print(f"  max |dy| {run.max_y_err:.2e}  max rel dLambda {run.max_lam_err:.2e} (floor 1e-6: "
+          f"{run.max_lam_err_strict:.2e})  borderline {run.borderline}  evicted {sum(r.n_dead for r in run.reports)}", flush=True)
     return run
 
 
@@ -199,6 +199,37 @@ def test_fused_term_subsets(terms):
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (24, 8), (64, 8)])
 def test_fused_group_sizes(hq, hkv):
     _run_fused(config("1b-decode", B=2, H_q=hq, H_kv=hkv), 4, 0.15)
+
+
+def test_fused_group8_head128():
+    """Group size 8 at head dim 128 (64 query heads over 8 KV heads, 3B-shape cache)."""
+    _run_fused(config("3b-decode", B=2, H_q=64, H_kv=8), 6, 0.15)
+
+
+def test_group8_head128_3b_cache():
+    _run(config("3b-decode", B=2, H_q=64, H_kv=8), 6, 0.15)
+
+
+# ---- every configuration over its stated number of steps (eviction is monotone:
+# an entry once evicted never returns, so long runs are what exercise it) ----
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["1b-decode", "3b-decode", "ragged-decode"])
+def test_all_steps_two_calls(name):
+    """ua_decode_step then ua_compact, every step of the configuration at its full batch."""
+    cfg = config(name)
+    run = _run(cfg, cfg.steps, cfg.p)
+    assert len(run.reports) == cfg.steps
+    assert sum(r.n_dead for r in run.reports) > 0
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["1b-decode", "3b-decode", "ragged-decode"])
+def test_all_steps_fused(name):
+    """ua_decode_compact_step, every step of the configuration at its full batch."""
+    cfg = config(name)
+    run = _run_fused(cfg, cfg.steps, cfg.p)
+    assert len(run.reports) == cfg.steps
+    assert sum(r.n_dead for r in run.reports) > 0
 
 
 @pytest.mark.parametrize("p", [0.0, 0.02])

@@ -18,4 +18,7 @@ from .gen import (  # noqa: F401
     config,
     GradInputs,
     make_grad_inputs,
+    MASK_PATTERNS,
+    mask_pattern,
+    make_mask_cache,
 )

@@ -312,3 +312,69 @@ def make_grad_inputs(B: int, N: int, H_q: int, H_kv: int, d: int, bf16: bool = T
         gates.append((-np.logaddexp(0.0, -z)).astype(np.float32))
     dO = rng.normal(0, 1, (B, N, H_q, d)).astype(np.float32)
     return GradInputs(q, k, v, gates[0], gates[1], gates[2], dO)
+
+
+# ---------------------------------------------------------------------------
+# caches with constructed keep masks (compaction exactness)
+# ---------------------------------------------------------------------------
+MASK_PATTERNS = ("dead", "live", "alt", "first_only", "last_only", "first_dead", "last_dead", "random", "front_dead")
+
+
+def mask_pattern(kind: str, n: int, rng: np.random.Generator) -> np.ndarray:
+    """A keep mask of n entries: every entry dead or live, alternating (the
+    first live), a single survivor first or last, everything but the first
+    or the last entry, a seeded coin per entry, or the first half dead (so
+    every survivor moves)."""
+    m = np.zeros(n, bool)
+    if n == 0:
+        return m
+    if kind == "live":
+        m[:] = True
+    elif kind == "alt":
+        m[0::2] = True
+    elif kind == "first_only":
+        m[0] = True
+    elif kind == "last_only":
+        m[-1] = True
+    elif kind == "first_dead":
+        m[1:] = True
+    elif kind == "last_dead":
+        m[:-1] = True
+    elif kind == "random":
+        m = rng.random(n) < 0.5
+    elif kind == "front_dead":
+        m[n // 2 :] = True
+    elif kind != "dead":
+        raise ValueError(kind)
+    return m
+
+
+def make_mask_cache(lengths, kinds, d: int, bf16: bool, log_p: float, seed: int = 0, extra: int = 16,
+                    B: Optional[int] = None) -> CacheInit:
+    """A cache whose segment s holds lengths[s] entries with keep mask kinds[s].
+
+    Live entries get log-biases uniform in [log_p + 1e-3, 0], dead ones
+    uniform in [log_p - 2, log_p - 1e-3] (every decision is 1e-3 or more
+    away from the threshold); keys, values and key gates are N(0, 1) draws
+    (bf16-exact in bf16 caches), distinct per row so a misplaced row shows.
+    ``B`` sequences share the segments evenly (default: one KV head each).
+    """
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed)))
+    lengths = np.asarray(lengths, np.int64)
+    S = lengths.size
+    off, cap, slots = make_layout(lengths, extra)
+    K = rng.standard_normal((slots, d), dtype=np.float32)
+    V = rng.standard_normal((slots, d), dtype=np.float32)
+    lk = -np.abs(rng.standard_normal(slots, dtype=np.float32))
+    lam = np.zeros(slots, np.float32)
+    for s in range(S):
+        n = int(lengths[s])
+        m = mask_pattern(kinds[s], n, rng)
+        live = rng.uniform(log_p + 1e-3, 0.0, n)
+        dead = rng.uniform(log_p - 2.0, log_p - 1e-3, n)
+        lam[off[s] : off[s] + n] = np.where(m, live, dead).astype(np.float32)
+    if bf16:
+        K, V = bf16_exact(K), bf16_exact(V)
+    nb = S if B is None else B
+    return CacheInit(K=K, V=V, lam=lam, lk=lk, seg_off=off, seg_len=lengths.astype(np.int32), seg_cap=cap,
+                     next_pos=np.zeros(nb, np.int32))
