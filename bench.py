@@ -441,7 +441,12 @@ def main():
         over["B"] = args.batch
     if args.q_heads:
         over["H_q"] = args.q_heads
+    def note(what, t0):
+        print(f"[bench] {what} done ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+    t0 = time.time()
     head = bench_decode(args, args.workload, over)
+    note(f"decode {args.workload}", t0)
     out = {
         "metric": "UA decode tokens/s + achieved HBM GB/s on pruned KV cache; prefill tok/s",
         "value": head["value"],
@@ -467,15 +472,23 @@ def main():
         out["decode_configs"] = {}
         for name in DECODE_WORKLOADS:
             if name != args.workload:
+                t0 = time.time()
                 out["decode_configs"][name] = bench_decode(args, name)
+                note(f"decode {name}", t0)
         if not args.no_prefill:
+            t0 = time.time()
             out["prefill"] = bench_prefill(args)
+            note("prefill", t0)
             if not args.no_prefill_variants:
+                t0 = time.time()
                 out["prefill_pruned"] = bench_prefill_pruned(args)
                 out["prefill_chunked"] = bench_prefill_pruned(args, chunked=True)
                 out["prefill_varlen"] = bench_prefill_varlen(args)
+                note("prefill variants", t0)
         if not args.no_backward:
+            t0 = time.time()
             out["backward"] = bench_backward(args)
+            note("backward", t0)
     print(json.dumps(out), flush=True)
 
 

@@ -8,6 +8,7 @@ of the spec: y max-abs 1e-2 (bf16) / 1e-4 (fp32); log-biases
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import List, Optional
 
@@ -314,23 +315,6 @@ def run_prefill_parity(cfg: LayerConfig, calls: Optional[int] = None, terms: int
     return rep
 
 
-def _segment_oracle(args):
-    """Worker: final log-biases and sampled outputs of one prefill segment.
-
-    Runs the oracle's dense definitions (O5 as column sums, O7 per row) on the
-    GPU-stored keys (R17); a module-level function so a process pool can run
-    segments side by side.
-    """
-    (terms, Kt, V, lq, lk, lb, q_rows, gam_rows, rows, scale, base) = args
-    N = Kt.shape[0]
-    lam_rows = U.dense_logbias(terms, Kt, lq, lk, lb, rows=np.append(rows, N - 1))
-    ys = []
-    for ri, i in enumerate(rows):
-        qt = U.rope(q_rows[ri], np.full(q_rows.shape[1], i), base)
-        ys.append(gam_rows[ri] * U.attend(qt, Kt[: i + 1], V[: i + 1], lam_rows[ri, : i + 1], scale))
-    return lam_rows[-1], np.stack(ys)
-
-
 def run_prefill_full(cfg: LayerConfig, rows_per_call: int = 16, log_p: Optional[float] = None, seed: int = 0,
                      terms: int = 7, workers: int = 8, segments=None) -> dict:
     """Full-size prefill from an empty cache, then one eviction at log_p.
@@ -400,11 +384,15 @@ def run_prefill_full(cfg: LayerConfig, rows_per_call: int = 16, log_p: Optional[
         q_rows = q_all[b][rows, h * G : (h + 1) * G].astype(np.float64)
         gam_rows = np.stack([U.output_gate(od, op, x_all[b][i])[h * G : (h + 1) * G] for i in rows])
         jobs.append((terms, Kt, V, lq[:, h], lk[:, h], lb[:, h], q_rows, gam_rows, rows, od.scale, od.rope_base))
+    from tests.oracle_worker import segment_prefill_oracle
+
     print(f"    GPU calls done; oracle on {len(jobs)} segments in {min(workers, len(jobs))} processes", flush=True)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"  # one BLAS thread per worker process
     ctx = mp.get_context("spawn")
     results = [None] * len(jobs)
     with cf.ProcessPoolExecutor(max_workers=min(workers, len(jobs)), mp_context=ctx) as ex:
-        futs = {ex.submit(_segment_oracle, j): i for i, j in enumerate(jobs)}
+        futs = {ex.submit(segment_prefill_oracle, j): i for i, j in enumerate(jobs)}
         for n_done, f in enumerate(cf.as_completed(futs)):
             results[futs[f]] = f.result()
             print(f"    oracle segment {n_done + 1}/{len(jobs)} done", flush=True)

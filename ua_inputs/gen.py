@@ -25,7 +25,6 @@ from dataclasses import dataclass, field, replace
 from typing import Dict, List, Optional
 
 import numpy as np
-import torch
 
 
 # ---------------------------------------------------------------------------
@@ -33,6 +32,8 @@ import torch
 # ---------------------------------------------------------------------------
 def bf16_exact(a: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 and return them as float32."""
+    import torch
+
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(torch.bfloat16).to(torch.float32).numpy()
 
