@@ -10,30 +10,31 @@
 // out of the step's softmax and are evicted; the output is the low-rank
 // sigmoid gate times the attention output; the new entry is appended.
 //
-// Launch 1, decode_token_kernel (B + 1 workgroups): everything that depends
-// on the token alone, once per sequence -- the gate projection x [W_dec |
-// W_dn], the log-gates of every KV head, the output gate sigmoid(u W_up +
-// b_up) of every query head, the rotated queries, the stored key (normalised,
-// rotated, rounded like the cache) and the token's logit against its own key
-// -- written to the workspace.  The last workgroup numbers the tiles of the
+// Launch 1, decode_token_kernel (4 workgroups per sequence, one more): what
+// depends on the token alone -- the projections x W_dec and u = x W_dn (each
+// of the 4 workgroups a slice of the rows; readers add the partials), the
+// rotated queries and the stored key (normalised, rotated, rounded like the
+// cache), each workgroup a quarter -- written to the workspace.  The last workgroup numbers the tiles of the
 // step from the segment lengths (a tile is TWG consecutive entries of one
 // segment), writes one record per tile, and clears the per-segment counters
 // and the look-back words of the second launch.
 //
-// Launch 2, decode_tile_kernel (one workgroup per possible tile, four waves):
-// a workgroup past the step's tile count exits at once; the others read their
-// tile record, issue every cache load of the tile together with the token's
-// rotated queries and key, and read each entry once: the key row feeds the G
+// Launch 2, decode_tile_kernel (a persistent grid of four-wave workgroups,
+// every one resident at once, taking the tiles in turn; the next tile's rows
+// are loaded straight into LDS while the current one runs): a workgroup
+// reads its tile record, the token's rotated queries and key, and reads each
+// entry once: the key row feeds the G
 // query dot products and the key-similarity dot product (reduced over the
 // d/8 lanes that hold the row, with DPP), the pair term updates the log-bias,
 // entries below log p drop out, and an online-softmax partial (max, sum,
-// weighted V) is formed per wave and merged across the waves in LDS.  The
-// workgroups of a segment's tiles draw the tile numbers from a per-segment
-// ticket, so a tile's predecessors in its segment are held by workgroups that
-// started earlier: every wait below is on one of them.
+// weighted V) is formed per wave and merged across the waves in LDS.  Every
+// wait below is on a lower tile of the same segment.
 //  * A one-tile segment combines at once; otherwise each tile publishes its
-//    partial and the last to arrive (an atomic counter) merges them.  The
-//    combine adds the token's own term and multiplies by the output gate.
+//    partial before its flag word, and the segment's last tile, once its
+//    look-back has seen every earlier tile publish, merges them.  The
+//    combine adds the token's own term (every tile forms the token's logit
+//    against its own key from the queries and key it holds) and multiplies
+//    by the output gate sigmoid(u W_up + b_up) of its outputs.
 //  * With COMPACT the survivors move down in place: a tile publishes its live
 //    count once every row of the tile is in registers and looks back over the
 //    earlier tiles of its segment for its destination (decoupled look-back);
@@ -43,12 +44,14 @@
 //    segment's last tile learns the new length, appends the new entry after
 //    the survivors and writes the length.
 //  * Without COMPACT the log-biases are updated in place and the segment's
-//    first tile appends the new entry at the old length.
+//    last tile appends the new entry at the old length.
 // No launch reads a length another workgroup of the same launch writes: the
 // tile records carry the lengths at the start of the step.
 //
 // Cross-workgroup data go through relaxed agent-scope atomics (coherent across
 // the XCDs without cache-wide write-back or invalidation).
+
+#include <algorithm>
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -77,6 +80,7 @@ __device__ __forceinline__ unsigned long long ld64_coh(const unsigned long long*
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 constexpr int kTokThreads = 256;
+constexpr int kTokParts = 4;  // token-launch workgroups per sequence
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
 constexpr int kSpinLimitDec = 1 << 22;
@@ -143,7 +147,7 @@ __device__ __forceinline__ void row_f32(const Row8<BF16>& r, float (&o)[8]) {
 // query heads per KV head: four keeps a tile's loads in flight together; at
 // group size 8 the queries and the weighted-V sums of eight heads leave room
 // for two.
-constexpr int decode_nb(int d, int g) { return g >= 8 ? 2 : 4; }
+constexpr int decode_nb(int d, int g) { return g >= 8 ? 4 : 8; }
 
 template <int D, int NB_>
 struct TileShape {
@@ -172,81 +176,107 @@ struct DecodeKArgs {
 // ---------------------------------------------------------------------------
 // launch 1: the token's own quantities, once per sequence; the tile records
 // ---------------------------------------------------------------------------
-// z[c] = x . M[:, c] for the ncols columns of a row-major [D, ncols] matrix,
-// into s_z.  Threads take 16-byte column chunks (or single columns) and split
-// the rows; partial sums meet in LDS.
-template <bool BF16>
-__device__ void token_gemv(const LayerArgs& a, const void* Mv, int ncols, const char* xrow, float* s_z,
-                           float (*s_red)[8]) {
+// Partial sums of z[c] = x . M[:, c] for the ncols columns of a row-major [D,
+// ncols] matrix by NTH threads (thread t of them): threads take 16-byte column
+// chunks (or single columns) and split the rows, every load of a pass in
+// flight together; the partials go to s_red (rows [0, NTH)).  gemv_finish
+// adds them up after a barrier.
+struct GemvPlan {
+  int ncols, CWv, nch, npow, R, reff;
+  bool vec;
+};
+
+template <bool BF16, int NTH>
+__device__ __forceinline__ GemvPlan gemv_plan(int ncols) {
   constexpr int CW = BF16 ? 8 : 4;  // elements per 16-byte chunk
-  constexpr int NT = kTokThreads;
-  constexpr int KR = 16;  // rows per thread per pass, all loads in flight together
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int Dm = a.D_model;
+  GemvPlan p;
+  p.ncols = ncols;
+  p.vec = ncols % CW == 0;
+  p.CWv = p.vec ? CW : 1;
+  p.nch = p.vec ? ncols / CW : ncols;
+  p.npow = 1;
+  while (p.npow < p.nch) p.npow <<= 1;
+  p.R = NTH / p.npow;  // row subsets (>= 1: at most 256 columns)
+  p.reff = p.npow <= 64 ? NTH / 64 : p.R;
+  return p;
+}
+
+struct RopeTable {  // the RoPE table of a position, formed while a gemv's loads fly
+  const double* inv_freq;
+  int pos, half;
+  float *cs, *sn;
+};
+
+__device__ __forceinline__ void rope_entry(const RopeTable& rt, int i) {  // fp64 angle
+  double sn, cs;
+  sincos((double)rt.pos * rt.inv_freq[i], &sn, &cs);
+  rt.cs[i] = (float)cs;
+  rt.sn[i] = (float)sn;
+}
+
+template <bool BF16, int NTH>
+__device__ __forceinline__ void gemv_partial(const GemvPlan& p, int t, int r0, int r1, const void* Mv,
+                                             const char* xrow, float (*s_red)[8], const RopeTable* rt = nullptr) {
+  constexpr int KR = 16;  // rows per thread per pass
+  const int lane = t & 63;
+  const int wv = t >> 6;
   const char* const mbase = reinterpret_cast<const char*>(Mv);
-  const bool vec = ncols % CW == 0;
-  const int nch = vec ? ncols / CW : ncols;  // column groups (16-byte chunks or single columns)
-  int npow = 1;
-  while (npow < nch) npow <<= 1;
-  const int R = NT / npow;  // row subsets (>= 1: ncols <= 3 * 64 + 64 columns)
-  const int kc = tid & (npow - 1), rsub = tid / npow;
-  const bool own = kc < nch;
-  const int mc0 = own ? (vec ? kc * CW : kc) : 0;
+  const int kc = t & (p.npow - 1), rsub = t / p.npow;
+  const bool own = kc < p.nch;
+  const int mc0 = own ? kc * p.CWv : 0;
   float acc[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) acc[t] = 0.0f;
-  for (int rb = rsub; rb < Dm; rb += KR * R) {
+  for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+  bool tdone = false;
+  for (int rb = r0 + rsub; rb < r1; rb += KR * p.R) {
     float xr[KR];
     u32x4 raw[KR];
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
-      const int row = min(rb + q * R, Dm - 1);
+      const int row = min(rb + q * p.R, r1 - 1);
       xr[q] = elem_at<BF16>(xrow, (uint32_t)row * (BF16 ? 2 : 4));
-      const uint32_t e = (uint32_t)(row * ncols + mc0) * (BF16 ? 2 : 4);
-      if (vec) {
+      const uint32_t e = (uint32_t)(row * p.ncols + mc0) * (BF16 ? 2 : 4);
+      if (p.vec) {
         raw[q] = ld_at<u32x4>(mbase, e);
       } else {
         raw[q] = u32x4{__float_as_uint(elem_at<BF16>(mbase, e)), 0u, 0u, 0u};
       }
     }
+    if (rt && !tdone && t < rt->half) rope_entry(*rt, t);
+    tdone = true;
 #pragma unroll
     for (int q = 0; q < KR; ++q) {
-      const float xv = (own && rb + q * R < Dm) ? xr[q] : 0.0f;
-      if (vec) {
+      const float xv = (own && rb + q * p.R < r1) ? xr[q] : 0.0f;
+      if (p.vec) {
 #pragma unroll
-        for (int t = 0; t < CW; ++t) acc[t] = fmaf(xv, chunk_elem<BF16>(raw[q], t), acc[t]);
+        for (int e = 0; e < (BF16 ? 8 : 4); ++e) acc[e] = fmaf(xv, chunk_elem<BF16>(raw[q], e), acc[e]);
       } else {
         acc[0] = fmaf(xv, __uint_as_float(raw[q][0]), acc[0]);
       }
     }
   }
-  int reff;
-  if (npow <= 64) {  // a wave holds every column group: reduce its row subsets in registers
-    for (int o = npow; o < 64; o <<= 1) {
+  if (rt && !tdone && t < rt->half) rope_entry(*rt, t);  // no rows for this thread
+  if (p.npow <= 64) {  // a wave holds every column group: reduce its row subsets in registers
+    for (int o = p.npow; o < 64; o <<= 1) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) acc[t] += __shfl_xor(acc[t], o, 64);
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
     }
-    if (lane < npow) {
+    if (lane < p.npow) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) s_red[wv * npow + lane][t] = acc[t];
+      for (int e = 0; e < 8; ++e) s_red[wv * p.npow + lane][e] = acc[e];
     }
-    reff = NT / 64;
   } else {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) s_red[tid][t] = acc[t];
-    reff = R;
+    for (int e = 0; e < 8; ++e) s_red[t][e] = acc[e];
   }
-  __syncthreads();
-  for (int c = tid; c < ncols; c += NT) {
-    const int grp = vec ? c / CW : c;
-    const int t = vec ? c % CW : 0;
-    float z = 0.0f;
-    for (int rr = 0; rr < reff; ++rr) z += s_red[rr * npow + grp][t];
-    s_z[c] = z;
-  }
-  __syncthreads();
+}
+
+__device__ __forceinline__ float gemv_finish(const GemvPlan& p, int c, const float (*s_red)[8]) {
+  const int grp = c / p.CWv;
+  const int e = c - grp * p.CWv;
+  float z = 0.0f;
+  for (int rr = 0; rr < p.reff; ++rr) z += s_red[rr * p.npow + grp][e];
+  return z;
 }
 
 template <int D, bool BF16>
@@ -255,20 +285,23 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
   const LayerArgs& a = K.a;
   const DecodeWs& w = K.w;
   constexpr int NT = kTokThreads;
+  constexpr int NH = NT / 2;  // threads per projection
   constexpr int HALF = D / 2;
+  constexpr int P = kTokParts;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = tid >> 6;
-  const int Hkv = a.H_kv, Hq = a.H_q, G = Hq / Hkv;
+  const int Hkv = a.H_kv, Hq = a.H_q;
   const int S = a.B * Hkv;
-  const int b = blockIdx.x;
 
   __shared__ float s_red[NT][8];
-  __shared__ float s_z[3 * kMaxHkv + kMaxRank];
   __shared__ float s_cs[HALF], s_sn[HALF];
   __shared__ int s_scan[NT / 64 + 1];
+  constexpr int kMapSegs = 2048;  // segments whose tile records are written in parallel
+  __shared__ int s_first[kMapSegs + 1], s_len[kMapSegs];
+  __shared__ int64_t s_off[kMapSegs];
 
-  if (b == a.B) {
+  if ((int)blockIdx.x == a.B * P) {
     // ---- the tile records of this step, from the lengths at its start
     const int twg = K.twg;
     const int per = (S + NT - 1) / NT;
@@ -277,17 +310,44 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
     for (int s = sb; s < se; ++s) mine += tiles_of(a.seg_len[s], twg);
     int total;
     int run = block_exclusive_scan<NT>(mine, s_scan, &total);
-    for (int s = sb; s < se; ++s) {
-      const int len = a.seg_len[s];
-      const int nt = tiles_of(len, twg);
-      const int64_t off = a.seg_off[s];
-      for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {  // lengths beyond capacity break the bound
-        w.map[2 * (run + t) + 0] = make_int4(s, t, len, nt);
-        w.map[2 * (run + t) + 1] = make_int4(run, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+    if (S <= kMapSegs) {
+      // every thread writes records t = tid, tid + NT, ...: its segment by
+      // binary search over the segments' first tiles, all read from LDS
+      for (int s = sb; s < se; ++s) {
+        const int len = a.seg_len[s];
+        s_first[s] = run;
+        s_len[s] = len;
+        s_off[s] = a.seg_off[s];
+        run += tiles_of(len, twg);
       }
+      if (tid == 0) s_first[S] = total;
+      __syncthreads();
+      for (int t = tid; t < total && t < w.max_tiles; t += NT) {  // lengths beyond capacity break the bound
+        int lo = 0, hi = S - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_first[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        const int f = s_first[lo];
+        const int64_t off = s_off[lo];
+        w.map[2 * t + 0] = make_int4(lo, t - f, s_len[lo], s_first[lo + 1] - f);
+        w.map[2 * t + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+      }
+    } else {
+      for (int s = sb; s < se; ++s) {
+        const int len = a.seg_len[s];
+        const int nt = tiles_of(len, twg);
+        const int64_t off = a.seg_off[s];
+        for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {  // lengths beyond capacity break the bound
+          w.map[2 * (run + t) + 0] = make_int4(s, t, len, nt);
+          w.map[2 * (run + t) + 1] = make_int4(run, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+        }
+        run += nt;
+      }
+    }
+    for (int s = sb; s < se; ++s) {
       w.cnt[s] = 0;
       w.segtk[s] = 0;
-      run += nt;
     }
     if (total > w.max_tiles) {  // a segment length above its capacity: no tile runs
       if (tid == 0) atomicOr(a.status, 4);
@@ -297,87 +357,128 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
     if (tid == 0) *w.ntiles = total;
     return;
   }
-
-  // ---- sequence b: position, RoPE table (fp64 angles)
-  const int pos = a.next_pos[b];
-  if (tid < HALF) {
-    double sn, cs;
-    sincos((double)pos * a.inv_freq[tid], &sn, &cs);
-    s_cs[tid] = (float)cs;
-    s_sn[tid] = (float)sn;
-  }
-  // ---- gate projection x [W_dec | W_dn]
+  // Workgroup (b, p): part p of P of sequence b's token work.  Every load of
+  // the part is issued first: its slice of x and of the rows of W_dec and
+  // W_dn, its queries and keys.
+  const int b = blockIdx.x / P;
+  const int p = blockIdx.x - b * P;
   const char* const xrow = reinterpret_cast<const char*>(a.x) + (int64_t)b * a.D_model * (BF16 ? 2 : 4);
-  token_gemv<BF16>(a, a.W_dec, 3 * Hkv, xrow, s_z, s_red);
-  token_gemv<BF16>(a, a.W_dn, a.r, xrow, s_z + 3 * Hkv, s_red);
-  if (tid == 0) a.next_pos[b] = pos + 1;
-
-  // ---- per KV head: the query/similarity part of the pair term (log2 units,
-  // divided by the number of enabled terms) and the new key's gate
-  const PairCoef pc = pair_coef(a.terms);
-  for (int h = tid; h < Hkv; h += NT) {
-    const float lq = log_sigmoid(s_z[h] + a.b_dec[h]);
-    const float lkn = log_sigmoid(s_z[Hkv + h] + a.b_dec[Hkv + h]);
-    const float lb = log_sigmoid(s_z[2 * Hkv + h] + a.b_dec[2 * Hkv + h]);
-    const float row2 = (((a.terms & 1) ? lq : 0.0f) + ((a.terms & 4) ? lb : 0.0f)) * pc.inv_n2;
-    w.tokf[(b * Hkv + h) * 2 + 0] = row2;
-    w.tokf[(b * Hkv + h) * 2 + 1] = lkn;
+  const int Dm = a.D_model;
+  const int r0 = (p * Dm) / P, r1 = ((p + 1) * Dm) / P;
+  const GemvPlan pd = gemv_plan<BF16, NH>(3 * Hkv);
+  const GemvPlan pn = gemv_plan<BF16, NH>(a.r);
+  // queries: item e = (head, pair) of the sequence, every P-th block of NT items
+  constexpr int QI = 4;  // items per thread in flight together
+  float q0v[QI], q1v[QI];
+#pragma unroll
+  for (int j = 0; j < QI; ++j) {
+    const int e = min(p * NT + tid + j * P * NT, Hq * HALF - 1);
+    const int hq = e / HALF, i = e - hq * HALF;
+    const int64_t qi = ((int64_t)b * Hq + hq) * D + i;
+    q0v[j] = load_elem<BF16>(a.q, qi);
+    q1v[j] = load_elem<BF16>(a.q, qi + HALF);
   }
-  // ---- output gate of every query head: sigmoid(u W_up + b_up)
-  const float* const u = s_z + 3 * Hkv;
-  const int HD = Hq * D;
-  for (int col = tid; col < HD; col += NT) {
-    float z = a.b_up ? a.b_up[col] : 0.0f;
-    for (int q = 0; q < a.r; ++q) z = fmaf(u[q], load_elem<BF16>(a.W_up, (int64_t)q * HD + col), z);
-    w.gam[(int64_t)b * HD + col] = sigmoid(z);
+  // keys of KV heads p + P wv, p + P (wv + 4), ...: the first one loaded now
+  const int h0 = p + P * wv;
+  float k0 = 0.0f, k1 = 0.0f;
+  if (h0 < Hkv && lane < HALF) {
+    k0 = load_elem<BF16>(a.k, (int64_t)(b * Hkv + h0) * D + lane);
+    k1 = load_elem<BF16>(a.k, (int64_t)(b * Hkv + h0) * D + lane + HALF);
   }
-  // ---- per KV head (one wave each): the stored key (L2-normalised, rotated,
-  // rounded like the cache), then for each of its G query heads the rotated
-  // query and the token's logit against its own key (log2 units)
-  const float qs2 = a.scale * kLog2e;
-  for (int h = wv; h < Hkv; h += NT / 64) {
+  // ---- x W_dn and x W_dec over rows [p D / P, (p + 1) D / P), half the
+  // threads each; the RoPE table of the position is formed while the
+  // first loads of x W_dn fly
+  const RopeTable rt{a.inv_freq, a.next_pos[b], HALF, s_cs, s_sn};
+  static_assert(HALF <= NH, "the table threads take part in x W_dn");
+  if (tid < NH) {
+    gemv_partial<BF16, NH>(pn, tid, r0, r1, a.W_dn, xrow, s_red, &rt);
+  } else {
+    gemv_partial<BF16, NH>(pd, tid - NH, r0, r1, a.W_dec, xrow, s_red + NH);
+  }
+  __syncthreads();
+  const int ZC = 3 * Hkv + a.r;
+  if (tid < a.r) w.zdec[((int64_t)b * P + p) * ZC + 3 * Hkv + tid] = gemv_finish(pn, tid, s_red);
+  if (tid < 3 * Hkv) w.zdec[((int64_t)b * P + p) * ZC + tid] = gemv_finish(pd, tid, s_red + NH);
+  // ---- rotated queries
+#pragma unroll
+  for (int j = 0; j < QI; ++j) {
+    const int e = p * NT + tid + j * P * NT;
+    if (e < Hq * HALF) {
+      const int hq = e / HALF, i = e - hq * HALF;
+      const int64_t qi = ((int64_t)b * Hq + hq) * D + i;
+      w.tq[qi] = fmaf(q0v[j], s_cs[i], -q1v[j] * s_sn[i]);
+      w.tq[qi + HALF] = fmaf(q1v[j], s_cs[i], q0v[j] * s_sn[i]);
+    }
+  }
+  for (int e = p * NT + tid + QI * P * NT; e < Hq * HALF; e += P * NT) {  // more than QI blocks
+    const int hq = e / HALF, i = e - hq * HALF;
+    const int64_t qi = ((int64_t)b * Hq + hq) * D + i;
+    const float a0 = load_elem<BF16>(a.q, qi), a1 = load_elem<BF16>(a.q, qi + HALF);
+    w.tq[qi] = fmaf(a0, s_cs[i], -a1 * s_sn[i]);
+    w.tq[qi + HALF] = fmaf(a1, s_cs[i], a0 * s_sn[i]);
+  }
+  // ---- the stored keys (L2-normalised, rotated, rounded like the cache), one wave per head
+  for (int h = h0; h < Hkv; h += P * (NT / 64)) {
     const int s = b * Hkv + h;
-    float k0 = 0.0f, k1 = 0.0f;
-    if (lane < HALF) {
+    if (h != h0 && lane < HALF) {
       k0 = load_elem<BF16>(a.k, (int64_t)s * D + lane);
       k1 = load_elem<BF16>(a.k, (int64_t)s * D + lane + HALF);
     }
     const float inv = 1.0f / fmaxf(sqrtf(wave_sum(k0 * k0 + k1 * k1)), 1e-12f);
-    float r0 = 0.0f, r1 = 0.0f;
     if (lane < HALF) {
       const float n0 = k0 * inv, n1 = k1 * inv;
-      r0 = fmaf(n0, s_cs[lane], -n1 * s_sn[lane]);
-      r1 = fmaf(n1, s_cs[lane], n0 * s_sn[lane]);
+      float rr0 = fmaf(n0, s_cs[lane], -n1 * s_sn[lane]);
+      float rr1 = fmaf(n1, s_cs[lane], n0 * s_sn[lane]);
       if constexpr (BF16) {
-        r0 = bf16_to_f32(f32_to_bf16(r0));
-        r1 = bf16_to_f32(f32_to_bf16(r1));
+        rr0 = bf16_to_f32(f32_to_bf16(rr0));
+        rr1 = bf16_to_f32(f32_to_bf16(rr1));
       }
-      w.tkey[(int64_t)s * D + lane] = r0;
-      w.tkey[(int64_t)s * D + lane + HALF] = r1;
-    }
-    for (int g = 0; g < G; ++g) {
-      const int hq = h * G + g;
-      const int64_t qi = ((int64_t)b * Hq + hq) * D + lane;
-      float e = 0.0f;
-      if (lane < HALF) {
-        const float q0 = load_elem<BF16>(a.q, qi), q1 = load_elem<BF16>(a.q, qi + HALF);
-        const float t0 = fmaf(q0, s_cs[lane], -q1 * s_sn[lane]);
-        const float t1 = fmaf(q1, s_cs[lane], q0 * s_sn[lane]);
-        w.tq[qi] = t0;
-        w.tq[qi + HALF] = t1;
-        e = fmaf(t0, r0, t1 * r1);
-      }
-      e = wave_sum(e);
-      if (lane == 0) w.es[(int64_t)b * Hq + hq] = e * qs2;
+      w.tkey[(int64_t)s * D + lane] = rr0;
+      w.tkey[(int64_t)s * D + lane + HALF] = rr1;
     }
   }
+}
+
+// Column col of z = x [W_dec | W_dn] of sequence b (the P row-slice partials
+// added), and log sigmoid(z + b_dec) of a gate column
+__device__ __forceinline__ float token_z(const LayerArgs& a, const DecodeWs& w, int b, int col) {
+  const int ZC = 3 * a.H_kv + a.r;
+  float z = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kTokParts; ++p) z += w.zdec[((int64_t)b * kTokParts + p) * ZC + col];
+  return z;
+}
+__device__ __forceinline__ float token_gate(const LayerArgs& a, const DecodeWs& w, int b, int col) {
+  return log_sigmoid(token_z(a, w, b, col) + a.b_dec[col]);
 }
 
 // ---------------------------------------------------------------------------
 // launch 2: the tiles
 // ---------------------------------------------------------------------------
+// Wait encodings (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8): everything outstanding, or only the LDS/scalar counter.
+constexpr int kWaitAll = 0;
+constexpr int kWaitLgkm = 0xC07F;  // vmcnt 63, expcnt 7, lgkmcnt 0
+
+// Load the V rows of a wave's entries straight into LDS at dst: for entry
+// slot bb, each lane's 16-byte pieces (a lane reads back exactly what it
+// loaded).
+template <int D, int NB, bool BF16>
+__device__ __forceinline__ void stage_v(const char* vseg, int f0, int relmax, int c, u32x4* dst) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int RP = BF16 ? 1 : 2;
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const int rel = min(f0 + bb, relmax);
+    const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+#pragma unroll
+    for (int pp = 0; pp < RP; ++pp)
+      __builtin_amdgcn_global_load_lds(vseg + ro + 16 * pp, to_lds(dst + (bb * RP + pp) * 64), 16, 0, 0);
+  }
+}
+
 template <int D, int G, bool BF16, bool COMPACT>
-__global__ __launch_bounds__(kTileThreads) void decode_tile_kernel(DecodeKArgs karg) {
+__global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArgs karg) {
   const DecodeKArgs& K = *(const DecodeKArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   const LayerArgs& a = K.a;
   const DecodeWs& w = K.w;
@@ -385,323 +486,290 @@ __global__ __launch_bounds__(kTileThreads) void decode_tile_kernel(DecodeKArgs k
   constexpr int LPE = Sh::LPE, NGW = Sh::NGW, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
   constexpr int NT = kTileThreads;
   constexpr int OPT = (G * D + NT - 1) / NT;  // outputs (g, i) per thread
+  constexpr int EB = BF16 ? 2 : 4;            // bytes per element
+  constexpr int RP = BF16 ? 1 : 2;            // 16-byte pieces of a lane's 8 elements
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane / LPE;
+  const int c = lane - grp * LPE;
+  const int Hkv = a.H_kv;
+  const int Hq = a.H_q;
 
-  __shared__ int s_kt;
-  __shared__ int s_flag;
   __shared__ int s_pre;
   __shared__ int s_cnt[kTileWaves];
   __shared__ float s_tp[kTileWaves][NGW * D];                   // per-wave transpose of the weighted V
   __shared__ float s_po[kTileWaves * G * D];                    // wave partials: weighted V
   __shared__ float s_pm[kTileWaves * G], s_pl[kTileWaves * G];  // wave partials: max (log2), sum
+  __shared__ float s_es[G];                                     // the token's own logits (log2 units)
+  __shared__ float s_u[kMaxRank];                               // u = x W_dn
+  __shared__ int s_kt;
+  __shared__ int s_flag;
+  __shared__ u32x4 s_v[kTileWaves][NB * RP][64];  // the wave's V rows (loaded straight into LDS)
 
-  if ((int)blockIdx.x >= *w.ntiles) return;  // past this step's tiles
-  const int4 m0 = w.map[2 * blockIdx.x + 0];
-  const int4 m1 = w.map[2 * blockIdx.x + 1];
-  const int seg = m0.x;
-  const int len = m0.z;
-  const int ntile = m0.w;
-  const int pbase = m1.x;  // record number of the segment's first tile
-  const int64_t off = (int64_t)(uint32_t)m1.y | ((int64_t)m1.z << 32);
-  const bool single = ntile == 1;
-  int kt = 0;
-  if (!single) {  // tile numbers in arrival order: a tile's predecessors have started
-    if (tid == 0) s_kt = add_coh(&w.segtk[seg], 1);
-    __syncthreads();
-    kt = s_kt;
-  }
-  const int Hkv = a.H_kv;
-  const int b = seg / Hkv;
-  const int h = seg - b * Hkv;
-  const int grp = lane / LPE;
-  const int c = lane - grp * LPE;
-  const int e0 = kt * TWG + wv * TW + grp * NB;
-
-  // ---- cached entries: every load issued first, from the segment's base with
-  // 32-bit offsets; slots past the end read the last entry (masked below)
-  constexpr int EB = BF16 ? 2 : 4;  // bytes per element
-  char* const Kseg = reinterpret_cast<char*>(a.K) + off * (D * EB);
-  char* const Vseg = reinterpret_cast<char*>(a.V) + off * (D * EB);
-  const char* const lamseg = reinterpret_cast<const char*>(a.lam + off);
-  const char* const lkseg = reinterpret_cast<const char*>(a.lk + off);
-  const int relmax = max(len - 1, 0);
-  Row8<BF16> kr[NB], vr[NB];
-  float lamv[NB], lkv[NB];
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    const int rel = min(e0 + bb, relmax);
-    const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
-    row_load_at<BF16>(kr[bb], Kseg, ro);
-    row_load_at<BF16>(vr[bb], Vseg, ro);
-    lamv[bb] = ld_at<float>(lamseg, (uint32_t)rel * 4);
-    lkv[bb] = ld_at<float>(lkseg, (uint32_t)rel * 4);
-  }
-  // ---- the token: rotated queries of the group and the stored key (8 dims
-  // per lane), the query/similarity part of the pair term
-  float qv[G][8], ktv[8];
+  // One workgroup per tile.  The tile number within its segment comes from a
+  // per-segment ticket, so a tile's predecessors in its segment are held by
+  // workgroups that started earlier and every wait below ends.  The record's
+  // own number (the ticket's value when workgroups start in order) is used
+  // to start the loads at once; another ticket value reloads.
+  const int tile = blockIdx.x;
+  const int4 m0 = w.map[2 * tile + 0];  // read with the tile count (a record past it is never used)
+  const int4 m1 = w.map[2 * tile + 1];
+  if (tile >= *w.ntiles) return;
   {
-    const float* qrow = w.tq + ((int64_t)b * a.H_q + h * G) * D + 8 * c;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float4 x0 = *reinterpret_cast<const float4*>(qrow + g * D);
-      const float4 x1 = *reinterpret_cast<const float4*>(qrow + g * D + 4);
-      qv[g][0] = x0.x; qv[g][1] = x0.y; qv[g][2] = x0.z; qv[g][3] = x0.w;
-      qv[g][4] = x1.x; qv[g][5] = x1.y; qv[g][6] = x1.z; qv[g][7] = x1.w;
-    }
-    const float* krow = w.tkey + (int64_t)seg * D + 8 * c;
-    const float4 x0 = *reinterpret_cast<const float4*>(krow);
-    const float4 x1 = *reinterpret_cast<const float4*>(krow + 4);
-    ktv[0] = x0.x; ktv[1] = x0.y; ktv[2] = x0.z; ktv[3] = x0.w;
-    ktv[4] = x1.x; ktv[5] = x1.y; ktv[6] = x1.z; ktv[7] = x1.w;
-  }
-  const float row2 = w.tokf[2 * seg];
-  const float tau = K.tau;
-  const float qs2 = a.scale * kLog2e;
-  const PairCoef pc = pair_coef(a.terms);
-  const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+    const int seg = m0.x;
+    const int len = m0.z;
+    const int ntile = m0.w;
+    const int pbase = m1.x;  // record number of the segment's first tile
+    const int64_t off = (int64_t)(uint32_t)m1.y | ((int64_t)m1.z << 32);
+    const bool single = ntile == 1;
+    const int b = seg / Hkv;
+    const int h = seg - b * Hkv;
+    char* const Kseg = reinterpret_cast<char*>(a.K) + off * (D * EB);
+    char* const Vseg = reinterpret_cast<char*>(a.V) + off * (D * EB);
+    const char* const lamseg = reinterpret_cast<const char*>(a.lam + off);
+    const char* const lkseg = reinterpret_cast<const char*>(a.lk + off);
+    const int relmax = max(len - 1, 0);
+    int kt = m0.y;
+    if (!single && tid == 0) s_kt = add_coh(&w.segtk[seg], 1);
 
-  // ---- dot products, pair term, bias update, logits
-  float e2[G][NB];
-  float newlam[NB];
-  bool live[NB], changed[NB];
+    // ---- cached entries: every load issued first, from the segment's base
+    // with 32-bit offsets; slots past the end read the last entry (masked below)
+    Row8<BF16> kr[NB];
+    float lamv[NB], lkv[NB];
+    auto load_rows = [&](int k) {
+      const int f0 = k * TWG + wv * TW + grp * NB;
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    const bool valid = e0 + bb < len;
-    row_zero_if<BF16>(kr[bb], !valid);  // slots past the end may hold anything
-    row_zero_if<BF16>(vr[bb], !valid);
-    float kf[8];
-    row_f32<BF16>(kr[bb], kf);
-    float ps = 0.0f;
-    float pq[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) pq[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ps = fmaf(ktv[i], kf[i], ps);
-#pragma unroll
-      for (int g = 0; g < G; ++g) pq[g] = fmaf(qv[g][i], kf[i], pq[g]);
-    }
-    ps = group_sum<LPE>(ps);
-#pragma unroll
-    for (int g = 0; g < G; ++g) pq[g] = group_sum<LPE>(pq[g]);
-    const float l0 = valid ? lamv[bb] : kNegInf;
-    const bool alive = valid && (l0 >= tau);
-    const float A = pair_A(pc, row2, lkv[bb] * kscale, ps);
-    const float l1 = alive ? l0 + A : l0;
-    live[bb] = alive && (l1 >= tau);
-    newlam[bb] = l1;
-    changed[bb] = alive;
-    const float lb2 = l1 * kLog2e;
-#pragma unroll
-    for (int g = 0; g < G; ++g) e2[g][bb] = live[bb] ? fmaf(pq[g], qs2, lb2) : kNegInf;
-  }
-
-  // ---- this tile's live entries (compaction): lane grp * LPE + bb owns
-  // entry bb of its group; entries in tile order are (wave, group, entry)
-  uint64_t mask = 0;
-  if constexpr (COMPACT) {
-    bool mine_live = false;
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) mine_live = (c == bb) ? live[bb] : mine_live;
-    mask = __ballot(c < NB && mine_live);
-    if (lane == 0) s_cnt[wv] = __popcll(mask);
-  }
-
-  // ---- wave partial per head: max over the wave first, then sums relative to it
-  float ms[G], lw[G], o8[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = e2[g][0];
-#pragma unroll
-    for (int bb = 1; bb < NB; ++bb) m = fmaxf(m, e2[g][bb]);
-    ms[g] = across_groups_max<LPE>(m);
-    lw[g] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o8[g][i] = 0.0f;
-  }
-#pragma unroll
-  for (int bb = 0; bb < NB; ++bb) {
-    float vf[8];
-    row_f32<BF16>(vr[bb], vf);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float p = __builtin_amdgcn_exp2f(e2[g][bb] - ((ms[g] == kNegInf) ? 0.0f : ms[g]));
-      lw[g] += p;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o8[g][i] = fmaf(p, vf[i], o8[g][i]);
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float l = across_groups_sum<LPE>(lw[g]);
-    // the groups' weighted V summed through a per-wave LDS transpose: each
-    // lane writes its 8 sums, then lane j adds dimension j (and j + 64) over
-    // the groups.  LDS operations of one wave complete in order.
-    float* tp = s_tp[wv];  // [group][D]
-    {
-      float4* dst = reinterpret_cast<float4*>(tp + grp * D + 8 * c);
-      dst[0] = make_float4(o8[g][0], o8[g][1], o8[g][2], o8[g][3]);
-      dst[1] = make_float4(o8[g][4], o8[g][5], o8[g][6], o8[g][7]);
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int half = 0; half < D / 64; ++half) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int q = 0; q < NGW; ++q) sum += tp[q * D + half * 64 + lane];
-      s_po[(wv * G + g) * D + half * 64 + lane] = sum;
-    }
-    __builtin_amdgcn_wave_barrier();  // the next head reuses the scratch
-    if (lane == 0) {
-      s_pm[wv * G + g] = ms[g];
-      s_pl[wv * G + g] = l;
-    }
-  }
-  __syncthreads();  // partials and live counts in LDS; every row of the tile is in registers
-
-  int count = 0, wbase = 0;
-  if constexpr (COMPACT) {
-#pragma unroll
-    for (int w2 = 0; w2 < kTileWaves; ++w2) {
-      wbase += (w2 < wv) ? s_cnt[w2] : 0;
-      count += s_cnt[w2];
-    }
-    // this tile's count (the first tile's is already its inclusive prefix)
-    if (!single && tid == 0)
-      st64_coh(&K.ctl.dec_state[pbase + kt], (unsigned long long)((count << 2) | (kt == 0 ? 2 : 1)));
-  } else {
-    if (c < NB) {  // lane c of a group stores entry c's bias
-      float val = newlam[0];
-      bool ch = changed[0];
-#pragma unroll
-      for (int bb = 1; bb < NB; ++bb) {
-        val = (c == bb) ? newlam[bb] : val;
-        ch = (c == bb) ? changed[bb] : ch;
+      for (int bb = 0; bb < NB; ++bb) {
+        const int rel = min(f0 + bb, relmax);
+        const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+        row_load_at<BF16>(kr[bb], Kseg, ro);
+        lamv[bb] = ld_at<float>(lamseg, (uint32_t)rel * 4);
+        lkv[bb] = ld_at<float>(lkseg, (uint32_t)rel * 4);
       }
-      if (ch) a.lam[off + e0 + c] = val;
+    };
+    load_rows(kt);
+    // ---- the token: rotated queries of the group and the stored key (8 dims
+    // per lane), the query/similarity part of the pair term
+    float qv[G][8], ktv[8];
+    {
+      const float* qrow = w.tq + ((int64_t)b * Hq + h * G) * D + 8 * c;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float4 x0 = *reinterpret_cast<const float4*>(qrow + g * D);
+        const float4 x1 = *reinterpret_cast<const float4*>(qrow + g * D + 4);
+        qv[g][0] = x0.x; qv[g][1] = x0.y; qv[g][2] = x0.z; qv[g][3] = x0.w;
+        qv[g][4] = x1.x; qv[g][5] = x1.y; qv[g][6] = x1.z; qv[g][7] = x1.w;
+      }
+      const float* krow = w.tkey + (int64_t)seg * D + 8 * c;
+      const float4 x0 = *reinterpret_cast<const float4*>(krow);
+      const float4 x1 = *reinterpret_cast<const float4*>(krow + 4);
+      ktv[0] = x0.x; ktv[1] = x0.y; ktv[2] = x0.z; ktv[3] = x0.w;
+      ktv[4] = x1.x; ktv[5] = x1.y; ktv[6] = x1.z; ktv[7] = x1.w;
     }
-  }
-
-  // ---- the tile's partial per output (g, i): merge of the wave partials
-  float Mo[OPT], Lo[OPT], Oo[OPT];
-#pragma unroll
-  for (int u = 0; u < OPT; ++u) {
-    const int idx = min(u * NT + tid, G * D - 1);
-    const int g = idx / D;
-    const int i = idx - g * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w2 = 0; w2 < kTileWaves; ++w2) M = fmaxf(M, s_pm[w2 * G + g]);
-    const float Ms = (M == kNegInf) ? 0.0f : M;
-    float L = 0.0f, O = 0.0f;
-#pragma unroll
-    for (int w2 = 0; w2 < kTileWaves; ++w2) {
-      const float wgt = __builtin_amdgcn_exp2f(s_pm[w2 * G + g] - Ms);
-      L = fmaf(s_pl[w2 * G + g], wgt, L);
-      O = fmaf(s_po[(w2 * G + g) * D + i], wgt, O);
+    const PairCoef pc = pair_coef(a.terms);
+    const float lq = (a.terms & 1) ? token_gate(a, w, b, h) : 0.0f;
+    const float lbt = (a.terms & 4) ? token_gate(a, w, b, 2 * Hkv + h) : 0.0f;
+    const float row2 = (lq + lbt) * pc.inv_n2;
+    if (!single) {
+      __syncthreads();
+      if (s_kt != kt) {  // started out of order: this workgroup takes the ticket's tile
+        kt = s_kt;
+        load_rows(kt);
+      }
     }
-    Mo[u] = M;
-    Lo[u] = L;
-    Oo[u] = O;
-  }
+    const int e0 = kt * TWG + wv * TW + grp * NB;
+    // the V rows, needed after the logits: straight into LDS, no registers held
+    stage_v<D, NB, BF16>(Vseg, e0, relmax, c, &s_v[wv][0][0]);
 
-  bool combines = single;
-  if (!single) {
-    // ---- publish the partial; the last tile of the segment to arrive merges
-    const int64_t prow = (int64_t)(pbase + kt);
+    const float tau = K.tau;
+    const float qs2 = a.scale * kLog2e;
+    const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+    // the token's logit against its own key, per head (log2 units)
+    if (wv == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float e = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) e = fmaf(qv[g][i], ktv[i], e);
+        e = group_sum<LPE>(e);
+        if (lane == 0) s_es[g] = e * qs2;
+      }
+    }
+
+    // ---- dot products, pair term, bias update, logits
+    float e2[G][NB];
+    float newlam[NB];
+    bool live[NB], changed[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const bool valid = e0 + bb < len;
+      row_zero_if<BF16>(kr[bb], !valid);  // slots past the end may hold anything
+      float kf[8];
+      row_f32<BF16>(kr[bb], kf);
+      float ps = 0.0f;
+      float pq[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) pq[g] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ps = fmaf(ktv[i], kf[i], ps);
+#pragma unroll
+        for (int g = 0; g < G; ++g) pq[g] = fmaf(qv[g][i], kf[i], pq[g]);
+      }
+      ps = group_sum<LPE>(ps);
+#pragma unroll
+      for (int g = 0; g < G; ++g) pq[g] = group_sum<LPE>(pq[g]);
+      const float l0 = valid ? lamv[bb] : kNegInf;
+      const bool alive = valid && (l0 >= tau);
+      const float A = pair_A(pc, row2, lkv[bb] * kscale, ps);
+      const float l1 = alive ? l0 + A : l0;
+      live[bb] = alive && (l1 >= tau);
+      newlam[bb] = l1;
+      changed[bb] = alive;
+      const float lb2 = l1 * kLog2e;
+#pragma unroll
+      for (int g = 0; g < G; ++g) e2[g][bb] = live[bb] ? fmaf(pq[g], qs2, lb2) : kNegInf;
+    }
+
+    // ---- this tile's live entries (compaction): lane grp * LPE + bb owns
+    // entry bb of its group; entries in tile order are (wave, group, entry)
+    uint64_t mask = 0;
+    if constexpr (COMPACT) {
+      bool mine_live = false;
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) mine_live = (c == bb) ? live[bb] : mine_live;
+      mask = __ballot(c < NB && mine_live);
+      if (lane == 0) s_cnt[wv] = __popcll(mask);
+    }
+
+    // ---- wave partial per head: max over the wave first, then sums relative to it
+    float ms[G], lw[G], o8[G][8];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float m = e2[g][0];
+#pragma unroll
+      for (int bb = 1; bb < NB; ++bb) m = fmaxf(m, e2[g][bb]);
+      ms[g] = across_groups_max<LPE>(m);
+      lw[g] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[g][i] = 0.0f;
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);  // the V rows are in LDS
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      float vf[8];
+      Row8<BF16> vrow;
+#pragma unroll
+      for (int pp = 0; pp < RP; ++pp) vrow.w[pp] = s_v[wv][bb * RP + pp][lane];
+      row_zero_if<BF16>(vrow, e0 + bb >= len);  // slots past the end may hold anything
+      row_f32<BF16>(vrow, vf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = __builtin_amdgcn_exp2f(e2[g][bb] - ((ms[g] == kNegInf) ? 0.0f : ms[g]));
+        lw[g] += p;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o8[g][i] = fmaf(p, vf[i], o8[g][i]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float l = across_groups_sum<LPE>(lw[g]);
+      // the groups' weighted V summed through a per-wave LDS transpose: each
+      // lane writes its 8 sums, then lane j adds dimension j (and j + 64) over
+      // the groups.  LDS operations of one wave complete in order.
+      float* tp = s_tp[wv];  // [group][D]
+      {
+        float4* dst = reinterpret_cast<float4*>(tp + grp * D + 8 * c);
+        dst[0] = make_float4(o8[g][0], o8[g][1], o8[g][2], o8[g][3]);
+        dst[1] = make_float4(o8[g][4], o8[g][5], o8[g][6], o8[g][7]);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int half = 0; half < D / 64; ++half) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NGW; ++q) sum += tp[q * D + half * 64 + lane];
+        s_po[(wv * G + g) * D + half * 64 + lane] = sum;
+      }
+      __builtin_amdgcn_wave_barrier();  // the next head reuses the scratch
+      if (lane == 0) {
+        s_pm[wv * G + g] = ms[g];
+        s_pl[wv * G + g] = l;
+      }
+    }
+    __syncthreads();  // partials and live counts in LDS
+
+    int count = 0, wbase = 0;
+    if constexpr (COMPACT) {
+#pragma unroll
+      for (int w2 = 0; w2 < kTileWaves; ++w2) {
+        wbase += (w2 < wv) ? s_cnt[w2] : 0;
+        count += s_cnt[w2];
+      }
+    } else {
+      if (c < NB) {  // lane c of a group stores entry c's bias
+        float val = newlam[0];
+        bool ch = changed[0];
+#pragma unroll
+        for (int bb = 1; bb < NB; ++bb) {
+          val = (c == bb) ? newlam[bb] : val;
+          ch = (c == bb) ? changed[bb] : ch;
+        }
+        if (ch) a.lam[off + e0 + c] = val;
+      }
+    }
+
+    // ---- the tile's partial per output (g, i): merge of the wave partials
+    float Mo[OPT], Lo[OPT], Oo[OPT];
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
-      const int idx = u * NT + tid;
-      if (idx < G * D) {
-        const int g = idx / D;
-        const int i = idx - g * D;
-        st_coh(w.part_o + (prow * G + g) * D + i, Oo[u]);
-        if (i == 0) {
-          st_coh(w.part_ml + (prow * G + g) * 2 + 0, Mo[u]);
-          st_coh(w.part_ml + (prow * G + g) * 2 + 1, Lo[u]);
-        }
+      const int idx = min(u * NT + tid, G * D - 1);
+      const int g = idx / D;
+      const int i = idx - g * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w2 = 0; w2 < kTileWaves; ++w2) M = fmaxf(M, s_pm[w2 * G + g]);
+      const float Ms = (M == kNegInf) ? 0.0f : M;
+      float L = 0.0f, O = 0.0f;
+#pragma unroll
+      for (int w2 = 0; w2 < kTileWaves; ++w2) {
+        const float wgt = __builtin_amdgcn_exp2f(s_pm[w2 * G + g] - Ms);
+        L = fmaf(s_pl[w2 * G + g], wgt, L);
+        O = fmaf(s_po[(w2 * G + g) * D + i], wgt, O);
       }
+      Mo[u] = M;
+      Lo[u] = L;
+      Oo[u] = O;
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) s_flag = (add_coh(&w.cnt[seg], 1) == ntile - 1);
-    __syncthreads();
-    combines = s_flag;
-    if (combines) {
-      constexpr int TC = 8;  // tiles per pass, loads in flight together
+
+    // ---- a segment of several tiles: the live count first (successors' look-back
+    // needs only counts; the first tile's is its inclusive prefix), then the
+    // partial; the last tile of the segment to arrive merges the partials
+    bool combines = single;
+    if (!single) {
+      const int64_t prow = (int64_t)(pbase + kt);
+      if (COMPACT && tid == 0)
+        st64_coh(&K.ctl.dec_state[prow], (unsigned long long)((count << 2) | (kt == 0 ? 2 : 1)));
 #pragma unroll
       for (int u = 0; u < OPT; ++u) {
-        const int idx = min(u * NT + tid, G * D - 1);
-        const int g = idx / D;
-        const int i = idx - g * D;
-        float M = kNegInf, L = 0.0f, O = 0.0f;
-        for (int p0 = 0; p0 < ntile; p0 += TC) {
-          float pm[TC], pl[TC], po[TC];
-#pragma unroll
-          for (int p = 0; p < TC; ++p) {
-            const int64_t pr = (int64_t)(pbase + min(p0 + p, ntile - 1));
-            pm[p] = ld_coh(w.part_ml + (pr * G + g) * 2 + 0);
-            pl[p] = ld_coh(w.part_ml + (pr * G + g) * 2 + 1);
-            po[p] = ld_coh(w.part_o + (pr * G + g) * D + i);
+        const int idx = u * NT + tid;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const int i = idx - g * D;
+          st_coh(w.part_o + (prow * G + g) * D + i, Oo[u]);
+          if (i == 0) {
+            st_coh(w.part_ml + (prow * G + g) * 2 + 0, Mo[u]);
+            st_coh(w.part_ml + (prow * G + g) * 2 + 1, Lo[u]);
           }
-          float Mn = M;
-#pragma unroll
-          for (int p = 0; p < TC; ++p) Mn = (p0 + p < ntile) ? fmaxf(Mn, pm[p]) : Mn;
-          const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
-          const float rs = __builtin_amdgcn_exp2f(M - Ms);
-          L *= rs;
-          O *= rs;
-#pragma unroll
-          for (int p = 0; p < TC; ++p) {
-            if (p0 + p < ntile) {
-              const float wgt = __builtin_amdgcn_exp2f(pm[p] - Ms);
-              L = fmaf(pl[p], wgt, L);
-              O = fmaf(po[p], wgt, O);
-            }
-          }
-          M = Mn;
-        }
-        Mo[u] = M;
-        Lo[u] = L;
-        Oo[u] = O;
-      }
-    }
-  }
-
-  // ---- combine: the token's own term, the output gate, y
-  if (combines) {
-    const int Hq = a.H_q;
-#pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-      const int idx = u * NT + tid;
-      if (idx < G * D) {
-        const int g = idx / D;
-        const int i = idx - g * D;
-        const int col = (h * G) * D + idx;
-        const float es = w.es[(int64_t)b * Hq + h * G + g];
-        const float vn = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + i) * EB));
-        const float M = fmaxf(Mo[u], es);
-        const float rs = __builtin_amdgcn_exp2f(Mo[u] - M);  // Mo = -inf gives 0
-        const float pe = __builtin_amdgcn_exp2f(es - M);
-        const float L = fmaf(Lo[u], rs, pe);
-        const float O = fmaf(Oo[u], rs, pe * vn);
-        const int64_t yo = (int64_t)b * Hq * D + col;
-        const float yv = w.gam[yo] * (O / L);
-        if (a.y_bf16) {
-          reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16(yv);
-        } else {
-          reinterpret_cast<float*>(a.y)[yo] = yv;
         }
       }
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      __syncthreads();
+      if (tid == 0) s_flag = (add_coh(&w.cnt[seg], 1) == ntile - 1);
     }
-  }
-
-  int npos = len;  // where the new entry goes
-  if constexpr (COMPACT) {
-    // ---- destination of the survivors: look back over the earlier tiles
-    if (single || kt == 0) {
+    // ---- look back over the earlier tiles of the segment: the survivors' destination
+    if (!COMPACT || single || kt == 0) {
       if (tid == 0) s_pre = 0;
     } else if (wv == 0) {
       const unsigned long long* st = K.ctl.dec_state + pbase;
@@ -735,59 +803,172 @@ __global__ __launch_bounds__(kTileThreads) void decode_tile_kernel(DecodeKArgs k
       }
     }
     __syncthreads();
-    // ---- the survivors, in order; rows already in place are not rewritten
-    const int P = s_pre;
-    int32_t* const kept = K.kept;
-    const int myrank =
-        wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int rk = __shfl(myrank, grp * LPE + bb, 64);
-      if (live[bb]) {
-        const int rel = P + rk;
-        const int64_t dst = off + rel;
-        const bool moves = rel != e0 + bb;
-        if (moves) {
-          const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
-          row_store_at<BF16>(kr[bb], Kseg, ro);
-          row_store_at<BF16>(vr[bb], Vseg, ro);
-        }
-        if (c == bb) {
-          a.lam[dst] = newlam[bb];
-          if (moves) a.lk[dst] = lkv[bb];
-          if (kept) kept[dst] = e0 + bb;
-        }
-      }
-    }
-    npos = P + count;
-  }
+    if (!single) combines = s_flag;
+    const bool last = kt == ntile - 1;
 
-  // ---- the new entry: the segment's last tile after the survivors when
-  // compacting, else the first tile at the old length; then the new length
-  const bool appends = COMPACT ? (kt == ntile - 1) : (kt == 0);
-  if (appends) {
-    const bool room = len < a.seg_cap[seg];
-    if (room && tid < D) {
-      const int64_t dst = (off + npos) * D + tid;
-      const float kv = w.tkey[(int64_t)seg * D + tid];
-      const float vv = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + tid) * EB));
-      if constexpr (BF16) {
-        reinterpret_cast<uint16_t*>(a.K)[dst] = f32_to_bf16(kv);  // exact: kv is bf16-rounded
-        reinterpret_cast<uint16_t*>(a.V)[dst] = f32_to_bf16(vv);  // exact: a bf16 input
-      } else {
-        reinterpret_cast<float*>(a.K)[dst] = kv;
-        reinterpret_cast<float*>(a.V)[dst] = vv;
+    int npos = len;  // where the new entry goes
+    if constexpr (COMPACT) {
+      // ---- the survivors, in order; rows already in place are not rewritten
+      const int P = s_pre;
+      int32_t* const kept = K.kept;
+      const int myrank =
+          wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const int rk = __shfl(myrank, grp * LPE + bb, 64);
+        if (live[bb]) {
+          const int rel = P + rk;
+          const int64_t dst = off + rel;
+          const bool moves = rel != e0 + bb;
+          if (moves) {
+            const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+            row_store_at<BF16>(kr[bb], Kseg, ro);
+            Row8<BF16> vrow;
+#pragma unroll
+            for (int pp = 0; pp < RP; ++pp) vrow.w[pp] = s_v[wv][bb * RP + pp][lane];
+            row_store_at<BF16>(vrow, Vseg, ro);
+          }
+          if (c == bb) {
+            a.lam[dst] = newlam[bb];
+            if (moves) a.lk[dst] = lkv[bb];
+            if (kept) kept[dst] = e0 + bb;
+          }
+        }
+      }
+      npos = P + count;
+    }
+
+    if (combines) {
+      // ---- the segment's output: every tile's partial (this one's in
+      // registers when it is the only one), the token's own term, the gate
+      // what the combine needs of the token: its value, u = x W_dn (the P
+      // partials added, into LDS) and this thread's columns of W_up
+      constexpr int kUp = 16;
+      constexpr int UPF = OPT <= 2 ? OPT : 0;  // outputs whose W_up column is loaded together
+      float vnv[OPT], wup[UPF > 0 ? UPF : 1][kUp];
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) {
+        const int idx = min(u * NT + tid, G * D - 1);
+        vnv[u] = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + idx % D) * EB));
+        if (u < UPF) {
+#pragma unroll
+          for (int q = 0; q < kUp; ++q)
+            wup[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, a.r - 1) * Hq * D + (h * G) * D + idx);
+        }
+      }
+      if (tid < a.r) s_u[tid] = token_z(a, w, b, 3 * Hkv + tid);
+      if (!single) {
+        // every tile's (max, sum) per head through LDS (the per-wave transpose
+        // scratch, free here), then the weighted V in passes of TC tiles
+        float* s_ml = &s_tp[0][0];
+        constexpr int MLC = (kTileWaves * NGW * D) / (2 * G);  // tiles per LDS chunk
+        constexpr int TC = 16;                                // tiles per pass, loads in flight together
+        float M[OPT], L[OPT], O[OPT];
+#pragma unroll
+        for (int u = 0; u < OPT; ++u) {
+          M[u] = kNegInf;
+          L[u] = 0.0f;
+          O[u] = 0.0f;
+        }
+        for (int t0 = 0; t0 < ntile; t0 += MLC) {
+          const int tn = min(MLC, ntile - t0);
+          __syncthreads();
+          for (int j = tid; j < tn * G * 2; j += NT) s_ml[j] = ld_coh(w.part_ml + (int64_t)(pbase + t0) * G * 2 + j);
+          __syncthreads();
+#pragma unroll
+          for (int u = 0; u < OPT; ++u) {
+            const int idx = min(u * NT + tid, G * D - 1);
+            const int g = idx / D;
+            const int i = idx - g * D;
+            float Mn = M[u];
+            for (int t = 0; t < tn; ++t) Mn = fmaxf(Mn, s_ml[(t * G + g) * 2]);
+            const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
+            const float rs = __builtin_amdgcn_exp2f(M[u] - Ms);
+            L[u] *= rs;
+            O[u] *= rs;
+            for (int p0 = 0; p0 < tn; p0 += TC) {
+              float po[TC];
+#pragma unroll
+              for (int p = 0; p < TC; ++p)
+                po[p] = ld_coh(w.part_o + ((int64_t)(pbase + t0 + min(p0 + p, tn - 1)) * G + g) * D + i);
+#pragma unroll
+              for (int p = 0; p < TC; ++p) {
+                if (p0 + p < tn) {
+                  const float wgt = __builtin_amdgcn_exp2f(s_ml[((p0 + p) * G + g) * 2] - Ms);
+                  L[u] = fmaf(s_ml[((p0 + p) * G + g) * 2 + 1], wgt, L[u]);
+                  O[u] = fmaf(po[p], wgt, O[u]);
+                }
+              }
+            }
+            M[u] = Mn;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < OPT; ++u) {
+          Mo[u] = M[u];
+          Lo[u] = L[u];
+          Oo[u] = O[u];
+        }
+      }
+      __syncthreads();  // s_u
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) {
+        const int idx = u * NT + tid;
+        if (idx < G * D) {
+          const int g = idx / D;
+          const int col = (h * G) * D + idx;
+          const float es = s_es[g];
+          const float M = fmaxf(Mo[u], es);
+          const float rs = __builtin_amdgcn_exp2f(Mo[u] - M);  // Mo = -inf gives 0
+          const float pe = __builtin_amdgcn_exp2f(es - M);
+          const float L = fmaf(Lo[u], rs, pe);
+          const float O = fmaf(Oo[u], rs, pe * vnv[u]);
+          float z = a.b_up ? a.b_up[col] : 0.0f;
+          if (u < UPF) {
+#pragma unroll
+            for (int q = 0; q < kUp; ++q)
+              if (q < a.r) z = fmaf(s_u[q], wup[u < UPF ? u : 0][q], z);
+          } else {
+            for (int q = 0; q < min(a.r, kUp); ++q)
+              z = fmaf(s_u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
+          }
+          for (int q = kUp; q < a.r; ++q) z = fmaf(s_u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
+          const int64_t yo = (int64_t)b * Hq * D + col;
+          const float yv = sigmoid(z) * (O / L);
+          if (a.y_bf16) {
+            reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16(yv);
+          } else {
+            reinterpret_cast<float*>(a.y)[yo] = yv;
+          }
+        }
       }
     }
-    if (tid == 0) {
-      if (room) {
-        a.lam[off + npos] = 0.0f;
-        a.lk[off + npos] = w.tokf[2 * seg + 1];
-        if (COMPACT && K.kept) K.kept[off + npos] = len;
-      } else {
-        atomicOr(a.status, 1);
+    if (COMPACT ? last : combines) {
+      // ---- the new entry (after the survivors when compacting), the new length
+      const bool room = len < a.seg_cap[seg];
+      if (room && tid < D) {
+        const int64_t dst = (off + npos) * D + tid;
+        const float kv = w.tkey[(int64_t)seg * D + tid];
+        const float vv = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + tid) * EB));
+        if constexpr (BF16) {
+          reinterpret_cast<uint16_t*>(a.K)[dst] = f32_to_bf16(kv);  // exact: kv is bf16-rounded
+          reinterpret_cast<uint16_t*>(a.V)[dst] = f32_to_bf16(vv);  // exact: a bf16 input
+        } else {
+          reinterpret_cast<float*>(a.K)[dst] = kv;
+          reinterpret_cast<float*>(a.V)[dst] = vv;
+        }
       }
-      a.seg_len[seg] = room ? npos + 1 : npos;
+      if (tid == 0) {
+        if (room) {
+          a.lam[off + npos] = 0.0f;
+          a.lk[off + npos] = token_gate(a, w, b, Hkv + h);
+          if (COMPACT && K.kept) K.kept[off + npos] = len;
+        } else {
+          atomicOr(a.status, 1);
+        }
+        a.seg_len[seg] = room ? npos + 1 : npos;
+        if (h == 0) a.next_pos[b] += 1;  // once per sequence; no tile reads it
+      }
     }
   }
 }
@@ -816,25 +997,21 @@ static size_t decode_layout(const LayerArgs& a, int twg, DecodeWs* w, char* base
     n += align_up(bytes, 256);
     return q;
   };
-  int* segtk = reinterpret_cast<int*>(take(sizeof(int) * S));
   int* ntiles = reinterpret_cast<int*>(take(sizeof(int)));
+  int* segtk = reinterpret_cast<int*>(take(sizeof(int) * S));
   int4* map = reinterpret_cast<int4*>(take(sizeof(int4) * 2 * mt));
   float* tq = reinterpret_cast<float*>(take(sizeof(float) * a.B * a.H_q * a.d));
   float* tkey = reinterpret_cast<float*>(take(sizeof(float) * S * a.d));
-  float* gam = reinterpret_cast<float*>(take(sizeof(float) * a.B * a.H_q * a.d));
-  float* tokf = reinterpret_cast<float*>(take(sizeof(float) * S * 2));
-  float* es = reinterpret_cast<float*>(take(sizeof(float) * a.B * a.H_q));
+  float* zdec = reinterpret_cast<float*>(take(sizeof(float) * a.B * kTokParts * (3 * a.H_kv + a.r)));
   float* part_o = reinterpret_cast<float*>(take(sizeof(float) * mt * G * a.d));
   float* part_ml = reinterpret_cast<float*>(take(sizeof(float) * mt * G * 2));
   if (w) {
-    w->segtk = segtk;
     w->ntiles = ntiles;
+    w->segtk = segtk;
     w->map = map;
     w->tq = tq;
     w->tkey = tkey;
-    w->gam = gam;
-    w->tokf = tokf;
-    w->es = es;
+    w->zdec = zdec;
     w->part_o = part_o;
     w->part_ml = part_ml;
     w->max_tiles = (int)mt;
@@ -856,7 +1033,7 @@ static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Contr
                               int32_t* kept, hipStream_t st) {
   const int twg = TileShape<D, decode_nb(D, G)>::TWG;
   const DecodeKArgs k{a, w, ctl, tau, kept, twg};
-  hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B + 1), dim3(kTokThreads), 0, st, k);
+  hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B * kTokParts + 1), dim3(kTokThreads), 0, st, k);
   const int64_t mt = decode_max_tiles(a, twg);
   if (mt > (1 << 30)) return hipErrorInvalidValue;
   const int grid = (int)mt;

@@ -67,6 +67,17 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, float (&out)[8])
 }
 
 // ---------------------------------------------------------------------------
+// loads straight into LDS
+// ---------------------------------------------------------------------------
+// An LDS pointer in the LDS address space, as the global->LDS load builtins
+// take it: the low 32 bits of a generic pointer to a __shared__ object are
+// its LDS offset.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t to_lds(const void* p) {
+  return reinterpret_cast<lds_ptr_t>(static_cast<size_t>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p))));
+}
+
+// ---------------------------------------------------------------------------
 // cross-lane reductions inside groups of 8 / 16 lanes (DPP, no LDS)
 // ---------------------------------------------------------------------------
 template <int CTRL>

@@ -79,16 +79,14 @@ Control control_carve(const LayerArgs& a, void* ws, size_t ws_bytes);
 // token launch writes the per-sequence quantities and the tile records, and
 // clears the per-segment counters and look-back words the tile launch uses.
 struct DecodeWs {
-  int* cnt;        // [S]  arrivals per segment (control block)
+  int* cnt;        // [S]  arrivals per segment (control block; unused by decode)
   int* segtk;      // [S]  tile tickets per segment
   int* ntiles;     // [1]  tiles of the step
-  int4* map;       // [max_tiles, 2]  per tile: {segment, unused, length, tiles of the segment},
+  int4* map;       // [max_tiles, 2]  per tile: {segment, tile of the segment, length, tiles of the segment},
                    //                 {record of the segment's first tile, offset low, offset high, 0}
   float* tq;       // [B, H_q, d]  rotated queries
   float* tkey;     // [B * H_kv, d]  stored new keys (rounded like the cache)
-  float* gam;      // [B, H_q * d]  output gate
-  float* tokf;     // [B * H_kv, 2]  query/similarity part of the pair term (log2 units / terms), new key gate
-  float* es;       // [B, H_q]  the token's logit against its own key (log2 units)
+  float* zdec;     // [B, 4, 3 * H_kv + r]  x [W_dec | W_dn] over four slices of the rows (summed by the readers)
   float* part_o;   // [max_tiles, G, d]   partials of segments held by several tiles
   float* part_ml;  // [max_tiles, G, 2]   max (log2 units), sum
   int max_tiles;
