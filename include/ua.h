@@ -215,6 +215,28 @@ ua_status ua_decode_compact_step(const ua_dims* dims, const ua_params* params, c
                                  const ua_tokens* in, float log_p, void* y, int32_t* kept_idx, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* Size of the library's own decode workspace (16 MiB per GPU). */
+#define UA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as ua_decode_compact_step, with the same arguments, results and status
+ * words, but its workspace is a UA_NOALLOC_SCRATCH_BYTES array inside the
+ * library, one per GPU, held from the first call on that GPU until the process
+ * ends.  The call allocates and frees nothing.  Steps whose workspace
+ * (ua_workspace_bytes with max_tokens_per_call = 1 bounds it from above) would
+ * exceed the array return UA_ERR_WORKSPACE before anything is launched; the
+ * decode step fits for caches of about two million slots at d_head = 64.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (several streams or host threads) race and must be serialised by the caller.
+ * The first call on a GPU looks up the array's address (a host-side query,
+ * made once, under a lock).
+ */
+ua_status ua_decode_compact_step_noalloc(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                                         const ua_tokens* in, float log_p, void* y, int32_t* kept_idx,
+                                         void* stream);
+
 /*
  * Chunked prefill: appends n_tokens tokens to every sequence and writes their
  * outputs y [B, n_tokens, H_q, d_head] (paperlayer.ai sections 4.2, 5 and

@@ -20,12 +20,14 @@ UA_OK, UA_ERR_INVALID_ARG, UA_ERR_UNSUPPORTED, UA_ERR_WORKSPACE, UA_ERR_HIP = ra
 UA_F32, UA_BF16 = 0, 1
 UA_TERM_Q, UA_TERM_K, UA_TERM_SIM, UA_TERMS_ALL = 1, 2, 4, 7
 UA_STATUS_SEGMENT_FULL, UA_STATUS_WAIT_TIMEOUT, UA_STATUS_BAD_LENGTH = 1, 2, 4
+UA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = (
     "ua_workspace_bytes",
     "ua_workspace_init",
     "ua_decode_step",
     "ua_decode_compact_step",
+    "ua_decode_compact_step_noalloc",
     "ua_prefill",
     "ua_prefill_pruned",
     "ua_prefill_chunked",
@@ -116,6 +118,9 @@ def load(path: Optional[str] = None) -> C.CDLL:
     lib.ua_decode_compact_step.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_float,
                                            C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_decode_compact_step.restype = C.c_int
+    lib.ua_decode_compact_step_noalloc.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_float,
+                                                   C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.ua_decode_compact_step_noalloc.restype = C.c_int
     lib.ua_prefill.argtypes = [P(ua_dims), P(ua_params), P(ua_cache), P(ua_tokens), C.c_int32, C.c_void_p,
                                C.c_void_p, C.c_size_t, C.c_void_p]
     lib.ua_prefill.restype = C.c_int
@@ -173,6 +178,12 @@ def ua_decode_compact_step(dims, params, cache, tokens, log_p: float, y, kept_id
     _check(load().ua_decode_compact_step(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens),
                                          float(log_p), _ptr(y), _ptr(kept_idx), _ptr(ws), ws_bytes,
                                          _stream(stream)), "ua_decode_compact_step")
+
+
+def ua_decode_compact_step_noalloc(dims, params, cache, tokens, log_p: float, y, kept_idx, stream=None) -> None:
+    _check(load().ua_decode_compact_step_noalloc(C.byref(dims), C.byref(params), C.byref(cache), C.byref(tokens),
+                                                 float(log_p), _ptr(y), _ptr(kept_idx), _stream(stream)),
+           "ua_decode_compact_step_noalloc")
 
 
 def ua_prefill(dims, params, cache, tokens, n_tokens: int, y, ws, ws_bytes: int, stream=None) -> None:

@@ -4,12 +4,40 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/ua.h"
 #include "ua_kernels.hpp"
 
 namespace {
 
 using ua::LayerArgs;
+
+// Workspace of ua_decode_compact_step_noalloc: one copy per GPU, loaded with
+// the code object and held until the process ends.  In host code `scratch`
+// only names the symbol; its device address (different on every GPU) comes
+// from hipGetSymbolAddress and is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[UA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current GPU's copy of `scratch` (looked up once per GPU).
+ua_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return UA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return UA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return UA_ERR_HIP;
+    if (reinterpret_cast<uintptr_t>(p) % 256 != 0) return UA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return UA_OK;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -152,6 +180,18 @@ ua_status ua_decode_compact_step(const ua_dims* dims, const ua_params* params, c
                                  const ua_tokens* in, float log_p, void* y, int32_t* kept_idx, void* ws,
                                  size_t ws_bytes, void* stream) {
   return decode_common(dims, params, cache, in, log_p, y, true, kept_idx, ws, ws_bytes, stream);
+}
+
+// The decode step's first launch clears every counter and look-back word the
+// step uses, so the shared array needs no clearing between calls; a step whose
+// workspace would not fit the array is rejected before anything is launched.
+ua_status ua_decode_compact_step_noalloc(const ua_dims* dims, const ua_params* params, const ua_cache* cache,
+                                         const ua_tokens* in, float log_p, void* y, int32_t* kept_idx,
+                                         void* stream) {
+  void* ws = nullptr;
+  const ua_status s = noalloc_scratch(&ws);
+  if (s != UA_OK) return s;
+  return decode_common(dims, params, cache, in, log_p, y, true, kept_idx, ws, UA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // Shared checks and workspace carving of the prefill entry points.

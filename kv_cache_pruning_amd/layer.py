@@ -128,6 +128,14 @@ class Layer:
                                  self.ws.nbytes, stream)
         return y, ts
 
+    def decode_compact_step_noalloc(self, q, k, v, x, log_p: float, y: torch.Tensor,
+                                    kept: Optional[torch.Tensor] = None, stream=None):
+        """decode_compact_step on the library's own per-GPU workspace: the call
+        allocates nothing, so y (and kept, if wanted) must be given."""
+        ts, tok = self._tokens(q, k, v, x)
+        L.ua_decode_compact_step_noalloc(self.dims, self.w.params, self.cache.struct, tok, log_p, y, kept, stream)
+        return y, ts
+
     def prefill(self, q, k, v, x, y: Optional[torch.Tensor] = None, stream=None):
         s = self.shape
         n = q.shape[1]
