@@ -138,7 +138,7 @@ size_t ua_workspace_bytes(const ua_dims* dims, int32_t max_tokens_per_call, int6
   ua_cache c{};
   c.total_slots = total_slots;
   LayerArgs a = make_args(dims, nullptr, &c, nullptr, nullptr);
-  size_t n = ua::decode_ws_bytes(a, ua::decode_tile_entries(a.d, a.H_q / a.H_kv));
+  size_t n = ua::decode_ws_bytes(a, ua::decode_tile_entries(a.d, a.H_q / a.H_kv, a.bf16 != 0));
   const size_t np = ua::prefill_ws_bytes(a, max_tokens_per_call, max_seg_cap);
   if (np > n) n = np;
   return ua::control_bytes(a) + n + ua::control_tail_bytes(a);
@@ -162,7 +162,7 @@ static ua_status decode_common(const ua_dims* dims, const ua_params* params, con
   if (kept_idx && !aligned(kept_idx, 4)) return UA_ERR_INVALID_ARG;
   if (!ws || !aligned(ws, 256)) return UA_ERR_INVALID_ARG;
   LayerArgs a = make_args(dims, params, cache, in, y);
-  const int twg = ua::decode_tile_entries(a.d, a.H_q / a.H_kv);
+  const int twg = ua::decode_tile_entries(a.d, a.H_q / a.H_kv, a.bf16 != 0);
   const size_t cb = ua::control_bytes(a);
   if (ws_bytes < cb + ua::decode_ws_bytes(a, twg) + ua::control_tail_bytes(a)) return UA_ERR_WORKSPACE;
   const ua::Control ctl = ua::control_carve(a, ws, ws_bytes);

@@ -279,6 +279,18 @@ __device__ __forceinline__ float gemv_finish(const GemvPlan& p, int c, const flo
   return z;
 }
 
+// A rotated query element: fp32, and for bf16 caches also split into a high
+// and a low bf16 part (x = hi + lo up to 2^-17 relative) for the matrix cores.
+template <bool BF16>
+__device__ __forceinline__ void store_query(const DecodeWs& w, int64_t i, float x) {
+  w.tq[i] = x;
+  if constexpr (BF16) {
+    const uint16_t hi = f32_to_bf16(x);
+    w.tqh[i] = hi;
+    w.tql[i] = f32_to_bf16(x - bf16_to_f32(hi));
+  }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs karg) {
   const DecodeKArgs& K = *(const DecodeKArgs*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -406,16 +418,16 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
     if (e < Hq * HALF) {
       const int hq = e / HALF, i = e - hq * HALF;
       const int64_t qi = ((int64_t)b * Hq + hq) * D + i;
-      w.tq[qi] = fmaf(q0v[j], s_cs[i], -q1v[j] * s_sn[i]);
-      w.tq[qi + HALF] = fmaf(q1v[j], s_cs[i], q0v[j] * s_sn[i]);
+      store_query<BF16>(w, qi, fmaf(q0v[j], s_cs[i], -q1v[j] * s_sn[i]));
+      store_query<BF16>(w, qi + HALF, fmaf(q1v[j], s_cs[i], q0v[j] * s_sn[i]));
     }
   }
   for (int e = p * NT + tid + QI * P * NT; e < Hq * HALF; e += P * NT) {  // more than QI blocks
     const int hq = e / HALF, i = e - hq * HALF;
     const int64_t qi = ((int64_t)b * Hq + hq) * D + i;
     const float a0 = load_elem<BF16>(a.q, qi), a1 = load_elem<BF16>(a.q, qi + HALF);
-    w.tq[qi] = fmaf(a0, s_cs[i], -a1 * s_sn[i]);
-    w.tq[qi + HALF] = fmaf(a1, s_cs[i], a0 * s_sn[i]);
+    store_query<BF16>(w, qi, fmaf(a0, s_cs[i], -a1 * s_sn[i]));
+    store_query<BF16>(w, qi + HALF, fmaf(a1, s_cs[i], a0 * s_sn[i]));
   }
   // ---- the stored keys (L2-normalised, rotated, rounded like the cache), one wave per head
   for (int h = h0; h < Hkv; h += P * (NT / 64)) {
@@ -430,8 +442,11 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
       float rr0 = fmaf(n0, s_cs[lane], -n1 * s_sn[lane]);
       float rr1 = fmaf(n1, s_cs[lane], n0 * s_sn[lane]);
       if constexpr (BF16) {
-        rr0 = bf16_to_f32(f32_to_bf16(rr0));
-        rr1 = bf16_to_f32(f32_to_bf16(rr1));
+        const uint16_t h0 = f32_to_bf16(rr0), h1 = f32_to_bf16(rr1);
+        w.tkb[(int64_t)s * D + lane] = h0;
+        w.tkb[(int64_t)s * D + lane + HALF] = h1;
+        rr0 = bf16_to_f32(h0);
+        rr1 = bf16_to_f32(h1);
       }
       w.tkey[(int64_t)s * D + lane] = rr0;
       w.tkey[(int64_t)s * D + lane + HALF] = rr1;
@@ -460,6 +475,298 @@ __device__ __forceinline__ float token_gate(const LayerArgs& a, const DecodeWs& 
 constexpr int kWaitAll = 0;
 constexpr int kWaitLgkm = 0xC07F;  // vmcnt 63, expcnt 7, lgkmcnt 0
 
+// A tile's record and what follows from it.
+struct TileInfo {
+  int seg, len, ntile, pbase, kt, b, h;
+  int64_t off;
+  bool single;
+};
+
+__device__ __forceinline__ TileInfo tile_info(const int4& m0, const int4& m1, int Hkv) {
+  TileInfo t;
+  t.seg = m0.x;
+  t.kt = m0.y;
+  t.len = m0.z;
+  t.ntile = m0.w;
+  t.pbase = m1.x;  // record number of the segment's first tile
+  t.off = (int64_t)(uint32_t)m1.y | ((int64_t)m1.z << 32);
+  t.single = t.ntile == 1;
+  t.b = t.seg / Hkv;
+  t.h = t.seg - t.b * Hkv;
+  return t;
+}
+
+// LDS of the part both tile kernels share.
+template <int D, int G>
+struct TailLds {
+  float pm[kTileWaves * G], pl[kTileWaves * G];  // wave partials: max (log2 units), sum
+  float po[kTileWaves * G * D];                  // wave partials: weighted V
+  float es[G];                                   // the token's own logits (log2 units)
+  float u[kMaxRank];                             // u = x W_dn
+  int cnt[kTileWaves];                           // live entries per wave
+  int kt, pre, flag;
+};
+
+template <int D, int G>
+constexpr int tail_opt() {  // outputs (g, i) per thread
+  return (G * D + kTileThreads - 1) / kTileThreads;
+}
+
+// After the wave partials and live counts are in LDS: the tile's partial per
+// output (g, i) in registers; for a segment of several tiles the live count
+// (COMPACT; the first tile's is its inclusive prefix) and the partial are
+// published, and the tile that arrives last is marked as the one that merges
+// them (L.flag); with COMPACT, the look-back over the earlier tiles of the
+// segment gives the survivors' destination (L.pre).  Ends with a barrier.
+template <int D, int G, bool COMPACT>
+__device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInfo& t, TailLds<D, G>& L, int count,
+                                             float* Mo, float* Lo, float* Oo) {
+  constexpr int NT = kTileThreads, OPT = tail_opt<D, G>();
+  const DecodeWs& w = K.w;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+#pragma unroll
+  for (int u = 0; u < OPT; ++u) {
+    const int idx = min(u * NT + tid, G * D - 1);
+    const int g = idx / D;
+    const int i = idx - g * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w2 = 0; w2 < kTileWaves; ++w2) M = fmaxf(M, L.pm[w2 * G + g]);
+    const float Ms = (M == kNegInf) ? 0.0f : M;
+    float Ls = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w2 = 0; w2 < kTileWaves; ++w2) {
+      const float wgt = __builtin_amdgcn_exp2f(L.pm[w2 * G + g] - Ms);
+      Ls = fmaf(L.pl[w2 * G + g], wgt, Ls);
+      O = fmaf(L.po[(w2 * G + g) * D + i], wgt, O);
+    }
+    Mo[u] = M;
+    Lo[u] = Ls;
+    Oo[u] = O;
+  }
+  if (!t.single) {
+    const int64_t prow = (int64_t)(t.pbase + t.kt);
+    if (COMPACT && tid == 0)
+      st64_coh(&K.ctl.dec_state[prow], (unsigned long long)((count << 2) | (t.kt == 0 ? 2 : 1)));
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = u * NT + tid;
+      if (idx < G * D) {
+        const int g = idx / D;
+        const int i = idx - g * D;
+        st_coh(w.part_o + (prow * G + g) * D + i, Oo[u]);
+        if (i == 0) {
+          st_coh(w.part_ml + (prow * G + g) * 2 + 0, Mo[u]);
+          st_coh(w.part_ml + (prow * G + g) * 2 + 1, Lo[u]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __syncthreads();
+    if (tid == 0) L.flag = (add_coh(&w.cnt[t.seg], 1) == t.ntile - 1);
+  }
+  if (!COMPACT || t.single || t.kt == 0) {
+    if (tid == 0) L.pre = 0;
+  } else if (wv == 0) {
+    const unsigned long long* st = K.ctl.dec_state + t.pbase;
+    int prefix = 0;
+    int cpos = t.kt - 1;  // next predecessor to examine
+    int spins = 0;
+    while (true) {
+      const int pc2 = cpos - lane;  // lane l reads predecessor cpos - l
+      const unsigned long long sv = (pc2 >= 0) ? ld64_coh(&st[pc2]) : 0ull;
+      const int flag = (pc2 < 0) ? 2 : (int)(sv & 3u);  // tile -1 acts as prefix 0
+      const int val = (pc2 < 0) ? 0 : (int)((uint32_t)sv >> 2);
+      const uint64_t inc = __ballot(flag == 2);
+      const uint64_t none = __ballot(flag == 0);
+      const int stop = inc ? (int)__builtin_ctzll(inc) : 64;
+      const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1);
+      if ((none & need) == 0) {
+        prefix += wave_isum((lane <= stop) ? val : 0);
+        if (stop < 64) break;
+        cpos -= 64;
+        continue;
+      }
+      if (++spins > kSpinLimitDec) {
+        if (lane == 0) atomicOr(K.a.status, 2);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (lane == 0) {
+      st64_coh(&K.ctl.dec_state[t.pbase + t.kt], (unsigned long long)(((prefix + count) << 2) | 2));
+      L.pre = prefix;
+    }
+  }
+  __syncthreads();
+}
+
+// The segment's output (by the tile that merges: every tile's partial, this
+// one's in registers when it is the only one, the token's own term, the
+// output gate), then the new entry and the new length (by the segment's last
+// tile when compacting, else by the merging tile).  ml: LDS scratch of mlc
+// tiles' (max, sum) per head, free by now.
+template <int D, int G, bool BF16, bool COMPACT>
+__device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo& t, TailLds<D, G>& L, float* ml,
+                                            int mlc, bool combines, int npos, float* Mo, float* Lo, float* Oo) {
+  constexpr int NT = kTileThreads, OPT = tail_opt<D, G>();
+  constexpr int EB = BF16 ? 2 : 4;
+  const LayerArgs& a = K.a;
+  const DecodeWs& w = K.w;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int Hkv = a.H_kv, Hq = a.H_q;
+  const int seg = t.seg, b = t.b, h = t.h;
+  if (combines) {
+    // what the merge needs of the token: its value, u = x W_dn (the partials
+    // added, into LDS), this thread's columns of W_up, and its logit against
+    // its own key per head (wave 0, from the fp32 rotated query and key)
+    constexpr int kUp = 16;
+    constexpr int UPF = OPT <= 2 ? OPT : 0;  // outputs whose W_up column is loaded together
+    float vnv[OPT], wup[UPF > 0 ? UPF : 1][kUp];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = min(u * NT + tid, G * D - 1);
+      vnv[u] = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + idx % D) * EB));
+      if (u < UPF) {
+#pragma unroll
+        for (int q = 0; q < kUp; ++q)
+          wup[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, a.r - 1) * Hq * D + (h * G) * D + idx);
+      }
+    }
+    if (tid < a.r) L.u[tid] = token_z(a, w, b, 3 * Hkv + tid);
+    if (wv == 0) {
+      const float qs2 = a.scale * kLog2e;
+      const float* kt = w.tkey + (int64_t)seg * D;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float* qt = w.tq + ((int64_t)b * Hq + h * G + g) * D;
+        float e = 0.0f;
+#pragma unroll
+        for (int i = lane; i < D; i += 64) e = fmaf(qt[i], kt[i], e);
+        e = wave_sum(e);
+        if (lane == 0) L.es[g] = e * qs2;
+      }
+    }
+    if (!t.single) {
+      // every tile's (max, sum) per head through LDS, then the weighted V in
+      // passes of TC tiles
+      constexpr int TC = 16;  // tiles per pass, loads in flight together
+      float M[OPT], Ls[OPT], O[OPT];
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) {
+        M[u] = kNegInf;
+        Ls[u] = 0.0f;
+        O[u] = 0.0f;
+      }
+      for (int t0 = 0; t0 < t.ntile; t0 += mlc) {
+        const int tn = min(mlc, t.ntile - t0);
+        __syncthreads();
+        for (int j = tid; j < tn * G * 2; j += NT) ml[j] = ld_coh(w.part_ml + (int64_t)(t.pbase + t0) * G * 2 + j);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < OPT; ++u) {
+          const int idx = min(u * NT + tid, G * D - 1);
+          const int g = idx / D;
+          const int i = idx - g * D;
+          float Mn = M[u];
+          for (int q = 0; q < tn; ++q) Mn = fmaxf(Mn, ml[(q * G + g) * 2]);
+          const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
+          const float rs = __builtin_amdgcn_exp2f(M[u] - Ms);
+          Ls[u] *= rs;
+          O[u] *= rs;
+          for (int p0 = 0; p0 < tn; p0 += TC) {
+            float po[TC];
+#pragma unroll
+            for (int p = 0; p < TC; ++p)
+              po[p] = ld_coh(w.part_o + ((int64_t)(t.pbase + t0 + min(p0 + p, tn - 1)) * G + g) * D + i);
+#pragma unroll
+            for (int p = 0; p < TC; ++p) {
+              if (p0 + p < tn) {
+                const float wgt = __builtin_amdgcn_exp2f(ml[((p0 + p) * G + g) * 2] - Ms);
+                Ls[u] = fmaf(ml[((p0 + p) * G + g) * 2 + 1], wgt, Ls[u]);
+                O[u] = fmaf(po[p], wgt, O[u]);
+              }
+            }
+          }
+          M[u] = Mn;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) {
+        Mo[u] = M[u];
+        Lo[u] = Ls[u];
+        Oo[u] = O[u];
+      }
+    }
+    __syncthreads();  // u and the token's logits
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = u * NT + tid;
+      if (idx < G * D) {
+        const int g = idx / D;
+        const int col = (h * G) * D + idx;
+        const float es = L.es[g];
+        const float M = fmaxf(Mo[u], es);
+        const float rs = __builtin_amdgcn_exp2f(Mo[u] - M);  // Mo = -inf gives 0
+        const float pe = __builtin_amdgcn_exp2f(es - M);
+        const float Lt = fmaf(Lo[u], rs, pe);
+        const float O = fmaf(Oo[u], rs, pe * vnv[u]);
+        float z = a.b_up ? a.b_up[col] : 0.0f;
+        if (u < UPF) {
+#pragma unroll
+          for (int q = 0; q < kUp; ++q)
+            if (q < a.r) z = fmaf(L.u[q], wup[u < UPF ? u : 0][q], z);
+        } else {
+          for (int q = 0; q < min(a.r, kUp); ++q)
+            z = fmaf(L.u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
+        }
+        for (int q = kUp; q < a.r; ++q) z = fmaf(L.u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
+        const int64_t yo = (int64_t)b * Hq * D + col;
+        const float yv = sigmoid(z) * (O / Lt);
+        if (a.y_bf16) {
+          reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16(yv);
+        } else {
+          reinterpret_cast<float*>(a.y)[yo] = yv;
+        }
+      }
+    }
+  }
+  const bool last = t.kt == t.ntile - 1;
+  if (COMPACT ? last : combines) {
+    const bool room = t.len < a.seg_cap[seg];
+    if (room && tid < D) {
+      const int64_t dst = (t.off + npos) * D + tid;
+      const float kv = w.tkey[(int64_t)seg * D + tid];
+      const float vv = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + tid) * EB));
+      if constexpr (BF16) {
+        reinterpret_cast<uint16_t*>(a.K)[dst] = f32_to_bf16(kv);  // exact: kv is bf16-rounded
+        reinterpret_cast<uint16_t*>(a.V)[dst] = f32_to_bf16(vv);  // exact: a bf16 input
+      } else {
+        reinterpret_cast<float*>(a.K)[dst] = kv;
+        reinterpret_cast<float*>(a.V)[dst] = vv;
+      }
+    }
+    if (tid == 0) {
+      if (room) {
+        a.lam[t.off + npos] = 0.0f;
+        a.lk[t.off + npos] = token_gate(a, w, b, Hkv + h);
+        if (COMPACT && K.kept) K.kept[t.off + npos] = t.len;
+      } else {
+        atomicOr(a.status, 1);
+      }
+      a.seg_len[seg] = room ? npos + 1 : npos;
+      if (h == 0) a.next_pos[b] += 1;  // once per sequence; no tile reads it
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 caches: the dot products on the vector ALUs
+// ---------------------------------------------------------------------------
 // Load the V rows of a wave's entries straight into LDS at dst: for entry
 // slot bb, each lane's 16-byte pieces (a lane reads back exactly what it
 // loaded).
@@ -484,10 +791,9 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArg
   const DecodeWs& w = K.w;
   using Sh = TileShape<D, decode_nb(D, G)>;
   constexpr int LPE = Sh::LPE, NGW = Sh::NGW, NB = Sh::NB, TW = Sh::TW, TWG = Sh::TWG;
-  constexpr int NT = kTileThreads;
-  constexpr int OPT = (G * D + NT - 1) / NT;  // outputs (g, i) per thread
-  constexpr int EB = BF16 ? 2 : 4;            // bytes per element
-  constexpr int RP = BF16 ? 1 : 2;            // 16-byte pieces of a lane's 8 elements
+  constexpr int OPT = tail_opt<D, G>();
+  constexpr int EB = BF16 ? 2 : 4;  // bytes per element
+  constexpr int RP = BF16 ? 1 : 2;  // 16-byte pieces of a lane's 8 elements
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -496,15 +802,8 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArg
   const int Hkv = a.H_kv;
   const int Hq = a.H_q;
 
-  __shared__ int s_pre;
-  __shared__ int s_cnt[kTileWaves];
-  __shared__ float s_tp[kTileWaves][NGW * D];                   // per-wave transpose of the weighted V
-  __shared__ float s_po[kTileWaves * G * D];                    // wave partials: weighted V
-  __shared__ float s_pm[kTileWaves * G], s_pl[kTileWaves * G];  // wave partials: max (log2), sum
-  __shared__ float s_es[G];                                     // the token's own logits (log2 units)
-  __shared__ float s_u[kMaxRank];                               // u = x W_dn
-  __shared__ int s_kt;
-  __shared__ int s_flag;
+  __shared__ TailLds<D, G> L;
+  __shared__ float s_tp[kTileWaves][NGW * D];     // per-wave transpose of the weighted V
   __shared__ u32x4 s_v[kTileWaves][NB * RP][64];  // the wave's V rows (loaded straight into LDS)
 
   // One workgroup per tile.  The tile number within its segment comes from a
@@ -516,461 +815,544 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArg
   const int4 m0 = w.map[2 * tile + 0];  // read with the tile count (a record past it is never used)
   const int4 m1 = w.map[2 * tile + 1];
   if (tile >= *w.ntiles) return;
+  TileInfo t = tile_info(m0, m1, Hkv);
+  const int len = t.len;
+  const int b = t.b, h = t.h, seg = t.seg;
+  char* const Kseg = reinterpret_cast<char*>(a.K) + t.off * (D * EB);
+  char* const Vseg = reinterpret_cast<char*>(a.V) + t.off * (D * EB);
+  const char* const lamseg = reinterpret_cast<const char*>(a.lam + t.off);
+  const char* const lkseg = reinterpret_cast<const char*>(a.lk + t.off);
+  const int relmax = max(len - 1, 0);
+  if (!t.single && tid == 0) L.kt = add_coh(&w.segtk[seg], 1);
+
+  // ---- cached entries: every load issued first, from the segment's base
+  // with 32-bit offsets; slots past the end read the last entry (masked below)
+  Row8<BF16> kr[NB];
+  float lamv[NB], lkv[NB];
+  auto load_rows = [&](int k) {
+    const int f0 = k * TWG + wv * TW + grp * NB;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int rel = min(f0 + bb, relmax);
+      const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+      row_load_at<BF16>(kr[bb], Kseg, ro);
+      lamv[bb] = ld_at<float>(lamseg, (uint32_t)rel * 4);
+      lkv[bb] = ld_at<float>(lkseg, (uint32_t)rel * 4);
+    }
+  };
+  load_rows(t.kt);
+  // ---- the token: rotated queries of the group and the stored key (8 dims
+  // per lane), the query/similarity part of the pair term
+  float qv[G][8], ktv[8];
   {
-    const int seg = m0.x;
-    const int len = m0.z;
-    const int ntile = m0.w;
-    const int pbase = m1.x;  // record number of the segment's first tile
-    const int64_t off = (int64_t)(uint32_t)m1.y | ((int64_t)m1.z << 32);
-    const bool single = ntile == 1;
-    const int b = seg / Hkv;
-    const int h = seg - b * Hkv;
-    char* const Kseg = reinterpret_cast<char*>(a.K) + off * (D * EB);
-    char* const Vseg = reinterpret_cast<char*>(a.V) + off * (D * EB);
-    const char* const lamseg = reinterpret_cast<const char*>(a.lam + off);
-    const char* const lkseg = reinterpret_cast<const char*>(a.lk + off);
-    const int relmax = max(len - 1, 0);
-    int kt = m0.y;
-    if (!single && tid == 0) s_kt = add_coh(&w.segtk[seg], 1);
-
-    // ---- cached entries: every load issued first, from the segment's base
-    // with 32-bit offsets; slots past the end read the last entry (masked below)
-    Row8<BF16> kr[NB];
-    float lamv[NB], lkv[NB];
-    auto load_rows = [&](int k) {
-      const int f0 = k * TWG + wv * TW + grp * NB;
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        const int rel = min(f0 + bb, relmax);
-        const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
-        row_load_at<BF16>(kr[bb], Kseg, ro);
-        lamv[bb] = ld_at<float>(lamseg, (uint32_t)rel * 4);
-        lkv[bb] = ld_at<float>(lkseg, (uint32_t)rel * 4);
-      }
-    };
-    load_rows(kt);
-    // ---- the token: rotated queries of the group and the stored key (8 dims
-    // per lane), the query/similarity part of the pair term
-    float qv[G][8], ktv[8];
-    {
-      const float* qrow = w.tq + ((int64_t)b * Hq + h * G) * D + 8 * c;
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float4 x0 = *reinterpret_cast<const float4*>(qrow + g * D);
-        const float4 x1 = *reinterpret_cast<const float4*>(qrow + g * D + 4);
-        qv[g][0] = x0.x; qv[g][1] = x0.y; qv[g][2] = x0.z; qv[g][3] = x0.w;
-        qv[g][4] = x1.x; qv[g][5] = x1.y; qv[g][6] = x1.z; qv[g][7] = x1.w;
-      }
-      const float* krow = w.tkey + (int64_t)seg * D + 8 * c;
-      const float4 x0 = *reinterpret_cast<const float4*>(krow);
-      const float4 x1 = *reinterpret_cast<const float4*>(krow + 4);
-      ktv[0] = x0.x; ktv[1] = x0.y; ktv[2] = x0.z; ktv[3] = x0.w;
-      ktv[4] = x1.x; ktv[5] = x1.y; ktv[6] = x1.z; ktv[7] = x1.w;
-    }
-    const PairCoef pc = pair_coef(a.terms);
-    const float lq = (a.terms & 1) ? token_gate(a, w, b, h) : 0.0f;
-    const float lbt = (a.terms & 4) ? token_gate(a, w, b, 2 * Hkv + h) : 0.0f;
-    const float row2 = (lq + lbt) * pc.inv_n2;
-    if (!single) {
-      __syncthreads();
-      if (s_kt != kt) {  // started out of order: this workgroup takes the ticket's tile
-        kt = s_kt;
-        load_rows(kt);
-      }
-    }
-    const int e0 = kt * TWG + wv * TW + grp * NB;
-    // the V rows, needed after the logits: straight into LDS, no registers held
-    stage_v<D, NB, BF16>(Vseg, e0, relmax, c, &s_v[wv][0][0]);
-
-    const float tau = K.tau;
-    const float qs2 = a.scale * kLog2e;
-    const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
-    // the token's logit against its own key, per head (log2 units)
-    if (wv == 0) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float e = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e = fmaf(qv[g][i], ktv[i], e);
-        e = group_sum<LPE>(e);
-        if (lane == 0) s_es[g] = e * qs2;
-      }
-    }
-
-    // ---- dot products, pair term, bias update, logits
-    float e2[G][NB];
-    float newlam[NB];
-    bool live[NB], changed[NB];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const bool valid = e0 + bb < len;
-      row_zero_if<BF16>(kr[bb], !valid);  // slots past the end may hold anything
-      float kf[8];
-      row_f32<BF16>(kr[bb], kf);
-      float ps = 0.0f;
-      float pq[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) pq[g] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ps = fmaf(ktv[i], kf[i], ps);
-#pragma unroll
-        for (int g = 0; g < G; ++g) pq[g] = fmaf(qv[g][i], kf[i], pq[g]);
-      }
-      ps = group_sum<LPE>(ps);
-#pragma unroll
-      for (int g = 0; g < G; ++g) pq[g] = group_sum<LPE>(pq[g]);
-      const float l0 = valid ? lamv[bb] : kNegInf;
-      const bool alive = valid && (l0 >= tau);
-      const float A = pair_A(pc, row2, lkv[bb] * kscale, ps);
-      const float l1 = alive ? l0 + A : l0;
-      live[bb] = alive && (l1 >= tau);
-      newlam[bb] = l1;
-      changed[bb] = alive;
-      const float lb2 = l1 * kLog2e;
-#pragma unroll
-      for (int g = 0; g < G; ++g) e2[g][bb] = live[bb] ? fmaf(pq[g], qs2, lb2) : kNegInf;
-    }
-
-    // ---- this tile's live entries (compaction): lane grp * LPE + bb owns
-    // entry bb of its group; entries in tile order are (wave, group, entry)
-    uint64_t mask = 0;
-    if constexpr (COMPACT) {
-      bool mine_live = false;
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) mine_live = (c == bb) ? live[bb] : mine_live;
-      mask = __ballot(c < NB && mine_live);
-      if (lane == 0) s_cnt[wv] = __popcll(mask);
-    }
-
-    // ---- wave partial per head: max over the wave first, then sums relative to it
-    float ms[G], lw[G], o8[G][8];
+    const float* qrow = w.tq + ((int64_t)b * Hq + h * G) * D + 8 * c;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float m = e2[g][0];
-#pragma unroll
-      for (int bb = 1; bb < NB; ++bb) m = fmaxf(m, e2[g][bb]);
-      ms[g] = across_groups_max<LPE>(m);
-      lw[g] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o8[g][i] = 0.0f;
+      const float4 x0 = *reinterpret_cast<const float4*>(qrow + g * D);
+      const float4 x1 = *reinterpret_cast<const float4*>(qrow + g * D + 4);
+      qv[g][0] = x0.x; qv[g][1] = x0.y; qv[g][2] = x0.z; qv[g][3] = x0.w;
+      qv[g][4] = x1.x; qv[g][5] = x1.y; qv[g][6] = x1.z; qv[g][7] = x1.w;
     }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);  // the V rows are in LDS
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      float vf[8];
-      Row8<BF16> vrow;
-#pragma unroll
-      for (int pp = 0; pp < RP; ++pp) vrow.w[pp] = s_v[wv][bb * RP + pp][lane];
-      row_zero_if<BF16>(vrow, e0 + bb >= len);  // slots past the end may hold anything
-      row_f32<BF16>(vrow, vf);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = __builtin_amdgcn_exp2f(e2[g][bb] - ((ms[g] == kNegInf) ? 0.0f : ms[g]));
-        lw[g] += p;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o8[g][i] = fmaf(p, vf[i], o8[g][i]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float l = across_groups_sum<LPE>(lw[g]);
-      // the groups' weighted V summed through a per-wave LDS transpose: each
-      // lane writes its 8 sums, then lane j adds dimension j (and j + 64) over
-      // the groups.  LDS operations of one wave complete in order.
-      float* tp = s_tp[wv];  // [group][D]
-      {
-        float4* dst = reinterpret_cast<float4*>(tp + grp * D + 8 * c);
-        dst[0] = make_float4(o8[g][0], o8[g][1], o8[g][2], o8[g][3]);
-        dst[1] = make_float4(o8[g][4], o8[g][5], o8[g][6], o8[g][7]);
-      }
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int half = 0; half < D / 64; ++half) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int q = 0; q < NGW; ++q) sum += tp[q * D + half * 64 + lane];
-        s_po[(wv * G + g) * D + half * 64 + lane] = sum;
-      }
-      __builtin_amdgcn_wave_barrier();  // the next head reuses the scratch
-      if (lane == 0) {
-        s_pm[wv * G + g] = ms[g];
-        s_pl[wv * G + g] = l;
-      }
-    }
-    __syncthreads();  // partials and live counts in LDS
-
-    int count = 0, wbase = 0;
-    if constexpr (COMPACT) {
-#pragma unroll
-      for (int w2 = 0; w2 < kTileWaves; ++w2) {
-        wbase += (w2 < wv) ? s_cnt[w2] : 0;
-        count += s_cnt[w2];
-      }
-    } else {
-      if (c < NB) {  // lane c of a group stores entry c's bias
-        float val = newlam[0];
-        bool ch = changed[0];
-#pragma unroll
-        for (int bb = 1; bb < NB; ++bb) {
-          val = (c == bb) ? newlam[bb] : val;
-          ch = (c == bb) ? changed[bb] : ch;
-        }
-        if (ch) a.lam[off + e0 + c] = val;
-      }
-    }
-
-    // ---- the tile's partial per output (g, i): merge of the wave partials
-    float Mo[OPT], Lo[OPT], Oo[OPT];
-#pragma unroll
-    for (int u = 0; u < OPT; ++u) {
-      const int idx = min(u * NT + tid, G * D - 1);
-      const int g = idx / D;
-      const int i = idx - g * D;
-      float M = kNegInf;
-#pragma unroll
-      for (int w2 = 0; w2 < kTileWaves; ++w2) M = fmaxf(M, s_pm[w2 * G + g]);
-      const float Ms = (M == kNegInf) ? 0.0f : M;
-      float L = 0.0f, O = 0.0f;
-#pragma unroll
-      for (int w2 = 0; w2 < kTileWaves; ++w2) {
-        const float wgt = __builtin_amdgcn_exp2f(s_pm[w2 * G + g] - Ms);
-        L = fmaf(s_pl[w2 * G + g], wgt, L);
-        O = fmaf(s_po[(w2 * G + g) * D + i], wgt, O);
-      }
-      Mo[u] = M;
-      Lo[u] = L;
-      Oo[u] = O;
-    }
-
-    // ---- a segment of several tiles: the live count first (successors' look-back
-    // needs only counts; the first tile's is its inclusive prefix), then the
-    // partial; the last tile of the segment to arrive merges the partials
-    bool combines = single;
-    if (!single) {
-      const int64_t prow = (int64_t)(pbase + kt);
-      if (COMPACT && tid == 0)
-        st64_coh(&K.ctl.dec_state[prow], (unsigned long long)((count << 2) | (kt == 0 ? 2 : 1)));
-#pragma unroll
-      for (int u = 0; u < OPT; ++u) {
-        const int idx = u * NT + tid;
-        if (idx < G * D) {
-          const int g = idx / D;
-          const int i = idx - g * D;
-          st_coh(w.part_o + (prow * G + g) * D + i, Oo[u]);
-          if (i == 0) {
-            st_coh(w.part_ml + (prow * G + g) * 2 + 0, Mo[u]);
-            st_coh(w.part_ml + (prow * G + g) * 2 + 1, Lo[u]);
-          }
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      __syncthreads();
-      if (tid == 0) s_flag = (add_coh(&w.cnt[seg], 1) == ntile - 1);
-    }
-    // ---- look back over the earlier tiles of the segment: the survivors' destination
-    if (!COMPACT || single || kt == 0) {
-      if (tid == 0) s_pre = 0;
-    } else if (wv == 0) {
-      const unsigned long long* st = K.ctl.dec_state + pbase;
-      int prefix = 0;
-      int cpos = kt - 1;  // next predecessor to examine
-      int spins = 0;
-      while (true) {
-        const int pc2 = cpos - lane;  // lane l reads predecessor cpos - l
-        const unsigned long long sv = (pc2 >= 0) ? ld64_coh(&st[pc2]) : 0ull;
-        const int flag = (pc2 < 0) ? 2 : (int)(sv & 3u);  // tile -1 acts as prefix 0
-        const int val = (pc2 < 0) ? 0 : (int)((uint32_t)sv >> 2);
-        const uint64_t inc = __ballot(flag == 2);
-        const uint64_t none = __ballot(flag == 0);
-        const int stop = inc ? (int)__builtin_ctzll(inc) : 64;
-        const uint64_t need = (stop >= 63) ? ~0ull : ((2ull << stop) - 1);
-        if ((none & need) == 0) {
-          prefix += wave_isum((lane <= stop) ? val : 0);
-          if (stop < 64) break;
-          cpos -= 64;
-          continue;
-        }
-        if (++spins > kSpinLimitDec) {
-          if (lane == 0) atomicOr(a.status, 2);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      if (lane == 0) {
-        st64_coh(&K.ctl.dec_state[pbase + kt], (unsigned long long)(((prefix + count) << 2) | 2));
-        s_pre = prefix;
-      }
-    }
+    const float* krow = w.tkey + (int64_t)seg * D + 8 * c;
+    const float4 x0 = *reinterpret_cast<const float4*>(krow);
+    const float4 x1 = *reinterpret_cast<const float4*>(krow + 4);
+    ktv[0] = x0.x; ktv[1] = x0.y; ktv[2] = x0.z; ktv[3] = x0.w;
+    ktv[4] = x1.x; ktv[5] = x1.y; ktv[6] = x1.z; ktv[7] = x1.w;
+  }
+  const PairCoef pc = pair_coef(a.terms);
+  const float lq = (a.terms & 1) ? token_gate(a, w, b, h) : 0.0f;
+  const float lbt = (a.terms & 4) ? token_gate(a, w, b, 2 * Hkv + h) : 0.0f;
+  const float row2 = (lq + lbt) * pc.inv_n2;
+  if (!t.single) {
     __syncthreads();
-    if (!single) combines = s_flag;
-    const bool last = kt == ntile - 1;
-
-    int npos = len;  // where the new entry goes
-    if constexpr (COMPACT) {
-      // ---- the survivors, in order; rows already in place are not rewritten
-      const int P = s_pre;
-      int32_t* const kept = K.kept;
-      const int myrank =
-          wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-#pragma unroll
-      for (int bb = 0; bb < NB; ++bb) {
-        const int rk = __shfl(myrank, grp * LPE + bb, 64);
-        if (live[bb]) {
-          const int rel = P + rk;
-          const int64_t dst = off + rel;
-          const bool moves = rel != e0 + bb;
-          if (moves) {
-            const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
-            row_store_at<BF16>(kr[bb], Kseg, ro);
-            Row8<BF16> vrow;
-#pragma unroll
-            for (int pp = 0; pp < RP; ++pp) vrow.w[pp] = s_v[wv][bb * RP + pp][lane];
-            row_store_at<BF16>(vrow, Vseg, ro);
-          }
-          if (c == bb) {
-            a.lam[dst] = newlam[bb];
-            if (moves) a.lk[dst] = lkv[bb];
-            if (kept) kept[dst] = e0 + bb;
-          }
-        }
-      }
-      npos = P + count;
-    }
-
-    if (combines) {
-      // ---- the segment's output: every tile's partial (this one's in
-      // registers when it is the only one), the token's own term, the gate
-      // what the combine needs of the token: its value, u = x W_dn (the P
-      // partials added, into LDS) and this thread's columns of W_up
-      constexpr int kUp = 16;
-      constexpr int UPF = OPT <= 2 ? OPT : 0;  // outputs whose W_up column is loaded together
-      float vnv[OPT], wup[UPF > 0 ? UPF : 1][kUp];
-#pragma unroll
-      for (int u = 0; u < OPT; ++u) {
-        const int idx = min(u * NT + tid, G * D - 1);
-        vnv[u] = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + idx % D) * EB));
-        if (u < UPF) {
-#pragma unroll
-          for (int q = 0; q < kUp; ++q)
-            wup[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, a.r - 1) * Hq * D + (h * G) * D + idx);
-        }
-      }
-      if (tid < a.r) s_u[tid] = token_z(a, w, b, 3 * Hkv + tid);
-      if (!single) {
-        // every tile's (max, sum) per head through LDS (the per-wave transpose
-        // scratch, free here), then the weighted V in passes of TC tiles
-        float* s_ml = &s_tp[0][0];
-        constexpr int MLC = (kTileWaves * NGW * D) / (2 * G);  // tiles per LDS chunk
-        constexpr int TC = 16;                                // tiles per pass, loads in flight together
-        float M[OPT], L[OPT], O[OPT];
-#pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-          M[u] = kNegInf;
-          L[u] = 0.0f;
-          O[u] = 0.0f;
-        }
-        for (int t0 = 0; t0 < ntile; t0 += MLC) {
-          const int tn = min(MLC, ntile - t0);
-          __syncthreads();
-          for (int j = tid; j < tn * G * 2; j += NT) s_ml[j] = ld_coh(w.part_ml + (int64_t)(pbase + t0) * G * 2 + j);
-          __syncthreads();
-#pragma unroll
-          for (int u = 0; u < OPT; ++u) {
-            const int idx = min(u * NT + tid, G * D - 1);
-            const int g = idx / D;
-            const int i = idx - g * D;
-            float Mn = M[u];
-            for (int t = 0; t < tn; ++t) Mn = fmaxf(Mn, s_ml[(t * G + g) * 2]);
-            const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
-            const float rs = __builtin_amdgcn_exp2f(M[u] - Ms);
-            L[u] *= rs;
-            O[u] *= rs;
-            for (int p0 = 0; p0 < tn; p0 += TC) {
-              float po[TC];
-#pragma unroll
-              for (int p = 0; p < TC; ++p)
-                po[p] = ld_coh(w.part_o + ((int64_t)(pbase + t0 + min(p0 + p, tn - 1)) * G + g) * D + i);
-#pragma unroll
-              for (int p = 0; p < TC; ++p) {
-                if (p0 + p < tn) {
-                  const float wgt = __builtin_amdgcn_exp2f(s_ml[((p0 + p) * G + g) * 2] - Ms);
-                  L[u] = fmaf(s_ml[((p0 + p) * G + g) * 2 + 1], wgt, L[u]);
-                  O[u] = fmaf(po[p], wgt, O[u]);
-                }
-              }
-            }
-            M[u] = Mn;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-          Mo[u] = M[u];
-          Lo[u] = L[u];
-          Oo[u] = O[u];
-        }
-      }
-      __syncthreads();  // s_u
-#pragma unroll
-      for (int u = 0; u < OPT; ++u) {
-        const int idx = u * NT + tid;
-        if (idx < G * D) {
-          const int g = idx / D;
-          const int col = (h * G) * D + idx;
-          const float es = s_es[g];
-          const float M = fmaxf(Mo[u], es);
-          const float rs = __builtin_amdgcn_exp2f(Mo[u] - M);  // Mo = -inf gives 0
-          const float pe = __builtin_amdgcn_exp2f(es - M);
-          const float L = fmaf(Lo[u], rs, pe);
-          const float O = fmaf(Oo[u], rs, pe * vnv[u]);
-          float z = a.b_up ? a.b_up[col] : 0.0f;
-          if (u < UPF) {
-#pragma unroll
-            for (int q = 0; q < kUp; ++q)
-              if (q < a.r) z = fmaf(s_u[q], wup[u < UPF ? u : 0][q], z);
-          } else {
-            for (int q = 0; q < min(a.r, kUp); ++q)
-              z = fmaf(s_u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
-          }
-          for (int q = kUp; q < a.r; ++q) z = fmaf(s_u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
-          const int64_t yo = (int64_t)b * Hq * D + col;
-          const float yv = sigmoid(z) * (O / L);
-          if (a.y_bf16) {
-            reinterpret_cast<uint16_t*>(a.y)[yo] = f32_to_bf16(yv);
-          } else {
-            reinterpret_cast<float*>(a.y)[yo] = yv;
-          }
-        }
-      }
-    }
-    if (COMPACT ? last : combines) {
-      // ---- the new entry (after the survivors when compacting), the new length
-      const bool room = len < a.seg_cap[seg];
-      if (room && tid < D) {
-        const int64_t dst = (off + npos) * D + tid;
-        const float kv = w.tkey[(int64_t)seg * D + tid];
-        const float vv = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + tid) * EB));
-        if constexpr (BF16) {
-          reinterpret_cast<uint16_t*>(a.K)[dst] = f32_to_bf16(kv);  // exact: kv is bf16-rounded
-          reinterpret_cast<uint16_t*>(a.V)[dst] = f32_to_bf16(vv);  // exact: a bf16 input
-        } else {
-          reinterpret_cast<float*>(a.K)[dst] = kv;
-          reinterpret_cast<float*>(a.V)[dst] = vv;
-        }
-      }
-      if (tid == 0) {
-        if (room) {
-          a.lam[off + npos] = 0.0f;
-          a.lk[off + npos] = token_gate(a, w, b, Hkv + h);
-          if (COMPACT && K.kept) K.kept[off + npos] = len;
-        } else {
-          atomicOr(a.status, 1);
-        }
-        a.seg_len[seg] = room ? npos + 1 : npos;
-        if (h == 0) a.next_pos[b] += 1;  // once per sequence; no tile reads it
-      }
+    if (L.kt != t.kt) {  // started out of order: this workgroup takes the ticket's tile
+      t.kt = L.kt;
+      load_rows(t.kt);
     }
   }
+  const int e0 = t.kt * TWG + wv * TW + grp * NB;
+  // the V rows, needed after the logits: straight into LDS, no registers held
+  stage_v<D, NB, BF16>(Vseg, e0, relmax, c, &s_v[wv][0][0]);
+
+  const float tau = K.tau;
+  const float qs2 = a.scale * kLog2e;
+  const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+
+  // ---- dot products, pair term, bias update, logits
+  float e2[G][NB];
+  float newlam[NB];
+  bool live[NB], changed[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    const bool valid = e0 + bb < len;
+    row_zero_if<BF16>(kr[bb], !valid);  // slots past the end may hold anything
+    float kf[8];
+    row_f32<BF16>(kr[bb], kf);
+    float ps = 0.0f;
+    float pq[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) pq[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ps = fmaf(ktv[i], kf[i], ps);
+#pragma unroll
+      for (int g = 0; g < G; ++g) pq[g] = fmaf(qv[g][i], kf[i], pq[g]);
+    }
+    ps = group_sum<LPE>(ps);
+#pragma unroll
+    for (int g = 0; g < G; ++g) pq[g] = group_sum<LPE>(pq[g]);
+    const float l0 = valid ? lamv[bb] : kNegInf;
+    const bool alive = valid && (l0 >= tau);
+    const float A = pair_A(pc, row2, lkv[bb] * kscale, ps);
+    const float l1 = alive ? l0 + A : l0;
+    live[bb] = alive && (l1 >= tau);
+    newlam[bb] = l1;
+    changed[bb] = alive;
+    const float lb2 = l1 * kLog2e;
+#pragma unroll
+    for (int g = 0; g < G; ++g) e2[g][bb] = live[bb] ? fmaf(pq[g], qs2, lb2) : kNegInf;
+  }
+
+  // ---- this tile's live entries (compaction): lane grp * LPE + bb owns
+  // entry bb of its group; entries in tile order are (wave, group, entry)
+  uint64_t mask = 0;
+  if constexpr (COMPACT) {
+    bool mine_live = false;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) mine_live = (c == bb) ? live[bb] : mine_live;
+    mask = __ballot(c < NB && mine_live);
+    if (lane == 0) L.cnt[wv] = __popcll(mask);
+  }
+
+  // ---- wave partial per head: max over the wave first, then sums relative to it
+  float ms[G], lw[G], o8[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m = e2[g][0];
+#pragma unroll
+    for (int bb = 1; bb < NB; ++bb) m = fmaxf(m, e2[g][bb]);
+    ms[g] = across_groups_max<LPE>(m);
+    lw[g] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o8[g][i] = 0.0f;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);  // the V rows are in LDS
+#pragma unroll
+  for (int bb = 0; bb < NB; ++bb) {
+    float vf[8];
+    Row8<BF16> vrow;
+#pragma unroll
+    for (int pp = 0; pp < RP; ++pp) vrow.w[pp] = s_v[wv][bb * RP + pp][lane];
+    row_zero_if<BF16>(vrow, e0 + bb >= len);  // slots past the end may hold anything
+    row_f32<BF16>(vrow, vf);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float p = __builtin_amdgcn_exp2f(e2[g][bb] - ((ms[g] == kNegInf) ? 0.0f : ms[g]));
+      lw[g] += p;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[g][i] = fmaf(p, vf[i], o8[g][i]);
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float l = across_groups_sum<LPE>(lw[g]);
+    // the groups' weighted V summed through a per-wave LDS transpose: each
+    // lane writes its 8 sums, then lane j adds dimension j (and j + 64) over
+    // the groups.  LDS operations of one wave complete in order.
+    float* tp = s_tp[wv];  // [group][D]
+    {
+      float4* dst = reinterpret_cast<float4*>(tp + grp * D + 8 * c);
+      dst[0] = make_float4(o8[g][0], o8[g][1], o8[g][2], o8[g][3]);
+      dst[1] = make_float4(o8[g][4], o8[g][5], o8[g][6], o8[g][7]);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int half = 0; half < D / 64; ++half) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NGW; ++q) sum += tp[q * D + half * 64 + lane];
+      L.po[(wv * G + g) * D + half * 64 + lane] = sum;
+    }
+    __builtin_amdgcn_wave_barrier();  // the next head reuses the scratch
+    if (lane == 0) {
+      L.pm[wv * G + g] = ms[g];
+      L.pl[wv * G + g] = l;
+    }
+  }
+  __syncthreads();  // partials and live counts in LDS
+
+  int count = 0, wbase = 0;
+  if constexpr (COMPACT) {
+#pragma unroll
+    for (int w2 = 0; w2 < kTileWaves; ++w2) {
+      wbase += (w2 < wv) ? L.cnt[w2] : 0;
+      count += L.cnt[w2];
+    }
+  } else {
+    if (c < NB) {  // lane c of a group stores entry c's bias
+      float val = newlam[0];
+      bool ch = changed[0];
+#pragma unroll
+      for (int bb = 1; bb < NB; ++bb) {
+        val = (c == bb) ? newlam[bb] : val;
+        ch = (c == bb) ? changed[bb] : ch;
+      }
+      if (ch) a.lam[t.off + e0 + c] = val;
+    }
+  }
+
+  float Mo[OPT], Lo[OPT], Oo[OPT];
+  tile_publish<D, G, COMPACT>(K, t, L, count, Mo, Lo, Oo);
+  const bool combines = t.single || L.flag;
+
+  int npos = len;  // where the new entry goes
+  if constexpr (COMPACT) {
+    // ---- the survivors, in order; rows already in place are not rewritten
+    const int P = L.pre;
+    int32_t* const kept = K.kept;
+    const int myrank =
+        wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const int rk = __shfl(myrank, grp * LPE + bb, 64);
+      if (live[bb]) {
+        const int rel = P + rk;
+        const int64_t dst = t.off + rel;
+        const bool moves = rel != e0 + bb;
+        if (moves) {
+          const uint32_t ro = (uint32_t)(rel * D + 8 * c) * EB;
+          row_store_at<BF16>(kr[bb], Kseg, ro);
+          Row8<BF16> vrow;
+#pragma unroll
+          for (int pp = 0; pp < RP; ++pp) vrow.w[pp] = s_v[wv][bb * RP + pp][lane];
+          row_store_at<BF16>(vrow, Vseg, ro);
+        }
+        if (c == bb) {
+          a.lam[dst] = newlam[bb];
+          if (moves) a.lk[dst] = lkv[bb];
+          if (kept) kept[dst] = e0 + bb;
+        }
+      }
+    }
+    npos = P + count;
+  }
+  constexpr int MLC = (kTileWaves * NGW * D) / (2 * G);  // tiles per chunk of the (max, sum) scratch
+  tile_finish<D, G, BF16, COMPACT>(K, t, L, &s_tp[0][0], MLC, combines, npos, Mo, Lo, Oo);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 caches: the dot products on the matrix cores
+// ---------------------------------------------------------------------------
+// A wave takes TW entries (8 KB of keys and 8 KB of values).  The q.k
+// products of 16 entries are one 16 x 16 tile S^T = K [q | k~]^T over the
+// head dimension in 32-wide steps: row e of the tile is entry e, column j <
+// G is query head j of the group (the rotated query as the sum of a high and
+// a low bf16 part, two products into one accumulator, so the logit keeps
+// about 16 bits of the fp32 query), column G is the token's stored key (the
+// similarity).  Lane l holds rows 4 (l >> 4) .. + 3 of column l & 15, which
+// is exactly the A operand layout of P V with P as heads x entries: k index
+// 8 q + i of lane group q is entry 4 q + i of the first 16-entry block (i <
+// 4) and entry 16 + 4 q + i - 4 of the second.  V comes through LDS, where
+// the B operand (8 entries of one dimension per lane) is read as bf16
+// halves.  The bias arithmetic runs once per entry, lane e of the wave
+// holding entry e.
+template <int D>
+struct MfShape {
+  static constexpr int TW = 4096 / D;   // entries per wave: 64 (d = 64) or 32 (d = 128)
+  static constexpr int NBLK = TW / 16;  // 16-entry blocks of the q.k products
+  static constexpr int KS = D / 32;     // 32-dim steps of the q.k products
+  static constexpr int PS = TW / 32;    // 32-entry steps of the P V products
+  static constexpr int NBD = D / 16;    // 16-dim blocks of the output
+  static constexpr int TWG = TW * kTileWaves;
+  static constexpr int RB = 2 * D;             // bytes per row
+  static constexpr int RPI = 1024 / RB;        // V rows per staging load (64 lanes x 16 bytes)
+  static constexpr int NI = TW / RPI;          // staging loads per wave
+  static constexpr int VSTR = 1024 + 2048 / D;  // bytes between staged blocks (padding spreads the
+                                                // B-operand reads over the LDS banks)
+};
+
+template <int D, int G, bool COMPACT>
+__global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeKArgs karg) {
+  const DecodeKArgs& K = *(const DecodeKArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  const LayerArgs& a = K.a;
+  const DecodeWs& w = K.w;
+  using Sh = MfShape<D>;
+  constexpr int TW = Sh::TW, NBLK = Sh::NBLK, KS = Sh::KS, PS = Sh::PS, NBD = Sh::NBD, TWG = Sh::TWG;
+  constexpr int RB = Sh::RB, RPI = Sh::RPI, NI = Sh::NI, VSTR = Sh::VSTR;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  constexpr int OPT = tail_opt<D, G>();
+  static_assert(G < 16, "the similarity column follows the query columns");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gq = lane >> 4, c16 = lane & 15;
+  const int Hkv = a.H_kv;
+  const int Hq = a.H_q;
+
+  __shared__ TailLds<D, G> L;
+  __shared__ __attribute__((aligned(16))) char s_v[kTileWaves][NI * VSTR];  // staged V rows
+  __shared__ __attribute__((aligned(16))) float s_sim[kTileWaves][TW];       // similarity per entry
+  __shared__ __attribute__((aligned(16))) float s_lb[kTileWaves][TW];        // bias (log2 units), -inf if out
+
+  const int tile = blockIdx.x;
+  const int4 m0 = w.map[2 * tile + 0];  // read with the tile count (a record past it is never used)
+  const int4 m1 = w.map[2 * tile + 1];
+  if (tile >= *w.ntiles) return;
+  TileInfo t = tile_info(m0, m1, Hkv);
+  const int len = t.len;
+  const int b = t.b, h = t.h, seg = t.seg;
+  char* const Kseg = reinterpret_cast<char*>(a.K) + t.off * RB;
+  char* const Vseg = reinterpret_cast<char*>(a.V) + t.off * RB;
+  const char* const lamseg = reinterpret_cast<const char*>(a.lam + t.off);
+  const char* const lkseg = reinterpret_cast<const char*>(a.lk + t.off);
+  const int relmax = max(len - 1, 0);
+  if (!t.single && tid == 0) L.kt = add_coh(&w.segtk[seg], 1);
+
+  // ---- cached entries, every load issued first: key rows as the A operand
+  // (entry 16 blk + c16, dims 32 ks + 8 gq .. + 7), bias and key gate of
+  // entry `lane`; slots past the end read the last entry
+  u32x4 kb[NBLK][KS];
+  float lamv, lkv;
+  auto load_rows = [&](int k) {
+    const int f0 = k * TWG + wv * TW;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const int rel = min(f0 + 16 * blk + c16, relmax);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[blk][ks] = ld_at<u32x4>(Kseg, (uint32_t)(rel * RB + (32 * ks + 8 * gq) * 2));
+    }
+    const int rl = min(f0 + lane, relmax);
+    lamv = ld_at<float>(lamseg, (uint32_t)rl * 4);
+    lkv = ld_at<float>(lkseg, (uint32_t)rl * 4);
+  };
+  load_rows(t.kt);
+  // ---- the token as the B operand: column c16 < G is query head h G + c16
+  // (high and low bf16 parts), column G the stored key, the rest zero
+  u32x4 qh[KS], ql[KS];
+  {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const bool isq = c16 < G, isk = c16 == G;
+    const int64_t qrow = ((int64_t)b * Hq + h * G + min(c16, G - 1)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int dd = 32 * ks + 8 * gq;
+      const u32x4 vh = *reinterpret_cast<const u32x4*>(w.tqh + qrow + dd);
+      const u32x4 vl = *reinterpret_cast<const u32x4*>(w.tql + qrow + dd);
+      const u32x4 vk = *reinterpret_cast<const u32x4*>(w.tkb + (int64_t)seg * D + dd);
+      qh[ks] = isq ? vh : (isk ? vk : zero);
+      ql[ks] = isq ? vl : zero;
+    }
+  }
+  const PairCoef pc = pair_coef(a.terms);
+  const float lq = (a.terms & 1) ? token_gate(a, w, b, h) : 0.0f;
+  const float lbt = (a.terms & 4) ? token_gate(a, w, b, 2 * Hkv + h) : 0.0f;
+  const float row2 = (lq + lbt) * pc.inv_n2;
+  if (!t.single) {
+    __syncthreads();
+    if (L.kt != t.kt) {  // started out of order: this workgroup takes the ticket's tile
+      t.kt = L.kt;
+      load_rows(t.kt);
+    }
+  }
+  const int e0 = t.kt * TWG + wv * TW;             // the wave's first entry
+  const int nvalid = min(max(len - e0, 0), TW);  // wave-uniform
+  char* const sv = s_v[wv];
+  // the V rows, needed after the logits: straight into LDS (staging load i,
+  // lane l: chunk l % CPR of entry RPI i + l / CPR)
+  if (nvalid > 0) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int rel = min(e0 + RPI * i + lane / CPR, relmax);
+      __builtin_amdgcn_global_load_lds(Vseg + (uint32_t)(rel * RB + (lane % CPR) * 16), to_lds(sv + i * VSTR), 16, 0,
+                                       0);
+    }
+  }
+
+  const float tau = K.tau;
+  const float qs2 = a.scale * kLog2e;
+  const float kscale = (a.terms & 2) ? pc.inv_n2 : 0.0f;
+  float newlam = 0.0f;
+  bool live = false, changed = false;
+  if (nvalid > 0) {
+    // ---- q.k and the similarity
+    f32x4 acc[NBLK];
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma_bf16(kb[blk][ks], qh[ks], s);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = mfma_bf16(kb[blk][ks], ql[ks], s);
+      acc[blk] = s;
+    }
+    // the similarity of entry 16 blk + 4 gq + i (column G) to the entry's lane
+    if (c16 == G) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk)
+        *reinterpret_cast<float4*>(&s_sim[wv][16 * blk + 4 * gq]) =
+            make_float4(acc[blk][0], acc[blk][1], acc[blk][2], acc[blk][3]);
+    }
+    __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+    {
+      // ---- pair term and bias update, once per entry
+      const bool valid = lane < nvalid;
+      const float sim = s_sim[wv][min(lane, TW - 1)];
+      const float l0 = valid ? lamv : kNegInf;
+      const bool alive = valid && (l0 >= tau);
+      const float A = pair_A(pc, row2, lkv * kscale, sim);
+      const float l1 = alive ? l0 + A : l0;
+      live = alive && (l1 >= tau);
+      newlam = l1;
+      changed = alive;
+      if (lane < TW) s_lb[wv][lane] = live ? l1 * kLog2e : kNegInf;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- logits of head c16 for entries 16 blk + 4 gq + i; max and sum per head
+    float e2[NBLK][4];
+    float m = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const float4 lb = *reinterpret_cast<const float4*>(&s_lb[wv][16 * blk + 4 * gq]);
+      const float lbv[4] = {lb.x, lb.y, lb.z, lb.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        e2[blk][i] = (c16 < G) ? fmaf(acc[blk][i], qs2, lbv[i]) : kNegInf;  // rows past the end: lb = -inf
+        m = fmaxf(m, e2[blk][i]);
+      }
+    }
+    m = across_groups_max<16>(m);
+    const float msub = (m == kNegInf) ? 0.0f : m;
+    float p[NBLK][4];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[blk][i] = __builtin_amdgcn_exp2f(e2[blk][i] - msub);
+        lsum += p[blk][i];
+      }
+    }
+    lsum = across_groups_sum<16>(lsum);
+    // ---- P V (P in high and low bf16 parts), V^T from LDS
+    __builtin_amdgcn_s_waitcnt(kWaitAll);  // the V rows are in LDS
+    f32x4 o[NBD];
+#pragma unroll
+    for (int nb = 0; nb < NBD; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) {
+      u32x4 ph, pl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = (j < 2) ? p[2 * ps][2 * j] : p[2 * ps + 1][2 * j - 4];
+        const float x1 = (j < 2) ? p[2 * ps][2 * j + 1] : p[2 * ps + 1][2 * j - 3];
+        const uint32_t hi = pack2_bf16(x0, x1);
+        ph[j] = hi;
+        pl[j] = pack2_bf16(x0 - bf16_lo(hi), x1 - bf16_hi(hi));
+      }
+      // the LDS offsets of the lane's 8 entries (k index order), row part
+      int eo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = 32 * ps + ((j < 4) ? 4 * gq + j : 16 + 4 * gq + j - 4);
+        eo[j] = (e / RPI) * VSTR + (e % RPI) * RB;
+      }
+#pragma unroll
+      for (int nb = 0; nb < NBD; ++nb) {
+        const int dof = 2 * (16 * nb + c16);
+        u32x4 vb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo16 = *reinterpret_cast<const uint16_t*>(sv + eo[2 * j] + dof);
+          const uint32_t hi16 = *reinterpret_cast<const uint16_t*>(sv + eo[2 * j + 1] + dof);
+          vb[j] = lo16 | (hi16 << 16);
+        }
+        o[nb] = mfma_bf16(ph, vb, o[nb]);
+        o[nb] = mfma_bf16(pl, vb, o[nb]);
+      }
+    }
+    // ---- wave partials: lane l holds heads 4 gq + i, dimension 16 nb + c16
+#pragma unroll
+    for (int nb = 0; nb < NBD; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = 4 * gq + i;
+        if (g < G) L.po[(wv * G + g) * D + 16 * nb + c16] = o[nb][i];
+      }
+    }
+    if (gq == 0 && c16 < G) {
+      L.pm[wv * G + c16] = m;
+      L.pl[wv * G + c16] = lsum;
+    }
+  } else {
+    // a wave past the end of the segment: neutral partials
+    for (int idx = lane; idx < G * D; idx += 64) L.po[wv * G * D + idx] = 0.0f;
+    if (lane < G) {
+      L.pm[wv * G + lane] = kNegInf;
+      L.pl[wv * G + lane] = 0.0f;
+    }
+  }
+  uint64_t mask = 0;
+  if constexpr (COMPACT) {
+    mask = __ballot(live);
+    if (lane == 0) L.cnt[wv] = __popcll(mask);
+  }
+  __syncthreads();  // partials and live counts in LDS
+
+  int count = 0, wbase = 0;
+  if constexpr (COMPACT) {
+#pragma unroll
+    for (int w2 = 0; w2 < kTileWaves; ++w2) {
+      wbase += (w2 < wv) ? L.cnt[w2] : 0;
+      count += L.cnt[w2];
+    }
+  } else {
+    if (changed) a.lam[t.off + e0 + lane] = newlam;
+  }
+
+  float Mo[OPT], Lo[OPT], Oo[OPT];
+  tile_publish<D, G, COMPACT>(K, t, L, count, Mo, Lo, Oo);
+  const bool combines = t.single || L.flag;
+
+  int npos = len;  // where the new entry goes
+  if constexpr (COMPACT) {
+    // ---- the survivors, in order; rows already in place are not rewritten.
+    // rank of entry e: (its rank among the tile's survivors) or -1, from lane e
+    const int P = L.pre;
+    const int myrank =
+        wbase + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+    const int rk_e = live ? myrank : -1;
+    if (nvalid > 0) {
+#pragma unroll
+      for (int blk = 0; blk < NBLK; ++blk) {  // keys from registers
+        const int e = 16 * blk + c16;
+        const int rk = __shfl(rk_e, e, 64);
+        if (rk >= 0 && P + rk != e0 + e) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<u32x4*>(Kseg + (uint32_t)((P + rk) * RB + (32 * ks + 8 * gq) * 2)) = kb[blk][ks];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {  // values from LDS
+        const int e = RPI * i + lane / CPR;
+        const int rk = __shfl(rk_e, e, 64);
+        if (rk >= 0 && P + rk != e0 + e) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sv + i * VSTR + lane * 16);
+          *reinterpret_cast<u32x4*>(Vseg + (uint32_t)((P + rk) * RB + (lane % CPR) * 16)) = v;
+        }
+      }
+    }
+    if (live) {
+      const int64_t dst = t.off + P + myrank;
+      a.lam[dst] = newlam;
+      if (P + myrank != e0 + lane) a.lk[dst] = lkv;
+      if (K.kept) K.kept[dst] = e0 + lane;
+    }
+    npos = P + count;
+  }
+  constexpr int MLC = (kTileWaves * NI * VSTR) / (4 * 2 * G);  // tiles per chunk of the (max, sum) scratch
+  tile_finish<D, G, true, COMPACT>(K, t, L, reinterpret_cast<float*>(&s_v[0][0]), MLC, combines, npos, Mo, Lo, Oo);
 }
 
 // ---------------------------------------------------------------------------
@@ -979,7 +1361,10 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArg
 static int tile_entries(int d, int nb) { return (64 / (d / 8)) * nb * kTileWaves; }
 
 // Entries per tile (sizes the per-tile workspace rows and flags).
-int decode_tile_entries(int d, int g) { return tile_entries(d, decode_nb(d, g)); }
+int decode_tile_entries(int d, int g, bool bf16) {
+  if (bf16) return d == 64 ? MfShape<64>::TWG : MfShape<128>::TWG;
+  return tile_entries(d, decode_nb(d, g));
+}
 
 static int64_t decode_max_tiles(const LayerArgs& a, int twg) {
   const int64_t S = (int64_t)a.B * a.H_kv;
@@ -1002,6 +1387,10 @@ static size_t decode_layout(const LayerArgs& a, int twg, DecodeWs* w, char* base
   int4* map = reinterpret_cast<int4*>(take(sizeof(int4) * 2 * mt));
   float* tq = reinterpret_cast<float*>(take(sizeof(float) * a.B * a.H_q * a.d));
   float* tkey = reinterpret_cast<float*>(take(sizeof(float) * S * a.d));
+  const size_t nh = a.bf16 ? 1 : 0;  // bf16 planes only for bf16 caches
+  uint16_t* tqh = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * a.B * a.H_q * a.d * nh));
+  uint16_t* tql = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * a.B * a.H_q * a.d * nh));
+  uint16_t* tkb = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * S * a.d * nh));
   float* zdec = reinterpret_cast<float*>(take(sizeof(float) * a.B * kTokParts * (3 * a.H_kv + a.r)));
   float* part_o = reinterpret_cast<float*>(take(sizeof(float) * mt * G * a.d));
   float* part_ml = reinterpret_cast<float*>(take(sizeof(float) * mt * G * 2));
@@ -1011,6 +1400,9 @@ static size_t decode_layout(const LayerArgs& a, int twg, DecodeWs* w, char* base
     w->map = map;
     w->tq = tq;
     w->tkey = tkey;
+    w->tqh = tqh;
+    w->tql = tql;
+    w->tkb = tkb;
     w->zdec = zdec;
     w->part_o = part_o;
     w->part_ml = part_ml;
@@ -1031,16 +1423,24 @@ DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, 
 template <int D, int G, bool BF16>
 static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Control& ctl, float tau, bool compact,
                               int32_t* kept, hipStream_t st) {
-  const int twg = TileShape<D, decode_nb(D, G)>::TWG;
+  const int twg = decode_tile_entries(D, G, BF16);
   const DecodeKArgs k{a, w, ctl, tau, kept, twg};
   hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B * kTokParts + 1), dim3(kTokThreads), 0, st, k);
   const int64_t mt = decode_max_tiles(a, twg);
   if (mt > (1 << 30)) return hipErrorInvalidValue;
   const int grid = (int)mt;
-  if (compact) {
-    hipLaunchKernelGGL((decode_tile_kernel<D, G, BF16, true>), dim3(grid), dim3(kTileThreads), 0, st, k);
+  if constexpr (BF16) {
+    if (compact) {
+      hipLaunchKernelGGL((decode_tile_mf_kernel<D, G, true>), dim3(grid), dim3(kTileThreads), 0, st, k);
+    } else {
+      hipLaunchKernelGGL((decode_tile_mf_kernel<D, G, false>), dim3(grid), dim3(kTileThreads), 0, st, k);
+    }
   } else {
-    hipLaunchKernelGGL((decode_tile_kernel<D, G, BF16, false>), dim3(grid), dim3(kTileThreads), 0, st, k);
+    if (compact) {
+      hipLaunchKernelGGL((decode_tile_kernel<D, G, false, true>), dim3(grid), dim3(kTileThreads), 0, st, k);
+    } else {
+      hipLaunchKernelGGL((decode_tile_kernel<D, G, false, false>), dim3(grid), dim3(kTileThreads), 0, st, k);
+    }
   }
   return hipGetLastError();
 }

@@ -72,6 +72,17 @@ __device__ __forceinline__ void load8(const void* p, int64_t i, float (&out)[8])
 // An LDS pointer in the LDS address space, as the global->LDS load builtins
 // take it: the low 32 bits of a generic pointer to a __shared__ object are
 // its LDS offset.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One 16 x 16 x 32 bf16 matrix-core product: lane l supplies row (of A) and
+// column (of B) l & 15 over k group l >> 4 (8 bf16 each), and gets rows
+// 4 (l >> 4) .. + 3 of column l & 15 of the fp32 result.
+__device__ __forceinline__ f32x4 mfma_bf16(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                  0, 0);
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ lds_ptr_t to_lds(const void* p) {
   return reinterpret_cast<lds_ptr_t>(static_cast<size_t>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p))));

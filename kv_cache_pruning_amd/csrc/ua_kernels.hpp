@@ -86,6 +86,9 @@ struct DecodeWs {
                    //                 {record of the segment's first tile, offset low, offset high, 0}
   float* tq;       // [B, H_q, d]  rotated queries
   float* tkey;     // [B * H_kv, d]  stored new keys (rounded like the cache)
+  uint16_t* tqh;   // [B, H_q, d]  bf16 caches: rotated queries, high bf16 part
+  uint16_t* tql;   // [B, H_q, d]  and low part (the rest of the fp32 value, rounded)
+  uint16_t* tkb;   // [B * H_kv, d]  bf16 caches: the stored new keys as bf16
   float* zdec;     // [B, 4, 3 * H_kv + r]  x [W_dec | W_dn] over four slices of the rows (summed by the readers)
   float* part_o;   // [max_tiles, G, d]   partials of segments held by several tiles
   float* part_ml;  // [max_tiles, G, 2]   max (log2 units), sum
@@ -93,7 +96,7 @@ struct DecodeWs {
 };
 
 size_t decode_ws_bytes(const LayerArgs& a, int tile_entries);
-int decode_tile_entries(int d, int g);  // g: query heads per KV head
+int decode_tile_entries(int d, int g, bool bf16);  // g: query heads per KV head
 DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, int tile_entries);
 // One decode step; with compact, the in-place compaction of every segment in
 // the same launch (kept: optional kept-index output).

@@ -28,7 +28,7 @@ int compact_chunk_entries(const LayerArgs& a) {
 // Flags for compaction chunks and for the tiles of a decode step that compacts
 // in the same launch (the finer of the two).
 static int64_t compact_max_chunks(const LayerArgs& a) {
-  const int unit = std::min(compact_chunk_entries(a), decode_tile_entries(a.d, a.H_q / a.H_kv));
+  const int unit = std::min(compact_chunk_entries(a), decode_tile_entries(a.d, a.H_q / a.H_kv, a.bf16 != 0));
   return a.total_slots / unit + (int64_t)a.B * a.H_kv + 1;
 }
 
