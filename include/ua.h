@@ -69,7 +69,7 @@ enum { UA_TERM_Q = 1, UA_TERM_K = 2, UA_TERM_SIM = 4, UA_TERMS_ALL = 7 };
  * unchanged); bit 1: a wait on another workgroup of the same call timed out
  * (never expected; the outputs and the cache contents are then undefined);
  * bit 2: a decode step found a segment length above its capacity (a broken
- * cache table; the step changed nothing but next_pos, and y is undefined). */
+ * cache table; the step changed nothing, and y is undefined). */
 enum { UA_STATUS_SEGMENT_FULL = 1, UA_STATUS_WAIT_TIMEOUT = 2, UA_STATUS_BAD_LENGTH = 4 };
 
 /*

@@ -10,41 +10,42 @@
 // out of the step's softmax and are evicted; the output is the low-rank
 // sigmoid gate times the attention output; the new entry is appended.
 //
-// Launch 1, decode_token_kernel (4 workgroups per sequence, one more): what
-// depends on the token alone -- the projections x W_dec and u = x W_dn (each
-// of the 4 workgroups a slice of the rows; readers add the partials), the
-// rotated queries and the stored key (normalised, rotated, rounded like the
-// cache), each workgroup a quarter -- written to the workspace.  The last workgroup numbers the tiles of the
-// step from the segment lengths (a tile is TWG consecutive entries of one
-// segment), writes one record per tile, and clears the per-segment counters
-// and the look-back words of the second launch.
+// Launch 1, decode_token_kernel (one workgroup for the tile records, then 4
+// per sequence): workgroup 0 numbers the tiles of the step from the segment
+// lengths (a tile is TWG consecutive entries of one segment), writes one
+// record per tile, clears the per-segment counters and the look-back words of
+// the second launch, and reports a length above its capacity (status bit 2;
+// then no tile runs).  Workgroup (b, p) forms what depends on the token alone:
+// the projections x W_dec and u = x W_dn over a quarter of the rows (readers
+// add the quarters), a quarter of the rotated queries (fp32, and for bf16
+// caches also as high and low bf16 parts) and of the stored keys (normalised,
+// rotated, rounded like the cache); a fifth wave forms the RoPE table of the
+// position (fp64 angles) while the projections load.
 //
-// Launch 2, decode_tile_kernel (a persistent grid of four-wave workgroups,
-// every one resident at once, taking the tiles in turn; the next tile's rows
-// are loaded straight into LDS while the current one runs): a workgroup
-// reads its tile record, the token's rotated queries and key, and reads each
-// entry once: the key row feeds the G
-// query dot products and the key-similarity dot product (reduced over the
-// d/8 lanes that hold the row, with DPP), the pair term updates the log-bias,
-// entries below log p drop out, and an online-softmax partial (max, sum,
-// weighted V) is formed per wave and merged across the waves in LDS.  Every
-// wait below is on a lower tile of the same segment.
+// Launch 2, one four-wave workgroup per tile (decode_tile_mf_kernel for bf16
+// caches, decode_tile_kernel for fp32): the tile's key rows, biases and key
+// gates are loaded once; every entry gets its q.k products (one per query head
+// of the group) and its key similarity in the same pass, the pair term
+// updates its log-bias, entries below log p drop out, and an online-softmax
+// partial (max, sum, weighted V) is formed per wave and merged across the
+// waves in LDS.  With bf16 caches the products run on the matrix cores and V
+// is staged in LDS by direct loads; with fp32 caches they run on the vector
+// ALUs with the rows in registers.  Every wait below is on a lower tile of
+// the same segment.
 //  * A one-tile segment combines at once; otherwise each tile publishes its
-//    partial before its flag word, and the segment's last tile, once its
-//    look-back has seen every earlier tile publish, merges them.  The
-//    combine adds the token's own term (every tile forms the token's logit
-//    against its own key from the queries and key it holds) and multiplies
-//    by the output gate sigmoid(u W_up + b_up) of its outputs.
+//    partial before its flag word, and the segment's last tile to arrive
+//    merges them.  The combine adds the token's own term and multiplies by the
+//    output gate sigmoid(u W_up + b_up).
 //  * With COMPACT the survivors move down in place: a tile publishes its live
-//    count once every row of the tile is in registers and looks back over the
-//    earlier tiles of its segment for its destination (decoupled look-back);
-//    the look-back cannot finish before every earlier tile has published,
-//    which orders the stores after the loads they overwrite.  Rows already in
-//    place are not rewritten; every survivor's new log-bias is stored.  The
-//    segment's last tile learns the new length, appends the new entry after
-//    the survivors and writes the length.
-//  * Without COMPACT the log-biases are updated in place and the segment's
-//    last tile appends the new entry at the old length.
+//    count once every row of the tile is in registers or LDS and looks back
+//    over the earlier tiles of its segment for its destination (decoupled
+//    look-back); the look-back cannot finish before every earlier tile has
+//    published, which orders the stores after the loads they overwrite.  Rows
+//    already in place are not rewritten; every survivor's new log-bias is
+//    stored.  The segment's last tile appends the new entry after the
+//    survivors and writes the length.
+//  * Without COMPACT the log-biases are updated in place and the merging tile
+//    appends the new entry at the old length.
 // No launch reads a length another workgroup of the same launch writes: the
 // tile records carry the lengths at the start of the step.
 //
@@ -79,7 +80,7 @@ __device__ __forceinline__ unsigned long long ld64_coh(const unsigned long long*
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-constexpr int kTokThreads = 256;
+constexpr int kTokThreads = 320;  // two projections of 128 threads each, and one wave for the RoPE table
 constexpr int kTokParts = 4;  // token-launch workgroups per sequence
 constexpr int kTileThreads = 256;
 constexpr int kTileWaves = kTileThreads / 64;
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
   const LayerArgs& a = K.a;
   const DecodeWs& w = K.w;
   constexpr int NT = kTokThreads;
-  constexpr int NH = NT / 2;  // threads per projection
+  constexpr int NH = 128;  // threads per projection
   constexpr int HALF = D / 2;
   constexpr int P = kTokParts;
   const int tid = threadIdx.x;
@@ -309,48 +310,90 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
   __shared__ float s_red[NT][8];
   __shared__ float s_cs[HALF], s_sn[HALF];
   __shared__ int s_scan[NT / 64 + 1];
-  constexpr int kMapSegs = 2048;  // segments whose tile records are written in parallel
-  __shared__ int s_first[kMapSegs + 1], s_len[kMapSegs];
+  constexpr int kMapSegs = 2048;      // segments whose records go through LDS
+  constexpr int kMapTiles = 4096;     // tiles whose segment is looked up in LDS
+  __shared__ int s_seg[kMapTiles];    // tile -> segment
+  __shared__ int s_first[kMapSegs], s_len[kMapSegs];
   __shared__ int64_t s_off[kMapSegs];
 
-  if ((int)blockIdx.x == a.B * P) {
-    // ---- the tile records of this step, from the lengths at its start
+  if (blockIdx.x == 0) {
+    // ---- the tile records of this step, from the lengths at its start: a
+    // thread holds S / NT segments (all loaded in one round when there are at
+    // most MP), scans their tile counts with the others, then writes its own
+    // segments' records
+    constexpr int MP = 8;
     const int twg = K.twg;
     const int per = (S + NT - 1) / NT;
     const int sb = min(S, tid * per), se = min(S, sb + per);
-    int mine = 0;
-    for (int s = sb; s < se; ++s) mine += tiles_of(a.seg_len[s], twg);
-    int total;
-    int run = block_exclusive_scan<NT>(mine, s_scan, &total);
-    if (S <= kMapSegs) {
-      // every thread writes records t = tid, tid + NT, ...: its segment by
-      // binary search over the segments' first tiles, all read from LDS
+    int lenr[MP], capr[MP];
+    int64_t offr[MP];
+    int mine = 0, badl = 0;
+    if (per <= MP) {
+#pragma unroll
+      for (int k = 0; k < MP; ++k) {
+        const bool in = sb + k < se;
+        lenr[k] = in ? a.seg_len[sb + k] : 0;
+        capr[k] = in ? a.seg_cap[sb + k] : 0;
+        offr[k] = in ? a.seg_off[sb + k] : 0;
+      }
+#pragma unroll
+      for (int k = 0; k < MP; ++k) {
+        if (sb + k < se) {
+          mine += tiles_of(lenr[k], twg);
+          badl |= (lenr[k] < 0 || lenr[k] > capr[k]) ? 1 : 0;
+        }
+      }
+    } else {
       for (int s = sb; s < se; ++s) {
         const int len = a.seg_len[s];
-        s_first[s] = run;
-        s_len[s] = len;
-        s_off[s] = a.seg_off[s];
-        run += tiles_of(len, twg);
+        mine += tiles_of(len, twg);
+        badl |= (len < 0 || len > a.seg_cap[s]) ? 1 : 0;
       }
-      if (tid == 0) s_first[S] = total;
+    }
+    int total;
+    int run = block_exclusive_scan<NT>(mine, s_scan, &total);
+    const bool bad = __syncthreads_or(badl) != 0;
+    if (S <= kMapSegs && total <= kMapTiles) {
+      // the tile -> segment table and the segments' first tile, length and
+      // offset into LDS, then the records written evenly by every thread
+#pragma unroll
+      for (int k = 0; k < MP; ++k) {
+        if (sb + k < se) {
+          const int nt = tiles_of(lenr[k], twg);
+          s_first[sb + k] = run;
+          s_len[sb + k] = lenr[k];
+          s_off[sb + k] = offr[k];
+          for (int t = 0; t < nt; ++t) s_seg[run + t] = sb + k;
+          run += nt;
+        }
+      }
       __syncthreads();
       for (int t = tid; t < total && t < w.max_tiles; t += NT) {  // lengths beyond capacity break the bound
-        int lo = 0, hi = S - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_first[mid] <= t) lo = mid; else hi = mid - 1;
-        }
-        const int f = s_first[lo];
-        const int64_t off = s_off[lo];
-        w.map[2 * t + 0] = make_int4(lo, t - f, s_len[lo], s_first[lo + 1] - f);
+        const int sg = s_seg[t];
+        const int f = s_first[sg];
+        const int len = s_len[sg];
+        const int64_t off = s_off[sg];
+        w.map[2 * t + 0] = make_int4(sg, t - f, len, tiles_of(len, twg));
         w.map[2 * t + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+      }
+    } else if (per <= MP) {
+#pragma unroll
+      for (int k = 0; k < MP; ++k) {
+        if (sb + k < se) {
+          const int nt = tiles_of(lenr[k], twg);
+          for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {
+            w.map[2 * (run + t) + 0] = make_int4(sb + k, t, lenr[k], nt);
+            w.map[2 * (run + t) + 1] = make_int4(run, (int)(uint32_t)(offr[k] & 0xffffffff), (int)(offr[k] >> 32), 0);
+          }
+          run += nt;
+        }
       }
     } else {
       for (int s = sb; s < se; ++s) {
         const int len = a.seg_len[s];
         const int nt = tiles_of(len, twg);
         const int64_t off = a.seg_off[s];
-        for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {  // lengths beyond capacity break the bound
+        for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {
           w.map[2 * (run + t) + 0] = make_int4(s, t, len, nt);
           w.map[2 * (run + t) + 1] = make_int4(run, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
         }
@@ -361,7 +404,7 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
       w.cnt[s] = 0;
       w.segtk[s] = 0;
     }
-    if (total > w.max_tiles) {  // a segment length above its capacity: no tile runs
+    if (bad || total > w.max_tiles) {  // a segment length above its capacity: no tile runs
       if (tid == 0) atomicOr(a.status, 4);
       total = 0;
     }
@@ -372,8 +415,8 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
   // Workgroup (b, p): part p of P of sequence b's token work.  Every load of
   // the part is issued first: its slice of x and of the rows of W_dec and
   // W_dn, its queries and keys.
-  const int b = blockIdx.x / P;
-  const int p = blockIdx.x - b * P;
+  const int b = (blockIdx.x - 1) / P;
+  const int p = (blockIdx.x - 1) - b * P;
   const char* const xrow = reinterpret_cast<const char*>(a.x) + (int64_t)b * a.D_model * (BF16 ? 2 : 4);
   const int Dm = a.D_model;
   const int r0 = (p * Dm) / P, r1 = ((p + 1) * Dm) / P;
@@ -397,15 +440,16 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
     k0 = load_elem<BF16>(a.k, (int64_t)(b * Hkv + h0) * D + lane);
     k1 = load_elem<BF16>(a.k, (int64_t)(b * Hkv + h0) * D + lane + HALF);
   }
-  // ---- x W_dn and x W_dec over rows [p D / P, (p + 1) D / P), half the
-  // threads each; the RoPE table of the position is formed while the
-  // first loads of x W_dn fly
-  const RopeTable rt{a.inv_freq, a.next_pos[b], HALF, s_cs, s_sn};
-  static_assert(HALF <= NH, "the table threads take part in x W_dn");
+  // ---- x W_dn and x W_dec over rows [p D / P, (p + 1) D / P), 128
+  // threads each; the last wave forms the RoPE table of the position
+  // meanwhile
   if (tid < NH) {
-    gemv_partial<BF16, NH>(pn, tid, r0, r1, a.W_dn, xrow, s_red, &rt);
-  } else {
+    gemv_partial<BF16, NH>(pn, tid, r0, r1, a.W_dn, xrow, s_red);
+  } else if (tid < 2 * NH) {
     gemv_partial<BF16, NH>(pd, tid - NH, r0, r1, a.W_dec, xrow, s_red + NH);
+  } else {
+    const RopeTable rt{a.inv_freq, a.next_pos[b], HALF, s_cs, s_sn};
+    for (int i = tid - 2 * NH; i < HALF; i += 64) rope_entry(rt, i);
   }
   __syncthreads();
   const int ZC = 3 * Hkv + a.r;
