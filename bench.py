@@ -55,6 +55,10 @@ def kernel_source_hash(path: str) -> str:
     return h.hexdigest()[:16]
 
 
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def load_traffic(name: str, path: str):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if current."""
     p = os.path.join(ROOT, "profiles", f"{name}_counters.json")
@@ -192,10 +196,11 @@ def cache_desc(cfg) -> str:
 
 def bench_decode(args, name: str, over=None, cpu: bool = True):
     """One decode workload: a ring of R layer instances (>= ring-bytes of live
-    cache), each step one fused decode + eviction + compaction launch per
-    instance, captured in a HIP graph and timed with events around every step.
-    The same steps are replayed as two calls (decode, then ua_compact) from the
-    same state, and once more untimed to count live entries and moved rows."""
+    cache), each step one fused decode + eviction + compaction call per
+    instance (a token launch and a tile launch), captured in a HIP graph and
+    timed with events around every step.  The same steps are replayed as two
+    calls (decode, then ua_compact) from the same state, and once more untimed
+    to count live entries and moved rows."""
     import torch
 
     from kv_cache_pruning_amd.layer import DeviceCache, DeviceWeights, Layer, LayerShape, Workspace
@@ -235,6 +240,7 @@ def bench_decode(args, name: str, over=None, cpu: bool = True):
     y = torch.empty((cfg.B, cfg.H_q, cfg.d), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     setup_s = time.time() - t0
+    progress(f"{cfg.name}: {R} layer instances ready ({setup_s:.1f} s)")
     static_in = [t.clone() for t in toks[0]]
 
     def load_inputs(s):
@@ -287,6 +293,7 @@ def bench_decode(args, name: str, over=None, cpu: bool = True):
     torch.cuda.synchronize()
     total_ms = ev_s[0][0].elapsed_time(ev_s[-1][1])
     fused_ms = [e[0].elapsed_time(e[1]) / R for e in ev_s]
+    progress(f"{cfg.name}: timed steps done")
     st = int(sum(int(c.status.item()) for c in caches))
 
     # ---- the same steps as two calls (decode, then compaction), from the same state
@@ -302,6 +309,7 @@ def bench_decode(args, name: str, over=None, cpu: bool = True):
     torch.cuda.synchronize()
     dec_ms = [e[0].elapsed_time(e[1]) / R for e in ev]
     cmp_ms = [e[1].elapsed_time(e[2]) / R for e in ev]
+    progress(f"{cfg.name}: two-call steps done")
 
     # ---- untimed replay of the same steps: live entries scanned, rows moved
     restore()
@@ -336,6 +344,8 @@ def bench_decode(args, name: str, over=None, cpu: bool = True):
     # compaction: 4 B per entry scanned, plus each moved row read and written
     cmp_bytes = cmp_scanned * 4 + moved * 2 * row_bytes
     fused_bytes = dec_bytes + moved_fused * (row_bytes - 4)  # moved rows: K, V, key gate written
+    tile_kernel = (f"decode_tile_mf_kernel<{cfg.d}, {cfg.H_q // cfg.H_kv}, true>" if cfg.bf16
+                   else f"decode_tile_kernel<{cfg.d}, {cfg.H_q // cfg.H_kv}, false, true>")
     dec_avg_ms, cmp_avg_ms = float(np.mean(dec_ms)), float(np.mean(cmp_ms))
     fused_avg_ms = float(np.mean(fused_ms))
     achieved = fused_bytes / n_calls / (fused_avg_ms * 1e-3) / 1e9
@@ -349,7 +359,8 @@ def bench_decode(args, name: str, over=None, cpu: bool = True):
         "ms_per_step": ms_per_step,
         "dtype": "bf16" if cfg.bf16 else "f32",
         "workload": f"{cfg.name}: UA decode layer B={cfg.B} H_q={cfg.H_q} H_kv={cfg.H_kv} d={cfg.d} D={cfg.D}, "
-                    f"{cache_desc(cfg)}, p={cfg.p}, decode + eviction + compaction every step (one fused launch), "
+                    f"{cache_desc(cfg)}, p={cfg.p}, decode + eviction + compaction every step (one fused call: "
+                    f"token launch + tile launch), "
                     f"ring of {R} layer instances",
         "ring_instances": R,
         "tokens_per_step": tokens,
@@ -365,8 +376,10 @@ def bench_decode(args, name: str, over=None, cpu: bool = True):
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": load_traffic(f"decode_{cfg.name}", "decode"),
-            "kernel": "ua_decode_compact_step, one launch per layer step (average launch from events around "
-                      "the R launches of each step)",
+            "kernel": f"ua_decode_compact_step = decode_token_kernel<{cfg.d}, {'true' if cfg.bf16 else 'false'}> + "
+                      f"{tile_kernel} (the tile launch is about 85% of the call): one call per layer step, its "
+                      "average duration from events around each timed step's R back-to-back calls",
+            "launch_us": fused_avg_ms * 1e3,
             "alg_bytes_per_launch": fused_bytes / n_calls,
         },
         "two_calls": {
@@ -413,6 +426,8 @@ def main():
     ap.add_argument("--no-prefill-variants", action="store_true",
                     help="skip the pruned, chunk-boundary and variable-length prefill figures")
     ap.add_argument("--no-backward", action="store_true", help="skip the attention-backward figures")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="time the 1b-prefill pass only and print its object (profiles)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first run three plain device copies of MIB MiB (a known-size reference for the HBM "
                          "byte counters of a rocprofv3 --pmc run)")
@@ -443,6 +458,12 @@ def main():
         over["H_q"] = args.q_heads
     def note(what, t0):
         print(f"[bench] {what} done ({time.time() - t0:.1f} s)", file=sys.stderr, flush=True)
+
+    if args.only_prefill:
+        t0 = time.time()
+        print(json.dumps({"prefill": bench_prefill(args)}), flush=True)
+        note("prefill", t0)
+        return
 
     t0 = time.time()
     head = bench_decode(args, args.workload, over)
