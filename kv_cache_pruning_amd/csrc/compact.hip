@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
   using Sh = CompactShape<RB, kCompactThreads>;
   constexpr int CH = Sh::CH, P16 = Sh::P16, PPT = Sh::PPT;
   __shared__ int s_scan[kCompactThreads / 64 + 1];
-  __shared__ int s_info[4];
+  __shared__ int s_info[6];
   __shared__ int s_ticket;
   __shared__ int s_src[CH];
   __shared__ int s_cnt[kCompactThreads / 64];
@@ -76,17 +76,38 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
   const int lane = tid & 63;
   const int wv = tid >> 6;
 
-  // ---- numbering from the lengths at the start of the call
+  // ---- numbering from the lengths at the start of the call; a thread's
+  // segments (up to MP of them) stay in registers, so finding a chunk's
+  // segment later reads nothing
+  constexpr int MP = 4;
   const int per = (S + kCompactThreads - 1) / kCompactThreads;
   const int sb = min(S, tid * per);
   const int se = min(S, sb + per);
+  if (tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobTicket], 1);
+  int lenr[MP];
+  int64_t offr[MP];
   int mine = 0;
-  for (int s = sb; s < se; ++s) mine += chunks_of(a.seg_len[s], CH);
+  if (per <= MP) {
+#pragma unroll
+    for (int k = 0; k < MP; ++k) {
+      lenr[k] = (sb + k < se) ? a.seg_len[sb + k] : 0;
+      offr[k] = (sb + k < se) ? a.seg_off[sb + k] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < MP; ++k) mine += chunks_of(lenr[k], CH);
+  } else {
+    for (int s = sb; s < se; ++s) mine += chunks_of(a.seg_len[s], CH);
+  }
   int total;
   const int excl = block_exclusive_scan<kCompactThreads>(mine, s_scan, &total);
 
+  bool first_draw = true;
   while (true) {
-    if (tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobTicket], 1);
+    // a ticket per chunk, drawn when the previous chunk is done (a ticket
+    // drawn ahead would leave a low id waiting behind a busy workgroup, and
+    // every later chunk's look-back on it)
+    if (!first_draw && tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobTicket], 1);
+    first_draw = false;
     __syncthreads();
     const int id = s_ticket;
 
@@ -126,25 +147,45 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
       break;
     }
 
-    // ---- chunk id -> (segment, chunk)
+    // ---- chunk id -> (segment, chunk, first chunk of the segment, length, offset)
     if (id >= excl && id < excl + mine) {
       int run = excl;
-      for (int s = sb; s < se; ++s) {
-        const int n = chunks_of(a.seg_len[s], CH);
-        if (id >= run && id < run + n) {
-          s_info[0] = s;
-          s_info[1] = id - run;
-          s_info[2] = run;
+      if (per <= MP) {
+#pragma unroll
+        for (int k = 0; k < MP; ++k) {
+          const int n = chunks_of(lenr[k], CH);
+          if (id >= run && id < run + n) {
+            s_info[0] = sb + k;
+            s_info[1] = id - run;
+            s_info[2] = run;
+            s_info[3] = (int)(uint32_t)(offr[k] & 0xffffffff);
+            s_info[4] = (int)(offr[k] >> 32);
+            s_info[5] = lenr[k];
+          }
+          run += n;
         }
-        run += n;
+      } else {
+        for (int s = sb; s < se; ++s) {
+          const int n = chunks_of(a.seg_len[s], CH);
+          if (id >= run && id < run + n) {
+            const int64_t o = a.seg_off[s];
+            s_info[5] = a.seg_len[s];
+            s_info[0] = s;
+            s_info[1] = id - run;
+            s_info[2] = run;
+            s_info[3] = (int)(uint32_t)(o & 0xffffffff);
+            s_info[4] = (int)(o >> 32);
+          }
+          run += n;
+        }
       }
     }
     __syncthreads();
     const int seg = s_info[0];
     const int c = s_info[1];
     const int first = s_info[2];
-    const int len = a.seg_len[seg];
-    const int64_t off = a.seg_off[seg];
+    const int len = s_info[5];
+    const int64_t off = (int64_t)(uint32_t)s_info[3] | ((int64_t)s_info[4] << 32);
     const int j0 = c * CH;
     const int nvalid = min(CH, len - j0);  // >= 1: only chunks with entries are numbered
 
