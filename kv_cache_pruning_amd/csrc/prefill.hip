@@ -1014,7 +1014,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
 // store and no progress word.  The next token block loads the words of a key
 // block before its pair terms and checks the tags after them, reloading only
 // the words still stale.  The tag is a signalling-NaN pattern holding the
-// call counter (glob[kGlobSeq], which decode calls advance too); arithmetic
+// call counter (glob[kGlobSeq], which every prefill call advances); arithmetic
 // never produces it, so no stale word of the workspace carries it.
 // ---------------------------------------------------------------------------
 constexpr float kStaticRef = 6.0f;
