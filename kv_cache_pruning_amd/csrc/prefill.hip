@@ -1188,8 +1188,11 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
       float car[4];
       unsigned long long cw[4];
       if (!chain) {
+        // unconditional loads of clamped slots, the keys of this call zeroed
+        // where they are used: a load under a condition would be a branch of
+        // its own with an immediate wait
 #pragma unroll
-        for (int i = 0; i < 4; ++i) car[i] = (jk + i < len0) ? ldf_coh_p(&a.lam[slot(jk + i)]) : 0.0f;
+        for (int i = 0; i < 4; ++i) car[i] = ldf_coh_p(&a.lam[slot(jk + i)]);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) cw[i] = ld64_coh_p(&cin[slot(jk + i)]);
@@ -1305,7 +1308,11 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
       // carry into this token block (log2 units)
       if (!chain) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) car[i] *= kLog2e;
+        for (int i = 0; i < 4; ++i) {
+          float c = car[i];
+          asm volatile("" : "+v"(c));  // first use here: the loads' wait stays after the pair terms
+          car[i] = (jk + i < len0) ? c * kLog2e : 0.0f;
+        }
       } else {
         int spins = 0;
         for (;;) {
@@ -1505,12 +1512,14 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
         // one loop per reference mode, so each holds only its own state
         auto softmax_loop = [&](auto stat_c) {
           for (int J = 0; J < nJ; ++J) {
-            if constexpr (NH > 0) softmax_block(J, stat_c);
-            // K of block J + 2 and V of block J + 1 to LDS, then the loads of the blocks after
+            // K of block J + 2 and V of block J + 1 to LDS (buffers no role
+            // reads in this block), then the loads of the blocks after, which
+            // have a whole block to arrive
             if (J + 2 < nJ) store_k((J + 2) % 3);
             if (J + 1 < nJ) store_v((J + 1) & 1);
             if (J + 3 < nJ) load_k(J + 3);
             if (J + 2 < nJ) load_v(J + 2);
+            if constexpr (NH > 0) softmax_block(J, stat_c);
             __syncthreads();
           }
         };
