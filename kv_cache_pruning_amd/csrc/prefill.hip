@@ -62,6 +62,8 @@ constexpr int kPrefillSpinLimit = 1 << 22;
 // ---------------------------------------------------------------------------
 // workspace
 // ---------------------------------------------------------------------------
+constexpr int kXcds = 8;  // XCDs of the chip, each with its own L2
+
 struct PrefillWs {
   int* sync;       // [2 + S*nrb]  ticket, arrivals, carry progress per (segment, token block)
   uint16_t* wt;    // [cp, D_model] bf16  [W_dec | W_dn]^T, rows >= 3 H_kv + r zero
@@ -120,7 +122,7 @@ static size_t prefill_layout(const LayerArgs& a, int n, char* base, PrefillWs* w
     off += align_up(bytes, 256);
     return p;
   };
-  char* sync = take(sizeof(int) * (2 + S * nrb));
+  char* sync = take(sizeof(int) * (2 + S * nrb + kXcds));
   char* wt = take(sizeof(uint16_t) * (size_t)cp * a.D_model);
   char* qbf = take(sizeof(uint16_t) * (size_t)NT * a.H_q * a.d);
   char* gl = take(sizeof(float) * 2 * (size_t)NT * a.H_kv);
@@ -1061,13 +1063,25 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   const int Hq = a.H_q, Hkv = a.H_kv;
 
   if (tid == 0) {
-    s_id = addi_coh_p(&w.sync[0], 1);
+    if (S % kXcds == 0) {
+      // One ticket queue per XCD (workgroups go to the XCDs in turn): queue x
+      // serves the segments s = x mod kXcds, token-block major, so that the
+      // token blocks of a segment share one L2 and its K and V are fetched
+      // from below it once.
+      const int x = (int)(blockIdx.x % kXcds), per = S / kXcds;
+      const int t = addi_coh_p(&w.sync[2 + S * nrb + x], 1);
+      s_id = (t / per) * S + x + kXcds * (t % per);
+    } else {
+      s_id = addi_coh_p(&w.sync[0], 1);
+    }
     s_seq = (uint32_t)ldi_coh_p(&w.glob[kGlobSeq]) + 1u;  // this call's number
   }
   __syncthreads();
   const int id = s_id;
   const uint32_t tagv = carry_tag(s_seq);
-  const int s = id % S;  // token-block major: a chain predecessor always has a lower id
+  // token-block major: a chain predecessor always holds an earlier ticket of
+  // the same queue, so it is already running
+  const int s = id % S;
   const int I = id / S;
   const int b = s / Hkv, h = s - b * Hkv;
   const int len0 = a.seg_len[s];
@@ -1615,7 +1629,7 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n, int max
   w.total = total;
   w.tau2 = (log_p == -__builtin_huge_valf()) ? -__builtin_huge_valf() : log_p * kLog2e;
   const int S = a.B * a.H_kv;
-  const int nsync = 2 + S * w.nrb;
+  const int nsync = 2 + S * w.nrb + kXcds;
   const int64_t prep_items = std::max<int64_t>(std::max<int64_t>(nsync, (int64_t)w.cp * (a.D_model / 8)),
                                                (int64_t)a.H_q * a.d * (w.rp / 8));
   const int prep_grid = (int)std::min<int64_t>(1024, std::max<int64_t>(1, (prep_items + 255) / 256));

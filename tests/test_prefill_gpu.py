@@ -52,6 +52,13 @@ def test_prefill_ragged_chunks():
     _run(config("1b-prefill", B=2, H_q=8, H_kv=2, D=256, n_total=300, chunk=100))
 
 
+def test_prefill_per_xcd_ticket_queues():
+    """8 and 16 segments: workgroups take tickets from one queue per XCD."""
+    _run(config("1b-prefill", B=4, H_q=8, H_kv=2, D=256, n_total=300, chunk=150))
+    _run(config("1b-prefill", B=2, H_q=16, H_kv=8, D=256, n_total=200, chunk=100, len_kind="lognormal",
+                len_mean=120.0, len_min=16, len_max=400, nominal=400, lam_p0=0.15))
+
+
 def test_prefill_single_token_calls():
     _run(config("1b-prefill", B=1, H_q=4, H_kv=1, D=64, n_total=5, chunk=1))
 
