@@ -160,6 +160,22 @@ __device__ __forceinline__ void sti_coh_p(int* p, int v) {
 __device__ __forceinline__ int addi_coh_p(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The (token block, segment) id of an attention workgroup, token-block major
+// (id = I * S + s), taken from a ticket so that every wait is on a workgroup
+// that started earlier.  Workgroups go to the XCDs in turn; when the segment
+// count is a multiple of the XCD count, each XCD has its own queue serving the
+// segments s = x mod kXcds, so the token blocks of a segment share one L2 and
+// its K and V are fetched from below it once.  The grid is S * nrb, so every
+// queue is drained.
+__device__ __forceinline__ int prefill_ticket(const PrefillWs& w, int S, int nrb) {
+  if (S % kXcds == 0) {
+    const int x = (int)(blockIdx.x % kXcds), per = S / kXcds;
+    const int t = addi_coh_p(&w.sync[2 + S * nrb + x], 1);
+    return (t / per) * S + x + kXcds * (t % per);
+  }
+  return addi_coh_p(&w.sync[0], 1);
+}
+
 __device__ __forceinline__ unsigned long long ld64_coh_p(const unsigned long long* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -563,10 +579,12 @@ __global__ __launch_bounds__(kPThreads) void prefill_attn_kernel(LayerArgs a, Pr
   const int n = w.n, nrb = w.nrb;
   const int Hq = a.H_q, Hkv = a.H_kv;
 
-  if (tid == 0) s_id = addi_coh_p(&w.sync[0], 1);
+  if (tid == 0) s_id = prefill_ticket(w, S, nrb);
   __syncthreads();
   const int id = s_id;
-  const int s = id % S;  // token-block major: a chain predecessor always has a lower id
+  // token-block major: a chain predecessor always holds an earlier ticket of
+  // the same queue, so it is already running
+  const int s = id % S;
   const int I = id / S;
   const int b = s / Hkv, h = s - b * Hkv;
   const int len0 = a.seg_len[s];
@@ -1063,17 +1081,7 @@ __global__ __launch_bounds__(kPThreadsWS) void prefill_attn_ws_kernel(LayerArgs 
   const int Hq = a.H_q, Hkv = a.H_kv;
 
   if (tid == 0) {
-    if (S % kXcds == 0) {
-      // One ticket queue per XCD (workgroups go to the XCDs in turn): queue x
-      // serves the segments s = x mod kXcds, token-block major, so that the
-      // token blocks of a segment share one L2 and its K and V are fetched
-      // from below it once.
-      const int x = (int)(blockIdx.x % kXcds), per = S / kXcds;
-      const int t = addi_coh_p(&w.sync[2 + S * nrb + x], 1);
-      s_id = (t / per) * S + x + kXcds * (t % per);
-    } else {
-      s_id = addi_coh_p(&w.sync[0], 1);
-    }
+    s_id = prefill_ticket(w, S, nrb);
     s_seq = (uint32_t)ldi_coh_p(&w.glob[kGlobSeq]) + 1u;  // this call's number
   }
   __syncthreads();

@@ -57,6 +57,9 @@ def test_prefill_per_xcd_ticket_queues():
     _run(config("1b-prefill", B=4, H_q=8, H_kv=2, D=256, n_total=300, chunk=150))
     _run(config("1b-prefill", B=2, H_q=16, H_kv=8, D=256, n_total=200, chunk=100, len_kind="lognormal",
                 len_mean=120.0, len_min=16, len_max=400, nominal=400, lam_p0=0.15))
+    # the lock-step kernel: head dim 128 (group 3), and group 8 at head dim 64
+    _run(config("1b-prefill", B=1, H_q=24, H_kv=8, d=128, D=256, n_total=160, chunk=80))
+    _run(config("1b-prefill", B=1, H_q=64, H_kv=8, D=256, n_total=160, chunk=80))
 
 
 def test_prefill_single_token_calls():
