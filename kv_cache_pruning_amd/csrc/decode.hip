@@ -292,6 +292,18 @@ __device__ __forceinline__ void store_query(const DecodeWs& w, int64_t i, float 
   }
 }
 
+constexpr int kMapSegs = 2048;   // segments whose records go through LDS at most
+constexpr int kMapTiles = 4096;  // tiles whose segment is looked up in LDS at most
+
+// Dynamic LDS of the token launch: only the map workgroup uses it, and every
+// workgroup of the launch allocates it, so it is sized by this layer's
+// segments and tile bound rather than by the largest tables.
+static size_t token_map_lds(int S, int64_t max_tiles) {
+  const size_t segs = (size_t)std::min(S, kMapSegs);
+  const size_t tiles = (size_t)std::min<int64_t>(max_tiles, kMapTiles);
+  return segs * (sizeof(int64_t) + 2 * sizeof(int)) + tiles * sizeof(int);
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs karg) {
   const DecodeKArgs& K = *(const DecodeKArgs*)__builtin_amdgcn_kernarg_segment_ptr();
@@ -310,11 +322,14 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
   __shared__ float s_red[NT][8];
   __shared__ float s_cs[HALF], s_sn[HALF];
   __shared__ int s_scan[NT / 64 + 1];
-  constexpr int kMapSegs = 2048;      // segments whose records go through LDS
-  constexpr int kMapTiles = 4096;     // tiles whose segment is looked up in LDS
-  __shared__ int s_seg[kMapTiles];    // tile -> segment
-  __shared__ int s_first[kMapSegs], s_len[kMapSegs];
-  __shared__ int64_t s_off[kMapSegs];
+  // the map workgroup's tables, in LDS sized by the launch (token_map_lds):
+  // the segments' offsets, first tiles and lengths, and tile -> segment
+  extern __shared__ __attribute__((aligned(16))) int64_t s_map[];
+  const int mapSegs = min(S, kMapSegs), mapTiles = min(w.max_tiles, kMapTiles);
+  int64_t* const s_off = s_map;
+  int* const s_first = reinterpret_cast<int*>(s_off + mapSegs);
+  int* const s_len = s_first + mapSegs;
+  int* const s_seg = s_len + mapSegs;
 
   if (blockIdx.x == 0) {
     // ---- the tile records of this step, from the lengths at its start: a
@@ -353,7 +368,7 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
     int total;
     int run = block_exclusive_scan<NT>(mine, s_scan, &total);
     const bool bad = __syncthreads_or(badl) != 0;
-    if (S <= kMapSegs && total <= kMapTiles) {
+    if (S <= mapSegs && total <= mapTiles) {
       // the tile -> segment table and the segments' first tile, length and
       // offset into LDS, then the records written evenly by every thread
 #pragma unroll
@@ -1469,9 +1484,10 @@ static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Contr
                               int32_t* kept, hipStream_t st) {
   const int twg = decode_tile_entries(D, G, BF16);
   const DecodeKArgs k{a, w, ctl, tau, kept, twg};
-  hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B * kTokParts + 1), dim3(kTokThreads), 0, st, k);
   const int64_t mt = decode_max_tiles(a, twg);
   if (mt > (1 << 30)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B * kTokParts + 1), dim3(kTokThreads),
+                     token_map_lds(a.B * a.H_kv, mt), st, k);
   const int grid = (int)mt;
   if constexpr (BF16) {
     if (compact) {
