@@ -267,6 +267,62 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
   const int Hkv = a.H_kv, Hq = a.H_q;
   const int C3 = 3 * Hkv;
   const int Dm = a.D_model;
+  const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q);
+  const uint16_t* Kin = reinterpret_cast<const uint16_t*>(a.k);
+  const uint16_t* Vin = reinterpret_cast<const uint16_t*>(a.v);
+  __shared__ int64_t s_dst[kPTok * kMaxHkv];  // (token, KV head) -> cache row of its append, -1: none
+
+  // ---- every load that waits on no other phase, issued first so that their
+  // round trips overlap the RoPE table and the projection: the first batch of
+  // queries, the key row and segment words of item (token, KV head) = tid,
+  // the first batch of values
+  constexpr int QB = 4;  // query items per thread and batch
+  constexpr int VB = 4;  // value items per thread and batch
+  const int nitem = kPTok * Hq * (CH / 2);
+  const int nkv = kPTok * Hkv;
+  const int nv = nkv * CH;
+  u32x4 qlo[QB], qhi[QB];
+  auto load_q = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < QB; ++u) {
+      const int e = min(e0 + u * kTT + tid, nitem - 1);
+      const int c = e % (CH / 2);
+      const int rest = e / (CH / 2);
+      const int hd = rest % Hq, tt = rest / Hq;
+      const int tkc = min(tok0 + tt, NT - 1);
+      const int64_t qin = (io_row(w, tkc) * Hq + hd) * D + 8 * c;
+      qlo[u] = *reinterpret_cast<const u32x4*>(Q + qin);
+      qhi[u] = *reinterpret_cast<const u32x4*>(Q + qin + HALF);
+    }
+  };
+  load_q(0);
+  u32x4 kraw[CH];
+  int kl0 = 0, kcap = 0, knq = 0;
+  int64_t koff = 0;
+  auto load_key = [&](int e) {
+    const int tt = e / Hkv, h = e - tt * Hkv;
+    const int tkc = min(tok0 + tt, NT - 1);
+    const int b = tkc / n, s = b * Hkv + h;
+    kl0 = a.seg_len[s];
+    kcap = a.seg_cap[s];
+    koff = a.seg_off[s];
+    knq = seq_n(w, b);
+    const int64_t base = (io_row(w, tkc) * Hkv + h) * D;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) kraw[c] = *reinterpret_cast<const u32x4*>(Kin + base + 8 * c);
+  };
+  if (tid < nkv) load_key(tid);
+  u32x4 vv[VB];
+  auto load_v = [&](int e0) {
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+      const int e = min(e0 + u * kTT + tid, nv - 1);
+      const int c = e % CH, rest = e / CH;
+      const int h = rest % Hkv, tt = rest / Hkv;
+      vv[u] = *reinterpret_cast<const u32x4*>(Vin + (io_row(w, min(tok0 + tt, NT - 1)) * Hkv + h) * D + 8 * c);
+    }
+  };
+  load_v(0);
 
   for (int i = tid; i < kPTok * kMaxZ; i += kTT) (&s_z[0][0])[i] = 0.0f;
   for (int e = tid; e < kPTok * HALF; e += kTT) {
@@ -319,54 +375,48 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
   }
   __syncthreads();
 
-  // ---- gates and the append of the key gate
-  for (int e = tid; e < kPTok * Hkv; e += kTT) {
+  // ---- gates and the append of the key gate; the cache row of every
+  // (token, KV head) append goes to LDS for the value append
+  for (int e = tid; e < nkv; e += kTT) {
+    if (e != tid) load_key(e);  // more items than threads (H_kv > kTT / kPTok)
     const int tt = e / Hkv, h = e - tt * Hkv;
     const int tk = tok0 + tt;
-    if (tk >= NT) continue;
-    const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
-    const float lq = log_sigmoid(s_z[tt][h] + a.b_dec[h]);
-    const float lkk = log_sigmoid(s_z[tt][Hkv + h] + a.b_dec[Hkv + h]);
-    const float lb = log_sigmoid(s_z[tt][2 * Hkv + h] + a.b_dec[2 * Hkv + h]);
-    w.gl[2 * ((int64_t)tk * Hkv + h) + 0] = lq;
-    w.gl[2 * ((int64_t)tk * Hkv + h) + 1] = lb;
-    const int len0 = a.seg_len[s];
-    const int nq = seq_n(w, b);
-    if ((int64_t)len0 + nq <= a.seg_cap[s]) {
-      if (t < nq) a.lk[a.seg_off[s] + len0 + t] = lkk;
-    } else if (t == 0) {
-      atomicOr(a.status, 1);
+    int64_t dst = -1;
+    if (tk < NT) {
+      const int b = tk / n, t = tk - b * n;
+      const float lq = log_sigmoid(s_z[tt][h] + a.b_dec[h]);
+      const float lkk = log_sigmoid(s_z[tt][Hkv + h] + a.b_dec[Hkv + h]);
+      const float lb = log_sigmoid(s_z[tt][2 * Hkv + h] + a.b_dec[2 * Hkv + h]);
+      w.gl[2 * ((int64_t)tk * Hkv + h) + 0] = lq;
+      w.gl[2 * ((int64_t)tk * Hkv + h) + 1] = lb;
+      if ((int64_t)kl0 + knq <= kcap) {
+        if (t < knq) {
+          dst = koff + kl0 + t;
+          a.lk[dst] = lkk;
+        }
+      } else if (t == 0) {
+        atomicOr(a.status, 1);
+      }
     }
+    s_dst[e] = dst;
   }
+  if (nkv > kTT && tid < nkv) load_key(tid);  // the loop above moved on to later items
+  __syncthreads();  // s_dst complete before the value append reads other items' rows
 
   // ---- rotated queries (bf16 copy); chunk c pairs dims [8c, 8c+8) with
   // [HALF+8c, HALF+8c+8).  Items go in batches of QB per thread with every
   // load of a batch issued before any is used.
   {
-    constexpr int QB = 8;
-    const uint16_t* Q = reinterpret_cast<const uint16_t*>(a.q);
-    const int nitem = kPTok * Hq * (CH / 2);
     for (int e0 = 0; e0 < nitem; e0 += kTT * QB) {
-      u32x4 lo[QB], hi[QB];
-      int64_t base[QB];
-#pragma unroll
-      for (int u = 0; u < QB; ++u) {
-        const int e = min(e0 + u * kTT + tid, nitem - 1);
-        const int c = e % (CH / 2);
-        const int rest = e / (CH / 2);
-        const int hd = rest % Hq, tt = rest / Hq;
-        const int tkc = min(tok0 + tt, NT - 1);
-        base[u] = ((int64_t)tkc * Hq + hd) * D + 8 * c;
-        const int64_t qin = (io_row(w, tkc) * Hq + hd) * D + 8 * c;
-        lo[u] = *reinterpret_cast<const u32x4*>(Q + qin);
-        hi[u] = *reinterpret_cast<const u32x4*>(Q + qin + HALF);
-      }
+      if (e0 > 0) load_q(e0);  // the first batch was loaded at the start
 #pragma unroll
       for (int u = 0; u < QB; ++u) {
         const int e = e0 + u * kTT + tid;
         const int c = e % (CH / 2);
-        const int tt = (e / (CH / 2)) / Hq;
+        const int rest = e / (CH / 2);
+        const int hd = rest % Hq, tt = rest / Hq;
         if (e >= nitem || tok0 + tt >= NT) continue;
+        const int64_t qbase = ((int64_t)(tok0 + tt) * Hq + hd) * D + 8 * c;
         uint32_t olo[4], ohi[4];
 #pragma unroll
         for (int v = 0; v < 8; v += 2) {
@@ -374,37 +424,29 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
 #pragma unroll
           for (int v2 = 0; v2 < 2; ++v2) {
             const int i = 8 * c + v + v2;
-            const float xl = u32x4_bf16(lo[u], v + v2), xh = u32x4_bf16(hi[u], v + v2);
+            const float xl = u32x4_bf16(qlo[u], v + v2), xh = u32x4_bf16(qhi[u], v + v2);
             rl[v2] = fmaf(xl, s_cos[tt][i], -xh * s_sin[tt][i]);
             rh[v2] = fmaf(xh, s_cos[tt][i], xl * s_sin[tt][i]);
           }
           olo[v / 2] = pack_bf16(rl[0], rl[1]);
           ohi[v / 2] = pack_bf16(rh[0], rh[1]);
         }
-        *reinterpret_cast<u32x4*>(w.qbf + base[u]) = u32x4{olo[0], olo[1], olo[2], olo[3]};
-        *reinterpret_cast<u32x4*>(w.qbf + base[u] + HALF) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
+        *reinterpret_cast<u32x4*>(w.qbf + qbase) = u32x4{olo[0], olo[1], olo[2], olo[3]};
+        *reinterpret_cast<u32x4*>(w.qbf + qbase + HALF) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
       }
     }
   }
 
   // ---- keys: normalise, rotate, round, append; values: append
   {
-    const uint16_t* Kin = reinterpret_cast<const uint16_t*>(a.k);
-    const uint16_t* Vin = reinterpret_cast<const uint16_t*>(a.v);
     uint16_t* Kc = reinterpret_cast<uint16_t*>(a.K);
     uint16_t* Vc = reinterpret_cast<uint16_t*>(a.V);
-    for (int e = tid; e < kPTok * Hkv; e += kTT) {
-      const int tt = e / Hkv, h = e - tt * Hkv;
-      const int tk = tok0 + tt;
-      if (tk >= NT) continue;
-      const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
-      const int len0 = a.seg_len[s];
-      const int nq = seq_n(w, b);
-      if (t >= nq || (int64_t)len0 + nq > a.seg_cap[s]) continue;
-      const int64_t base = (io_row(w, tk) * Hkv + h) * D;
-      u32x4 raw[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) raw[c] = *reinterpret_cast<const u32x4*>(Kin + base + 8 * c);
+    for (int e = tid; e < nkv; e += kTT) {
+      if (e != tid) load_key(e);  // the first item's row was loaded at the start
+      const int tt = e / Hkv;
+      const int64_t dst = s_dst[e];
+      if (dst < 0) continue;
+      const u32x4* raw = kraw;
       float ss = 0.0f;
 #pragma unroll
       for (int c = 0; c < CH; ++c)
@@ -414,7 +456,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
           ss = fmaf(xv, xv, ss);
         }
       const float inv = 1.0f / fmaxf(sqrtf(ss), 1e-12f);
-      const int64_t dst = (a.seg_off[s] + len0 + t) * D;
+      const int64_t kd = dst * D;
 #pragma unroll
       for (int c = 0; c < CH / 2; ++c) {
         uint32_t olo[4], ohi[4];
@@ -432,33 +474,20 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
           olo[u / 2] = pack_bf16(rl[0], rl[1]);
           ohi[u / 2] = pack_bf16(rh[0], rh[1]);
         }
-        *reinterpret_cast<u32x4*>(Kc + dst + 8 * c) = u32x4{olo[0], olo[1], olo[2], olo[3]};
-        *reinterpret_cast<u32x4*>(Kc + dst + HALF + 8 * c) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
+        *reinterpret_cast<u32x4*>(Kc + kd + 8 * c) = u32x4{olo[0], olo[1], olo[2], olo[3]};
+        *reinterpret_cast<u32x4*>(Kc + kd + HALF + 8 * c) = u32x4{ohi[0], ohi[1], ohi[2], ohi[3]};
       }
     }
-    constexpr int VB = 4;
-    const int nv = kPTok * Hkv * CH;
     for (int e0 = 0; e0 < nv; e0 += kTT * VB) {
-      u32x4 vv[VB];
-#pragma unroll
-      for (int u = 0; u < VB; ++u) {
-        const int e = min(e0 + u * kTT + tid, nv - 1);
-        const int c = e % CH, rest = e / CH;
-        const int h = rest % Hkv, tt = rest / Hkv;
-        vv[u] = *reinterpret_cast<const u32x4*>(Vin + (io_row(w, min(tok0 + tt, NT - 1)) * Hkv + h) * D + 8 * c);
-      }
+      if (e0 > 0) load_v(e0);  // the first batch was loaded at the start
 #pragma unroll
       for (int u = 0; u < VB; ++u) {
         const int e = e0 + u * kTT + tid;
-        const int c = e % CH, rest = e / CH;
-        const int h = rest % Hkv, tt = rest / Hkv;
-        const int tk = tok0 + tt;
-        if (e >= nv || tk >= NT) continue;
-        const int b = tk / n, t = tk - b * n, s = b * Hkv + h;
-        const int len0 = a.seg_len[s];
-        const int nq = seq_n(w, b);
-        if (t >= nq || (int64_t)len0 + nq > a.seg_cap[s]) continue;
-        *reinterpret_cast<u32x4*>(Vc + (a.seg_off[s] + len0 + t) * D + 8 * c) = vv[u];
+        if (e >= nv) continue;
+        const int c = e % CH;
+        const int64_t dst = s_dst[e / CH];  // item (token, KV head) = e / CH
+        if (dst < 0) continue;
+        *reinterpret_cast<u32x4*>(Vc + dst * D + 8 * c) = vv[u];
       }
     }
   }
