@@ -257,6 +257,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
   constexpr int HALF = D / 2;
   constexpr int CH = D / 8;  // 16-byte chunks per head row
   __shared__ float s_z[kPTok][kMaxZ];
+  __shared__ float s_zp[kTT / 64][kPTok][48];  // the waves' partial z tiles of one three-tile group
     __shared__ float s_cos[kPTok][HALF];
   __shared__ float s_sin[kPTok][HALF];
   const int tid = threadIdx.x;
@@ -296,9 +297,16 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
     }
   };
   load_q(0);
+  constexpr bool kRowsEarly = D == 64;  // at head dim 128 the rows would not fit beside the projection
   u32x4 kraw[CH];
   int kl0 = 0, kcap = 0, knq = 0;
   int64_t koff = 0;
+  auto load_key_rows = [&](int e) {
+    const int tt = e / Hkv, h = e - tt * Hkv;
+    const int64_t base = (io_row(w, min(tok0 + tt, NT - 1)) * Hkv + h) * D;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) kraw[c] = *reinterpret_cast<const u32x4*>(Kin + base + 8 * c);
+  };
   auto load_key = [&](int e) {
     const int tt = e / Hkv, h = e - tt * Hkv;
     const int tkc = min(tok0 + tt, NT - 1);
@@ -307,9 +315,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
     kcap = a.seg_cap[s];
     koff = a.seg_off[s];
     knq = seq_n(w, b);
-    const int64_t base = (io_row(w, tkc) * Hkv + h) * D;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) kraw[c] = *reinterpret_cast<const u32x4*>(Kin + base + 8 * c);
+    if constexpr (kRowsEarly) load_key_rows(e);
   };
   if (tid < nkv) load_key(tid);
   u32x4 vv[VB];
@@ -336,18 +342,24 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
   }
   __syncthreads();
 
-  // ---- z = x [W_dec | W_dn]: A = x rows (tokens), B = W^T rows.  Each wave
-  // takes chunks of 8 k steps (256 columns of x); the weight fragments of up
-  // to three 16-column tiles are loaded together with the chunk's x.
+  // ---- z = x [W_dec | W_dn]: A = x rows (tokens), B = W^T rows.  For each
+  // group of three 16-column tiles, each wave takes chunks of 8 k steps (256
+  // columns of x), loading the weight fragments with the chunk's x; the waves'
+  // partial tiles meet in LDS and are summed in a fixed order (LDS float
+  // atomics from eight waves on the same entries cost a third of the kernel).
   {
     constexpr int KCH = 8;
+    constexpr int NW = kTT / 64;
     const uint16_t* X = reinterpret_cast<const uint16_t*>(a.x);
     const int nks = (Dm + 31) / 32;
     const int ntile = w.cp / 16;
     const int64_t xrow = io_row(w, min(tok0 + c16, NT - 1)) * Dm;
     const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
-    for (int k0 = wv * KCH; k0 < nks; k0 += (kTT / 64) * KCH) {
-      for (int nt0 = 0; nt0 < ntile; nt0 += 3) {
+    for (int nt0 = 0; nt0 < ntile; nt0 += 3) {  // the same count in every wave: the barriers below match
+      f32x4 acc[3];
+#pragma unroll
+      for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k0 = wv * KCH; k0 < nks; k0 += NW * KCH) {
         u32x4 av[KCH], bv[3][KCH];
 #pragma unroll
         for (int u = 0; u < KCH; ++u) {
@@ -362,18 +374,27 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
         for (int u = 0; u < KCH; ++u)
           if (32 * (k0 + u) + 8 * g >= Dm) av[u] = zero4;  // past the end of x (Dm is a multiple of 8)
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-          if (nt0 + q >= ntile) break;
-          f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < 3; ++q)
 #pragma unroll
-          for (int u = 0; u < KCH; ++u) acc = mfma_bf16(av[u], bv[q][u], acc);
+          for (int u = 0; u < KCH; ++u) acc[q] = mfma_bf16(av[u], bv[q][u], acc[q]);
+      }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) atomicAdd(&s_z[4 * g + i][16 * (nt0 + q) + c16], acc[i]);
+      for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s_zp[wv][4 * g + i][16 * q + c16] = acc[q][i];
+      __syncthreads();
+      for (int e = tid; e < kPTok * 48; e += kTT) {
+        const int row = e / 48, col = e - row * 48;
+        if (16 * nt0 + col < w.cp) {
+          float sum = 0.0f;
+#pragma unroll
+          for (int w2 = 0; w2 < NW; ++w2) sum += s_zp[w2][row][col];
+          s_z[row][16 * nt0 + col] = sum;
         }
       }
+      __syncthreads();
     }
   }
-  __syncthreads();
 
   // ---- gates and the append of the key gate; the cache row of every
   // (token, KV head) append goes to LDS for the value append
@@ -442,7 +463,7 @@ __global__ __launch_bounds__(kTT) void prefill_token_kernel(LayerArgs a, Prefill
     uint16_t* Kc = reinterpret_cast<uint16_t*>(a.K);
     uint16_t* Vc = reinterpret_cast<uint16_t*>(a.V);
     for (int e = tid; e < nkv; e += kTT) {
-      if (e != tid) load_key(e);  // the first item's row was loaded at the start
+      if (e != tid || !kRowsEarly) load_key_rows(e);  // at head dim 64 the first item's row came early
       const int tt = e / Hkv;
       const int64_t dst = s_dst[e];
       if (dst < 0) continue;
