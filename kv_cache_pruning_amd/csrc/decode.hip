@@ -292,6 +292,9 @@ __device__ __forceinline__ void store_query(const DecodeWs& w, int64_t i, float 
   }
 }
 
+// Tile numbering order: segments of at least kLongSegTiles tiles first, then
+// those of at least two, then the one-tile segments.
+constexpr int kLongSegTiles = 8;
 constexpr int kMapSegs = 2048;   // segments whose records go through LDS at most
 constexpr int kMapTiles = 4096;  // tiles whose segment is looked up in LDS at most
 
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
     const int sb = min(S, tid * per), se = min(S, sb + per);
     int lenr[MP], capr[MP];
     int64_t offr[MP];
-    int mine = 0, badl = 0;
+    int mine = 0, mineL = 0, mineM = 0, badl = 0;
     if (per <= MP) {
 #pragma unroll
       for (int k = 0; k < MP; ++k) {
@@ -354,19 +357,47 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
 #pragma unroll
       for (int k = 0; k < MP; ++k) {
         if (sb + k < se) {
-          mine += tiles_of(lenr[k], twg);
+          const int nt = tiles_of(lenr[k], twg);
+          mine += nt;
+          mineL += nt >= kLongSegTiles ? nt : 0;
+          mineM += (nt >= 2 && nt < kLongSegTiles) ? nt : 0;
           badl |= (lenr[k] < 0 || lenr[k] > capr[k]) ? 1 : 0;
         }
       }
     } else {
       for (int s = sb; s < se; ++s) {
         const int len = a.seg_len[s];
-        mine += tiles_of(len, twg);
+        const int nt = tiles_of(len, twg);
+        mine += nt;
+        mineL += nt >= kLongSegTiles ? nt : 0;
+        mineM += (nt >= 2 && nt < kLongSegTiles) ? nt : 0;
         badl |= (len < 0 || len > a.seg_cap[s]) ? 1 : 0;
       }
     }
-    int total;
-    int run = block_exclusive_scan<NT>(mine, s_scan, &total);
+    // Longer segments are numbered first: their tiles start in the first
+    // round, and the merge that ends each of them overlaps the shorter
+    // segments' tiles instead of ending the launch.  A segment's tiles stay
+    // consecutive, in segment order within each class.
+    int total, totalL, totalM;
+    const int run0 = block_exclusive_scan<NT>(mine, s_scan, &total);
+    int runL = block_exclusive_scan<NT>(mineL, s_scan, &totalL);
+    const int runM0 = block_exclusive_scan<NT>(mineM, s_scan, &totalM);
+    int runM = totalL + runM0;
+    int runS = totalL + totalM + (run0 - runL - runM0);  // one-tile segments of the threads before
+    auto first_of = [&](int nt) {
+      int f;
+      if (nt >= kLongSegTiles) {
+        f = runL;
+        runL += nt;
+      } else if (nt >= 2) {
+        f = runM;
+        runM += nt;
+      } else {
+        f = runS;
+        runS += nt;
+      }
+      return f;
+    };
     const bool bad = __syncthreads_or(badl) != 0;
     if (S <= mapSegs && total <= mapTiles) {
       // the tile -> segment table and the segments' first tile, length and
@@ -375,11 +406,11 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
       for (int k = 0; k < MP; ++k) {
         if (sb + k < se) {
           const int nt = tiles_of(lenr[k], twg);
-          s_first[sb + k] = run;
+          const int f = first_of(nt);
+          s_first[sb + k] = f;
           s_len[sb + k] = lenr[k];
           s_off[sb + k] = offr[k];
-          for (int t = 0; t < nt; ++t) s_seg[run + t] = sb + k;
-          run += nt;
+          for (int t = 0; t < nt; ++t) s_seg[f + t] = sb + k;
         }
       }
       __syncthreads();
@@ -396,11 +427,11 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
       for (int k = 0; k < MP; ++k) {
         if (sb + k < se) {
           const int nt = tiles_of(lenr[k], twg);
-          for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {
-            w.map[2 * (run + t) + 0] = make_int4(sb + k, t, lenr[k], nt);
-            w.map[2 * (run + t) + 1] = make_int4(run, (int)(uint32_t)(offr[k] & 0xffffffff), (int)(offr[k] >> 32), 0);
+          const int f = first_of(nt);
+          for (int t = 0; t < nt && f + t < w.max_tiles; ++t) {
+            w.map[2 * (f + t) + 0] = make_int4(sb + k, t, lenr[k], nt);
+            w.map[2 * (f + t) + 1] = make_int4(f, (int)(uint32_t)(offr[k] & 0xffffffff), (int)(offr[k] >> 32), 0);
           }
-          run += nt;
         }
       }
     } else {
@@ -408,11 +439,11 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
         const int len = a.seg_len[s];
         const int nt = tiles_of(len, twg);
         const int64_t off = a.seg_off[s];
-        for (int t = 0; t < nt && run + t < w.max_tiles; ++t) {
-          w.map[2 * (run + t) + 0] = make_int4(s, t, len, nt);
-          w.map[2 * (run + t) + 1] = make_int4(run, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+        const int f = first_of(nt);
+        for (int t = 0; t < nt && f + t < w.max_tiles; ++t) {
+          w.map[2 * (f + t) + 0] = make_int4(s, t, len, nt);
+          w.map[2 * (f + t) + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
         }
-        run += nt;
       }
     }
     for (int s = sb; s < se; ++s) {
