@@ -603,11 +603,14 @@ constexpr int tail_opt() {  // outputs (g, i) per thread
 }
 
 // After the wave partials and live counts are in LDS: the tile's partial per
-// output (g, i) in registers; for a segment of several tiles the live count
-// (COMPACT; the first tile's is its inclusive prefix) and the partial are
-// published, and the tile that arrives last is marked as the one that merges
-// them (L.flag); with COMPACT, the look-back over the earlier tiles of the
-// segment gives the survivors' destination (L.pre).  Ends with a barrier.
+// output (g, i) in registers; for a segment of several tiles the partial is
+// published and marks the tile that merges them (L.flag).  Without COMPACT
+// that is the tile that arrives last (an arrival counter).  With COMPACT the
+// live count (the first tile's is its inclusive prefix) is published once the
+// partial is visible, the look-back over the earlier tiles of the segment
+// gives the survivors' destination (L.pre), and the segment's last tile
+// merges: its look-back sees every earlier tile's count, so their partials
+// are visible too.  Ends with a barrier.
 template <int D, int G, bool COMPACT>
 __device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInfo& t, TailLds<D, G>& L, int count,
                                              float* Mo, float* Lo, float* Oo) {
@@ -638,8 +641,6 @@ __device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInf
   }
   if (!t.single) {
     const int64_t prow = (int64_t)(t.pbase + t.kt);
-    if (COMPACT && tid == 0)
-      st64_coh(&K.ctl.dec_state[prow], (unsigned long long)((count << 2) | (t.kt == 0 ? 2 : 1)));
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
       const int idx = u * NT + tid;
@@ -655,7 +656,14 @@ __device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInf
     }
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     __syncthreads();
-    if (tid == 0) L.flag = (add_coh(&w.cnt[t.seg], 1) == t.ntile - 1);
+    if constexpr (COMPACT) {
+      if (tid == 0) {
+        st64_coh(&K.ctl.dec_state[prow], (unsigned long long)((count << 2) | (t.kt == 0 ? 2 : 1)));
+        L.flag = t.kt == t.ntile - 1;
+      }
+    } else {
+      if (tid == 0) L.flag = (add_coh(&w.cnt[t.seg], 1) == t.ntile - 1);
+    }
   }
   if (!COMPACT || t.single || t.kt == 0) {
     if (tid == 0) L.pre = 0;
@@ -696,13 +704,16 @@ __device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInf
 // The segment's output (by the tile that merges: every tile's partial, this
 // one's in registers when it is the only one, the token's own term, the
 // output gate), then the new entry and the new length (by the segment's last
-// tile when compacting, else by the merging tile).  ml: LDS scratch of mlc
-// tiles' (max, sum) per head, free by now.
-template <int D, int G, bool BF16, bool COMPACT>
-__device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo& t, TailLds<D, G>& L, float* ml,
-                                            int mlc, bool combines, int npos, float* Mo, float* Lo, float* Oo) {
+// tile when compacting, else by the merging tile).  Every load the merge
+// needs (the first TC tiles' partials, the token's value, u, W_up, the rotated
+// query and key) is issued before any is used, so a merge of up to TC tiles
+// waits on memory once.
+template <int D, int G, bool BF16, bool COMPACT, int TC0>
+__device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo& t, TailLds<D, G>& L, bool combines,
+                                            int npos, float* Mo, float* Lo, float* Oo) {
   constexpr int NT = kTileThreads, OPT = tail_opt<D, G>();
   constexpr int EB = BF16 ? 2 : 4;
+  constexpr int TC = TC0 / OPT > 2 ? TC0 / OPT : 2;  // tiles whose partials are loaded together
   const LayerArgs& a = K.a;
   const DecodeWs& w = K.w;
   const int tid = threadIdx.x;
@@ -711,6 +722,54 @@ __device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo
   const int Hkv = a.H_kv, Hq = a.H_q;
   const int seg = t.seg, b = t.b, h = t.h;
   if (combines) {
+    // the partials (max, sum, weighted V) of tiles p0 .. p0 + TC - 1 for this
+    // thread's outputs (indices past the last tile reload it; they are skipped)
+    float xm[TC][OPT], xl[TC][OPT], xo[TC][OPT];
+    auto load_pass = [&](int p0) {
+#pragma unroll
+      for (int p = 0; p < TC; ++p) {
+        const int64_t tp = t.pbase + min(p0 + p, t.ntile - 1);
+#pragma unroll
+        for (int u = 0; u < OPT; ++u) {
+          const int idx = min(u * NT + tid, G * D - 1);
+          const int g = idx / D;
+          xo[p][u] = ld_coh(w.part_o + (tp * G + g) * D + (idx - g * D));
+          xm[p][u] = ld_coh(w.part_ml + (tp * G + g) * 2 + 0);
+          xl[p][u] = ld_coh(w.part_ml + (tp * G + g) * 2 + 1);
+        }
+      }
+    };
+    float M[OPT], Ls[OPT], O[OPT];
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      M[u] = kNegInf;
+      Ls[u] = 0.0f;
+      O[u] = 0.0f;
+    }
+    auto merge_pass = [&](int p0) {
+      const int tn = min(TC, t.ntile - p0);
+#pragma unroll
+      for (int u = 0; u < OPT; ++u) {
+        float Mn = M[u];
+#pragma unroll
+        for (int p = 0; p < TC; ++p) Mn = (p < tn) ? fmaxf(Mn, xm[p][u]) : Mn;
+        const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
+        const float rs = __builtin_amdgcn_exp2f(M[u] - Ms);
+        float l = Ls[u] * rs, o = O[u] * rs;
+#pragma unroll
+        for (int p = 0; p < TC; ++p) {
+          if (p < tn) {
+            const float wgt = __builtin_amdgcn_exp2f(xm[p][u] - Ms);
+            l = fmaf(xl[p][u], wgt, l);
+            o = fmaf(xo[p][u], wgt, o);
+          }
+        }
+        M[u] = Mn;
+        Ls[u] = l;
+        O[u] = o;
+      }
+    };
+    if (!t.single) load_pass(0);
     // what the merge needs of the token: its value, u = x W_dn (the partials
     // added, into LDS), this thread's columns of W_up, and its logit against
     // its own key per head (wave 0, from the fp32 rotated query and key)
@@ -731,59 +790,25 @@ __device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo
     if (wv == 0) {
       const float qs2 = a.scale * kLog2e;
       const float* kt = w.tkey + (int64_t)seg * D;
+      float e[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const float* qt = w.tq + ((int64_t)b * Hq + h * G + g) * D;
-        float e = 0.0f;
+        e[g] = 0.0f;
 #pragma unroll
-        for (int i = lane; i < D; i += 64) e = fmaf(qt[i], kt[i], e);
-        e = wave_sum(e);
-        if (lane == 0) L.es[g] = e * qs2;
+        for (int i = lane; i < D; i += 64) e[g] = fmaf(qt[i], kt[i], e[g]);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float eg = wave_sum(e[g]);
+        if (lane == 0) L.es[g] = eg * qs2;
       }
     }
     if (!t.single) {
-      // every tile's (max, sum) per head through LDS, then the weighted V in
-      // passes of TC tiles
-      constexpr int TC = 16;  // tiles per pass, loads in flight together
-      float M[OPT], Ls[OPT], O[OPT];
-#pragma unroll
-      for (int u = 0; u < OPT; ++u) {
-        M[u] = kNegInf;
-        Ls[u] = 0.0f;
-        O[u] = 0.0f;
-      }
-      for (int t0 = 0; t0 < t.ntile; t0 += mlc) {
-        const int tn = min(mlc, t.ntile - t0);
-        __syncthreads();
-        for (int j = tid; j < tn * G * 2; j += NT) ml[j] = ld_coh(w.part_ml + (int64_t)(t.pbase + t0) * G * 2 + j);
-        __syncthreads();
-#pragma unroll
-        for (int u = 0; u < OPT; ++u) {
-          const int idx = min(u * NT + tid, G * D - 1);
-          const int g = idx / D;
-          const int i = idx - g * D;
-          float Mn = M[u];
-          for (int q = 0; q < tn; ++q) Mn = fmaxf(Mn, ml[(q * G + g) * 2]);
-          const float Ms = (Mn == kNegInf) ? 0.0f : Mn;
-          const float rs = __builtin_amdgcn_exp2f(M[u] - Ms);
-          Ls[u] *= rs;
-          O[u] *= rs;
-          for (int p0 = 0; p0 < tn; p0 += TC) {
-            float po[TC];
-#pragma unroll
-            for (int p = 0; p < TC; ++p)
-              po[p] = ld_coh(w.part_o + ((int64_t)(t.pbase + t0 + min(p0 + p, tn - 1)) * G + g) * D + i);
-#pragma unroll
-            for (int p = 0; p < TC; ++p) {
-              if (p0 + p < tn) {
-                const float wgt = __builtin_amdgcn_exp2f(ml[((p0 + p) * G + g) * 2] - Ms);
-                Ls[u] = fmaf(ml[((p0 + p) * G + g) * 2 + 1], wgt, Ls[u]);
-                O[u] = fmaf(po[p], wgt, O[u]);
-              }
-            }
-          }
-          M[u] = Mn;
-        }
+      merge_pass(0);
+      for (int p0 = TC; p0 < t.ntile; p0 += TC) {
+        load_pass(p0);
+        merge_pass(p0);
       }
 #pragma unroll
       for (int u = 0; u < OPT; ++u) {
@@ -1126,8 +1151,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArg
     }
     npos = P + count;
   }
-  constexpr int MLC = (kTileWaves * NGW * D) / (2 * G);  // tiles per chunk of the (max, sum) scratch
-  tile_finish<D, G, BF16, COMPACT>(K, t, L, &s_tp[0][0], MLC, combines, npos, Mo, Lo, Oo);
+  tile_finish<D, G, BF16, COMPACT, 4>(K, t, L, combines, npos, Mo, Lo, Oo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1216,7 +1240,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
     lamv = ld_at<float>(lamseg, (uint32_t)rl * 4);
     lkv = ld_at<float>(lkseg, (uint32_t)rl * 4);
   };
-  load_rows(t.kt);
+  if (t.single) load_rows(t.kt);
   // ---- the token as the B operand: column c16 < G is query head h G + c16
   // (high and low bf16 parts), column G the stored key, the rest zero
   u32x4 qh[KS], ql[KS];
@@ -1240,10 +1264,8 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
   const float row2 = (lq + lbt) * pc.inv_n2;
   if (!t.single) {
     __syncthreads();
-    if (L.kt != t.kt) {  // started out of order: this workgroup takes the ticket's tile
-      t.kt = L.kt;
-      load_rows(t.kt);
-    }
+    t.kt = L.kt;  // this workgroup takes the ticket's tile
+    load_rows(t.kt);
   }
   const int e0 = t.kt * TWG + wv * TW;             // the wave's first entry
   const int nvalid = min(max(len - e0, 0), TW);  // wave-uniform
@@ -1441,8 +1463,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
     }
     npos = P + count;
   }
-  constexpr int MLC = (kTileWaves * NI * VSTR) / (4 * 2 * G);  // tiles per chunk of the (max, sum) scratch
-  tile_finish<D, G, true, COMPACT>(K, t, L, reinterpret_cast<float*>(&s_v[0][0]), MLC, combines, npos, Mo, Lo, Oo);
+  tile_finish<D, G, true, COMPACT, 16>(K, t, L, combines, npos, Mo, Lo, Oo);
 }
 
 // ---------------------------------------------------------------------------
@@ -1521,11 +1542,8 @@ static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Contr
                      token_map_lds(a.B * a.H_kv, mt), st, k);
   const int grid = (int)mt;
   if constexpr (BF16) {
-    if (compact) {
-      hipLaunchKernelGGL((decode_tile_mf_kernel<D, G, true>), dim3(grid), dim3(kTileThreads), 0, st, k);
-    } else {
-      hipLaunchKernelGGL((decode_tile_mf_kernel<D, G, false>), dim3(grid), dim3(kTileThreads), 0, st, k);
-    }
+    auto kern = compact ? decode_tile_mf_kernel<D, G, true> : decode_tile_mf_kernel<D, G, false>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kTileThreads), 0, st, k);
   } else {
     if (compact) {
       hipLaunchKernelGGL((decode_tile_kernel<D, G, false, true>), dim3(grid), dim3(kTileThreads), 0, st, k);
