@@ -53,6 +53,7 @@
 // the XCDs without cache-wide write-back or invalidation).
 
 #include <algorithm>
+#include <atomic>
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -172,6 +173,7 @@ struct DecodeKArgs {
   float tau;
   int32_t* kept;
   int twg;
+  int resident;  // tile workgroups that fit on the GPU at once (0: unknown)
 };
 
 // ---------------------------------------------------------------------------
@@ -398,6 +400,12 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
       }
       return f;
     };
+    // A segment whose tiles all fall among the first K.resident records runs
+    // without tickets: those workgroups fit on the GPU together, and one that
+    // waits on a workgroup not yet started holds no slot that workgroup needs
+    // (the later, ticketed workgroups always finish).  Other segments of
+    // several tiles take per-segment tickets.
+    auto ticketed = [&](int f, int nt) { return (nt > 1 && (K.resident <= 0 || f + nt > K.resident)) ? 1 : 0; };
     const bool bad = __syncthreads_or(badl) != 0;
     if (S <= mapSegs && total <= mapTiles) {
       // the tile -> segment table and the segments' first tile, length and
@@ -419,8 +427,9 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
         const int f = s_first[sg];
         const int len = s_len[sg];
         const int64_t off = s_off[sg];
-        w.map[2 * t + 0] = make_int4(sg, t - f, len, tiles_of(len, twg));
-        w.map[2 * t + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+        const int nt = tiles_of(len, twg);
+        w.map[2 * t + 0] = make_int4(sg, t - f, len, nt);
+        w.map[2 * t + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), ticketed(f, nt));
       }
     } else if (per <= MP) {
 #pragma unroll
@@ -430,7 +439,8 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
           const int f = first_of(nt);
           for (int t = 0; t < nt && f + t < w.max_tiles; ++t) {
             w.map[2 * (f + t) + 0] = make_int4(sb + k, t, lenr[k], nt);
-            w.map[2 * (f + t) + 1] = make_int4(f, (int)(uint32_t)(offr[k] & 0xffffffff), (int)(offr[k] >> 32), 0);
+            w.map[2 * (f + t) + 1] =
+                make_int4(f, (int)(uint32_t)(offr[k] & 0xffffffff), (int)(offr[k] >> 32), ticketed(f, nt));
           }
         }
       }
@@ -442,7 +452,7 @@ __global__ __launch_bounds__(kTokThreads) void decode_token_kernel(DecodeKArgs k
         const int f = first_of(nt);
         for (int t = 0; t < nt && f + t < w.max_tiles; ++t) {
           w.map[2 * (f + t) + 0] = make_int4(s, t, len, nt);
-          w.map[2 * (f + t) + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), 0);
+          w.map[2 * (f + t) + 1] = make_int4(f, (int)(uint32_t)(off & 0xffffffff), (int)(off >> 32), ticketed(f, nt));
         }
       }
     }
@@ -1213,6 +1223,14 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
   const int4 m1 = w.map[2 * tile + 1];
   if (tile >= *w.ntiles) return;
   TileInfo t = tile_info(m0, m1, Hkv);
+  // A tile waits only on earlier tiles of its segment.  A segment whose
+  // records all lie among the first that fit on the GPU at once runs without
+  // tickets: a tile takes its record's rows at once.  Otherwise the workgroups
+  // of the segment take per-segment tickets: the one that arrives j-th takes
+  // tile j, so it waits only on workgroups that started earlier.  (Loading the
+  // record's rows first and again when the ticket differs read most rows
+  // twice: tiles of one segment reach the ticket in no particular order.)
+  const bool ticketed = m1.w != 0;
   const int len = t.len;
   const int b = t.b, h = t.h, seg = t.seg;
   char* const Kseg = reinterpret_cast<char*>(a.K) + t.off * RB;
@@ -1220,7 +1238,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
   const char* const lamseg = reinterpret_cast<const char*>(a.lam + t.off);
   const char* const lkseg = reinterpret_cast<const char*>(a.lk + t.off);
   const int relmax = max(len - 1, 0);
-  if (!t.single && tid == 0) L.kt = add_coh(&w.segtk[seg], 1);
+  if (ticketed && tid == 0) L.kt = add_coh(&w.segtk[seg], 1);
 
   // ---- cached entries, every load issued first: key rows as the A operand
   // (entry 16 blk + c16, dims 32 ks + 8 gq .. + 7), bias and key gate of
@@ -1240,7 +1258,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
     lamv = ld_at<float>(lamseg, (uint32_t)rl * 4);
     lkv = ld_at<float>(lkseg, (uint32_t)rl * 4);
   };
-  if (t.single) load_rows(t.kt);
+  if (!ticketed) load_rows(t.kt);
   // ---- the token as the B operand: column c16 < G is query head h G + c16
   // (high and low bf16 parts), column G the stored key, the rest zero
   u32x4 qh[KS], ql[KS];
@@ -1262,7 +1280,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
   const float lq = (a.terms & 1) ? token_gate(a, w, b, h) : 0.0f;
   const float lbt = (a.terms & 4) ? token_gate(a, w, b, 2 * Hkv + h) : 0.0f;
   const float row2 = (lq + lbt) * pc.inv_n2;
-  if (!t.single) {
+  if (ticketed) {
     __syncthreads();
     t.kt = L.kt;  // this workgroup takes the ticket's tile
     load_rows(t.kt);
@@ -1531,13 +1549,45 @@ DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, 
   return w;
 }
 
+// Workgroups of a kernel that fit on the current GPU at once, from the
+// runtime's occupancy figure (cached per device).
+template <typename Kern>
+static hipError_t resident_workgroups(Kern kern, int threads, int* out) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDev;
+  if (cached) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return hipSuccess;
+    }
+  }
+  int per_cu = 0, cus = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), threads, 0);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  *out = per_cu > 0 && cus > 0 ? per_cu * cus : 0;
+  if (cached && *out > 0) cache[dev].store(*out, std::memory_order_relaxed);
+  return hipSuccess;
+}
+
 template <int D, int G, bool BF16>
 static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Control& ctl, float tau, bool compact,
                               int32_t* kept, hipStream_t st) {
   const int twg = decode_tile_entries(D, G, BF16);
-  const DecodeKArgs k{a, w, ctl, tau, kept, twg};
+  DecodeKArgs k{a, w, ctl, tau, kept, twg, 0};
   const int64_t mt = decode_max_tiles(a, twg);
   if (mt > (1 << 30)) return hipErrorInvalidValue;
+  if constexpr (BF16) {
+    auto kern = compact ? decode_tile_mf_kernel<D, G, true> : decode_tile_mf_kernel<D, G, false>;
+    const hipError_t e = resident_workgroups(kern, kTileThreads, &k.resident);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B * kTokParts + 1), dim3(kTokThreads),
                      token_map_lds(a.B * a.H_kv, mt), st, k);
   const int grid = (int)mt;
