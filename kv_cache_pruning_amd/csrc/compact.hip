@@ -22,11 +22,11 @@
 //     until every earlier chunk whose rows the destination range overwrites
 //     has loaded its own, then store.  Destinations never exceed sources, so
 //     this is the only hazard.
-// A workgroup draws tickets until one is past the last chunk; the one that
-// draws the last ticket waits until every workgroup has finished, writes the
-// new lengths (each segment's last inclusive prefix), clears the chunk flags
-// and resets the counters.  The lengths stay unchanged until then, so every
-// workgroup numbers the same chunks.  Flags use relaxed agent-scope atomics
+// A workgroup draws tickets until one is past the last chunk, then reports
+// done; the last one to report writes the new lengths (each segment's last
+// inclusive prefix), clears the chunk flags and resets the counters.  The
+// lengths stay unchanged until then, so every workgroup numbers the same
+// chunks.  Flags use relaxed agent-scope atomics
 // (coherent across XCDs without cache-wide maintenance); waits are bounded
 // and report a timeout in status bit 1.
 
@@ -112,22 +112,13 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(LayerArgs a, C
     const int id = s_ticket;
 
     if (id >= total || id < 0) {  // (a negative id only from a corrupted ticket word: touch no chunk)
-      // ---- exit: report done; the workgroup with the last ticket commits
+      // ---- exit: report done; the last workgroup to report commits (every
+      // other one has stored its rows and published its chunks by then)
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (tid == 0) addi_coh(&ctl.glob[kGlobArrive], 1);
-      if (id == total + (int)gridDim.x - 1) {
-        if (tid == 0) {
-          int spins = 0;
-          while (ldi_coh(&ctl.glob[kGlobArrive]) < (int)gridDim.x) {
-            if (++spins > kSpinLimit) {
-              atomicOr(a.status, 2);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-          }
-        }
-        __syncthreads();
+      if (tid == 0) s_ticket = addi_coh(&ctl.glob[kGlobArrive], 1);
+      __syncthreads();
+      if (s_ticket == (int)gridDim.x - 1) {
         int run = excl;
         for (int s = sb; s < se; ++s) {
           const int n = chunks_of(a.seg_len[s], CH);

@@ -53,7 +53,6 @@
 // the XCDs without cache-wide write-back or invalidation).
 
 #include <algorithm>
-#include <atomic>
 
 #include "ua_device.hpp"
 #include "ua_kernels.hpp"
@@ -1547,33 +1546,6 @@ DecodeWs decode_ws_carve(const LayerArgs& a, const Control& ctl, void* scratch, 
   decode_layout(a, twg, &w, reinterpret_cast<char*>(scratch));
   w.cnt = ctl.dec_cnt;
   return w;
-}
-
-// Workgroups of a kernel that fit on the current GPU at once, from the
-// runtime's occupancy figure (cached per device).
-template <typename Kern>
-static hipError_t resident_workgroups(Kern kern, int threads, int* out) {
-  constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[kMaxDev];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  const bool cached = dev >= 0 && dev < kMaxDev;
-  if (cached) {
-    const int c = cache[dev].load(std::memory_order_relaxed);
-    if (c > 0) {
-      *out = c;
-      return hipSuccess;
-    }
-  }
-  int per_cu = 0, cus = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), threads, 0);
-  if (e != hipSuccess) return e;
-  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return e;
-  *out = per_cu > 0 && cus > 0 ? per_cu * cus : 0;
-  if (cached && *out > 0) cache[dev].store(*out, std::memory_order_relaxed);
-  return hipSuccess;
 }
 
 template <int D, int G, bool BF16>

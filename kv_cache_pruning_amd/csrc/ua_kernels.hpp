@@ -5,6 +5,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 namespace ua {
 
 // Upper limits the kernels are written for (checked on the host).
@@ -132,5 +136,37 @@ hipError_t launch_prefill(const LayerArgs& a, const Control& ctl, int n_tokens, 
                           const int* cu = nullptr, int total = 0);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+// Workgroups of a kernel that fit on the current GPU at once, from the
+// runtime's occupancy figure, cached per (kernel, device).
+template <typename Kern>
+inline hipError_t resident_workgroups(Kern kern, int threads, int* out) {
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int>, int> cache;
+  const void* fn = reinterpret_cast<const void*>(kern);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const auto key = std::make_tuple(fn, threads, dev);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) {
+      *out = it->second;
+      return hipSuccess;
+    }
+  }
+  int per_cu = 0, cus = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, 0);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  *out = per_cu > 0 && cus > 0 ? per_cu * cus : 0;
+  if (*out > 0) {
+    std::lock_guard<std::mutex> lk(mu);
+    cache[key] = *out;
+  }
+  return hipSuccess;
+}
 
 }  // namespace ua
