@@ -710,6 +710,31 @@ __device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInf
   __syncthreads();
 }
 
+// The output gate's weights of this thread's outputs (g, i): the first kUp
+// rows of W_up's column and b_up.  A tile that will merge can load them when
+// it starts (they are usually cold in HBM), long before the merge needs them.
+template <int D, int G, bool BF16>
+struct GateUp {
+  static constexpr int kUp = 16;
+  static constexpr int OPT = tail_opt<D, G>();
+  static constexpr int UPF = OPT <= 2 ? OPT : 0;  // outputs whose W_up column is held in registers
+  float wup[UPF > 0 ? UPF : 1][kUp];
+  float bup[OPT];
+  __device__ __forceinline__ void load(const LayerArgs& a, int h) {
+    const int Hq = a.H_q;
+#pragma unroll
+    for (int u = 0; u < OPT; ++u) {
+      const int idx = min(u * kTileThreads + (int)threadIdx.x, G * D - 1);
+      const int col = (h * G) * D + idx;
+      bup[u] = a.b_up ? a.b_up[col] : 0.0f;
+      if (u < UPF) {
+#pragma unroll
+        for (int q = 0; q < kUp; ++q) wup[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, a.r - 1) * Hq * D + col);
+      }
+    }
+  }
+};
+
 // The segment's output (by the tile that merges: every tile's partial, this
 // one's in registers when it is the only one, the token's own term, the
 // output gate), then the new entry and the new length (by the segment's last
@@ -719,7 +744,8 @@ __device__ __forceinline__ void tile_publish(const DecodeKArgs& K, const TileInf
 // waits on memory once.
 template <int D, int G, bool BF16, bool COMPACT, int TC0>
 __device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo& t, TailLds<D, G>& L, bool combines,
-                                            int npos, float* Mo, float* Lo, float* Oo) {
+                                            int npos, float* Mo, float* Lo, float* Oo, GateUp<D, G, BF16>& gu,
+                                            bool gu_loaded) {
   constexpr int NT = kTileThreads, OPT = tail_opt<D, G>();
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int TC = TC0 / OPT > 2 ? TC0 / OPT : 2;  // tiles whose partials are loaded together
@@ -780,21 +806,18 @@ __device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo
     };
     if (!t.single) load_pass(0);
     // what the merge needs of the token: its value, u = x W_dn (the partials
-    // added, into LDS), this thread's columns of W_up, and its logit against
-    // its own key per head (wave 0, from the fp32 rotated query and key)
-    constexpr int kUp = 16;
-    constexpr int UPF = OPT <= 2 ? OPT : 0;  // outputs whose W_up column is loaded together
-    float vnv[OPT], wup[UPF > 0 ? UPF : 1][kUp];
+    // added, into LDS), the output gate's weights (unless loaded already), and
+    // its logit against its own key per head (wave 0, from the fp32 rotated
+    // query and key)
+    constexpr int kUp = GateUp<D, G, BF16>::kUp;
+    constexpr int UPF = GateUp<D, G, BF16>::UPF;
+    float vnv[OPT];
 #pragma unroll
     for (int u = 0; u < OPT; ++u) {
       const int idx = min(u * NT + tid, G * D - 1);
       vnv[u] = elem_at<BF16>(reinterpret_cast<const char*>(a.v), (uint32_t)((seg * D + idx % D) * EB));
-      if (u < UPF) {
-#pragma unroll
-        for (int q = 0; q < kUp; ++q)
-          wup[u][q] = load_elem<BF16>(a.W_up, (int64_t)min(q, a.r - 1) * Hq * D + (h * G) * D + idx);
-      }
     }
+    if (!gu_loaded) gu.load(a, h);
     if (tid < a.r) L.u[tid] = token_z(a, w, b, 3 * Hkv + tid);
     if (wv == 0) {
       const float qs2 = a.scale * kLog2e;
@@ -839,11 +862,11 @@ __device__ __forceinline__ void tile_finish(const DecodeKArgs& K, const TileInfo
         const float pe = __builtin_amdgcn_exp2f(es - M);
         const float Lt = fmaf(Lo[u], rs, pe);
         const float O = fmaf(Oo[u], rs, pe * vnv[u]);
-        float z = a.b_up ? a.b_up[col] : 0.0f;
+        float z = gu.bup[u];
         if (u < UPF) {
 #pragma unroll
           for (int q = 0; q < kUp; ++q)
-            if (q < a.r) z = fmaf(L.u[q], wup[u < UPF ? u : 0][q], z);
+            if (q < a.r) z = fmaf(L.u[q], gu.wup[u < UPF ? u : 0][q], z);
         } else {
           for (int q = 0; q < min(a.r, kUp); ++q)
             z = fmaf(L.u[q], load_elem<BF16>(a.W_up, (int64_t)q * Hq * D + col), z);
@@ -1160,7 +1183,8 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_kernel(DecodeKArg
     }
     npos = P + count;
   }
-  tile_finish<D, G, BF16, COMPACT, 4>(K, t, L, combines, npos, Mo, Lo, Oo);
+  GateUp<D, G, BF16> gu;
+  tile_finish<D, G, BF16, COMPACT, 4>(K, t, L, combines, npos, Mo, Lo, Oo, gu, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -1275,6 +1299,12 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
       ql[ks] = isq ? vl : zero;
     }
   }
+  // a tile that merges (one-tile segment, or with COMPACT the segment's last
+  // tile) loads the output gate's weights now, at head dim 64 (at 128 they
+  // would cost occupancy); the merge needs them at the end
+  GateUp<D, G, true> gu;
+  const bool gu_early = D == 64 && (t.single || (COMPACT && t.kt == t.ntile - 1));
+  if (gu_early) gu.load(a, h);
   const PairCoef pc = pair_coef(a.terms);
   const float lq = (a.terms & 1) ? token_gate(a, w, b, h) : 0.0f;
   const float lbt = (a.terms & 4) ? token_gate(a, w, b, 2 * Hkv + h) : 0.0f;
@@ -1480,7 +1510,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void decode_tile_mf_kernel(DecodeK
     }
     npos = P + count;
   }
-  tile_finish<D, G, true, COMPACT, 16>(K, t, L, combines, npos, Mo, Lo, Oo);
+  tile_finish<D, G, true, COMPACT, 16>(K, t, L, combines, npos, Mo, Lo, Oo, gu, gu_early);
 }
 
 // ---------------------------------------------------------------------------
