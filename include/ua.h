@@ -67,7 +67,10 @@ enum { UA_TERM_Q = 1, UA_TERM_K = 2, UA_TERM_SIM = 4, UA_TERMS_ALL = 7 };
 /* Sticky device status bits (ua_cache.status). */
 /* bit 0: an append or a prefill found its segment full (that segment was left
  * unchanged); bit 1: a wait on another workgroup of the same call timed out
- * (never expected; the outputs and the cache contents are then undefined);
+ * (never expected; the outputs and the cache contents are then undefined;
+ * every such wait is on a workgroup that is already running, or, in a decode
+ * step, on one of the first workgroups that fit on the GPU together, which
+ * other work on the device can delay but not block);
  * bit 2: a decode step found a segment length above its capacity (a broken
  * cache table; the step changed nothing, and y is undefined). */
 enum { UA_STATUS_SEGMENT_FULL = 1, UA_STATUS_WAIT_TIMEOUT = 2, UA_STATUS_BAD_LENGTH = 4 };
