@@ -1586,9 +1586,17 @@ static hipError_t launch_step(const LayerArgs& a, const DecodeWs& w, const Contr
   const int64_t mt = decode_max_tiles(a, twg);
   if (mt > (1 << 30)) return hipErrorInvalidValue;
   if constexpr (BF16) {
-    auto kern = compact ? decode_tile_mf_kernel<D, G, true> : decode_tile_mf_kernel<D, G, false>;
-    const hipError_t e = resident_workgroups(kern, kTileThreads, &k.resident);
+    // the occupancy figure is the current device's; a stream of another
+    // device runs every segment of several tiles with tickets (resident = 0)
+    int cur = 0, sdev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipStreamGetDevice(st, &sdev);
     if (e != hipSuccess) return e;
+    if (sdev == cur) {
+      auto kern = compact ? decode_tile_mf_kernel<D, G, true> : decode_tile_mf_kernel<D, G, false>;
+      e = resident_workgroups(kern, kTileThreads, &k.resident);
+      if (e != hipSuccess) return e;
+    }
   }
   hipLaunchKernelGGL((decode_token_kernel<D, BF16>), dim3(a.B * kTokParts + 1), dim3(kTokThreads),
                      token_map_lds(a.B * a.H_kv, mt), st, k);
